@@ -1,0 +1,391 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula: each checks it against an
+invariant, a special case that reduces to an independent implementation or
+a library routine, a closed form, or a scalar brute force on tiny inputs.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+from compressed_expert_ffn_amd import synth
+from compressed_expert_ffn_amd.workloads import WORKLOADS, Workload
+from oracle import moe_oracle as O
+from tests.layers import oracle_layer, make_parity_layer, margin_violations
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small_workload(G=2, K=4, kg=1, ke=2, r=3, d=16, f=24, act="swiglu", resid="f32",
+                   T=40, bias=0.0, x_dtype="f32", base_dtype="f32"):
+    return Workload("small", 90, T=T, d=d, f=f, G=G, K=K, top_groups=kg, top_experts=ke,
+                    r=r, act=act, x_dtype=x_dtype, base_dtype=base_dtype, resid=resid,
+                    bias_scale=bias)
+
+
+def small_layer(seed=1, **kw):
+    w = small_workload(**kw)
+    return w, oracle_layer(w, synth.make_layer(w, seed=seed))
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("G,K,kg,ke", [(2, 4, 1, 2), (4, 4, 2, 3), (8, 1, 2, 1), (3, 5, 3, 5), (16, 16, 2, 4)])
+def test_gate_weights_sum_to_one(G, K, kg, ke):
+    _, L = small_layer(G=G, K=K, kg=kg, ke=ke, d=32, bias=0.7)
+    rt = O.route(L)
+    assert np.allclose(rt["w"].sum(axis=1), 1.0, atol=1e-12)
+    assert (rt["w"] > 0).all()
+    # every chosen expert lies in a chosen group, groups distinct, experts distinct
+    for t in range(rt["idx"].shape[0]):
+        assert len(set(rt["gidx"][t])) == kg
+        assert len(set(rt["idx"][t])) == kg * ke
+        for a in range(kg):
+            grp = rt["gidx"][t, a]
+            assert all(i // K == grp for i in rt["idx"][t, a * ke:(a + 1) * ke])
+
+
+def test_single_group_weight_is_softmax_over_selected_experts():
+    # kg = 1: the group factor is exactly 1, so w is the softmax over the
+    # selected expert logits (the whitepaper's top-k-then-softmax).
+    _, L = small_layer(G=3, K=5, kg=1, ke=2)
+    rt = O.route(L)
+    sel = np.take_along_axis(rt["expert_logits"][:, 0, :], rt["idx"] % 5, axis=1)
+    e = np.exp(sel - sel.max(axis=1, keepdims=True))
+    assert np.allclose(rt["w"], e / e.sum(axis=1, keepdims=True), atol=1e-14)
+
+
+def test_one_expert_per_group_has_in_group_weight_one():
+    _, L = small_layer(G=6, K=1, kg=2, ke=1, r=0, resid="none")
+    rt = O.route(L)
+    assert (rt["idx"] == rt["gidx"]).all()
+    s = np.take_along_axis(rt["group_logits"], rt["gidx"].astype(np.int64), axis=1)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    assert np.allclose(rt["w"], e / e.sum(axis=1, keepdims=True), atol=1e-14)
+
+
+def test_exact_ties_go_to_lower_index():
+    d, G, K = 8, 4, 4
+    L = dict(G=G, K=K, top_groups=2, top_experts=2, x_dtype="f32")
+    X = np.ones((3, d), dtype=np.float32)
+    X[1] *= 2.0
+    X[2] *= -1.0
+    # groups 1 and 3 tie on top, group 0 and 2 tie below
+    Wg = np.zeros((d, G), dtype=np.float32)
+    Wg[:, 1] = Wg[:, 3] = 0.25
+    Wg[:, 0] = Wg[:, 2] = 0.125
+    # experts: columns 2 and 0 tie on top, 1 and 3 tie below
+    We = np.zeros((G, d, K), dtype=np.float32)
+    We[:, :, 0] = We[:, :, 2] = 0.5
+    We[:, :, 1] = We[:, :, 3] = -0.5
+    L.update(X=X, W_grp=Wg, W_exp=We, group_bias=None, expert_bias=None)
+    rt = O.route(L)
+    assert rt["gidx"][0].tolist() == [1, 3]
+    assert rt["idx"][0].tolist() == [1 * K + 0, 1 * K + 2, 3 * K + 0, 3 * K + 2]
+    # token 2 flips every sign: groups 0, 2 win; experts 1, 3 win
+    assert rt["gidx"][2].tolist() == [0, 2]
+    assert rt["idx"][2].tolist() == [0 * K + 1, 0 * K + 3, 2 * K + 1, 2 * K + 3]
+    assert np.allclose(rt["w"], 0.25)
+
+
+def _argmax_router(layer):
+    """Independent router: repeated arg-max with a strict '>' scan (so the
+    lower index wins ties), in pure Python on float64 sums, decisions on the
+    float32 value of each logit."""
+    X = O.as_f64(layer["X"], layer["x_dtype"])
+    G, K, kg, ke = layer["G"], layer["K"], layer["top_groups"], layer["top_experts"]
+    Wg = np.asarray(layer["W_grp"], dtype=np.float64)
+    out_idx, out_w = [], []
+    for x in X:
+        s = [float(sum(x[i] * Wg[i, g] for i in range(len(x)))) for g in range(G)]
+        if layer.get("group_bias") is not None:
+            s = [s[g] + float(layer["group_bias"][g]) for g in range(G)]
+
+        def topk(vals, k):
+            left = list(range(len(vals)))
+            chosen = []
+            for _ in range(k):
+                best = left[0]
+                for c in left[1:]:
+                    if np.float32(vals[c]) > np.float32(vals[best]):
+                        best = c
+                chosen.append(best)
+                left.remove(best)
+            return chosen
+
+        gs = topk(s, kg)
+        m = max(s[g] for g in gs)
+        pz = sum(math.exp(s[g] - m) for g in gs)
+        idx, wt = [], []
+        for g in gs:
+            pg = math.exp(s[g] - m) / pz
+            if K == 1:
+                idx.append(g)
+                wt.append(pg)
+                continue
+            We = np.asarray(layer["W_exp"][g], dtype=np.float64)
+            e = [float(sum(x[i] * We[i, j] for i in range(len(x)))) for j in range(K)]
+            if layer.get("expert_bias") is not None:
+                e = [e[j] + float(layer["expert_bias"][g * K + j]) for j in range(K)]
+            js = topk(e, ke)
+            me = max(e[j] for j in js)
+            qz = sum(math.exp(e[j] - me) for j in js)
+            for j in js:
+                idx.append(g * K + j)
+                wt.append(pg * math.exp(e[j] - me) / qz)
+        out_idx.append(idx)
+        out_w.append(wt)
+    return np.array(out_idx), np.array(out_w)
+
+
+@pytest.mark.parametrize("G,K,kg,ke,bias", [(2, 4, 1, 2, 0.0), (4, 4, 2, 2, 1.0), (8, 1, 2, 1, 0.5), (4, 6, 3, 4, 1.0)])
+def test_router_matches_repeated_argmax(G, K, kg, ke, bias):
+    _, L = small_layer(G=G, K=K, kg=kg, ke=ke, T=30, d=12, bias=bias, r=0, resid="none")
+    rt = O.route(L)
+    idx, w = _argmax_router(L)
+    assert (rt["idx"] == idx).all()
+    assert np.allclose(rt["w"], w, atol=1e-13)
+
+
+def test_margin_redraw_enforces_gaps():
+    w = WORKLOADS[4]
+    wT, inputs, L = make_parity_layer(w.with_T(64))
+    assert margin_violations(L).size == 0
+
+
+# -------------------------------------------------------------- permutation
+@pytest.mark.parametrize("G,K,kg,ke", [(2, 4, 1, 2), (4, 4, 2, 2), (16, 16, 2, 4), (8, 1, 2, 1)])
+def test_permutation_is_stable_argsort(G, K, kg, ke):
+    _, L = small_layer(G=G, K=K, kg=kg, ke=ke, T=200, d=16, r=0, resid="none", bias=1.0)
+    rt = O.route(L)
+    E, k = G * K, kg * ke
+    counts, offsets, perm = O.permutation(rt["idx"], E)
+    assert counts.sum() == 200 * k
+    assert offsets[0] == 0 and offsets[-1] == 200 * k and (np.diff(offsets) >= 0).all()
+    assert (perm == np.argsort(rt["idx"].reshape(-1), kind="stable") // k).all()
+    assert (counts == np.bincount(rt["idx"].reshape(-1), minlength=E)).all()
+    gc, go, gp = O.permutation(rt["gidx"], G)
+    assert gc.sum() == 200 * kg and go[-1] == 200 * kg
+    assert (gp == np.argsort(rt["gidx"].reshape(-1), kind="stable") // kg).all()
+
+
+def test_permutation_empty_bins_and_no_tokens():
+    assign = np.array([[3, 1], [1, 0], [3, 0]])
+    c, o, p = O.permutation(assign, 5)
+    assert c.tolist() == [2, 2, 0, 2, 0]
+    assert o.tolist() == [0, 2, 4, 4, 6, 6]
+    assert p.tolist() == [1, 2, 0, 1, 0, 2]
+    c, o, p = O.permutation(np.zeros((0, 2), dtype=np.int32), 3)
+    assert c.tolist() == [0, 0, 0] and o.tolist() == [0, 0, 0, 0] and p.size == 0
+
+
+# --------------------------------------------------------------------- INT4
+def test_int4_nearest_code_range_and_exact_dequant():
+    rng = np.random.default_rng(5)
+    M = (rng.standard_normal((256, 16)) * 0.05).astype(np.float32)
+    M[:32, 3] = 0.0                       # an all-zero block
+    M[64:96, 5] *= 1e-3                   # a block of small values
+    q, s = O.quantize_int4_g32(M)
+    assert q.dtype == np.int8 and s.dtype == np.float16 and s.shape == (8, 16)
+    assert q.min() >= -8 and q.max() <= 7
+    dq = O.dequantize_int4_g32(q, s)
+    # dequantisation is exact: float32 product equals the float64 product
+    s64 = np.repeat(s.astype(np.float64), 32, axis=0)
+    assert (dq.astype(np.float64) == q.astype(np.float64) * s64).all()
+    # zero block: scale 0, codes 0
+    assert s[0, 3] == 0 and (q[:32, 3] == 0).all()
+    # nearest code: |v - q*s| <= s/2 everywhere (no entry is clipped here)
+    err = np.abs(M.astype(np.float64) - dq)
+    assert (err <= s64 / 2 * (1 + 1e-6)).all()
+    # the block's largest magnitude maps to +-7
+    blocks = np.abs(M.reshape(8, 32, 16))
+    arg = blocks.argmax(axis=1)
+    qa = np.take_along_axis(q.reshape(8, 32, 16), arg[:, None, :], axis=1)[:, 0, :]
+    nz = s > 0
+    assert (np.abs(qa[nz]) == 7).all()
+    # scale is amax/7 within half an fp16 ulp (relative for normal fp16
+    # scales, absolute 2^-25 in the subnormal range below 2^-14)
+    amax = blocks.max(axis=1).astype(np.float64)
+    dev = np.abs(s.astype(np.float64)[nz] - amax[nz] / 7)
+    normal = s.astype(np.float64)[nz] >= 2.0 ** -14
+    assert (dev[normal] <= (amax[nz] / 7)[normal] * 2.0 ** -11).all()
+    assert (dev[~normal] <= 2.0 ** -25).all() and (~normal).any()
+
+
+def test_int4_half_even_ties_hand_example():
+    # amax = 7 gives scale = 1 exactly; v = k + 1/2 sits on a tie.
+    col = np.zeros(32, dtype=np.float32)
+    col[:8] = [7.0, 2.5, -3.5, 0.5, -0.5, 1.5, -6.5, 3.0]
+    q, s = O.quantize_int4_g32(col[:, None])
+    assert float(s[0, 0]) == 1.0
+    assert q[:8, 0].tolist() == [7, 2, -4, 0, 0, 2, -6, 3]
+    # amax = 1.75 -> scale 0.25 exactly; 0.625 = 2.5 * 0.25 -> 2
+    col2 = np.zeros(32, dtype=np.float32)
+    col2[:3] = [-1.75, 0.625, 0.875]
+    q2, s2 = O.quantize_int4_g32(col2[:, None])
+    assert float(s2[0, 0]) == 0.25
+    assert q2[:3, 0].tolist() == [-7, 2, 4]
+
+
+# ------------------------------------------------------------------ experts
+def test_materialized_equals_factored():
+    rng = np.random.default_rng(2)
+    din, dout, r = 24, 40, 5          # non-square: a transposed factor fails
+    base = rng.standard_normal((din, dout))
+    A = rng.standard_normal((din, r))
+    B = rng.standard_normal((dout, r))
+    x = rng.standard_normal((7, din))
+    Wm = O.materialize(base, A, B)
+    assert Wm.shape == (din, dout)
+    fact = x @ base + (x @ A) @ B.T
+    assert np.allclose(x @ Wm, fact, rtol=1e-12, atol=1e-12)
+
+
+def test_activations_against_library_forms():
+    z = np.linspace(-6, 6, 97)
+    # odd-part identities: act(z) - act(-z) == z for both
+    assert np.allclose(O.silu(z) - O.silu(-z), z, atol=1e-14)
+    assert np.allclose(O.gelu_tanh(z) - O.gelu_tanh(-z), z, atol=1e-14)
+    # SiLU is z times the logistic function
+    assert np.allclose(O.silu(z), z * 0.5 * (1 + np.tanh(z / 2)), atol=1e-14)
+    # the tanh GELU approximates the exact erf GELU to a few 1e-4
+    exact = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in z])
+    assert np.abs(O.gelu_tanh(z) - exact).max() < 1e-3
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+
+
+@pytest.mark.parametrize("kg", [1, 2])
+def test_zero_residual_reduces_to_group_base(kg):
+    w = small_workload(G=3, K=4, kg=kg, ke=2, r=4, T=25)
+    inputs = synth.make_layer(w, seed=3, zero_residual=True)
+    L = oracle_layer(w, inputs)
+    rt = O.route(L)
+    Y = O.forward(L, routing=rt)
+    X = O.as_f64(L["X"], "f32")
+    # expected: sum over chosen groups of p_g * FFN_base^g(x)
+    s = rt["group_logits"]
+    ref = np.zeros_like(Y)
+    for t in range(w.T):
+        gs = rt["gidx"][t]
+        pe = np.exp(s[t, gs] - s[t, gs].max())
+        pe /= pe.sum()
+        for a, g in enumerate(gs):
+            Wb = [np.asarray(L["base"][p][g], dtype=np.float64) for p in range(3)]
+            h = X[t] @ Wb[0]
+            h = h / (1 + np.exp(-h)) * (X[t] @ Wb[1])
+            ref[t] += pe[a] * (h @ Wb[2])
+    assert np.allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_flat_case_matches_independent_flat_moe():
+    # G = E, K = 1, r = 0: plain flat top-k MoE (the whitepaper's top-2
+    # snippet: top-k logits, softmax over them, weighted sum of expert FFNs).
+    E, k, d, f, T = 6, 2, 10, 14, 30
+    w = small_workload(G=E, K=1, kg=k, ke=1, r=0, resid="none", d=d, f=f, T=T, bias=0.5)
+    inputs = synth.make_layer(w, seed=4)
+    Y = O.forward(oracle_layer(w, inputs))
+    X = inputs["X"].astype(np.float64)
+    Wr = inputs["W_grp"].astype(np.float64)
+    b = inputs["group_bias"].astype(np.float64)
+    ref = np.zeros((T, d))
+    for t in range(T):
+        logits = X[t] @ Wr + b
+        top = sorted(range(E), key=lambda i: (-np.float32(logits[i]), i))[:k]
+        z = np.array([logits[i] for i in top])
+        gate = np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+        for gw, i in zip(gate, top):
+            W1, W3, W2 = (inputs["base"][p][i].astype(np.float64) for p in range(3))
+            a = X[t] @ W1
+            ref[t] += gw * (((a / (1 + np.exp(-a))) * (X[t] @ W3)) @ W2)
+    assert np.allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("act,kg", [("swiglu", 1), ("swiglu", 2), ("gelu_tanh", 1)])
+def test_scalar_bruteforce_tiny(act, kg):
+    """Every value from scalar loops: W~[i][j] = base[i][j] + sum_rho A[i][rho] B[j][rho]."""
+    w = small_workload(G=2, K=3, kg=kg, ke=2, r=2, d=5, f=7, T=6, act=act, bias=0.3)
+    inputs = synth.make_layer(w, seed=6)
+    L = oracle_layer(w, inputs)
+    rt = O.route(L)
+    Y = O.forward(L, routing=rt)
+
+    def wt(p, i):
+        g = i // w.K
+        bse, A, B = inputs["base"][p][g], inputs["A"][p][i], inputs["B"][p][i]
+        din, dout = bse.shape
+        return [[float(bse[a][c]) + sum(float(A[a][q]) * float(B[c][q]) for q in range(w.r))
+                 for c in range(dout)] for a in range(din)]
+
+    def vecmat(v, M):
+        return [sum(v[a] * M[a][c] for a in range(len(v))) for c in range(len(M[0]))]
+
+    for t in range(w.T):
+        x = [float(v) for v in inputs["X"][t]]
+        y = [0.0] * w.d
+        for s in range(w.k):
+            i, gw = int(rt["idx"][t, s]), float(rt["w"][t, s])
+            if act == "swiglu":
+                zg, zu = vecmat(x, wt(0, i)), vecmat(x, wt(1, i))
+                h = [zg[c] / (1 + math.exp(-zg[c])) * zu[c] for c in range(w.f)]
+                o = vecmat(h, wt(2, i))
+            else:
+                z = vecmat(x, wt(0, i))
+                h = [0.5 * v * (1 + math.tanh(math.sqrt(2 / math.pi) * (v + 0.044715 * v ** 3))) for v in z]
+                o = vecmat(h, wt(1, i))
+            y = [y[c] + gw * o[c] for c in range(w.d)]
+        assert np.allclose(Y[t], y, rtol=1e-12, atol=1e-12)
+
+
+def test_int4_layer_uses_dequantised_factors():
+    w = small_workload(G=2, K=2, kg=1, ke=1, r=2, d=32, f=64, T=5, resid="int4_g32")
+    inputs = synth.make_layer(w, seed=8)
+    L = oracle_layer(w, inputs)
+    rt = O.route(L)
+    Y = O.forward(L, routing=rt)
+    X = inputs["X"].astype(np.float64)
+    for t in range(w.T):
+        i = int(rt["idx"][t, 0])
+        Ws = []
+        for p in range(3):
+            qa, sa = O.quantize_int4_g32(inputs["A"][p][i])
+            qb, sb = O.quantize_int4_g32(inputs["B"][p][i])
+            A = qa.astype(np.float64) * np.repeat(sa.astype(np.float64), 32, axis=0)
+            B = qb.astype(np.float64) * np.repeat(sb.astype(np.float64), 32, axis=0)
+            Ws.append(inputs["base"][p][i // w.K].astype(np.float64) + A @ B.T)
+        a = X[t] @ Ws[0]
+        ref = ((a / (1 + np.exp(-a))) * (X[t] @ Ws[1])) @ Ws[2]
+        assert np.allclose(Y[t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_token_subset_equals_full_rows():
+    w = WORKLOADS[0]
+    _, inputs, L = make_parity_layer(w)
+    Y = O.forward(L)
+    sub = [3, 17, 63, 0]
+    assert np.allclose(O.forward(L, tokens=sub), Y[sub], rtol=1e-13, atol=1e-13)
+
+
+# -------------------------------------------------------------- bookkeeping
+def test_compression_ratio_golden():
+    """The page's compression-ratio example (d = 4096, K = 8, r = 16)."""
+    vals = {}
+    with open(os.path.join(GOLDEN, "compression_ratio_example.txt")) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if line:
+                k, v = line.split("=")
+                vals[k.strip()] = v.strip()
+    d, K, r = int(vals["d"]), int(vals["K"]), int(vals["r"])
+    num, den = (int(v) for v in vals["cr_exact"].split("/"))
+    assert abs(O.compression_ratio(d, d, K, r) - num / den) < 1e-15
+    # the page prints about 6.6x; the formula it states does not give that
+    assert abs(O.compression_ratio(d, d, K, r) - float(vals["printed_approx"])) > 0.5
+
+
+def test_stored_params_counts_the_arrays():
+    for w in (WORKLOADS[0], small_workload(G=3, K=2, r=4, d=32, f=48)):
+        inputs = synth.make_layer(w, seed=9)
+        n = sum(a.size for a in inputs["base"]) + sum(a.size for a in inputs["A"] + inputs["B"])
+        assert O.stored_params(w.G, w.K, w.r, w.proj_dims()) == n
