@@ -1,0 +1,831 @@
+// C ABI of the compressed-expert MoE FFN layer (declared in include/moe.h).
+//
+// moe_create validates the shape, quantises and re-lays-out the weights
+// (pack.cpp) and allocates a workspace sized for T_max tokens.  moe_forward
+// enqueues, on the caller's stream and without host synchronisation:
+//   router    two-level top-k and gate weights, assignment counts per chunk
+//   scatter   counts -> offsets -> stable per-expert and per-group lists
+//   ugemm     u = x A for every expert of each chosen group   (r > 0)
+//   gemm1     base input projections once per (token, group) + residual,
+//             activation, gate-weighted sum and h A_down in the epilogue
+//   gemm2     base output projection + stacked residual tail
+//   combine   sum over chosen groups                           (kg > 1)
+// The per-chunk counters are zero between calls: create clears them and the
+// last GEMM of every forward (or a small clear kernel after moe_route)
+// clears them again.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+#include "pack.h"
+
+using namespace cefn;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+long roundup(long x, long m) { return (x + m - 1) / m * m; }
+
+const char* kStageNames[] = {"router", "scatter", "ugemm", "gemm1", "gemm2", "combine", "clear"};
+constexpr int kStages = 7;
+
+}  // namespace
+
+struct moe_handle {
+  moe_config cfg{};
+  int E = 0, k = 0, P = 0, P_in = 0, mma = 0, NU = 0, NV = 0;
+  int nch_e_max = 0, nch_g_max = 0;
+  int device = 0;
+  bool dirty = false;
+  // weights
+  float *Wg = nullptr, *We = nullptr, *gbias = nullptr, *ebias = nullptr;
+  void *W1 = nullptr, *W2 = nullptr, *At = nullptr, *B1 = nullptr, *Ad = nullptr, *Bd = nullptr;
+  uint16_t *At_s = nullptr, *B1_s = nullptr, *Ad_s = nullptr, *Bd_s = nullptr;
+  long w1_gs = 0, w2_gs = 0, at_gs = 0, at_sgs = 0, bd_gs = 0;
+  // workspace
+  int *idx = nullptr, *gidx = nullptr, *counts = nullptr, *offsets = nullptr, *perm = nullptr;
+  int *gcounts = nullptr, *goffsets = nullptr, *gperm = nullptr, *garow = nullptr, *cc = nullptr;
+  float* w = nullptr;
+  int cc_n = 0;
+  // where the last routing pass left the lists the GEMMs read
+  int *gcounts_live = nullptr, *goffsets_live = nullptr, *idx_live = nullptr;
+  float* w_live = nullptr;
+  void* U = nullptr;
+  float* V = nullptr;
+  void* H = nullptr;
+  float* ypart = nullptr;
+  std::vector<void*> allocs;
+  int64_t weight_bytes = 0;
+  // profiling
+  bool prof = false;
+  int prof_max = 0, prof_calls = 0;
+  std::vector<hipEvent_t> ev;          // [prof_max][kStages][2]
+  std::vector<unsigned char> ev_used;  // [prof_max][kStages]
+};
+
+namespace {
+
+int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+int validate(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "null config");
+  if (c->T_max < 0 || c->d <= 0 || c->f <= 0 || c->G <= 0 || c->K <= 0 || c->top_groups <= 0 ||
+      c->top_experts <= 0 || c->r < 0)
+    return fail(MOE_ERR_INVALID_ARG, "config sizes must be positive (r >= 0, T_max >= 0)");
+  if (c->act != MOE_ACT_GELU_TANH && c->act != MOE_ACT_SWIGLU)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", c->act);
+  if (c->x_dtype < 0 || c->x_dtype > 2 || c->base_dtype < 0 || c->base_dtype > 2)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (c->resid < 0 || c->resid > 3) return fail(MOE_ERR_INVALID_ARG, "unknown residual kind");
+  if (c->top_groups > c->G) return fail(MOE_ERR_INVALID_ARG, "top_groups %d > G %d", c->top_groups, c->G);
+  if (c->top_experts > c->K) return fail(MOE_ERR_INVALID_ARG, "top_experts %d > K %d", c->top_experts, c->K);
+  if ((c->r == 0) != (c->resid == MOE_RESID_NONE))
+    return fail(MOE_ERR_INVALID_ARG, "r == 0 exactly when the residual kind is NONE");
+  const long E = (long)c->G * c->K;
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "G*K = %ld > 1024", E);
+  if (c->G > 256 || c->K > 256) return fail(MOE_ERR_UNSUPPORTED, "G and K must be <= 256");
+  if (c->top_groups > MAX_KG) return fail(MOE_ERR_UNSUPPORTED, "top_groups > %d", MAX_KG);
+  if (c->top_groups * c->top_experts > MAX_SLOTS)
+    return fail(MOE_ERR_UNSUPPORTED, "top_groups*top_experts > %d", MAX_SLOTS);
+  if (c->r > RPAD) return fail(MOE_ERR_UNSUPPORTED, "r > %d", RPAD);
+  if (c->r > 0 && c->K > 64) return fail(MOE_ERR_UNSUPPORTED, "residual experts need K <= 64");
+  if (c->d % 64 || c->f % 64) return fail(MOE_ERR_UNSUPPORTED, "d and f must be multiples of 64");
+  const int x = c->x_dtype, b = c->base_dtype;
+  const bool pair_ok = (x == MOE_F32 && b == MOE_F32) || (x == MOE_F16 && b == MOE_F16) ||
+                       (x == MOE_BF16 && b == MOE_BF16) || (x == MOE_BF16 && b == MOE_F16);
+  if (!pair_ok) return fail(MOE_ERR_UNSUPPORTED, "unsupported (x, base) dtype pair (%d, %d)", x, b);
+  if (c->resid == MOE_RESID_F32 && b != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "F32 residual needs an F32 base");
+  if (c->resid == MOE_RESID_F16 && b != MOE_F16) return fail(MOE_ERR_UNSUPPORTED, "F16 residual needs an F16 base");
+  if (c->resid == MOE_RESID_INT4_G32 && b == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "INT4 residual needs an F16 or BF16 base");
+  return MOE_OK;
+}
+
+void dims(const moe_config& c, int p, int& din, int& dout) {
+  const int P = c.act == MOE_ACT_SWIGLU ? 3 : 2;
+  if (p < P - 1) {
+    din = c.d;
+    dout = c.f;
+  } else {
+    din = c.f;
+    dout = c.d;
+  }
+}
+
+void compute_stats(const moe_config& c, moe_stats* s) {
+  const int P = c.act == MOE_ACT_SWIGLU ? 3 : 2;
+  const long E = (long)c.G * c.K;
+  int64_t params = 0, dense = 0, bytes = 0;
+  for (int p = 0; p < P; ++p) {
+    int di, dn;
+    dims(c, p, di, dn);
+    params += (int64_t)c.G * di * dn + E * c.r * (int64_t)(di + dn);
+    dense += E * (int64_t)di * dn;
+    bytes += (int64_t)c.G * di * dn * elem_bytes(c.base_dtype);
+    if (c.resid == MOE_RESID_INT4_G32)
+      bytes += E * ((int64_t)(di + dn) * c.r / 2 + (int64_t)(di + dn) / 32 * c.r * 2);
+    else if (c.resid != MOE_RESID_NONE)
+      bytes += E * (int64_t)(di + dn) * c.r * (c.resid == MOE_RESID_F32 ? 4 : 2);
+  }
+  s->stored_params = params;
+  s->dense_equiv_params = dense;
+  s->stored_bytes = bytes;
+}
+
+template <class T>
+int dalloc(moe_handle* h, T** p, size_t n) {
+  *p = nullptr;
+  if (n == 0) return MOE_OK;
+  void* q = nullptr;
+  if (hipMalloc(&q, n * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_OOM, "hipMalloc of %zu bytes failed", n * sizeof(T));
+  }
+  h->allocs.push_back(q);
+  *p = static_cast<T*>(q);
+  return MOE_OK;
+}
+
+template <class T>
+int upload(moe_handle* h, T** dst, const std::vector<T>& src) {
+  int rc = dalloc(h, dst, src.size());
+  if (rc) return rc;
+  if (src.empty()) return MOE_OK;
+  if (hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess)
+    return fail(MOE_ERR_HIP, "hipMemcpy to device failed");
+  h->weight_bytes += src.size() * sizeof(T);
+  return MOE_OK;
+}
+
+template <class T>
+int upload_raw(moe_handle* h, void** dst, const std::vector<T>& src) {
+  T* p = nullptr;
+  int rc = upload(h, &p, src);
+  *dst = p;
+  return rc;
+}
+
+#define TRY(x)            \
+  do {                    \
+    int rc_ = (x);        \
+    if (rc_) return rc_;  \
+  } while (0)
+
+// Build every device weight array.  TS is the storage type of the MFMA
+// dtype: float (F32) or uint16_t bits (F16/BF16), which is also the storage
+// type of the base and of F32/F16 residuals.
+template <class TS>
+int build_weights(moe_handle* h, const moe_weights* w) {
+  const moe_config& c = h->cfg;
+  const int G = c.G, K = c.K, E = h->E, P = h->P, Pin = h->P_in, d = c.d, f = c.f, r = c.r;
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  auto base_ptr = [&](int p) { return static_cast<const TS*>(w->base[p]); };
+
+  // base input projections, gate/up interleaved in 32-column blocks for SwiGLU
+  {
+    const int N = Pin * f;
+    std::vector<TS> buf((size_t)G * N * d);
+    h->w1_gs = (long)N * d;
+    for (int g = 0; g < G; ++g) {
+      pack_frag(buf.data() + (size_t)g * N * d, N, d, [&](int n, int k) -> TS {
+        int p = 0, col = n;
+        if (swiglu) {
+          const int blk = n / 32;
+          p = blk & 1;
+          col = (blk >> 1) * 32 + (n & 31);
+        }
+        return base_ptr(p)[((size_t)g * d + k) * f + col];
+      });
+    }
+    TRY(upload_raw(h, &h->W1, buf));
+  }
+  // base output projection [f][d]
+  {
+    std::vector<TS> buf((size_t)G * d * f);
+    h->w2_gs = (long)d * f;
+    for (int g = 0; g < G; ++g)
+      pack_frag(buf.data() + (size_t)g * d * f, d, f,
+                [&](int n, int k) -> TS { return base_ptr(P - 1)[((size_t)g * f + k) * d + n]; });
+    TRY(upload_raw(h, &h->W2, buf));
+  }
+  if (r == 0) return MOE_OK;
+
+  const int NU = h->NU, NV = h->NV;
+  if (c.resid == MOE_RESID_INT4_G32) {
+    // quantise every factor once
+    std::vector<Q4> qa((size_t)P * E), qb((size_t)P * E);
+    for (int p = 0; p < P; ++p) {
+      int di, dn;
+      dims(c, p, di, dn);
+      const float* Ap = static_cast<const float*>(w->A[p]);
+      const float* Bp = static_cast<const float*>(w->B[p]);
+      parallel_for(E, [&](int i) {
+        qa[(size_t)p * E + i] = quantize_g32(Ap + (size_t)i * di * r, di, r);
+        qb[(size_t)p * E + i] = quantize_g32(Bp + (size_t)i * dn * r, dn, r);
+      });
+    }
+    auto QA = [&](int p, int i) -> const Q4& { return qa[(size_t)p * E + i]; };
+    auto QB = [&](int p, int i) -> const Q4& { return qb[(size_t)p * E + i]; };
+    // At: [G] frag(NU, d) + scales [G][NU/32][d/32][32]
+    {
+      std::vector<uint32_t> wbuf((size_t)G * NU * d / 8);
+      std::vector<uint16_t> sbuf((size_t)G * (NU / 32) * (d / 32) * 32, 0);
+      h->at_gs = (long)NU * d / 8;
+      h->at_sgs = (long)(NU / 32) * (d / 32) * 32;
+      for (int g = 0; g < G; ++g) {
+        auto col = [&](int n, int& j, int& p, int& rho) {
+          j = n / (Pin * RPAD);
+          p = (n / RPAD) % Pin;
+          rho = n % RPAD;
+          return j < K && rho < r;
+        };
+        pack_frag_int4(wbuf.data() + (size_t)g * h->at_gs, NU, d, [&](int n, int k) {
+          int j, p, rho;
+          return col(n, j, p, rho) ? QA(p, g * K + j).code(k, rho) : 0;
+        });
+        for (int n = 0; n < NU; ++n) {
+          int j, p, rho;
+          if (!col(n, j, p, rho)) continue;
+          for (int kb = 0; kb < d / 32; ++kb)
+            sbuf[(size_t)g * h->at_sgs + ((size_t)(n / 32) * (d / 32) + kb) * 32 + (n % 32)] =
+                QA(p, g * K + j).scale(kb * 32, rho);
+        }
+      }
+      TRY(upload_raw(h, &h->At, wbuf));
+      TRY(upload(h, &h->At_s, sbuf));
+    }
+    // B1: [E][Pin] frag(f, 16) + scales [E][Pin][f/32][16]
+    {
+      std::vector<uint32_t> wbuf((size_t)E * Pin * f * 16 / 8);
+      std::vector<uint16_t> sbuf((size_t)E * Pin * (f / 32) * RPAD, 0);
+      for (int i = 0; i < E; ++i)
+        for (int p = 0; p < Pin; ++p) {
+          const Q4& q = QB(p, i);
+          pack_frag_int4(wbuf.data() + (size_t)(i * Pin + p) * f * 2, f, RPAD,
+                         [&](int n, int k) { return k < r ? q.code(n, k) : 0; });
+          for (int fb = 0; fb < f / 32; ++fb)
+            for (int rho = 0; rho < r; ++rho)
+              sbuf[((size_t)(i * Pin + p) * (f / 32) + fb) * RPAD + rho] = q.scale(fb * 32, rho);
+        }
+      TRY(upload_raw(h, &h->B1, wbuf));
+      TRY(upload(h, &h->B1_s, sbuf));
+    }
+    // Ad: [E][f/32][64] words + scales [E][f/32][16]
+    {
+      std::vector<uint32_t> wbuf((size_t)E * (f / 32) * 64);
+      std::vector<uint16_t> sbuf((size_t)E * (f / 32) * RPAD, 0);
+      for (int i = 0; i < E; ++i) {
+        const Q4& q = QA(P - 1, i);
+        for (int fb = 0; fb < f / 32; ++fb) {
+          for (int lane = 0; lane < 64; ++lane) {
+            const int rho = lane & 15;
+            uint32_t word = 0;
+            for (int e = 0; e < 8; ++e) {
+              const int kk = fb * 32 + 8 * (lane >> 4) + e;
+              const int qv = rho < r ? q.code(kk, rho) : 0;
+              word |= static_cast<uint32_t>(qv + 8) << (4 * e);
+            }
+            wbuf[((size_t)i * (f / 32) + fb) * 64 + lane] = word;
+          }
+          for (int rho = 0; rho < r; ++rho) sbuf[((size_t)i * (f / 32) + fb) * RPAD + rho] = q.scale(fb * 32, rho);
+        }
+      }
+      TRY(upload_raw(h, &h->Ad, wbuf));
+      TRY(upload(h, &h->Ad_s, sbuf));
+    }
+    // Bd: [G] frag(d, NV) + scales [E][d/32][16]
+    {
+      std::vector<uint32_t> wbuf((size_t)G * d * NV / 8);
+      std::vector<uint16_t> sbuf((size_t)E * (d / 32) * RPAD, 0);
+      h->bd_gs = (long)d * NV / 8;
+      for (int g = 0; g < G; ++g)
+        pack_frag_int4(wbuf.data() + (size_t)g * h->bd_gs, d, NV, [&](int n, int k) {
+          const int j = k / RPAD, rho = k % RPAD;
+          return (j < K && rho < r) ? QB(P - 1, g * K + j).code(n, rho) : 0;
+        });
+      for (int i = 0; i < E; ++i)
+        for (int nb = 0; nb < d / 32; ++nb)
+          for (int rho = 0; rho < r; ++rho)
+            sbuf[((size_t)i * (d / 32) + nb) * RPAD + rho] = QB(P - 1, i).scale(nb * 32, rho);
+      TRY(upload_raw(h, &h->Bd, wbuf));
+      TRY(upload(h, &h->Bd_s, sbuf));
+    }
+    return MOE_OK;
+  }
+
+  // F32 / F16 residuals stored in the MFMA type directly
+  auto Aval = [&](int p, int i, int k, int rho) -> TS {
+    int di, dn;
+    dims(c, p, di, dn);
+    return static_cast<const TS*>(w->A[p])[((size_t)i * di + k) * r + rho];
+  };
+  auto Bval = [&](int p, int i, int n, int rho) -> TS {
+    int di, dn;
+    dims(c, p, di, dn);
+    return static_cast<const TS*>(w->B[p])[((size_t)i * dn + n) * r + rho];
+  };
+  const TS zero = TS(0);
+  {
+    std::vector<TS> buf((size_t)G * NU * d);
+    h->at_gs = (long)NU * d;
+    for (int g = 0; g < G; ++g)
+      pack_frag(buf.data() + (size_t)g * NU * d, NU, d, [&](int n, int k) -> TS {
+        const int j = n / (Pin * RPAD), p = (n / RPAD) % Pin, rho = n % RPAD;
+        return (j < K && rho < r) ? Aval(p, g * K + j, k, rho) : zero;
+      });
+    TRY(upload_raw(h, &h->At, buf));
+  }
+  {
+    std::vector<TS> buf((size_t)E * Pin * f * RPAD);
+    for (int i = 0; i < E; ++i)
+      for (int p = 0; p < Pin; ++p)
+        pack_frag(buf.data() + (size_t)(i * Pin + p) * f * RPAD, f, RPAD,
+                  [&](int n, int k) -> TS { return k < r ? Bval(p, i, n, k) : zero; });
+    TRY(upload_raw(h, &h->B1, buf));
+  }
+  {
+    std::vector<TS> buf((size_t)E * f * RPAD);
+    for (int i = 0; i < E; ++i)
+      for (int fb = 0; fb < f / 32; ++fb)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e) {
+            const int rho = lane & 15, kk = fb * 32 + 8 * (lane >> 4) + e;
+            buf[(((size_t)i * (f / 32) + fb) * 64 + lane) * 8 + e] = rho < r ? Aval(P - 1, i, kk, rho) : zero;
+          }
+    TRY(upload_raw(h, &h->Ad, buf));
+  }
+  {
+    std::vector<TS> buf((size_t)G * d * NV);
+    h->bd_gs = (long)d * NV;
+    for (int g = 0; g < G; ++g)
+      pack_frag(buf.data() + (size_t)g * d * NV, d, NV, [&](int n, int k) -> TS {
+        const int j = k / RPAD, rho = k % RPAD;
+        return (j < K && rho < r) ? Bval(P - 1, g * K + j, n, rho) : zero;
+      });
+    TRY(upload_raw(h, &h->Bd, buf));
+  }
+  return MOE_OK;
+}
+
+int pick_bm(int rows, int ntiles, bool f32) {
+  if (!f32 && (long)(rows / 128) * ntiles >= 512) return 128;
+  if ((long)(rows / 64) * ntiles >= 256) return 64;
+  return 32;
+}
+
+int max_mtiles(int T, int kg, int G, int bm) {
+  const long rows = (long)T * kg;
+  return (int)((rows + bm - 1) / bm + std::min<long>(G, rows));
+}
+
+struct Prof {
+  moe_handle* h;
+  hipStream_t st;
+  int call;
+  void begin(int s) {
+    if (call >= 0) (void)hipEventRecord(h->ev[((size_t)call * kStages + s) * 2], st);
+  }
+  void end(int s) {
+    if (call >= 0) {
+      (void)hipEventRecord(h->ev[((size_t)call * kStages + s) * 2 + 1], st);
+      h->ev_used[(size_t)call * kStages + s] = 1;
+    }
+  }
+};
+
+int hip_fail(moe_handle* h, hipError_t e, const char* what) {
+  h->dirty = true;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// router + scatter into the workspace (and the caller's buffers where given)
+int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, hipStream_t st, Prof& pf) {
+  const moe_config& c = h->cfg;
+  hipError_t e;
+  if (h->dirty) {
+    e = launch_zero(h->cc, h->cc_n, st);
+    if (e != hipSuccess) return hip_fail(h, e, "clear counters");
+    h->dirty = false;
+  }
+  int* idx = (ro && ro->idx) ? ro->idx : h->idx;
+  float* wts = (ro && ro->w) ? ro->w : h->w;
+  int* gidx = (ro && ro->gidx) ? ro->gidx : h->gidx;
+  RouteArgs ra{};
+  ra.X = X;
+  ra.T = T;
+  ra.d = c.d;
+  ra.G = c.G;
+  ra.K = c.K;
+  ra.kg = c.top_groups;
+  ra.ke = c.top_experts;
+  ra.k = h->k;
+  ra.E = h->E;
+  ra.Wg = h->Wg;
+  ra.We = h->We;
+  ra.gbias = h->gbias;
+  ra.ebias = h->ebias;
+  ra.idx = idx;
+  ra.w = wts;
+  ra.gidx = gidx;
+  ra.ccount = h->cc;
+  ra.cgcount = h->cc + (size_t)h->nch_e_max * h->E;
+  pf.begin(0);
+  e = launch_router(c.x_dtype, ra, st);
+  if (e != hipSuccess) return hip_fail(h, e, "router launch");
+  pf.end(0);
+  ScatterArgs sa{};
+  sa.T = T;
+  sa.k = h->k;
+  sa.kg = c.top_groups;
+  sa.E = h->E;
+  sa.G = c.G;
+  sa.idx = idx;
+  sa.gidx = gidx;
+  sa.ccount = ra.ccount;
+  sa.cgcount = ra.cgcount;
+  sa.nch_e = (int)(((long)T * h->k + CHUNK - 1) / CHUNK);
+  sa.nch_g = (int)(((long)T * c.top_groups + CHUNK - 1) / CHUNK);
+  sa.counts = (ro && ro->counts) ? ro->counts : h->counts;
+  sa.offsets = (ro && ro->offsets) ? ro->offsets : h->offsets;
+  sa.perm = (ro && ro->perm) ? ro->perm : nullptr;
+  sa.gcounts = (ro && ro->gcounts) ? ro->gcounts : h->gcounts;
+  sa.goffsets = (ro && ro->goffsets) ? ro->goffsets : h->goffsets;
+  sa.gperm = (ro && ro->gperm) ? ro->gperm : nullptr;
+  sa.garow = h->garow;
+  pf.begin(1);
+  e = launch_scatter(sa, st);
+  if (e != hipSuccess) return hip_fail(h, e, "scatter launch");
+  pf.end(1);
+  // the GEMMs read the group lists from wherever the scatter put them
+  h->gcounts_live = sa.gcounts;
+  h->goffsets_live = sa.goffsets;
+  h->idx_live = idx;
+  h->w_live = wts;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_config_stats(const moe_config* cfg, moe_stats* out) {
+  TRY(validate(cfg));
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "null stats");
+  compute_stats(*cfg, out);
+  return MOE_OK;
+}
+
+int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_handle** out) {
+  (void)stream;
+  TRY(validate(cfg));
+  if (!w || !out) return fail(MOE_ERR_INVALID_ARG, "null weights or output handle");
+  *out = nullptr;
+  const moe_config& c = *cfg;
+  const int P = c.act == MOE_ACT_SWIGLU ? 3 : 2;
+  if (!w->W_grp) return fail(MOE_ERR_INVALID_ARG, "W_grp is required");
+  if (c.K > 1 && !w->W_exp) return fail(MOE_ERR_INVALID_ARG, "W_exp is required when K > 1");
+  for (int p = 0; p < P; ++p) {
+    if (!w->base[p]) return fail(MOE_ERR_INVALID_ARG, "base[%d] is null", p);
+    if (c.r > 0 && (!w->A[p] || !w->B[p])) return fail(MOE_ERR_INVALID_ARG, "A[%d]/B[%d] null with r > 0", p, p);
+  }
+  std::unique_ptr<moe_handle> h(new moe_handle());
+  h->cfg = c;
+  h->E = c.G * c.K;
+  h->k = c.top_groups * c.top_experts;
+  h->P = P;
+  h->P_in = P - 1;
+  h->mma = c.base_dtype;
+  h->NU = c.r > 0 ? (int)roundup((long)c.K * h->P_in * RPAD, 64) : 0;
+  h->NV = c.r > 0 ? (int)roundup((long)c.K * RPAD, 64) : 0;
+  if (hipGetDevice(&h->device) != hipSuccess) return fail(MOE_ERR_HIP, "no HIP device");
+
+  // router weights and biases
+  {
+    std::vector<float> wg(w->W_grp, w->W_grp + (size_t)c.d * c.G);
+    TRY(upload(h.get(), &h->Wg, wg));
+    if (c.K > 1) {
+      std::vector<float> we(w->W_exp, w->W_exp + (size_t)c.G * c.d * c.K);
+      TRY(upload(h.get(), &h->We, we));
+    }
+    if (w->group_bias) {
+      std::vector<float> gb(w->group_bias, w->group_bias + c.G);
+      TRY(upload(h.get(), &h->gbias, gb));
+    }
+    if (w->expert_bias && c.K > 1) {
+      std::vector<float> eb(w->expert_bias, w->expert_bias + h->E);
+      TRY(upload(h.get(), &h->ebias, eb));
+    }
+  }
+  int rc = (h->mma == MOE_F32) ? build_weights<float>(h.get(), w) : build_weights<uint16_t>(h.get(), w);
+  if (rc) {
+    moe_destroy(h.release());
+    return rc;
+  }
+
+  // workspace
+  const long T = c.T_max, k = h->k, kg = c.top_groups;
+  const size_t es = elem_bytes(h->mma);
+  h->nch_e_max = (int)((T * k + CHUNK - 1) / CHUNK);
+  h->nch_g_max = (int)((T * kg + CHUNK - 1) / CHUNK);
+  h->cc_n = h->nch_e_max * h->E + h->nch_g_max * c.G;
+  auto ws = [&]() -> int {
+    TRY(dalloc(h.get(), &h->idx, T * k + 1));
+    TRY(dalloc(h.get(), &h->w, T * k + 1));
+    TRY(dalloc(h.get(), &h->gidx, T * kg + 1));
+    TRY(dalloc(h.get(), &h->counts, h->E));
+    TRY(dalloc(h.get(), &h->offsets, h->E + 1));
+    TRY(dalloc(h.get(), &h->gcounts, c.G));
+    TRY(dalloc(h.get(), &h->goffsets, c.G + 1));
+    TRY(dalloc(h.get(), &h->garow, T * kg + 1));
+    TRY(dalloc(h.get(), &h->cc, (size_t)h->cc_n + 1));
+    char* tmp = nullptr;
+    if (c.r > 0) {
+      TRY(dalloc(h.get(), &tmp, T * kg * h->NU * es + 16));
+      h->U = tmp;
+      TRY(dalloc(h.get(), &h->V, T * kg * h->NV + 4));
+    }
+    TRY(dalloc(h.get(), &tmp, T * kg * (long)c.f * es + 16));
+    h->H = tmp;
+    if (kg > 1) TRY(dalloc(h.get(), &h->ypart, T * kg * (long)c.d + 4));
+    return MOE_OK;
+  };
+  rc = ws();
+  if (rc) {
+    moe_destroy(h.release());
+    return rc;
+  }
+  if (hipMemset(h->cc, 0, sizeof(int) * ((size_t)h->cc_n + 1)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    moe_destroy(h.release());
+    return fail(MOE_ERR_HIP, "initialising the workspace failed");
+  }
+  *out = h.release();
+  return MOE_OK;
+}
+
+int moe_destroy(moe_handle* h) {
+  if (!h) return MOE_OK;
+  (void)hipDeviceSynchronize();
+  for (void* p : h->allocs) (void)hipFree(p);
+  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  delete h;
+  return MOE_OK;
+}
+
+int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out, void* stream) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
+  if (T < 0 || T > h->cfg.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, h->cfg.T_max);
+  if (T > 0 && !X) return fail(MOE_ERR_INVALID_ARG, "null X");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Prof pf{h, st, -1};
+  TRY(run_route(h, X, T, out, st, pf));
+  hipError_t e = launch_zero(h->cc, h->cc_n, st);
+  if (e != hipSuccess) return hip_fail(h, e, "clear counters");
+  return MOE_OK;
+}
+
+int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_route_out* routing,
+                void* stream) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
+  const moe_config& c = h->cfg;
+  if (T < 0 || T > c.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, c.T_max);
+  if (T == 0) return MOE_OK;
+  if (!X || !Y) return fail(MOE_ERR_INVALID_ARG, "null X or Y");
+  if (X == Y) return fail(MOE_ERR_INVALID_ARG, "X and Y may not alias");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Prof pf{h, st, -1};
+  if (h->prof && h->prof_calls < h->prof_max) pf.call = h->prof_calls++;
+  TRY(run_route(h, X, T, routing, st, pf));
+
+  const int kg = c.top_groups;
+  const int rows = T * kg;
+  const bool f32 = h->mma == MOE_F32;
+  GemmArgs ga{};
+  ga.gcounts = h->gcounts_live;
+  ga.goffsets = h->goffsets_live;
+  ga.G = c.G;
+  ga.K = c.K;
+  ga.kg = kg;
+  ga.ke = c.top_experts;
+  ga.k = h->k;
+  ga.resid = c.resid;
+  ga.act = c.act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
+  ga.X = X;
+  ga.d = c.d;
+  ga.f = c.f;
+  ga.garow = h->garow;
+  ga.idx = h->idx_live;
+  ga.w = h->w_live;
+  ga.U = h->U;
+  ga.NU = h->NU;
+  ga.V = h->V;
+  ga.NV = h->NV;
+  ga.H = h->H;
+  ga.ypart = h->ypart;
+  ga.Y = Y;
+  hipError_t e;
+  if (c.r > 0) {
+    GemmArgs u = ga;
+    u.Bw = h->At;
+    u.bw_gstride = h->at_gs;
+    u.bw_scale = h->At_s;
+    u.bws_gstride = h->at_sgs;
+    const int nt = (h->NU + 255) / 256;
+    const int bm = pick_bm(rows, nt, f32);
+    pf.begin(2);
+    e = launch_gemm(GK_U, c.x_dtype, h->mma, bm, u, max_mtiles(T, kg, c.G, bm), nt, st);
+    if (e != hipSuccess) return hip_fail(h, e, "ugemm launch");
+    pf.end(2);
+  }
+  {
+    GemmArgs g1 = ga;
+    g1.Bw = h->W1;
+    g1.bw_gstride = h->w1_gs;
+    g1.B1 = h->B1;
+    g1.b1_scale = h->B1_s;
+    g1.Ad = h->Ad;
+    g1.ad_scale = h->Ad_s;
+    const int nt = (h->P_in * c.f + 255) / 256;
+    // the 128-row tile of this kernel does not fit the register file yet
+    const int bm = std::min(pick_bm(rows, nt, f32), 64);
+    pf.begin(3);
+    e = launch_gemm(GK_G1, c.x_dtype, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, st);
+    if (e != hipSuccess) return hip_fail(h, e, "gemm1 launch");
+    pf.end(3);
+  }
+  {
+    GemmArgs g2 = ga;
+    g2.Bw = h->W2;
+    g2.bw_gstride = h->w2_gs;
+    g2.Bd = h->Bd;
+    g2.bd_gstride = h->bd_gs;
+    g2.bd_scale = h->Bd_s;
+    g2.zero_ptr = h->cc;
+    g2.zero_n = h->cc_n;
+    const int nt = (c.d + 255) / 256;
+    const int bm = pick_bm(rows, nt, f32);
+    pf.begin(4);
+    e = launch_gemm(GK_G2, c.x_dtype, h->mma, bm, g2, max_mtiles(T, kg, c.G, bm), nt, st);
+    if (e != hipSuccess) return hip_fail(h, e, "gemm2 launch");
+    pf.end(4);
+  }
+  if (kg > 1) {
+    CombineArgs ca{h->ypart, Y, T, c.d, kg};
+    pf.begin(5);
+    e = launch_combine(c.x_dtype, ca, st);
+    if (e != hipSuccess) return hip_fail(h, e, "combine launch");
+    pf.end(5);
+  }
+  return MOE_OK;
+}
+
+int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t expert, float* values,
+                       int8_t* q, uint16_t* scale_bits) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
+  const moe_config& c = h->cfg;
+  if (c.r == 0) return fail(MOE_ERR_INVALID_ARG, "layer has no residual");
+  if (proj < 0 || proj >= h->P || (which != 0 && which != 1) || expert < 0 || expert >= h->E || !values)
+    return fail(MOE_ERR_INVALID_ARG, "bad residual selector");
+  int di, dn;
+  dims(c, proj, di, dn);
+  const int n = which == 0 ? di : dn, r = c.r;
+  const int K = c.K, g = expert / K, j = expert % K, nfb = c.f / 32;
+  const bool int4 = c.resid == MOE_RESID_INT4_G32;
+  const void* src = nullptr;
+  const uint16_t* sc = nullptr;
+  long base = 0, sbase = 0;
+  int kind = 0, aux0 = 0, aux1 = 0;
+  const bool down = proj == h->P - 1;
+  if (which == 0 && !down) {  // At
+    kind = 0;
+    src = h->At;
+    sc = h->At_s;
+    base = int4 ? g * h->at_gs : g * h->at_gs / 8;
+    sbase = g * h->at_sgs;
+    aux0 = (j * h->P_in + proj) * RPAD;
+    aux1 = c.d / 16;
+  } else if (which == 1 && !down) {  // B1
+    kind = 1;
+    src = h->B1;
+    sc = h->B1_s;
+    base = (long)(expert * h->P_in + proj) * nfb * 64;
+    sbase = (long)(expert * h->P_in + proj) * nfb * RPAD;
+    aux0 = 0;
+    aux1 = 1;
+  } else if (which == 0 && down) {  // Ad
+    kind = 2;
+    src = h->Ad;
+    sc = h->Ad_s;
+    base = (long)expert * nfb * 64;
+    sbase = (long)expert * nfb * RPAD;
+  } else {  // Bd
+    kind = 1;
+    src = h->Bd;
+    sc = h->Bd_s;
+    base = int4 ? g * h->bd_gs : g * h->bd_gs / 8;
+    sbase = (long)expert * (c.d / 32) * RPAD;
+    aux0 = j;
+    aux1 = h->NV / 16;
+  }
+  float* dout = nullptr;
+  if (hipMalloc(&dout, sizeof(float) * (size_t)n * r) != hipSuccess) return fail(MOE_ERR_OOM, "debug buffer");
+  hipError_t e = launch_debug_decode(h->mma, c.resid, kind, src, sc, base, sbase, n, r, aux0, aux1, dout, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(values, dout, sizeof(float) * (size_t)n * r, hipMemcpyDeviceToHost);
+  (void)hipFree(dout);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "debug decode: %s", hipGetErrorString(e));
+  if (int4 && (q || scale_bits)) {
+    // codes and scales follow from the decoded values and the stored scales
+    std::vector<uint16_t> sc_host;
+    const long ns = (long)(n / 32) * r;
+    sc_host.resize(ns);
+    for (int b = 0; b < n / 32; ++b)
+      for (int rho = 0; rho < r; ++rho) {
+        long off;
+        if (kind == 0) {
+          const int ncol = aux0 + rho;
+          off = sbase + ((long)(ncol / 32) * (c.d / 32) + b) * 32 + (ncol % 32);
+        } else {
+          off = sbase + (long)b * RPAD + rho;
+        }
+        if (hipMemcpy(&sc_host[(size_t)b * r + rho], sc + off, 2, hipMemcpyDeviceToHost) != hipSuccess)
+          return fail(MOE_ERR_HIP, "debug scale read");
+      }
+    if (scale_bits) std::memcpy(scale_bits, sc_host.data(), ns * 2);
+    if (q) {
+      for (int i = 0; i < n; ++i)
+        for (int rho = 0; rho < r; ++rho) {
+          const float s = host_f16_to_f32(sc_host[(size_t)(i / 32) * r + rho]);
+          const float v = values[(size_t)i * r + rho];
+          q[(size_t)i * r + rho] = s > 0.f ? static_cast<int8_t>(v / s) : 0;
+        }
+    }
+  }
+  return MOE_OK;
+}
+
+int moe_profile_begin(moe_handle* h, int32_t max_calls) {
+  if (!h || max_calls <= 0) return fail(MOE_ERR_INVALID_ARG, "bad profile request");
+  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  h->ev.assign((size_t)max_calls * kStages * 2, nullptr);
+  for (auto& e : h->ev)
+    if (hipEventCreate(&e) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreate");
+  h->ev_used.assign((size_t)max_calls * kStages, 0);
+  h->prof = true;
+  h->prof_max = max_calls;
+  h->prof_calls = 0;
+  return MOE_OK;
+}
+
+int moe_profile_end(moe_handle* h, float* stage_ms, int32_t n_stages_cap, int32_t* n_stages,
+                    int32_t* n_calls, char* names, int32_t names_cap) {
+  if (!h || !h->prof) return fail(MOE_ERR_INVALID_ARG, "profiling not active");
+  if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_ERR_HIP, "synchronise");
+  std::vector<float> tot(kStages, 0.f);
+  for (int call = 0; call < h->prof_calls; ++call)
+    for (int s = 0; s < kStages; ++s) {
+      if (!h->ev_used[(size_t)call * kStages + s]) continue;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, h->ev[((size_t)call * kStages + s) * 2],
+                              h->ev[((size_t)call * kStages + s) * 2 + 1]) == hipSuccess)
+        tot[s] += ms;
+    }
+  if (stage_ms)
+    for (int s = 0; s < std::min<int>(kStages, n_stages_cap); ++s) stage_ms[s] = tot[s];
+  if (n_stages) *n_stages = kStages;
+  if (n_calls) *n_calls = h->prof_calls;
+  if (names && names_cap > 0) {
+    std::string all;
+    for (int s = 0; s < kStages; ++s) {
+      if (s) all += ",";
+      all += kStageNames[s];
+    }
+    std::snprintf(names, names_cap, "%s", all.c_str());
+  }
+  h->prof = false;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Internal interface between the host layer (api.hip) and the kernels.
+//
+// Device weight layouts (built by pack.cpp at create time):
+//
+//  "fragment-major" for a matrix with N columns and depth Kd (the MFMA k):
+//     [N/32][Kd/16][64 lanes][8]   element (n, k) at lane (n%32) + 32*((k%16)/8),
+//     slot k%8 -- one 16-deep k-step of a 32-column block is 64 x 8 contiguous
+//     elements, so a wavefront reads it with one coalesced 16-byte load per lane.
+//  INT4 factors use the same order with 8 nibbles (q + 8, element e in bits
+//  4e..4e+3) in one 32-bit word per lane, plus fp16 scales.
+//
+//  W1   [G] x frag(N = P_in*f, Kd = d)  input projections of the base; for
+//       SwiGLU the N order interleaves 32-column blocks gate, up, gate, up...
+//  W2   [G] x frag(N = d, Kd = f)       output projection of the base
+//  At   [G] x frag(N = NU, Kd = d)      column (j*P_in + p)*RPAD + rho holds
+//       A_{p, gK+j}[:, rho] (zero for rho >= r and for padding columns);
+//       INT4 scales [G][NU/32][d/32][32]
+//  B1   [E][P_in] x frag(N = f, Kd = RPAD)  B_p^T; INT4 scales [E][P_in][f/32][RPAD]
+//  Ad   [E] x [f/32][64][8]   16x16x32 B-operand of A_down: lane rho + 16*((k%32)/8),
+//       slot k%8 (k = row of A_down); INT4 scales [E][f/32][RPAD]
+//  Bd   [G] x frag(N = d, Kd = NV)  row j*RPAD + rho of the k axis holds
+//       B_{down, gK+j}[:, rho]; INT4 scales [E][d/32][RPAD]
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cefn {
+
+struct RouteArgs {
+  const void* X;
+  int T, d, G, K, kg, ke, k, E;
+  const float* Wg;     // [d][G]
+  const float* We;     // [G][d][K]
+  const float* gbias;  // [G] or null
+  const float* ebias;  // [E] or null
+  int* idx;            // [T][k]
+  float* w;            // [T][k]
+  int* gidx;           // [T][kg]
+  int* ccount;         // [chunks of T*k][E], zero on entry
+  int* cgcount;        // [chunks of T*kg][G], zero on entry
+};
+
+struct ScatterArgs {
+  int T, k, kg, E, G;
+  const int* idx;
+  const int* gidx;
+  const int* ccount;
+  const int* cgcount;
+  int nch_e, nch_g;
+  int* counts;    // [E]
+  int* offsets;   // [E+1]
+  int* perm;      // [T*k] token ids, or null
+  int* gcounts;   // [G]
+  int* goffsets;  // [G+1]
+  int* gperm;     // [T*kg] token ids, or null
+  int* garow;     // [T*kg] group-list position -> t*kg + group rank
+};
+
+// Common to the three grouped GEMMs.  Rows are group-list positions
+// (goffsets[g] <= row < goffsets[g+1]); a tile is (group, BM rows) x (256 cols).
+struct GemmArgs {
+  const int* gcounts;
+  const int* goffsets;
+  int G, K, kg, ke, k;
+  int resid;            // RS_*
+  int act;              // ACT_*
+  // activations
+  const void* X;        // [T][d] x dtype (U, G1)
+  int d, f;
+  const int* garow;     // [T*kg]
+  const int* idx;       // [T][k]
+  const float* w;       // [T][k]
+  // weights (fragment-major, per group unless noted)
+  const void* Bw;       // W1 (G1), W2 (G2), At (U)
+  long bw_gstride;      // elements (or 32-bit words for INT4 At) per group
+  const uint16_t* bw_scale;  // INT4 scales of At
+  long bws_gstride;
+  const void* B1;       // G1 residual B (per expert)
+  const uint16_t* b1_scale;
+  const void* Ad;       // G1 A_down (per expert)
+  const uint16_t* ad_scale;
+  const void* Bd;       // G2 residual tail (per group)
+  long bd_gstride;
+  const uint16_t* bd_scale;
+  // workspace
+  void* U;              // [rows][NU] MFMA type
+  int NU;
+  float* V;             // [rows][NV] fp32
+  int NV;
+  void* H;              // [rows][f] MFMA type
+  float* ypart;         // [T*kg][d] (kg > 1)
+  void* Y;              // [T][d] x dtype (kg == 1)
+  int* zero_ptr;        // cleared by the output GEMM's first block
+  int zero_n;
+};
+
+struct CombineArgs {
+  const float* ypart;
+  void* Y;
+  int T, d, kg;
+};
+
+enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2 };
+
+hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st);
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
+size_t scatter_lds_bytes(int E, int G);
+hipError_t launch_zero(int* p, int n, hipStream_t st);
+
+// max_mtiles: upper bound of sum_g ceil(M_g / bm); ntiles: column tiles of 256.
+hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a,
+                       int max_mtiles, int ntiles, hipStream_t st);
+hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st);
+
+// Device-side decode of stored residual factors (test export).
+hipError_t launch_debug_decode(int mma_dtype, int resid, int kind, const void* src,
+                               const uint16_t* scales, long base, long sbase, int n, int r,
+                               int aux0, int aux1, float* out, hipStream_t st);
+
+}  // namespace cefn
