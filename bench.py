@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Throughput of one compressed-expert MoE FFN layer forward on one MI355X.
+
+A step is one moe_forward over one batch of T synthetic tokens already
+resident in HBM (router, token lists, the grouped GEMMs, combine).  The
+default workload is the compressed fp16 SwiGLU layer (T = 2048, d = 1024,
+f = 2816, 4 groups of 4 experts, top-1 group then top-2 experts, rank 16);
+``--workload N`` selects another of the five shapes.
+
+Prints one JSON line: routed tokens/s (T per forward), the roofline of the
+dominant kernel (algorithmic work per launch over its average duration,
+timed with HIP events on the launch stream inside the timed region), and
+the CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s per MoE layer fwd on 1 MI355X; % MFMA peak or % HBM BW"
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+STAGES = ("router", "scatter", "ugemm", "gemm1", "gemm2", "combine")
+
+
+def resid_bytes_per_entry(w) -> float:
+    return {"int4_g32": 0.5 + 2.0 / 32, "f16": 2.0, "f32": 4.0, "none": 0.0}[w.resid]
+
+
+def kernel_work(w, T, touched_groups, touched_experts) -> dict:
+    """Algorithmic FLOPs and bytes per launch of each kernel (the method's
+    own work: base projections once per (token, chosen group), residual
+    only for selected experts; bytes = weights of touched groups and
+    experts plus the layer's input and output, workspace excluded)."""
+    d, f, r, k, kg, K, G, Pin = w.d, w.f, w.r, w.k, w.top_groups, w.K, w.G, w.P_in
+    xb = 4 if w.x_dtype == "f32" else 2
+    bb = 4 if w.base_dtype == "f32" else 2
+    rb = resid_bytes_per_entry(w)
+    tg, te = touched_groups, touched_experts
+    flops = dict(
+        router=2 * T * d * (G + (kg * K if K > 1 else 0)),
+        scatter=0,
+        ugemm=2 * T * k * r * Pin * d,
+        gemm1=2 * T * kg * Pin * d * f + 2 * T * k * r * Pin * f + 2 * T * k * r * f + 2 * T * k * f,
+        gemm2=2 * T * kg * f * d + 2 * T * k * r * d,
+        combine=T * (kg - 1) * d,
+    )
+    nbytes = dict(
+        router=T * d * xb + d * G * 4 + (tg * d * K * 4 if K > 1 else 0),
+        scatter=T * k * 4 * 3,
+        ugemm=T * d * xb + te * Pin * d * r * rb,
+        gemm1=T * d * xb + tg * Pin * d * f * bb + te * (Pin * f * r + f * r) * rb,
+        gemm2=tg * f * d * bb + te * d * r * rb + T * d * xb,
+        combine=T * kg * d * 4 + T * d * xb,
+    )
+    return dict(flops=flops, bytes=nbytes)
+
+
+def traffic_for(workload_name: str, kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if the record
+    under profiles/ was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))[workload_name][kernel]
+    except (KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "compressed_expert_ffn_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return rec.get("bytes_per_launch") if rec.get("src_sha") == sha else None
+
+
+def cpu_baseline(w, inputs, budget_s: float) -> dict:
+    """The CPU oracle as it stands, on the same workload (the sample is the
+    whole batch, repeated while the time budget lasts)."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    fields = dict(G=w.G, K=w.K, top_groups=w.top_groups, top_experts=w.top_experts, r=w.r,
+                  d=w.d, f=w.f, act=w.act, x_dtype=w.x_dtype, base_dtype=w.base_dtype,
+                  resid=w.resid)
+    layer = O.layer_from(fields, inputs)
+    T = inputs["X"].shape[0]
+    # bound the sample for the large layers: route everything, FFN on a prefix
+    n_tok = T if w.index in (0, 1, 4) else min(T, 256)
+    toks = list(range(n_tok))
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        O.forward(layer, tokens=toks)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 3:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    return dict(value=n_tok / med, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{n_tok} of {T} tokens of the {w.name} layer, float64 NumPy oracle, "
+                       f"median of {len(times)} run(s) of {med:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--no-graph", action="store_true", help="plain stream launches only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this layer is built and measured on one GPU only; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from compressed_expert_ffn_amd import _lib as L
+    from compressed_expert_ffn_amd import synth
+    from compressed_expert_ffn_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    inputs = synth.make_layer(w)
+    lay = L.Layer(L.config_from_workload(w), inputs)
+    xt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.x_dtype]
+    Xh = inputs["X"]
+    if w.x_dtype == "bf16":
+        X = torch.from_numpy(Xh.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(Xh).cuda()
+    Y = torch.empty((w.T, w.d), dtype=xt, device="cuda")
+
+    # routing statistics of this batch (untimed)
+    rb = lay.route(X)
+    counts = rb["counts"].cpu().numpy()
+    gcounts = rb["gcounts"].cpu().numpy()
+    tg, te = int((gcounts > 0).sum()), int((counts > 0).sum())
+    work = kernel_work(w, w.T, tg, te)
+
+    # warm-up, with every stage timed to find the dominant kernel (the first
+    # call loads code objects and is left out)
+    lay.forward(X, Y)
+    torch.cuda.synchronize()
+    lay.profile_begin(max(1, args.warmup))
+    for _ in range(max(1, args.warmup)):
+        lay.forward(X, Y)
+    stage_warm = lay.profile_end()
+    calls = max(1, stage_warm["calls"])
+    stage_ms = {s: stage_warm["stage_ms"].get(s, 0.0) / calls for s in STAGES}
+    dominant = max(STAGES, key=lambda s: stage_ms[s])
+
+    # timed region: plain stream launches, HIP events around the dominant kernel
+    torch.cuda.synchronize()
+    lay.profile_begin(args.steps, stages=[dominant])
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lay.forward(X, Y)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = lay.profile_end()
+    ms_stream = (t1 - t0) * 1e3 / args.steps
+    dom_ms = prof["stage_ms"][dominant] / max(1, prof["calls"])
+
+    # the same step replayed from a captured HIP graph
+    ms_graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            lay.forward(X, Y)
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            lay.forward(X, Y)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms = ms_stream if ms_graph is None else min(ms_stream, ms_graph)
+    launch = "stream" if ms_graph is None or ms_stream <= ms_graph else "hipgraph"
+    value = w.T / (ms * 1e-3)
+
+    hbm_bound = w.index == 4
+    if hbm_bound:
+        achieved = work["bytes"][dominant] / (dom_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for(w.name, dominant),
+                    kernel=dominant, kernel_ms=round(dom_ms, 5),
+                    work_per_launch=work["bytes"][dominant])
+    else:
+        peak = MFMA_PEAK_TFLOPS[w.base_dtype]
+        achieved = work["flops"][dominant] / (dom_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=traffic_for(w.name, dominant),
+                    kernel=dominant, kernel_ms=round(dom_ms, 5),
+                    work_per_launch=work["flops"][dominant])
+
+    total_flops = w.algorithmic_flops()["total"]
+    out = dict(
+        metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype=w.base_dtype, data="synthetic",
+        config=dict(workload=w.name, T=w.T, d=w.d, f=w.f, G=w.G, K=w.K,
+                    top_groups=w.top_groups, top_experts=w.top_experts, r=w.r,
+                    residual=w.resid, act=w.act, x_dtype=w.x_dtype, launch=launch),
+        roofline=roof,
+        assignments_per_s=round(w.T * w.k / (ms * 1e-3), 1),
+        layer_tflops=round(total_flops / (ms * 1e-3) / 1e12, 2),
+        ms_stream=round(ms_stream, 5), ms_graph=None if ms_graph is None else round(ms_graph, 5),
+        stage_ms={k: round(v, 5) for k, v in stage_ms.items() if v > 0},
+        touched_groups=tg, touched_experts=te,
+        expert_load_max_over_avg=round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
+        expert_load_var=round(float(counts.var()), 2),
+    )
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    lay.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,6 +52,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m compressed_expert_ffn_amd.build`")
+    # PyTorch ships its own HIP runtime under the same soname as the system
+    # one this library links.  Only one can live in a process; load torch's
+    # first so the library and torch share it (the other order leaves torch
+    # unable to see the GPU).
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
     P = C.c_void_p
     sig = {
@@ -62,7 +67,7 @@ def _load():
         "moe_last_error": ([], C.c_char_p),
         "moe_config_stats": ([C.POINTER(moe_config), C.POINTER(moe_stats)], C.c_int),
         "moe_debug_residual": ([P, C.c_int32, C.c_int32, C.c_int32, P, P, P], C.c_int),
-        "moe_profile_begin": ([P, C.c_int32], C.c_int),
+        "moe_profile_begin": ([P, C.c_int32, C.c_int32], C.c_int),
         "moe_profile_end": ([P, P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                              C.c_char_p, C.c_int32], C.c_int),
     }
@@ -199,8 +204,11 @@ class Layer:
                                      q.ctypes.data, sc.ctypes.data))
         return vals, q, sc
 
-    def profile_begin(self, max_calls: int):
-        check(lib.moe_profile_begin(self.h, max_calls))
+    STAGES = ("router", "scatter", "ugemm", "gemm1", "gemm2", "combine")
+
+    def profile_begin(self, max_calls: int, stages=None):
+        mask = -1 if stages is None else sum(1 << self.STAGES.index(s) for s in stages)
+        check(lib.moe_profile_begin(self.h, max_calls, mask))
 
     def profile_end(self) -> dict:
         ms = (C.c_float * 16)()

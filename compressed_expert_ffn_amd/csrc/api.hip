@@ -78,7 +78,7 @@ struct moe_handle {
   int64_t weight_bytes = 0;
   // profiling
   bool prof = false;
-  int prof_max = 0, prof_calls = 0;
+  int prof_max = 0, prof_calls = 0, prof_mask = -1;
   std::vector<hipEvent_t> ev;          // [prof_max][kStages][2]
   std::vector<unsigned char> ev_used;  // [prof_max][kStages]
 };
@@ -402,11 +402,12 @@ struct Prof {
   moe_handle* h;
   hipStream_t st;
   int call;
+  bool on(int s) const { return call >= 0 && ((h->prof_mask >> s) & 1); }
   void begin(int s) {
-    if (call >= 0) (void)hipEventRecord(h->ev[((size_t)call * kStages + s) * 2], st);
+    if (on(s)) (void)hipEventRecord(h->ev[((size_t)call * kStages + s) * 2], st);
   }
   void end(int s) {
-    if (call >= 0) {
+    if (on(s)) {
       (void)hipEventRecord(h->ev[((size_t)call * kStages + s) * 2 + 1], st);
       h->ev_used[(size_t)call * kStages + s] = 1;
     }
@@ -786,7 +787,7 @@ int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t exper
   return MOE_OK;
 }
 
-int moe_profile_begin(moe_handle* h, int32_t max_calls) {
+int moe_profile_begin(moe_handle* h, int32_t max_calls, int32_t stage_mask) {
   if (!h || max_calls <= 0) return fail(MOE_ERR_INVALID_ARG, "bad profile request");
   for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
   h->ev.assign((size_t)max_calls * kStages * 2, nullptr);
@@ -794,6 +795,7 @@ int moe_profile_begin(moe_handle* h, int32_t max_calls) {
     if (hipEventCreate(&e) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreate");
   h->ev_used.assign((size_t)max_calls * kStages, 0);
   h->prof = true;
+  h->prof_mask = stage_mask;
   h->prof_max = max_calls;
   h->prof_calls = 0;
   return MOE_OK;

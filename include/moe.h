@@ -192,12 +192,15 @@ int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t exper
                        float* values, int8_t* q, uint16_t* scale_bits);
 
 /* Per-stage GPU timing: after moe_profile_begin, each moe_forward records
- * a pair of HIP events around every kernel it launches (at most max_calls
- * calls are recorded).  moe_profile_end synchronises, writes the summed
+ * a pair of HIP events, on the stream it was given, around every kernel it
+ * launches whose stage bit is set in stage_mask (bit s = stage s in the
+ * order router, scatter, ugemm, gemm1, gemm2, combine; -1 = all), for at
+ * most max_calls calls.  moe_profile_end synchronises, writes the summed
  * milliseconds per stage into stage_ms[n_stages_cap], the stage count into
  * *n_stages, the recorded calls into *n_calls and comma-separated stage
- * names into names[names_cap], then stops recording. */
-int moe_profile_begin(moe_handle* h, int32_t max_calls);
+ * names into names[names_cap], then stops recording.  Not for use under
+ * stream capture. */
+int moe_profile_begin(moe_handle* h, int32_t max_calls, int32_t stage_mask);
 int moe_profile_end(moe_handle* h, float* stage_ms, int32_t n_stages_cap,
                     int32_t* n_stages, int32_t* n_calls, char* names, int32_t names_cap);
 

@@ -93,7 +93,7 @@ def test_null_arguments():
     assert L.lib.moe_forward(None, None, 0, None, None, None) == L.MOE_ERR_INVALID_ARG
     assert L.lib.moe_route(None, None, 0, None, None) == L.MOE_ERR_INVALID_ARG
     assert L.lib.moe_config_stats(None, None) == L.MOE_ERR_INVALID_ARG
-    assert L.lib.moe_profile_begin(None, 1) == L.MOE_ERR_INVALID_ARG
+    assert L.lib.moe_profile_begin(None, 1, -1) == L.MOE_ERR_INVALID_ARG
     cfg = L.make_config(8, 64, 128, 2, 4, 1, 2, 4, "swiglu", "f16", "f16", "f16")
     h = C.c_void_p()
     assert L.lib.moe_create(C.byref(cfg), None, None, C.byref(h)) == L.MOE_ERR_INVALID_ARG

@@ -185,10 +185,12 @@ def test_repeated_calls_and_different_T_on_one_handle():
             assert rel_err(y, ref[:T]) <= TOL[w.x_dtype]
             ys.append(y)
         # same input twice: identical routing (checked above); outputs may
-        # differ by the order of the fp32 atomics that accumulate h A_down,
-        # which can move a value across one rounding boundary of the bf16
-        # output: at most one bf16 ulp (2^-7 relative)
+        # differ by the order of the fp32 atomics that accumulate h A_down:
+        # an absolute reordering error far below the output scale, which can
+        # move a value across one rounding boundary of the bf16 output
         a, b = ys[0], ys[2]
-        assert (np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b))).all()
+        scale = np.abs(ref).max()
+        bound = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-5 * scale
+        assert (np.abs(a - b) <= bound).all(), float((np.abs(a - b) - bound).max())
     finally:
         lay.close()
