@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "routed tokens/s per MoE layer fwd on 1 MI355X; % MFMA peak or % HBM BW"
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
-STAGES = ("router", "scatter", "ugemm", "gemm1", "gemm2", "combine")
+STAGES = ("router", "scatter", "ugemm", "gemm1", "vreduce", "gemm2", "combine")
 
 
 def resid_bytes_per_entry(w) -> float:
@@ -49,6 +49,7 @@ def kernel_work(w, T, touched_groups, touched_experts) -> dict:
         scatter=0,
         ugemm=2 * T * k * r * Pin * d,
         gemm1=2 * T * kg * Pin * d * f + 2 * T * k * r * Pin * f + 2 * T * k * r * f + 2 * T * k * f,
+        vreduce=0,
         gemm2=2 * T * kg * f * d + 2 * T * k * r * d,
         combine=T * (kg - 1) * d,
     )
@@ -57,6 +58,7 @@ def kernel_work(w, T, touched_groups, touched_experts) -> dict:
         scatter=T * k * 4 * 3,
         ugemm=T * d * xb + te * Pin * d * r * rb,
         gemm1=T * d * xb + tg * Pin * d * f * bb + te * (Pin * f * r + f * r) * rb,
+        vreduce=T * k * 16 * 4 * 2,
         gemm2=tg * f * d * bb + te * d * r * rb + T * d * xb,
         combine=T * kg * d * 4 + T * d * xb,
     )

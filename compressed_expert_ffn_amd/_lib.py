@@ -204,7 +204,7 @@ class Layer:
                                      q.ctypes.data, sc.ctypes.data))
         return vals, q, sc
 
-    STAGES = ("router", "scatter", "ugemm", "gemm1", "gemm2", "combine")
+    STAGES = ("router", "scatter", "ugemm", "gemm1", "vreduce", "gemm2", "combine")
 
     def profile_begin(self, max_calls: int, stages=None):
         mask = -1 if stages is None else sum(1 << self.STAGES.index(s) for s in stages)

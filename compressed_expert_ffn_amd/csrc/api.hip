@@ -18,12 +18,13 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <string>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.h"
 #include "kernels.h"
 #include "pack.h"
@@ -46,7 +47,7 @@ int fail(int code, const char* fmt, ...) {
 
 long roundup(long x, long m) { return (x + m - 1) / m * m; }
 
-const char* kStageNames[] = {"router", "scatter", "ugemm", "gemm1", "gemm2", "combine", "clear"};
+const char* kStageNames[] = {"router", "scatter", "ugemm", "gemm1", "vreduce", "gemm2", "combine"};
 constexpr int kStages = 7;
 
 }  // namespace
@@ -72,10 +73,16 @@ struct moe_handle {
   float* w_live = nullptr;
   void* U = nullptr;
   float* V = nullptr;
+  float* Vp = nullptr;
+  int nt1 = 0;          // column tiles of gemm1 (partials of V per row)
+  int* gidx_live = nullptr;
   void* H = nullptr;
   float* ypart = nullptr;
   std::vector<void*> allocs;
   int64_t weight_bytes = 0;
+  // tile rows and stage depth per GEMM (0 = chosen per call); set from the
+  // CEFN_BM_{U,G1,G2} / CEFN_BK_{U,G1,G2} environment variables at create
+  int bm_env[3] = {0, 0, 0}, bk_env[3] = {0, 0, 0};
   // profiling
   bool prof = false;
   int prof_max = 0, prof_calls = 0, prof_mask = -1;
@@ -387,10 +394,32 @@ int build_weights(moe_handle* h, const moe_weights* w) {
   return MOE_OK;
 }
 
-int pick_bm(int rows, int ntiles, bool f32) {
-  if (!f32 && (long)(rows / 128) * ntiles >= 512) return 128;
-  if ((long)(rows / 64) * ntiles >= 256) return 64;
+// Tile rows for a grouped GEMM with `rows` rows and `ntiles` column tiles:
+// the largest of 128 / 64 / 32 that still gives every compute unit work.
+int pick_bm(int rows, int ntiles, bool f32, int cap) {
+  if (!f32 && cap >= 128 && (long)(rows / 128) * ntiles >= 512) return 128;
+  if (cap >= 64 && (long)(rows / 64) * ntiles >= 256) return 64;
   return 32;
+}
+
+struct Tile {
+  int bm, bk;
+};
+
+// kdim: depth of the GEMM's main k loop (d for ugemm and gemm1, f for
+// gemm2); the stage depth must divide it.
+Tile choose_tile(const moe_handle* h, int which, int rows, int ntiles, int kdim) {
+  const bool f32 = h->mma == MOE_F32;
+  Tile t;
+  // gemm1 with GELU keeps two f-blocks of h per wavefront: 64 rows at most
+  const int cap = (which == 1 && h->cfg.act != MOE_ACT_SWIGLU) ? 64 : 128;
+  t.bm = pick_bm(rows, ntiles, f32, cap);
+  t.bk = f32 ? 64 : 128;
+  if (h->bm_env[which]) t.bm = h->bm_env[which];
+  if (h->bk_env[which]) t.bk = h->bk_env[which];
+  if (f32 || kdim % t.bk) t.bk = 64;
+  if (f32 && t.bm > 64) t.bm = 64;
+  return t;
 }
 
 int max_mtiles(int T, int kg, int G, int bm) {
@@ -482,6 +511,7 @@ int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, hipS
   h->goffsets_live = sa.goffsets;
   h->idx_live = idx;
   h->w_live = wts;
+  h->gidx_live = gidx;
   return MOE_OK;
 }
 
@@ -521,6 +551,16 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
   h->NU = c.r > 0 ? (int)roundup((long)c.K * h->P_in * RPAD, 64) : 0;
   h->NV = c.r > 0 ? (int)roundup((long)c.K * RPAD, 64) : 0;
   if (hipGetDevice(&h->device) != hipSuccess) return fail(MOE_ERR_HIP, "no HIP device");
+  {
+    const char* names[3] = {"U", "G1", "G2"};
+    for (int i = 0; i < 3; ++i) {
+      char key[32];
+      std::snprintf(key, sizeof(key), "CEFN_BM_%s", names[i]);
+      if (const char* v = std::getenv(key)) h->bm_env[i] = std::atoi(v);
+      std::snprintf(key, sizeof(key), "CEFN_BK_%s", names[i]);
+      if (const char* v = std::getenv(key)) h->bk_env[i] = std::atoi(v);
+    }
+  }
 
   // router weights and biases
   {
@@ -566,6 +606,8 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
       TRY(dalloc(h.get(), &tmp, T * kg * h->NU * es + 16));
       h->U = tmp;
       TRY(dalloc(h.get(), &h->V, T * kg * h->NV + 4));
+      h->nt1 = (h->P_in * c.f + 255) / 256;
+      TRY(dalloc(h.get(), &h->Vp, (size_t)h->nt1 * T * kg * c.top_experts * RPAD + 4));
     }
     TRY(dalloc(h.get(), &tmp, T * kg * (long)c.f * es + 16));
     h->H = tmp;
@@ -622,7 +664,6 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
 
   const int kg = c.top_groups;
   const int rows = T * kg;
-  const bool f32 = h->mma == MOE_F32;
   GemmArgs ga{};
   ga.gcounts = h->gcounts_live;
   ga.goffsets = h->goffsets_live;
@@ -643,6 +684,8 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   ga.NU = h->NU;
   ga.V = h->V;
   ga.NV = h->NV;
+  ga.Vp = h->Vp;
+  ga.vp_rows = (long)c.T_max * kg;
   ga.H = h->H;
   ga.ypart = h->ypart;
   ga.Y = Y;
@@ -654,9 +697,9 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     u.bw_scale = h->At_s;
     u.bws_gstride = h->at_sgs;
     const int nt = (h->NU + 255) / 256;
-    const int bm = pick_bm(rows, nt, f32);
+    const Tile tl = choose_tile(h, 0, rows, nt, c.d);
     pf.begin(2);
-    e = launch_gemm(GK_U, c.x_dtype, h->mma, bm, u, max_mtiles(T, kg, c.G, bm), nt, st);
+    e = launch_gemm(GK_U, c.x_dtype, h->mma, tl.bm, tl.bk, u, max_mtiles(T, kg, c.G, tl.bm), nt, st);
     if (e != hipSuccess) return hip_fail(h, e, "ugemm launch");
     pf.end(2);
   }
@@ -669,12 +712,31 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     g1.Ad = h->Ad;
     g1.ad_scale = h->Ad_s;
     const int nt = (h->P_in * c.f + 255) / 256;
-    // the 128-row tile of this kernel does not fit the register file yet
-    const int bm = std::min(pick_bm(rows, nt, f32), 64);
+    const Tile tl = choose_tile(h, 1, rows, nt, c.d);
     pf.begin(3);
-    e = launch_gemm(GK_G1, c.x_dtype, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, st);
+    e = launch_gemm(GK_G1, c.x_dtype, h->mma, tl.bm, tl.bk, g1, max_mtiles(T, kg, c.G, tl.bm), nt, st);
     if (e != hipSuccess) return hip_fail(h, e, "gemm1 launch");
     pf.end(3);
+  }
+  if (c.r > 0) {
+    VReduceArgs va{};
+    va.Vp = h->Vp;
+    va.V = h->V;
+    va.garow = h->garow;
+    va.gidx = h->gidx_live;
+    va.idx = h->idx_live;
+    va.vp_rows = (long)c.T_max * kg;
+    va.rows = rows;
+    va.ntiles = h->nt1;
+    va.NV = h->NV;
+    va.K = c.K;
+    va.kg = kg;
+    va.ke = c.top_experts;
+    va.k = h->k;
+    pf.begin(4);
+    e = launch_vreduce(va, st);
+    if (e != hipSuccess) return hip_fail(h, e, "vreduce launch");
+    pf.end(4);
   }
   {
     GemmArgs g2 = ga;
@@ -686,18 +748,18 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     g2.zero_ptr = h->cc;
     g2.zero_n = h->cc_n;
     const int nt = (c.d + 255) / 256;
-    const int bm = pick_bm(rows, nt, f32);
-    pf.begin(4);
-    e = launch_gemm(GK_G2, c.x_dtype, h->mma, bm, g2, max_mtiles(T, kg, c.G, bm), nt, st);
+    const Tile tl = choose_tile(h, 2, rows, nt, c.f);
+    pf.begin(5);
+    e = launch_gemm(GK_G2, c.x_dtype, h->mma, tl.bm, tl.bk, g2, max_mtiles(T, kg, c.G, tl.bm), nt, st);
     if (e != hipSuccess) return hip_fail(h, e, "gemm2 launch");
-    pf.end(4);
+    pf.end(5);
   }
   if (kg > 1) {
     CombineArgs ca{h->ypart, Y, T, c.d, kg};
-    pf.begin(5);
+    pf.begin(6);
     e = launch_combine(c.x_dtype, ca, st);
     if (e != hipSuccess) return hip_fail(h, e, "combine launch");
-    pf.end(5);
+    pf.end(6);
   }
   return MOE_OK;
 }

@@ -157,10 +157,10 @@ __device__ __forceinline__ typename Frag<TY>::T int4_frag_1scale(uint32_t word, 
   for (int e = 0; e < 8; ++e) v[e] = int4_value(word, e, scale);
   return to_frag<TY>(v);
 }
-// Decode 8 INT4 codes with one scale each (8 consecutive fp16 scales).
+// Decode 8 INT4 codes with one scale each (8 consecutive fp16 scales held
+// in a 16-byte vector).
 template <int TY>
-__device__ __forceinline__ typename Frag<TY>::T int4_frag_8scale(uint32_t word, const uint16_t* sc) {
-  u4v s = *reinterpret_cast<const u4v*>(sc);
+__device__ __forceinline__ typename Frag<TY>::T int4_frag_8scale(uint32_t word, u4v s) {
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -171,7 +171,11 @@ __device__ __forceinline__ typename Frag<TY>::T int4_frag_8scale(uint32_t word, 
 }
 
 // ----------------------------------------------------------- fast math ---
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp
+// each) instead of an IEEE division sequence.
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 __device__ __forceinline__ float gelu_tanh_f(float z) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
   float u = c * (z + 0.044715f * z * z * z);

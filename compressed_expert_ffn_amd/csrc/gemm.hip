@@ -23,6 +23,8 @@
 // A (activations) is staged through LDS (double-buffered, padded rows); B
 // (weights) is stored fragment-major and read straight into registers one
 // 64-deep stage ahead.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,27 +32,46 @@ namespace cefn {
 namespace {
 
 constexpr int BN = 256;
-constexpr int BK = 64;
-constexpr int APAD = 8;
-constexpr int AST = BK + APAD;  // LDS row stride of the A tile, elements
+constexpr int APAD = 8;  // LDS row padding of the A tile, elements (16 bytes)
 
 template <int TY> struct Chunk { using T = u4v; };
 template <> struct Chunk<DT_F32> { using T = f8; };
 
 template <int TY> using TE = typename Elem<TY>::T;
 
-__device__ bool find_tile(const int* gcounts, int G, int BM, int mt, int& g, int& m0, int& M) {
-  int acc = 0;
+// Tile of workgroup blockIdx.x in a 1-D grid over (group, row tile, column
+// tile).  Logical order: groups in turn; inside a group, blocks of nb column
+// tiles with the row tiles fastest inside a block, nb chosen so that a block
+// is about one XCD's worth of workgroups (32).  Workgroups are dealt
+// round-robin to the 8 XCDs (workgroup i runs on XCD i % 8), so logical
+// tiles are handed to each XCD in one contiguous run: tiles that share a
+// weight block or a row block run together behind the same L2.
+struct TileCoord {
+  int g, m0, M, nt;
+};
+
+__device__ bool map_tile(const int* gcounts, int G, int BM, int NT, TileCoord& tc) {
+  int total = 0;
+  for (int gg = 0; gg < G; ++gg) total += (gcounts[gg] + BM - 1) / BM * NT;
+  const int i = blockIdx.x;
+  if (i >= total) return false;
+  const int x = i & 7, j = i >> 3;
+  const int q = total >> 3, rem = total & 7;
+  int L = x * q + min(x, rem) + j;
   for (int gg = 0; gg < G; ++gg) {
     const int Mg = gcounts[gg];
-    const int n = (Mg + BM - 1) / BM;
-    if (mt < acc + n) {
-      g = gg;
-      m0 = (mt - acc) * BM;
-      M = Mg;
+    const int mt = (Mg + BM - 1) / BM;
+    if (L < mt * NT) {
+      const int nb = max(1, 32 / mt);
+      const int blk = L / (mt * nb);
+      const int within = L - blk * mt * nb;
+      tc.g = gg;
+      tc.M = Mg;
+      tc.m0 = (within % mt) * BM;
+      tc.nt = blk * nb + within / mt;
       return true;
     }
-    acc += n;
+    L -= mt * NT;
   }
   return false;
 }
@@ -79,33 +100,6 @@ __device__ __forceinline__ typename Chunk<TY>::T chunk_from_f32(const float* v) 
   }
 }
 
-// 8 consecutive activations of type XT converted to an MFMA chunk of type TY.
-template <int XT, int TY>
-__device__ __forceinline__ typename Chunk<TY>::T load_x_chunk(const TE<XT>* p) {
-  if constexpr (XT == TY) {
-    if constexpr (TY == DT_F32) {
-      const f4v* q = reinterpret_cast<const f4v*>(p);
-      f4v a = q[0], b = q[1];
-      f8 c;
-      c[0] = a[0]; c[1] = a[1]; c[2] = a[2]; c[3] = a[3];
-      c[4] = b[0]; c[5] = b[1]; c[6] = b[2]; c[7] = b[3];
-      return c;
-    } else {
-      return *reinterpret_cast<const u4v*>(p);
-    }
-  } else {
-    static_assert(XT == DT_BF16 && TY == DT_F16, "unsupported activation/MFMA type pair");
-    u4v raw = *reinterpret_cast<const u4v*>(p);
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint16_t b = static_cast<uint16_t>((raw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      v[i] = bf16_bits_to_f32(b);
-    }
-    return chunk_from_f32<TY>(v);
-  }
-}
-
 template <int TY>
 __device__ __forceinline__ void store_chunk(TE<TY>* dst, const typename Chunk<TY>::T& c) {
   if constexpr (TY == DT_F32) {
@@ -120,151 +114,214 @@ __device__ __forceinline__ void store_chunk(TE<TY>* dst, const typename Chunk<TY
 }
 
 // ------------------------------------------------------ A-operand loaders --
-// Gathered token rows of X (K axis = d).
-template <int XT, int TY, int BM>
-struct AGather {
-  static constexpr int CPT = BM * BK / 8 / 256;
-  const TE<XT>* rowp[CPT];
-  int lofs[CPT];
-  int kc[CPT];
-  __device__ void init(const GemmArgs& a, int row0, int m0, int M) {
-    const TE<XT>* X = static_cast<const TE<XT>*>(a.X);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      const int lr = c / (BK / 8);
-      kc[j] = c % (BK / 8);
-      lofs[j] = lr * AST + kc[j] * 8;
-      if (m0 + lr < M) {
-        const int t = a.garow[row0 + lr] / a.kg;
-        rowp[j] = X + (long)t * a.d;
-      } else {
-        rowp[j] = nullptr;
-      }
-    }
-  }
-  __device__ void fetch(int kt, typename Chunk<TY>::T (&r)[CPT]) const {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j)
-      r[j] = rowp[j] ? load_x_chunk<XT, TY>(rowp[j] + kt * BK + kc[j] * 8) : zero_chunk<TY>();
-  }
-  __device__ void store(const typename Chunk<TY>::T (&r)[CPT], TE<TY>* buf) const {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) store_chunk<TY>(buf + lofs[j], r[j]);
-  }
-};
+// Raw 8-element chunk of a source of type DT (16 bytes, or 32 for fp32).
+template <int DT> struct Raw8 { using T = u4v; };
+template <> struct Raw8<DT_F32> { using T = f8; };
 
-// Rows of [hbar | V] (K axis = f, then NV residual columns).
-template <int TY, int BM>
-struct AHV {
+template <int DT>
+__device__ __forceinline__ typename Raw8<DT>::T load_raw8(const TE<DT>* p) {
+  if constexpr (DT == DT_F32) {
+    const f4v* q = reinterpret_cast<const f4v*>(p);
+    f4v a = q[0], b = q[1];
+    f8 c;
+    c[0] = a[0]; c[1] = a[1]; c[2] = a[2]; c[3] = a[3];
+    c[4] = b[0]; c[5] = b[1]; c[6] = b[2]; c[7] = b[3];
+    return c;
+  } else {
+    return *reinterpret_cast<const u4v*>(p);
+  }
+}
+
+// Convert a raw chunk of type SRC to an MFMA chunk of type TY.
+template <int SRC, int TY>
+__device__ __forceinline__ typename Chunk<TY>::T convert8(const typename Raw8<SRC>::T& r) {
+  if constexpr (SRC == TY) {
+    return r;
+  } else if constexpr (SRC == DT_F32) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = r[i];
+    return chunk_from_f32<TY>(v);
+  } else {
+    static_assert(SRC == DT_BF16 && TY == DT_F16, "unsupported activation/MFMA type pair");
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t b = static_cast<uint16_t>((r[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      v[i] = bf16_bits_to_f32(b);
+    }
+    return chunk_from_f32<TY>(v);
+  }
+}
+
+// A-operand loader over rows of a [rows][ld] matrix of type SRC, staged to
+// LDS as type TY.  fetch() only issues the loads; store() converts, zeroes
+// rows past the tile's end and writes LDS, so no instruction waits on a
+// load until the stage's MFMAs have been issued.  GATHER: row r of the tile
+// is token garow[row0 + r] / kg of X (stride d); otherwise rows row0 + r of
+// base (stride ld).
+template <int SRC, int TY, int BM, int BK, bool GATHER>
+struct ALoader {
   static constexpr int CPT = BM * BK / 8 / 256;
-  const TE<TY>* hrow[CPT];
-  const float* vrow[CPT];
+  static constexpr int AST = BK + APAD;
+  using Raw = typename Raw8<SRC>::T;
+  const TE<SRC>* rowp[CPT];
   int lofs[CPT];
-  int kc[CPT];
-  int f;
-  __device__ void init(const GemmArgs& a, int row0, int m0, int M) {
-    f = a.f;
+  bool ok[CPT];
+  __device__ void init(const TE<SRC>* base, long ld, const int* garow, int kg, int row0, int m0,
+                       int M) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int c = threadIdx.x + 256 * j;
       const int lr = c / (BK / 8);
-      kc[j] = c % (BK / 8);
-      lofs[j] = lr * AST + kc[j] * 8;
-      if (m0 + lr < M) {
-        const long row = row0 + lr;
-        hrow[j] = static_cast<const TE<TY>*>(a.H) + row * a.f;
-        vrow[j] = a.V ? a.V + row * a.NV : nullptr;
-      } else {
-        hrow[j] = nullptr;
-        vrow[j] = nullptr;
-      }
+      const int kc = c % (BK / 8);
+      lofs[j] = lr * AST + kc * 8;
+      ok[j] = m0 + lr < M;
+      const int r = row0 + (ok[j] ? lr : 0);
+      const long src_row = GATHER ? (long)(garow[r] / kg) : (long)r;
+      rowp[j] = base + src_row * ld + kc * 8;
     }
   }
-  __device__ void fetch(int kt, typename Chunk<TY>::T (&r)[CPT]) const {
+  __device__ void fetch(int kt, Raw (&r)[CPT]) const {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) r[j] = load_raw8<SRC>(rowp[j] + kt * BK);
+  }
+  __device__ void store(const Raw (&r)[CPT], TE<TY>* buf) const {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int k0 = kt * BK + kc[j] * 8;
-      if (!hrow[j]) {
-        r[j] = zero_chunk<TY>();
-      } else if (k0 < f) {
-        r[j] = load_x_chunk<TY, TY>(hrow[j] + k0);
-      } else {
-        const f4v* q = reinterpret_cast<const f4v*>(vrow[j] + (k0 - f));
-        f4v x0 = q[0], x1 = q[1];
-        float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        r[j] = chunk_from_f32<TY>(v);
-      }
+      const typename Chunk<TY>::T c = convert8<SRC, TY>(r[j]);
+      store_chunk<TY>(buf + lofs[j], ok[j] ? c : zero_chunk<TY>());
     }
-  }
-  __device__ void store(const typename Chunk<TY>::T (&r)[CPT], TE<TY>* buf) const {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) store_chunk<TY>(buf + lofs[j], r[j]);
   }
 };
 
 // ------------------------------------------------------ B-operand loaders --
-// Fragment-major matrix of type TY: block nb, global k-step ks.
+// Each loader has load(ks, cb) -> Raw (loads only) and decode(Raw) -> Frag.
+
+// Fragment-major matrix of type TY: block nb0 + cb, k-step ks.
 template <int TY>
-__device__ __forceinline__ typename Frag<TY>::T frag_at(const TE<TY>* base, int KS, int nb, int ks,
-                                                        int lane) {
-  return load_frag<TY>(base + ((long)(nb * KS + ks) * 64 + lane) * 8);
-}
+struct BFrag {
+  using Raw = typename Frag<TY>::T;
+  const TE<TY>* base;
+  int KS, nb0, lane;
+  __device__ Raw load(int ks, int cb) const {
+    return load_frag<TY>(base + ((long)((nb0 + cb) * KS + ks) * 64 + lane) * 8);
+  }
+  __device__ typename Frag<TY>::T decode(const Raw& r) const { return r; }
+};
+
+// INT4 fragment-major factor with one scale per lane (blocks along k):
+// scales [N/32][Kd/32][32].
+template <int TY>
+struct BInt4K {
+  struct Raw {
+    uint32_t word;
+    uint16_t sc;
+  };
+  const uint32_t* words;
+  const uint16_t* scales;
+  int KS, nb0, lane;
+  __device__ Raw load(int ks, int cb) const {
+    const int nb = nb0 + cb;
+    Raw r;
+    r.word = words[(long)(nb * KS + ks) * 64 + lane];
+    r.sc = scales[((long)nb * (KS / 2) + (ks >> 1)) * 32 + (lane & 31)];
+    return r;
+  }
+  __device__ typename Frag<TY>::T decode(const Raw& r) const {
+    return int4_frag_1scale<TY>(r.word, f16_bits_to_f32(r.sc));
+  }
+};
+
+// INT4 residual tail of the down projection (k-step kt = expert kt of the
+// group, blocks along n): 8 scales per lane, scales [E][d/32][16].
+template <int TY>
+struct BInt4Tail {
+  struct Raw {
+    uint32_t word;
+    u4v sc;
+  };
+  const uint32_t* words;
+  const uint16_t* scales;  // of expert g*K
+  int KS, nb0, lane, K, nd32;
+  __device__ Raw load(int kt, int cb) const {
+    const int nb = nb0 + cb;
+    const int je = kt < K ? kt : K - 1;  // padding steps hold zero codes
+    Raw r;
+    r.word = words[(long)(nb * KS + kt) * 64 + lane];
+    r.sc = *reinterpret_cast<const u4v*>(scales + ((long)je * nd32 + nb) * RPAD + 8 * (lane >> 5));
+    return r;
+  }
+  __device__ typename Frag<TY>::T decode(const Raw& r) const {
+    return int4_frag_8scale<TY>(r.word, r.sc);
+  }
+};
 
 // ------------------------------------------------------------- mainloop --
-template <int TY, int BM, class AL, class BL>
-__device__ __forceinline__ void mainloop(int KT, const AL& al, const BL& bl, f16v (&acc)[BM / 32][2],
-                                         TE<TY>* As, bool active, int lane) {
+// KS_total 16-deep k-steps (a multiple of BK / 16) in stages of BK.  Two
+// register sets for B and two LDS buffers for A alternate (the loop body is
+// unrolled by two so no set is copied): the loads of stage kt+1 are issued
+// before stage kt's MFMAs, and their conversion, decoding and LDS stores
+// come after, so the load latency overlaps the stage's MFMAs.
+template <int TY, int BM, int BK, class AL, class BL>
+__device__ __forceinline__ void mainloop_stage(int kt, int KT, const AL& al, const BL& bl,
+                                               f16v (&acc)[BM / 32][2], TE<TY>* As, int lane,
+                                               typename AL::Raw (&regs)[AL::CPT],
+                                               const typename BL::Raw (&bcur)[BK / 16][2],
+                                               typename BL::Raw (&bnext)[BK / 16][2]) {
   constexpr int RB = BM / 32;
   constexpr int KSS = BK / 16;
+  constexpr int AST = BK + APAD;
   using Fr = typename Frag<TY>::T;
-  typename Chunk<TY>::T regs[AL::CPT];
-  Fr bcur[KSS][2], bnext[KSS][2];
-  al.fetch(0, regs);
-  al.store(regs, As);
-  if (active) {
+  const int kn = (kt + 1 < KT) ? kt + 1 : kt;  // the last stage re-reads itself
+  al.fetch(kn, regs);
 #pragma unroll
-    for (int ks = 0; ks < KSS; ++ks)
+  for (int ks = 0; ks < KSS; ++ks)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) bcur[ks][cb] = bl(ks, cb);
+    for (int cb = 0; cb < 2; ++cb) bnext[ks][cb] = bl.load(kn * KSS + ks, cb);
+  // keep the next stage's loads ahead of this stage's MFMAs (left alone,
+  // the scheduler sinks them next to their uses and the latency shows)
+  __builtin_amdgcn_sched_barrier(0);
+  const TE<TY>* buf = As + (kt & 1) * BM * AST;
+#pragma unroll
+  for (int ks = 0; ks < KSS; ++ks) {
+    Fr af[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      af[rb] = load_frag<TY>(buf + (rb * 32 + (lane & 31)) * AST + ks * 16 + 8 * (lane >> 5));
+    Fr bf[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) bf[cb] = bl.decode(bcur[ks][cb]);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32<TY>(af[rb], bf[cb], acc[rb][cb]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  al.store(regs, As + ((kt + 1) & 1) * BM * AST);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) {
-      al.fetch(kt + 1, regs);
-      if (active) {
+}
+
+template <int TY, int BM, int BK, class AL, class BL>
+__device__ __forceinline__ void mainloop(int KS_total, const AL& al, const BL& bl,
+                                         f16v (&acc)[BM / 32][2], TE<TY>* As, int lane) {
+  constexpr int KSS = BK / 16;
+  const int KT = KS_total / KSS;
+  typename AL::Raw regs[AL::CPT];
+  typename BL::Raw b0[KSS][2], b1[KSS][2];
+  al.fetch(0, regs);
 #pragma unroll
-        for (int ks = 0; ks < KSS; ++ks)
+  for (int ks = 0; ks < KSS; ++ks)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) bnext[ks][cb] = bl((kt + 1) * KSS + ks, cb);
-      }
-    }
-    const TE<TY>* buf = As + (kt & 1) * BM * AST;
-    if (active) {
-#pragma unroll
-      for (int ks = 0; ks < KSS; ++ks) {
-        Fr af[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          af[rb] = load_frag<TY>(buf + (rb * 32 + (lane & 31)) * AST + ks * 16 + 8 * (lane >> 5));
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32<TY>(af[rb], bcur[ks][cb], acc[rb][cb]);
-      }
-    }
-    if (more) {
-      al.store(regs, As + ((kt + 1) & 1) * BM * AST);
-      if (active) {
-#pragma unroll
-        for (int ks = 0; ks < KSS; ++ks)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) bcur[ks][cb] = bnext[ks][cb];
-      }
-    }
-    __syncthreads();
+    for (int cb = 0; cb < 2; ++cb) b0[ks][cb] = bl.load(ks, cb);
+  al.store(regs, As);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    mainloop_stage<TY, BM, BK>(kt, KT, al, bl, acc, As, lane, regs, b0, b1);
+    mainloop_stage<TY, BM, BK>(kt + 1, KT, al, bl, acc, As, lane, regs, b1, b0);
   }
+  if (kt < KT) mainloop_stage<TY, BM, BK>(kt, KT, al, bl, acc, As, lane, regs, b0, b1);
 }
 
 template <int BM>
@@ -278,44 +335,31 @@ __device__ __forceinline__ void zero_acc(f16v (&acc)[BM / 32][2]) {
 }
 
 // ------------------------------------------------------------- U = X . A --
-template <int XT, int TY, int BM>
+template <int XT, int TY, int BM, int BK>
 __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int g, m0, M;
-  if (!find_tile(a.gcounts, a.G, BM, blockIdx.y, g, m0, M)) return;
+  TileCoord tc;
+  if (!map_tile(a.gcounts, a.G, BM, (a.NU + BN - 1) / BN, tc)) return;
+  const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * BN + wave * 64;
+  const int n0 = tc.nt * BN + wave * 64;
   const bool active = n0 < a.NU;
   const int row0 = a.goffsets[g] + m0;
   TE<TY>* As = reinterpret_cast<TE<TY>*>(smem);
 
-  // V rows of this tile start at zero (G1 accumulates into them)
-  if (blockIdx.x == 0 && a.V) {
-    const int rows = min(BM, M - m0);
-    for (int i = threadIdx.x; i < rows * a.NV; i += 256) a.V[(long)(row0 + i / a.NV) * a.NV + i % a.NV] = 0.f;
-  }
-
-  AGather<XT, TY, BM> al;
-  al.init(a, row0, m0, M);
+  ALoader<XT, TY, BM, BK, true> al;
+  al.init(static_cast<const TE<XT>*>(a.X), a.d, a.garow, a.kg, row0, m0, M);
   const int KS = a.d / 16;
-  const int nb0 = n0 / 32;
+  const int nb0 = (active ? n0 : a.NU - 64) / 32;  // idle wavefronts read a valid block
   f16v acc[BM / 32][2];
   zero_acc<BM>(acc);
   if (a.resid == RS_INT4) {
-    const uint32_t* W = static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride;
-    const uint16_t* S = a.bw_scale + g * a.bws_gstride;
-    const int KB = a.d / 32;
-    auto bl = [&](int ks, int cb) {
-      const int nb = nb0 + cb;
-      const uint32_t word = W[(long)(nb * KS + ks) * 64 + lane];
-      const float sc = f16_bits_to_f32(S[((long)nb * KB + (ks >> 1)) * 32 + (lane & 31)]);
-      return int4_frag_1scale<TY>(word, sc);
-    };
-    mainloop<TY, BM>(a.d / BK, al, bl, acc, As, active, lane);
+    BInt4K<TY> bl{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride,
+                  KS, nb0, lane};
+    mainloop<TY, BM, BK>(KS, al, bl, acc, As, lane);
   } else {
-    const TE<TY>* W = static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride;
-    auto bl = [&](int ks, int cb) { return frag_at<TY>(W, KS, nb0 + cb, ks, lane); };
-    mainloop<TY, BM>(a.d / BK, al, bl, acc, As, active, lane);
+    BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride, KS, nb0, lane};
+    mainloop<TY, BM, BK>(KS, al, bl, acc, As, lane);
   }
   if (!active) return;
   TE<TY>* U = static_cast<TE<TY>*>(a.U);
@@ -331,32 +375,50 @@ __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
 }
 
 // --------------------------------------------- G1: base GEMM + epilogue --
-template <int XT, int TY, int BM, int ACT>
+// Per-expert operands of the G1 epilogue for one wavefront.
+template <int TY, int RB, int NF>
+struct ExpertOps {
+  typename Frag<TY>::T b[2];       // B_j fragments (gate, up) or (f-block 0, 1)
+  typename Frag<TY>::T u[RB][2];   // u_j = x A_j rows of this tile (gate, up)
+  typename Frag<TY>::T ad[NF];     // A_down,j fragments of this wavefront's f-blocks
+};
+
+template <int XT, int TY, int BM, int BK, int ACT>
 __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   constexpr int RB = BM / 32;
   constexpr int NF = (ACT == ACT_SWIGLU) ? 1 : 2;  // 32-column f-blocks per wavefront
+  constexpr int PIN = (ACT == ACT_SWIGLU) ? 2 : 1;
   constexpr int HST = NF * 32 + 8;                  // LDS row stride of the h tile
+  constexpr int AST = BK + APAD;
   using Fr = typename Frag<TY>::T;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int g, m0, M;
-  if (!find_tile(a.gcounts, a.G, BM, blockIdx.y, g, m0, M)) return;
+  const int N = PIN * a.f;
+  TileCoord tc;
+  if (!map_tile(a.gcounts, a.G, BM, (N + BN - 1) / BN, tc)) return;
+  const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int N = (ACT == ACT_SWIGLU) ? 2 * a.f : a.f;
-  const int n0 = blockIdx.x * BN + wave * 64;
+  const int n0 = tc.nt * BN + wave * 64;
   const bool active = n0 < N;
   const int row0 = a.goffsets[g] + m0;
   const int K = a.K;
 
-  // LDS: [A tiles | h tiles] (aliased) | per-row gate weights | used flags
+  // LDS: [A tiles | h tiles] (aliased) | gate weights [BM][K] | slot of
+  // expert j in the row's chosen list [BM][K] | used flags [K] | partial
+  // V of the 4 wavefronts [4][BM][16]
   const size_t abytes = sizeof(TE<TY>) * 2 * BM * AST;
   const size_t hbytes = sizeof(TE<TY>) * 4 * BM * HST;
   char* p = smem + (abytes > hbytes ? abytes : hbytes);
   float* s_w = reinterpret_cast<float*>(p);
-  int* s_used = reinterpret_cast<int*>(s_w + BM * K);
+  int* s_slot = reinterpret_cast<int*>(s_w + BM * K);
+  int* s_used = s_slot + BM * K;
+  float* s_red = reinterpret_cast<float*>(s_used + ((K + 3) & ~3));
   TE<TY>* As = reinterpret_cast<TE<TY>*>(smem);
   TE<TY>* Hs = reinterpret_cast<TE<TY>*>(smem) + wave * BM * HST;
 
-  for (int i = tid; i < BM * K; i += 256) s_w[i] = 0.f;
+  for (int i = tid; i < BM * K; i += 256) {
+    s_w[i] = 0.f;
+    s_slot[i] = -1;
+  }
   for (int j = tid; j < K; j += 256) s_used[j] = 0;
   __syncthreads();
   for (int i = tid; i < BM; i += 256) {
@@ -367,21 +429,19 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
         const int slot = t * a.k + ga * a.ke + s;
         const int j = a.idx[slot] - g * K;
         s_w[i * K + j] = a.w[slot];
+        s_slot[i * K + j] = s;
         s_used[j] = 1;
       }
     }
   }
 
-  AGather<XT, TY, BM> al;
-  al.init(a, row0, m0, M);
+  ALoader<XT, TY, BM, BK, true> al;
+  al.init(static_cast<const TE<XT>*>(a.X), a.d, a.garow, a.kg, row0, m0, M);
   const int KS = a.d / 16;
-  const int nb0 = n0 / 32;
-  const TE<TY>* W = static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride;
-  auto bl = [&](int ks, int cb) { return frag_at<TY>(W, KS, nb0 + cb, ks, lane); };
+  const int nb0 = (active ? n0 : N - 64) / 32;  // idle wavefronts read a valid block
+  BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride, KS, nb0, lane};
   f16v acc[RB][2];
   zero_acc<BM>(acc);
-  mainloop<TY, BM>(a.d / BK, al, bl, acc, As, active, lane);  // ends with a barrier
-
   // first 32-column f-block of this wavefront
   const int fb0 = (ACT == ACT_SWIGLU) ? n0 / 64 : n0 / 32;
   const int nfb = a.f / 32;
@@ -396,40 +456,69 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   const bool has_resid = a.resid != RS_NONE;
   const bool int4 = a.resid == RS_INT4;
   const TE<TY>* Ub = static_cast<const TE<TY>*>(a.U);
-  for (int j = 0; j < K; ++j) {
-    if (!s_used[j]) continue;
+
+  // loads of expert j's epilogue operands (issued one expert ahead)
+  auto load_ops = [&](int j, ExpertOps<TY, RB, NF>& o) {
     const int ex = g * K + j;
-    if (active) {
-      // B_j fragments for this wavefront's columns (one 16-deep step)
-      Fr bres[2];
-      if (has_resid) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          // SwiGLU: c = projection (gate, up) of f-block fb0; GELU: f-block fb0 + c
-          const int pj = (ACT == ACT_SWIGLU) ? c : 0;
-          const int fb = (ACT == ACT_SWIGLU) ? fb0 : fb0 + c;
-          const long fr = ((long)(ex * (NF == 1 ? 2 : 1) + pj) * nfb + fb);
-          if (int4) {
-            const uint32_t word = static_cast<const uint32_t*>(a.B1)[fr * 64 + lane];
-            bres[c] = int4_frag_8scale<TY>(word, a.b1_scale + fr * RPAD + 8 * (lane >> 5));
-          } else {
-            bres[c] = load_frag<TY>(static_cast<const TE<TY>*>(a.B1) + (fr * 64 + lane) * 8);
-          }
-        }
+    for (int c = 0; c < 2; ++c) {
+      // SwiGLU: c = projection (gate, up) of f-block fb0; GELU: f-block fb0 + c
+      const int pj = (ACT == ACT_SWIGLU) ? c : 0;
+      const int fb = (ACT == ACT_SWIGLU) ? fb0 : fb0 + c;
+      const long fr = (long)(ex * PIN + pj) * nfb + fb;
+      if (int4) {
+        const uint32_t word = static_cast<const uint32_t*>(a.B1)[fr * 64 + lane];
+        o.b[c] = int4_frag_8scale<TY>(word, *reinterpret_cast<const u4v*>(a.b1_scale + fr * RPAD + 8 * (lane >> 5)));
+      } else {
+        o.b[c] = load_frag<TY>(static_cast<const TE<TY>*>(a.B1) + (fr * 64 + lane) * 8);
       }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r_lane = rb * 32 + (lane & 31);
+      const bool rv = m0 + r_lane < M;
+      const long urow = row0 + (rv ? r_lane : 0);
+#pragma unroll
+      for (int c = 0; c < PIN; ++c) {
+        const Fr u = load_frag<TY>(Ub + urow * a.NU + (j * PIN + c) * RPAD + 8 * (lane >> 5));
+        o.u[rb][c] = rv ? u : zero_frag<TY>();
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NF; ++c) {
+      const long fr = (long)ex * nfb + fb0 + c;
+      if (int4) {
+        const uint32_t word = static_cast<const uint32_t*>(a.Ad)[fr * 64 + lane];
+        o.ad[c] = int4_frag_1scale<TY>(word, f16_bits_to_f32(a.ad_scale[fr * RPAD + (lane & 15)]));
+      } else {
+        o.ad[c] = load_frag<TY>(static_cast<const TE<TY>*>(a.Ad) + (fr * 64 + lane) * 8);
+      }
+    }
+  };
+  auto next_used = [&](int j) {
+    while (j < K && !s_used[j]) ++j;
+    return j;
+  };
+
+  // the first expert's operands do not depend on the main loop: their
+  // loads are in flight during it
+  ExpertOps<TY, RB, NF> cur, nxt;
+  __syncthreads();  // s_used is complete
+  int j = next_used(0);
+  if (has_resid && active && j < K) load_ops(j, cur);
+  mainloop<TY, BM, BK>(KS, al, bl, acc, As, lane);  // ends with a barrier
+
+  while (j < K) {
+    const int jn = next_used(j + 1);
+    if (has_resid && active && jn < K) load_ops(jn, nxt);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this expert's work
+    if (active) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f16v z[2];
-        const int r_lane = rb * 32 + (lane & 31);
         if (has_resid) {
-          const bool rv = m0 + r_lane < M;
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int pj = (ACT == ACT_SWIGLU) ? c : 0;
-            Fr u = rv ? load_frag<TY>(Ub + (long)(row0 + r_lane) * a.NU + (j * (NF == 1 ? 2 : 1) + pj) * RPAD + 8 * (lane >> 5))
-                      : zero_frag<TY>();
-            z[c] = mfma32<TY>(u, bres[c], acc[rb][c]);
-          }
+          for (int c = 0; c < 2; ++c) z[c] = mfma32<TY>(cur.u[rb][(ACT == ACT_SWIGLU) ? c : 0], cur.b[c], acc[rb][c]);
         } else {
           z[0] = acc[rb][0];
           z[1] = acc[rb][1];
@@ -440,7 +529,11 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
           const float wgt = s_w[r * K + j];
           if constexpr (ACT == ACT_SWIGLU) {
             float hw = 0.f;
-            if (wgt != 0.f) hw = wgt * (silu_f(z[0][v]) * z[1][v]);
+            // the two rows this register holds: skip when neither picked j
+            if (__any(wgt != 0.f)) {
+              const float h = silu_f(z[0][v]) * z[1][v];
+              hw = (wgt != 0.f) ? wgt * h : 0.f;
+            }
             hbar[rb][0][v] += hw;
             if (has_resid) Hs[r * HST + (lane & 31)] = from_f32<TY>(hw);
           } else {
@@ -457,34 +550,36 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
     }
     if (has_resid) {
       __syncthreads();
-      if (active) {
-        // V[row, j] += (w_j h_j)[row, this wavefront's f] . A_down,j[f, :]
+      // (w_j h_j)[row, this wavefront's f] . A_down,j[f, :], summed over the
+      // 4 wavefronts in LDS: one partial per (column tile, row, slot)
 #pragma unroll
-        for (int mb = 0; mb < BM / 16; ++mb) {
-          f4v vacc = {0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < BM / 16; ++mb) {
+        f4v vacc = {0.f, 0.f, 0.f, 0.f};
+        if (active) {
 #pragma unroll
           for (int c = 0; c < NF; ++c) {
             const Fr hf = load_frag<TY>(Hs + (mb * 16 + (lane & 15)) * HST + c * 32 + 8 * (lane >> 4));
-            const long fr = (long)ex * nfb + fb0 + c;
-            Fr adf;
-            if (int4) {
-              const uint32_t word = static_cast<const uint32_t*>(a.Ad)[fr * 64 + lane];
-              adf = int4_frag_1scale<TY>(word, f16_bits_to_f32(a.ad_scale[fr * RPAD + (lane & 15)]));
-            } else {
-              adf = load_frag<TY>(static_cast<const TE<TY>*>(a.Ad) + (fr * 64 + lane) * 8);
-            }
-            vacc = mfma16<TY>(hf, adf, vacc);
+            vacc = mfma16<TY>(hf, cur.ad[c], vacc);
           }
+        }
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r = mb * 16 + acc16_row(v, lane);
-            if (s_w[r * K + j] != 0.f)
-              atomicAdd(a.V + (long)(row0 + r) * a.NV + j * RPAD + (lane & 15), vacc[v]);
-          }
+        for (int v = 0; v < 4; ++v)
+          s_red[(wave * BM + mb * 16 + acc16_row(v, lane)) * RPAD + (lane & 15)] = vacc[v];
+      }
+      __syncthreads();
+      for (int e = tid; e < BM * RPAD; e += 256) {
+        const int r = e / RPAD, rho = e % RPAD;
+        const int sl = s_slot[r * K + j];
+        if (sl >= 0) {
+          const float sum = (s_red[e] + s_red[BM * RPAD + e]) +
+                            (s_red[2 * BM * RPAD + e] + s_red[3 * BM * RPAD + e]);
+          a.Vp[(((long)tc.nt * a.vp_rows + row0 + r) * a.ke + sl) * RPAD + rho] = sum;
         }
       }
       __syncthreads();
     }
+    cur = nxt;
+    j = jn;
   }
   if (!active) return;
   TE<TY>* H = static_cast<TE<TY>*>(a.H);
@@ -500,42 +595,47 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------- G2: down projection ------
-template <int XT, int TY, int BM>
+template <int XT, int TY, int BM, int BK>
 __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  if (blockIdx.x == 0 && blockIdx.y == 0 && a.zero_ptr) {
+  if (blockIdx.x == 0 && a.zero_ptr) {
     for (int i = threadIdx.x; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
   }
-  int g, m0, M;
-  if (!find_tile(a.gcounts, a.G, BM, blockIdx.y, g, m0, M)) return;
+  TileCoord tc;
+  if (!map_tile(a.gcounts, a.G, BM, (a.d + BN - 1) / BN, tc)) return;
+  const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * BN + wave * 64;
+  const int n0 = tc.nt * BN + wave * 64;
   const bool active = n0 < a.d;
   const int row0 = a.goffsets[g] + m0;
   TE<TY>* As = reinterpret_cast<TE<TY>*>(smem);
 
-  AHV<TY, BM> al;
-  al.init(a, row0, m0, M);
   const int KSm = a.f / 16;       // k-steps of the base part
   const int KSt = a.NV / 16;      // k-steps of the residual tail
-  const int nb0 = n0 / 32;
+  const int nb0 = (active ? n0 : a.d - 64) / 32;  // idle wavefronts read a valid block
   const int nd32 = a.d / 32;
-  const TE<TY>* W = static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride;
-  const bool int4 = a.resid == RS_INT4;
-  auto bl = [&](int ks, int cb) -> typename Frag<TY>::T {
-    const int nb = nb0 + cb;
-    if (ks < KSm) return frag_at<TY>(W, KSm, nb, ks, lane);
-    const int kt = ks - KSm;  // residual expert j = kt (16 = one padded rank)
-    if (kt >= a.K) return zero_frag<TY>();
-    if (int4) {
-      const uint32_t word = static_cast<const uint32_t*>(a.Bd)[g * a.bd_gstride + (long)(nb * KSt + kt) * 64 + lane];
-      return int4_frag_8scale<TY>(word, a.bd_scale + ((long)(g * a.K + kt) * nd32 + nb) * RPAD + 8 * (lane >> 5));
-    }
-    return frag_at<TY>(static_cast<const TE<TY>*>(a.Bd) + g * a.bd_gstride, KSt, nb, kt, lane);
-  };
   f16v acc[BM / 32][2];
   zero_acc<BM>(acc);
-  mainloop<TY, BM>((a.f + a.NV) / BK, al, bl, acc, As, active, lane);
+  {
+    // hbar . W2_base^g
+    ALoader<TY, TY, BM, BK, false> al;
+    al.init(static_cast<const TE<TY>*>(a.H), a.f, nullptr, 1, row0, m0, M);
+    BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride, KSm, nb0, lane};
+    mainloop<TY, BM, BK>(KSm, al, bl, acc, As, lane);
+  }
+  if (KSt > 0) {
+    // + V . [B_down,j^T]_j : one 16-deep k-step per expert of the group
+    ALoader<DT_F32, TY, BM, 64, false> al;
+    al.init(a.V, a.NV, nullptr, 1, row0, m0, M);
+    if (a.resid == RS_INT4) {
+      BInt4Tail<TY> bl{static_cast<const uint32_t*>(a.Bd) + g * a.bd_gstride,
+                       a.bd_scale + (long)g * a.K * nd32 * RPAD, KSt, nb0, lane, a.K, nd32};
+      mainloop<TY, BM, 64>(KSt, al, bl, acc, As, lane);
+    } else {
+      BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bd) + g * a.bd_gstride, KSt, nb0, lane};
+      mainloop<TY, BM, 64>(KSt, al, bl, acc, As, lane);
+    }
+  }
   if (!active) return;
 #pragma unroll
   for (int rb = 0; rb < BM / 32; ++rb)
@@ -554,6 +654,31 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
         }
       }
     }
+}
+
+// ----------------------------------------------------------------- V sum --
+// V[row, j*16 + rho] = sum over G1 column tiles of the partial for the slot
+// of expert j in the row's chosen list; zero for experts the row did not
+// pick.  One block of 256 threads per 16 rows.
+__global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
+  const int row_base = blockIdx.x * 16;
+  const int nrow = min(16, a.rows - row_base);
+  if (nrow <= 0) return;
+  for (int e = threadIdx.x; e < nrow * a.NV; e += 256) a.V[(long)row_base * a.NV + e] = 0.f;
+  __syncthreads();
+  const int per_row = a.ke * RPAD;
+  for (int e = threadIdx.x; e < nrow * per_row; e += 256) {
+    const int r = e / per_row, rem = e % per_row, sl = rem / RPAD, rho = rem % RPAD;
+    const int row = row_base + r;
+    const int aid = a.garow[row];
+    const int t = aid / a.kg, ga = aid - t * a.kg;
+    const int g = a.gidx[aid];
+    const int j = a.idx[t * a.k + ga * a.ke + sl] - g * a.K;
+    float sum = 0.f;
+    for (int nt = 0; nt < a.ntiles; ++nt)
+      sum += a.Vp[(((long)nt * a.vp_rows + row) * a.ke + sl) * RPAD + rho];
+    a.V[(long)row * a.NV + j * RPAD + rho] = sum;
+  }
 }
 
 // ---------------------------------------------------------------- combine --
@@ -625,12 +750,13 @@ __global__ void debug_decode_kernel(int resid, int kind, const void* src, const 
 }
 
 // ---------------------------------------------------------------- launch --
-size_t gemm_lds(int kind, int ty, int bm, int K) {
+size_t gemm_lds(int kind, int ty, int bm, int bk, int K) {
   const size_t es = ty == DT_F32 ? 4 : 2;
-  const size_t abytes = es * 2 * bm * AST;
+  const size_t abytes = es * 2 * bm * (bk + APAD);
   if (kind != GK_G1) return abytes;
   const size_t hbytes = es * 4 * bm * (2 * 32 + 8);
-  return (abytes > hbytes ? abytes : hbytes) + sizeof(float) * bm * K + sizeof(int) * K + 64;
+  return (abytes > hbytes ? abytes : hbytes) + (sizeof(float) + sizeof(int)) * bm * K +
+         sizeof(int) * ((K + 3) & ~3) + sizeof(float) * 4 * bm * RPAD + 64;
 }
 
 template <class KF>
@@ -644,40 +770,64 @@ hipError_t go(KF kfn, dim3 grid, size_t lds, const GemmArgs& a, hipStream_t st) 
   return hipGetLastError();
 }
 
-template <int XT, int TY, int BM>
+template <int XT, int TY, int BM, int BK>
 hipError_t launch_t(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
-  const size_t lds = gemm_lds(kind, TY, BM, a.K);
+  const size_t lds = gemm_lds(kind, TY, BM, BK, a.K);
   switch (kind) {
-    case GK_U: return go(ugemm_kernel<XT, TY, BM>, grid, lds, a, st);
+    case GK_U: return go(ugemm_kernel<XT, TY, BM, BK>, grid, lds, a, st);
     case GK_G1:
-      if (a.act == ACT_SWIGLU) return go(gemm1_kernel<XT, TY, BM, ACT_SWIGLU>, grid, lds, a, st);
-      return go(gemm1_kernel<XT, TY, BM, ACT_GELU>, grid, lds, a, st);
-    case GK_G2: return go(gemm2_kernel<XT, TY, BM>, grid, lds, a, st);
+      if (a.act == ACT_SWIGLU) return go(gemm1_kernel<XT, TY, BM, BK, ACT_SWIGLU>, grid, lds, a, st);
+      return go(gemm1_kernel<XT, TY, BM, BK, ACT_GELU>, grid, lds, a, st);
+    case GK_G2: return go(gemm2_kernel<XT, TY, BM, BK>, grid, lds, a, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <int XT, int TY>
-hipError_t launch_bm(int kind, int bm, const GemmArgs& a, dim3 grid, hipStream_t st) {
-  switch (bm) {
-    case 32: return launch_t<XT, TY, 32>(kind, a, grid, st);
-    case 64: return launch_t<XT, TY, 64>(kind, a, grid, st);
-    case 128: return launch_t<XT, TY, 128>(kind, a, grid, st);
+hipError_t launch_bm(int kind, int bm, int bk, const GemmArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (TY == DT_F32) {
+    // fp32 fragments are twice as large: small tiles only
+    if (bk != 64) return hipErrorInvalidValue;
+    switch (bm) {
+      case 32: return launch_t<XT, TY, 32, 64>(kind, a, grid, st);
+      case 64: return launch_t<XT, TY, 64, 64>(kind, a, grid, st);
+    }
+    return hipErrorInvalidValue;
+  } else {
+    if (bk == 64) {
+      switch (bm) {
+        case 32: return launch_t<XT, TY, 32, 64>(kind, a, grid, st);
+        case 64: return launch_t<XT, TY, 64, 64>(kind, a, grid, st);
+        case 128: return launch_t<XT, TY, 128, 64>(kind, a, grid, st);
+      }
+    } else if (bk == 128) {
+      switch (bm) {
+        case 32: return launch_t<XT, TY, 32, 128>(kind, a, grid, st);
+        case 64: return launch_t<XT, TY, 64, 128>(kind, a, grid, st);
+        case 128: return launch_t<XT, TY, 128, 128>(kind, a, grid, st);
+      }
+    }
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a,
+hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, int bk, const GemmArgs& a,
                        int max_mtiles, int ntiles, hipStream_t st) {
   if (max_mtiles <= 0 || ntiles <= 0) return hipSuccess;
-  dim3 grid(ntiles, max_mtiles);
-  if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_bm<DT_F32, DT_F32>(kind, bm, a, grid, st);
-  if (x_dtype == DT_F16 && mma_dtype == DT_F16) return launch_bm<DT_F16, DT_F16>(kind, bm, a, grid, st);
-  if (x_dtype == DT_BF16 && mma_dtype == DT_BF16) return launch_bm<DT_BF16, DT_BF16>(kind, bm, a, grid, st);
-  if (x_dtype == DT_BF16 && mma_dtype == DT_F16) return launch_bm<DT_BF16, DT_F16>(kind, bm, a, grid, st);
+  dim3 grid((unsigned)max_mtiles * (unsigned)ntiles);
+  if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_bm<DT_F32, DT_F32>(kind, bm, bk, a, grid, st);
+  if (x_dtype == DT_F16 && mma_dtype == DT_F16) return launch_bm<DT_F16, DT_F16>(kind, bm, bk, a, grid, st);
+  if (x_dtype == DT_BF16 && mma_dtype == DT_BF16) return launch_bm<DT_BF16, DT_BF16>(kind, bm, bk, a, grid, st);
+  if (x_dtype == DT_BF16 && mma_dtype == DT_F16) return launch_bm<DT_BF16, DT_F16>(kind, bm, bk, a, grid, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_vreduce(const VReduceArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(vreduce_kernel, dim3((a.rows + 15) / 16), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st) {

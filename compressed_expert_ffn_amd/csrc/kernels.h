@@ -85,13 +85,25 @@ struct GemmArgs {
   // workspace
   void* U;              // [rows][NU] MFMA type
   int NU;
-  float* V;             // [rows][NV] fp32
+  float* V;             // [rows][NV] fp32 (G2 tail input)
   int NV;
+  float* Vp;            // [G1 column tiles][vp_rows][ke][16] partials of V
+  long vp_rows;
   void* H;              // [rows][f] MFMA type
   float* ypart;         // [T*kg][d] (kg > 1)
   void* Y;              // [T][d] x dtype (kg == 1)
   int* zero_ptr;        // cleared by the output GEMM's first block
   int zero_n;
+};
+
+struct VReduceArgs {
+  const float* Vp;
+  float* V;
+  const int* garow;
+  const int* gidx;
+  const int* idx;
+  long vp_rows;
+  int rows, ntiles, NV, K, kg, ke, k;
 };
 
 struct CombineArgs {
@@ -107,9 +119,11 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
 size_t scatter_lds_bytes(int E, int G);
 hipError_t launch_zero(int* p, int n, hipStream_t st);
 
-// max_mtiles: upper bound of sum_g ceil(M_g / bm); ntiles: column tiles of 256.
-hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a,
+// bm x 256 tiles with bk-deep stages; max_mtiles: upper bound of
+// sum_g ceil(M_g / bm); ntiles: column tiles of 256.
+hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, int bk, const GemmArgs& a,
                        int max_mtiles, int ntiles, hipStream_t st);
+hipError_t launch_vreduce(const VReduceArgs& a, hipStream_t st);
 hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st);
 
 // Device-side decode of stored residual factors (test export).

@@ -2,10 +2,10 @@
 //
 // Router ("Breaking the MoE LLM Trilemma", papernotes.org note, key design 3:
 // groups first, then experts inside the chosen groups; FP32 router as in the
-// MoE routing page "混合专家模型的路由机制与工程落地", section 3.1): one 64-lane
-// wavefront per token.  Lanes split the logit columns and the model width,
+// MoE routing page "混合专家模型的路由机制与工程落地", section 3.1): 64-lane
+// wavefronts, each routing one to four tokens.  Lanes split the model width,
 // partial dot products are combined with cross-lane xor reductions, and the
-// top-k is a repeated wave arg-max (larger value, then lower index).
+// top-k keeps the larger score, then the lower index.
 //
 // Token lists (dropless dispatch, tokens ascending within each bin): the
 // router counts assignments per (chunk of 256 assignments, bin) with
@@ -130,7 +130,7 @@ __device__ void softmax_sel(const float (&val)[KMAX], int k, float (&p)[KMAX]) {
 }
 
 template <int XT>
-__global__ __launch_bounds__(256) void router_kernel(RouteArgs a) {
+__global__ __launch_bounds__(256) void router_generic_kernel(RouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
@@ -194,6 +194,173 @@ __global__ __launch_bounds__(256) void router_kernel(RouteArgs a) {
       const int gslot = t * a.kg + ga;
       a.gidx[gslot] = g;
       atomicAdd(&a.cgcount[(gslot / CHUNK) * a.G + g], 1);
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Router for the common shapes (G and K fixed at compile time, each a
+// multiple of 4 up to 16, or K = 1).  Wavefront w routes TPW tokens
+// together.  Lane l owns rows 4 (l + 64 m) .. +3 of d (m < d / 256) and
+// loads them as vectors: 4 activations per token and 4 rows of the router
+// matrix (row-major, so 4 * C consecutive floats, read as 16-byte vectors).
+// The group-level pass shares every weight load among the TPW tokens; the
+// expert-level pass runs once per (token, chosen group).  The loops carry no
+// branches, so the loads of a step are all in flight together.  One xor
+// butterfly per logit leaves every lane holding every logit, so the top-k
+// and the softmax run per lane without further cross-lane traffic.
+template <int XT>
+__device__ __forceinline__ void load4(const typename Elem<XT>::T* p, float (&v)[4]) {
+  if constexpr (XT == DT_F32) {
+    f4v q = *reinterpret_cast<const f4v*>(p);
+    v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+  } else {
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+    u2v q = *reinterpret_cast<const u2v*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t b = static_cast<uint16_t>((q[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      v[e] = (XT == DT_F16) ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
+    }
+  }
+}
+
+// acc[p][c] = sum over d of x_p[i] W[i][c] for NT token rows and the C
+// columns of W (row stride C); totals end up in every lane.
+template <int XT, int NT, int C>
+__device__ __forceinline__ void dot_pass(const typename Elem<XT>::T* const (&xs)[NT],
+                                         const float* W, int d, int lane, float (&acc)[NT][C]) {
+#pragma unroll
+  for (int p = 0; p < NT; ++p)
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[p][c] = 0.f;
+  const int steps = d / 256;
+#pragma unroll 2
+  for (int m = 0; m < steps; ++m) {
+    const int i0 = 4 * (lane + 64 * m);
+    float x[NT][4];
+#pragma unroll
+    for (int p = 0; p < NT; ++p) load4<XT>(xs[p] + i0, x[p]);
+    f4v wv[4][C / 4];
+    const float* w = W + (long)i0 * C;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int c4 = 0; c4 < C / 4; ++c4) wv[e][c4] = *reinterpret_cast<const f4v*>(w + e * C + 4 * c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int c4 = 0; c4 < C / 4; ++c4)
+#pragma unroll
+        for (int p = 0; p < NT; ++p)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) acc[p][4 * c4 + cc] = fmaf(x[p][e], wv[e][c4][cc], acc[p][4 * c4 + cc]);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+    for (int p = 0; p < NT; ++p)
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[p][c] += __shfl_xor(acc[p][c], off);
+}
+
+// k best of v[0..C) (descending, ties to the lower index), in every lane.
+template <int C, int KMAX>
+__device__ __forceinline__ void topk_local(const float (&v)[C], int k, int (&sel)[KMAX],
+                                           float (&val)[KMAX]) {
+  uint32_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    float bv = -INFINITY;
+    int bi = -1;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float x = (v[c] == v[c]) ? v[c] : -INFINITY;  // NaN ranks as -inf
+      if (!((taken >> c) & 1u) && (bi < 0 || x > bv)) {
+        bv = x;
+        bi = c;
+      }
+    }
+    if (j < k) {
+      sel[j] = bi;
+      val[j] = bv;
+      taken |= 1u << bi;
+    } else {
+      sel[j] = 0;
+      val[j] = 0.f;
+    }
+  }
+}
+
+template <int XT, int TPW, int CG, int CK>
+__global__ __launch_bounds__(256) void router_fast_kernel(RouteArgs a) {
+  using XE = typename Elem<XT>::T;
+  const int lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  if (t0 >= a.T) return;
+  const int nt = min(TPW, a.T - t0);
+  const XE* X = static_cast<const XE*>(a.X);
+  const XE* xs[TPW];
+#pragma unroll
+  for (int p = 0; p < TPW; ++p) xs[p] = X + (long)(t0 + (p < nt ? p : 0)) * a.d;
+
+  // level 1: group logits, one weight load shared by the TPW tokens
+  float s[TPW][CG];
+  dot_pass<XT, TPW, CG>(xs, a.Wg, a.d, lane, s);
+#pragma unroll
+  for (int p = 0; p < TPW; ++p) {
+    if (p >= nt) break;
+    const int t = t0 + p;
+    if (a.gbias) {
+#pragma unroll
+      for (int c = 0; c < CG; ++c) s[p][c] += a.gbias[c];
+    }
+    int gsel[MAX_KG];
+    float gval[MAX_KG], pg[MAX_KG];
+    topk_local<CG, MAX_KG>(s[p], a.kg, gsel, gval);
+    softmax_sel<MAX_KG>(gval, a.kg, pg);
+    // level 2: expert logits of each chosen group
+#pragma unroll
+    for (int ga = 0; ga < MAX_KG; ++ga) {
+      if (ga >= a.kg) break;
+      const int g = gsel[ga];
+      if constexpr (CK == 1) {
+        if (lane == 0) {
+          const int slot = t * a.k + ga;
+          a.idx[slot] = g;
+          a.w[slot] = pg[ga];
+          atomicAdd(&a.ccount[(slot / CHUNK) * a.E + g], 1);
+        }
+      } else {
+        const XE* x1[1] = {xs[p]};
+        float e[1][CK];
+        dot_pass<XT, 1, CK>(x1, a.We + (long)g * a.d * CK, a.d, lane, e);
+        if (a.ebias) {
+#pragma unroll
+          for (int c = 0; c < CK; ++c) e[0][c] += a.ebias[g * CK + c];
+        }
+        int js[MAX_SLOTS];
+        float jv[MAX_SLOTS], qw[MAX_SLOTS];
+        topk_local<CK, MAX_SLOTS>(e[0], a.ke, js, jv);
+        softmax_sel<MAX_SLOTS>(jv, a.ke, qw);
+        if (lane == 0) {
+#pragma unroll
+          for (int b = 0; b < MAX_SLOTS; ++b) {
+            if (b >= a.ke) break;
+            const int slot = t * a.k + ga * a.ke + b;
+            const int ex = g * CK + js[b];
+            a.idx[slot] = ex;
+            a.w[slot] = pg[ga] * qw[b];
+            atomicAdd(&a.ccount[(slot / CHUNK) * a.E + ex], 1);
+          }
+        }
+      }
+      if (lane == 0) {
+        const int gslot = t * a.kg + ga;
+        a.gidx[gslot] = g;
+        atomicAdd(&a.cgcount[(gslot / CHUNK) * a.G + g], 1);
+      }
     }
   }
 }
@@ -307,16 +474,47 @@ __global__ void zero_kernel(int* p, int n) {
 
 }  // namespace
 
+template <int XT, int TPW, int CG, int CK>
+hipError_t launch_fast(const RouteArgs& a, hipStream_t st) {
+  const int waves = (a.T + TPW - 1) / TPW;
+  hipLaunchKernelGGL((router_fast_kernel<XT, TPW, CG, CK>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int XT, int CG, int CK>
+hipError_t launch_tpw(const RouteArgs& a, hipStream_t st) {
+  // several tokens per wavefront once there are enough tokens to fill the chip
+  if (a.T >= 8192) return launch_fast<XT, 4, CG, CK>(a, st);
+  if (a.T >= 2048) return launch_fast<XT, 2, CG, CK>(a, st);
+  return launch_fast<XT, 1, CG, CK>(a, st);
+}
+
+template <int XT>
+hipError_t launch_router_t(const RouteArgs& a, hipStream_t st) {
+  if (a.d % 256 == 0) {
+    const int key = a.G * 100 + a.K;
+    switch (key) {
+      case 404: return launch_tpw<XT, 4, 4>(a, st);
+      case 808: return launch_tpw<XT, 8, 8>(a, st);
+      case 1616: return launch_tpw<XT, 16, 16>(a, st);
+      case 401: return launch_tpw<XT, 4, 1>(a, st);
+      case 801: return launch_tpw<XT, 8, 1>(a, st);
+      case 1601: return launch_tpw<XT, 16, 1>(a, st);
+      default: break;
+    }
+  }
+  hipLaunchKernelGGL(router_generic_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
-  dim3 grid((a.T + 3) / 4), block(256);
   switch (x_dtype) {
-    case DT_F32: hipLaunchKernelGGL(router_kernel<DT_F32>, grid, block, 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL(router_kernel<DT_F16>, grid, block, 0, st, a); break;
-    case DT_BF16: hipLaunchKernelGGL(router_kernel<DT_BF16>, grid, block, 0, st, a); break;
-    default: return hipErrorInvalidValue;
+    case DT_F32: return launch_router_t<DT_F32>(a, st);
+    case DT_F16: return launch_router_t<DT_F16>(a, st);
+    case DT_BF16: return launch_router_t<DT_BF16>(a, st);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 size_t scatter_lds_bytes(int E, int G) {

@@ -194,7 +194,8 @@ int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t exper
 /* Per-stage GPU timing: after moe_profile_begin, each moe_forward records
  * a pair of HIP events, on the stream it was given, around every kernel it
  * launches whose stage bit is set in stage_mask (bit s = stage s in the
- * order router, scatter, ugemm, gemm1, gemm2, combine; -1 = all), for at
+ * order router, scatter, ugemm, gemm1, vreduce, gemm2, combine; -1 =
+ * all), for at
  * most max_calls calls.  moe_profile_end synchronises, writes the summed
  * milliseconds per stage into stage_ms[n_stages_cap], the stage count into
  * *n_stages, the recorded calls into *n_calls and comma-separated stage

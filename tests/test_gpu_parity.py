@@ -194,3 +194,30 @@ def test_repeated_calls_and_different_T_on_one_handle():
         assert (np.abs(a - b) <= bound).all(), float((np.abs(a - b) - bound).max())
     finally:
         lay.close()
+
+
+TILE_VARIANTS = [
+    {"CEFN_BM_G1": "128", "CEFN_BK_G1": "64", "CEFN_BM_G2": "128", "CEFN_BK_G2": "128", "CEFN_BM_U": "64"},
+    {"CEFN_BM_G1": "32", "CEFN_BK_G1": "128", "CEFN_BM_G2": "64", "CEFN_BK_G2": "64", "CEFN_BK_U": "64"},
+    {"CEFN_BM_G1": "64", "CEFN_BK_G1": "64", "CEFN_BM_G2": "32", "CEFN_BK_G2": "128", "CEFN_BM_U": "128"},
+]
+
+
+@pytest.mark.parametrize("wi,T", [(1, 700), (3, 333), (4, 64), (2, 150)])
+@pytest.mark.parametrize("vi", range(len(TILE_VARIANTS)))
+def test_tile_variants_match_oracle(wi, T, vi, monkeypatch):
+    """Every tile shape and stage depth the library can pick gives the same
+    routing and outputs within tolerance (ragged tiles included)."""
+    L = _lib()
+    for k, v in TILE_VARIANTS[vi].items():
+        monkeypatch.setenv(k, v)
+    w = WORKLOADS[wi].with_T(T)
+    wT, inputs, layer = make_parity_layer(w)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        y = y_to_host(lay.forward(x_to_device(inputs["X"], w.x_dtype)))
+        err = rel_err(y, O.forward(layer))
+        say(f"[tiles {vi}] {w.name} T={T}: rel err {err:.3e}")
+        assert err <= TOL[w.x_dtype]
+    finally:
+        lay.close()
