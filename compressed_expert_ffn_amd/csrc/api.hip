@@ -81,8 +81,9 @@ struct moe_handle {
   std::vector<void*> allocs;
   int64_t weight_bytes = 0;
   // tile rows and stage depth per GEMM (0 = chosen per call); set from the
-  // CEFN_BM_{U,G1,G2} / CEFN_BK_{U,G1,G2} environment variables at create
-  int bm_env[3] = {0, 0, 0}, bk_env[3] = {0, 0, 0};
+  // tile overrides read from CEFN_BM_{U,G1,G2} (token rows per tile) and
+  // CEFN_KS_G2 (k splits of the down projection) at create, for tuning
+  int bm_env[3] = {0, 0, 0}, ks_env = 0;
   // profiling
   bool prof = false;
   int prof_max = 0, prof_calls = 0, prof_mask = -1;
@@ -214,7 +215,7 @@ int build_weights(moe_handle* h, const moe_weights* w) {
     std::vector<TS> buf((size_t)G * N * d);
     h->w1_gs = (long)N * d;
     for (int g = 0; g < G; ++g) {
-      pack_frag(buf.data() + (size_t)g * N * d, N, d, [&](int n, int k) -> TS {
+      pack_frag(buf.data() + (size_t)g * N * d, N, d, true, [&](int n, int k) -> TS {
         int p = 0, col = n;
         if (swiglu) {
           const int blk = n / 32;
@@ -231,7 +232,7 @@ int build_weights(moe_handle* h, const moe_weights* w) {
     std::vector<TS> buf((size_t)G * d * f);
     h->w2_gs = (long)d * f;
     for (int g = 0; g < G; ++g)
-      pack_frag(buf.data() + (size_t)g * d * f, d, f,
+      pack_frag(buf.data() + (size_t)g * d * f, d, f, true,
                 [&](int n, int k) -> TS { return base_ptr(P - 1)[((size_t)g * f + k) * d + n]; });
     TRY(upload_raw(h, &h->W2, buf));
   }
@@ -266,7 +267,7 @@ int build_weights(moe_handle* h, const moe_weights* w) {
           rho = n % RPAD;
           return j < K && rho < r;
         };
-        pack_frag_int4(wbuf.data() + (size_t)g * h->at_gs, NU, d, [&](int n, int k) {
+        pack_frag_int4(wbuf.data() + (size_t)g * h->at_gs, NU, d, true, [&](int n, int k) {
           int j, p, rho;
           return col(n, j, p, rho) ? QA(p, g * K + j).code(k, rho) : 0;
         });
@@ -288,7 +289,7 @@ int build_weights(moe_handle* h, const moe_weights* w) {
       for (int i = 0; i < E; ++i)
         for (int p = 0; p < Pin; ++p) {
           const Q4& q = QB(p, i);
-          pack_frag_int4(wbuf.data() + (size_t)(i * Pin + p) * f * 2, f, RPAD,
+          pack_frag_int4(wbuf.data() + (size_t)(i * Pin + p) * f * 2, f, RPAD, false,
                          [&](int n, int k) { return k < r ? q.code(n, k) : 0; });
           for (int fb = 0; fb < f / 32; ++fb)
             for (int rho = 0; rho < r; ++rho)
@@ -297,23 +298,24 @@ int build_weights(moe_handle* h, const moe_weights* w) {
       TRY(upload_raw(h, &h->B1, wbuf));
       TRY(upload(h, &h->B1_s, sbuf));
     }
-    // Ad: [E][f/32][64] words + scales [E][f/32][16]
+    // Ad: [E][f/32][2][64] words (see ad_row) + scales [E][f/32][16]
     {
-      std::vector<uint32_t> wbuf((size_t)E * (f / 32) * 64);
+      std::vector<uint32_t> wbuf((size_t)E * (f / 32) * 2 * 64);
       std::vector<uint16_t> sbuf((size_t)E * (f / 32) * RPAD, 0);
       for (int i = 0; i < E; ++i) {
         const Q4& q = QA(P - 1, i);
         for (int fb = 0; fb < f / 32; ++fb) {
-          for (int lane = 0; lane < 64; ++lane) {
-            const int rho = lane & 15;
-            uint32_t word = 0;
-            for (int e = 0; e < 8; ++e) {
-              const int kk = fb * 32 + 8 * (lane >> 4) + e;
-              const int qv = rho < r ? q.code(kk, rho) : 0;
-              word |= static_cast<uint32_t>(qv + 8) << (4 * e);
+          for (int st = 0; st < 2; ++st)
+            for (int lane = 0; lane < 64; ++lane) {
+              const int rho = lane & 31;
+              uint32_t word = 0;
+              for (int e = 0; e < 8; ++e) {
+                const int kk = fb * 32 + ad_row(st, lane >> 5, e);
+                const int qv = rho < r ? q.code(kk, rho) : 0;
+                word |= static_cast<uint32_t>(qv + 8) << (4 * e);
+              }
+              wbuf[(((size_t)i * (f / 32) + fb) * 2 + st) * 64 + lane] = word;
             }
-            wbuf[((size_t)i * (f / 32) + fb) * 64 + lane] = word;
-          }
           for (int rho = 0; rho < r; ++rho) sbuf[((size_t)i * (f / 32) + fb) * RPAD + rho] = q.scale(fb * 32, rho);
         }
       }
@@ -326,7 +328,7 @@ int build_weights(moe_handle* h, const moe_weights* w) {
       std::vector<uint16_t> sbuf((size_t)E * (d / 32) * RPAD, 0);
       h->bd_gs = (long)d * NV / 8;
       for (int g = 0; g < G; ++g)
-        pack_frag_int4(wbuf.data() + (size_t)g * h->bd_gs, d, NV, [&](int n, int k) {
+        pack_frag_int4(wbuf.data() + (size_t)g * h->bd_gs, d, NV, true, [&](int n, int k) {
           const int j = k / RPAD, rho = k % RPAD;
           return (j < K && rho < r) ? QB(P - 1, g * K + j).code(n, rho) : 0;
         });
@@ -356,7 +358,7 @@ int build_weights(moe_handle* h, const moe_weights* w) {
     std::vector<TS> buf((size_t)G * NU * d);
     h->at_gs = (long)NU * d;
     for (int g = 0; g < G; ++g)
-      pack_frag(buf.data() + (size_t)g * NU * d, NU, d, [&](int n, int k) -> TS {
+      pack_frag(buf.data() + (size_t)g * NU * d, NU, d, true, [&](int n, int k) -> TS {
         const int j = n / (Pin * RPAD), p = (n / RPAD) % Pin, rho = n % RPAD;
         return (j < K && rho < r) ? Aval(p, g * K + j, k, rho) : zero;
       });
@@ -366,26 +368,27 @@ int build_weights(moe_handle* h, const moe_weights* w) {
     std::vector<TS> buf((size_t)E * Pin * f * RPAD);
     for (int i = 0; i < E; ++i)
       for (int p = 0; p < Pin; ++p)
-        pack_frag(buf.data() + (size_t)(i * Pin + p) * f * RPAD, f, RPAD,
+        pack_frag(buf.data() + (size_t)(i * Pin + p) * f * RPAD, f, RPAD, false,
                   [&](int n, int k) -> TS { return k < r ? Bval(p, i, n, k) : zero; });
     TRY(upload_raw(h, &h->B1, buf));
   }
   {
-    std::vector<TS> buf((size_t)E * f * RPAD);
+    std::vector<TS> buf((size_t)E * f * 2 * 32);
     for (int i = 0; i < E; ++i)
       for (int fb = 0; fb < f / 32; ++fb)
-        for (int lane = 0; lane < 64; ++lane)
-          for (int e = 0; e < 8; ++e) {
-            const int rho = lane & 15, kk = fb * 32 + 8 * (lane >> 4) + e;
-            buf[(((size_t)i * (f / 32) + fb) * 64 + lane) * 8 + e] = rho < r ? Aval(P - 1, i, kk, rho) : zero;
-          }
+        for (int st = 0; st < 2; ++st)
+          for (int lane = 0; lane < 64; ++lane)
+            for (int e = 0; e < 8; ++e) {
+              const int rho = lane & 31, kk = fb * 32 + ad_row(st, lane >> 5, e);
+              buf[((((size_t)i * (f / 32) + fb) * 2 + st) * 64 + lane) * 8 + e] = rho < r ? Aval(P - 1, i, kk, rho) : zero;
+            }
     TRY(upload_raw(h, &h->Ad, buf));
   }
   {
     std::vector<TS> buf((size_t)G * d * NV);
     h->bd_gs = (long)d * NV;
     for (int g = 0; g < G; ++g)
-      pack_frag(buf.data() + (size_t)g * d * NV, d, NV, [&](int n, int k) -> TS {
+      pack_frag(buf.data() + (size_t)g * d * NV, d, NV, true, [&](int n, int k) -> TS {
         const int j = k / RPAD, rho = k % RPAD;
         return (j < K && rho < r) ? Bval(P - 1, g * K + j, n, rho) : zero;
       });
@@ -394,32 +397,46 @@ int build_weights(moe_handle* h, const moe_weights* w) {
   return MOE_OK;
 }
 
-// Tile rows for a grouped GEMM with `rows` rows and `ntiles` column tiles:
-// the largest of 128 / 64 / 32 that still gives every compute unit work.
-int pick_bm(int rows, int ntiles, bool f32, int cap) {
-  if (!f32 && cap >= 128 && (long)(rows / 128) * ntiles >= 512) return 128;
-  if (cap >= 64 && (long)(rows / 64) * ntiles >= 256) return 64;
-  return 32;
+constexpr int kMaxSplits = 4;  // k splits of the down projection (ypart holds this many)
+
+// Token rows per tile for a grouped GEMM with `rows` rows and `ntiles`
+// column tiles of 256.  Bigger tiles reuse each weight fragment over more
+// tokens (fewer bytes per MFMA) but give fewer workgroups; the estimate
+// below charges each choice its number of rounds over the 256 compute units
+// times the tile height, discounted by the main loop's measured efficiency
+// at that height.
+int pick_bm(const moe_handle* h, int which, int rows, int ntiles, int splits) {
+  const bool f32 = h->mma == MOE_F32;
+  if (h->bm_env[which]) return h->bm_env[which];
+  static const int cand[4] = {256, 128, 64, 32};
+  static const float eff[4] = {1.0f, 0.95f, 0.75f, 0.5f};
+  int best = 32;
+  float best_cost = 1e30f;
+  for (int i = 0; i < 4; ++i) {
+    const int bm = cand[i];
+    if (f32 && bm > 64) continue;
+    // GELU keeps two f-blocks of h per wavefront: up to 128 rows without spills
+    if (which == GK_G1 && h->cfg.act != MOE_ACT_SWIGLU && bm > 128) continue;
+    if (gemm_lds(which, h->mma, bm, h->cfg.K, h->cfg.top_experts) > 160 * 1024) continue;
+    const long tiles = ((long)(rows + bm - 1) / bm) * ntiles * splits;
+    const long rounds = (tiles + 255) / 256;
+    const float cost = rounds * bm / eff[i];
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = bm;
+    }
+  }
+  return best;
 }
 
-struct Tile {
-  int bm, bk;
-};
-
-// kdim: depth of the GEMM's main k loop (d for ugemm and gemm1, f for
-// gemm2); the stage depth must divide it.
-Tile choose_tile(const moe_handle* h, int which, int rows, int ntiles, int kdim) {
-  const bool f32 = h->mma == MOE_F32;
-  Tile t;
-  // gemm1 with GELU keeps two f-blocks of h per wavefront: 64 rows at most
-  const int cap = (which == 1 && h->cfg.act != MOE_ACT_SWIGLU) ? 64 : 128;
-  t.bm = pick_bm(rows, ntiles, f32, cap);
-  t.bk = f32 ? 64 : 128;
-  if (h->bm_env[which]) t.bm = h->bm_env[which];
-  if (h->bk_env[which]) t.bk = h->bk_env[which];
-  if (f32 || kdim % t.bk) t.bk = 64;
-  if (f32 && t.bm > 64) t.bm = 64;
-  return t;
+// k splits of the down projection: enough workgroups to cover the chip,
+// at least 8 stages of 64 per split.
+int pick_splits(const moe_handle* h, int rows, int ntiles) {
+  if (h->ks_env) return std::max(1, std::min(kMaxSplits, h->ks_env));
+  const int kt = h->cfg.f / 64;
+  int s = 1;
+  while (s < kMaxSplits && kt / (2 * s) >= 8 && ((long)(rows + 127) / 128) * ntiles * s < 256) s *= 2;
+  return s;
 }
 
 int max_mtiles(int T, int kg, int G, int bm) {
@@ -557,9 +574,8 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
       char key[32];
       std::snprintf(key, sizeof(key), "CEFN_BM_%s", names[i]);
       if (const char* v = std::getenv(key)) h->bm_env[i] = std::atoi(v);
-      std::snprintf(key, sizeof(key), "CEFN_BK_%s", names[i]);
-      if (const char* v = std::getenv(key)) h->bk_env[i] = std::atoi(v);
     }
+    if (const char* v = std::getenv("CEFN_KS_G2")) h->ks_env = std::atoi(v);
   }
 
   // router weights and biases
@@ -611,7 +627,7 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
     }
     TRY(dalloc(h.get(), &tmp, T * kg * (long)c.f * es + 16));
     h->H = tmp;
-    if (kg > 1) TRY(dalloc(h.get(), &h->ypart, T * kg * (long)c.d + 4));
+    TRY(dalloc(h.get(), &h->ypart, (size_t)kMaxSplits * T * kg * c.d + 4));
     return MOE_OK;
   };
   rc = ws();
@@ -689,6 +705,9 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   ga.H = h->H;
   ga.ypart = h->ypart;
   ga.Y = Y;
+  ga.ksplit = 1;
+  ga.rows_total = (long)rows;
+  int splits = 1;
   hipError_t e;
   if (c.r > 0) {
     GemmArgs u = ga;
@@ -697,9 +716,9 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     u.bw_scale = h->At_s;
     u.bws_gstride = h->at_sgs;
     const int nt = (h->NU + 255) / 256;
-    const Tile tl = choose_tile(h, 0, rows, nt, c.d);
+    const int bm = pick_bm(h, GK_U, rows, nt, 1);
     pf.begin(2);
-    e = launch_gemm(GK_U, c.x_dtype, h->mma, tl.bm, tl.bk, u, max_mtiles(T, kg, c.G, tl.bm), nt, st);
+    e = launch_gemm(GK_U, c.x_dtype, h->mma, bm, u, max_mtiles(T, kg, c.G, bm), nt, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "ugemm launch");
     pf.end(2);
   }
@@ -712,9 +731,9 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     g1.Ad = h->Ad;
     g1.ad_scale = h->Ad_s;
     const int nt = (h->P_in * c.f + 255) / 256;
-    const Tile tl = choose_tile(h, 1, rows, nt, c.d);
+    const int bm = pick_bm(h, GK_G1, rows, nt, 1);
     pf.begin(3);
-    e = launch_gemm(GK_G1, c.x_dtype, h->mma, tl.bm, tl.bk, g1, max_mtiles(T, kg, c.G, tl.bm), nt, st);
+    e = launch_gemm(GK_G1, c.x_dtype, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "gemm1 launch");
     pf.end(3);
   }
@@ -734,7 +753,7 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     va.ke = c.top_experts;
     va.k = h->k;
     pf.begin(4);
-    e = launch_vreduce(va, st);
+    e = launch_vreduce(h->mma, va, st);
     if (e != hipSuccess) return hip_fail(h, e, "vreduce launch");
     pf.end(4);
   }
@@ -748,14 +767,16 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     g2.zero_ptr = h->cc;
     g2.zero_n = h->cc_n;
     const int nt = (c.d + 255) / 256;
-    const Tile tl = choose_tile(h, 2, rows, nt, c.f);
+    splits = pick_splits(h, rows, nt);
+    const int bm = pick_bm(h, GK_G2, rows, nt, splits);
+    g2.ksplit = splits;
     pf.begin(5);
-    e = launch_gemm(GK_G2, c.x_dtype, h->mma, tl.bm, tl.bk, g2, max_mtiles(T, kg, c.G, tl.bm), nt, st);
+    e = launch_gemm(GK_G2, c.x_dtype, h->mma, bm, g2, max_mtiles(T, kg, c.G, bm), nt, splits, st);
     if (e != hipSuccess) return hip_fail(h, e, "gemm2 launch");
     pf.end(5);
   }
-  if (kg > 1) {
-    CombineArgs ca{h->ypart, Y, T, c.d, kg};
+  if (kg > 1 || splits > 1) {
+    CombineArgs ca{h->ypart, Y, T, c.d, kg, splits};
     pf.begin(6);
     e = launch_combine(c.x_dtype, ca, st);
     if (e != hipSuccess) return hip_fail(h, e, "combine launch");
@@ -801,10 +822,10 @@ int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t exper
     kind = 2;
     src = h->Ad;
     sc = h->Ad_s;
-    base = (long)expert * nfb * 64;
+    base = (long)expert * nfb * 2 * 64;
     sbase = (long)expert * nfb * RPAD;
   } else {  // Bd
-    kind = 1;
+    kind = 3;
     src = h->Bd;
     sc = h->Bd_s;
     base = int4 ? g * h->bd_gs : g * h->bd_gs / 8;

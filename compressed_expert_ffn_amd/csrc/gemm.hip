@@ -12,34 +12,31 @@
 //         z_j = Z + u_j B_j^T          (one 16-deep MFMA step, C operand = Z)
 //         h_j = SiLU(z_gate) * z_up    (or GELU_tanh(z))
 //         hbar += w_j h_j              (gate weight w_j = 0 if row did not pick j)
-//         V[row, j] += (w_j h_j) . A_down,j   (16x16x32 MFMA, atomics over column tiles)
-//  G2 : y = [hbar | V] . [W2_base^g ; B_down stacked]  -- the down projection
+//         V[row, slot of j] += (w_j h_j) . A_down,j   (MFMA straight from the
+//                                     registers of h, summed over the
+//                                     workgroup in LDS, over column tiles by
+//                                     the vreduce kernel)
+//  G2 : y = [hbar | V] . [W2_base^g ; B_down stacked] -- the down projection
 //       sum_j w_j h_j W~_down,j = hbar W2_base + sum_j (w_j h_j A_down,j) B_down,j^T
-//       with a K-tail of K*16 residual rows; writes Y (one group per token) or
-//       a per-(token, group) partial that the combine kernel sums.
+//       with a tail of K*16 residual k; writes Y (one group per token, one
+//       k split) or fp32 partials that the combine kernel sums.
 //
-// Tiles are BM rows x 256 columns; the 4 wavefronts of a workgroup split the
-// columns (64 each: one 32-column gate block and its up block for SwiGLU).
-// A (activations) is staged through LDS (double-buffered, padded rows); B
-// (weights) is stored fragment-major and read straight into registers one
-// 64-deep stage ahead.
+// Tiles: 4 wavefronts side by side along the features, 64 features (two
+// 32-column blocks: for SwiGLU one gate block and its up block) each, and
+// RT token blocks of 32; token rows are staged through LDS (see tile.h),
+// weights read straight from their fragment-major layout.
 #include <type_traits>
 
-#include "common.h"
 #include "kernels.h"
+#include "tile.h"
 
 namespace cefn {
 namespace {
 
-constexpr int BN = 256;
-constexpr int APAD = 8;  // LDS row padding of the A tile, elements (16 bytes)
+constexpr int CB = 2;     // feature blocks per wavefront
+constexpr int BNF = 256;  // features per tile (4 wavefronts x 64)
 
-template <int TY> struct Chunk { using T = u4v; };
-template <> struct Chunk<DT_F32> { using T = f8; };
-
-template <int TY> using TE = typename Elem<TY>::T;
-
-// Tile of workgroup blockIdx.x in a 1-D grid over (group, row tile, column
+// Tile of logical workgroup i in a 1-D grid over (group, row tile, column
 // tile).  Logical order: groups in turn; inside a group, blocks of nb column
 // tiles with the row tiles fastest inside a block, nb chosen so that a block
 // is about one XCD's worth of workgroups (32).  Workgroups are dealt
@@ -50,16 +47,30 @@ struct TileCoord {
   int g, m0, M, nt;
 };
 
-__device__ bool map_tile(const int* gcounts, int G, int BM, int NT, TileCoord& tc) {
+// The group counts (G <= 256) are loaded by all lanes at once and walked
+// with lane reads, so a workgroup pays one load latency here, not G.
+__device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileCoord& tc) {
+  const int lane = threadIdx.x & 63;
+  int cnt[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cnt[q] = (64 * q + lane < G) ? gcounts[64 * q + lane] : 0;
+  auto count_of = [&](int gg) {
+    const int l = gg & 63;
+    switch (gg >> 6) {
+      case 0: return __builtin_amdgcn_readlane(cnt[0], l);
+      case 1: return __builtin_amdgcn_readlane(cnt[1], l);
+      case 2: return __builtin_amdgcn_readlane(cnt[2], l);
+      default: return __builtin_amdgcn_readlane(cnt[3], l);
+    }
+  };
   int total = 0;
-  for (int gg = 0; gg < G; ++gg) total += (gcounts[gg] + BM - 1) / BM * NT;
-  const int i = blockIdx.x;
+  for (int gg = 0; gg < G; ++gg) total += (count_of(gg) + BM - 1) / BM * NT;
   if (i >= total) return false;
   const int x = i & 7, j = i >> 3;
   const int q = total >> 3, rem = total & 7;
   int L = x * q + min(x, rem) + j;
   for (int gg = 0; gg < G; ++gg) {
-    const int Mg = gcounts[gg];
+    const int Mg = count_of(gg);
     const int mt = (Mg + BM - 1) / BM;
     if (L < mt * NT) {
       const int nb = max(1, 32 / mt);
@@ -76,595 +87,363 @@ __device__ bool map_tile(const int* gcounts, int G, int BM, int NT, TileCoord& t
   return false;
 }
 
-template <int TY>
-__device__ __forceinline__ typename Chunk<TY>::T zero_chunk() {
-  typename Chunk<TY>::T c;
-  if constexpr (TY == DT_F32) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = 0.f;
-  } else {
-    c[0] = c[1] = c[2] = c[3] = 0u;
-  }
-  return c;
-}
+// Element v of a transposed 32x32 accumulator held by lane l: feature row
+// 8 (v / 4) + 4 (l / 32) + v % 4 of the block, token column l % 32.
+__device__ __forceinline__ int acc_feat(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-template <int TY>
-__device__ __forceinline__ typename Chunk<TY>::T chunk_from_f32(const float* v) {
-  if constexpr (TY == DT_F32) {
-    f8 c;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = v[i];
-    return c;
-  } else {
-    return __builtin_bit_cast(u4v, to_frag<TY>(v));
-  }
-}
-
-template <int TY>
-__device__ __forceinline__ void store_chunk(TE<TY>* dst, const typename Chunk<TY>::T& c) {
-  if constexpr (TY == DT_F32) {
-    f4v a, b;
-    a[0] = c[0]; a[1] = c[1]; a[2] = c[2]; a[3] = c[3];
-    b[0] = c[4]; b[1] = c[5]; b[2] = c[6]; b[3] = c[7];
-    reinterpret_cast<f4v*>(dst)[0] = a;
-    reinterpret_cast<f4v*>(dst)[1] = b;
-  } else {
-    *reinterpret_cast<u4v*>(dst) = c;
-  }
-}
-
-// ------------------------------------------------------ A-operand loaders --
-// Raw 8-element chunk of a source of type DT (16 bytes, or 32 for fp32).
-template <int DT> struct Raw8 { using T = u4v; };
-template <> struct Raw8<DT_F32> { using T = f8; };
-
+// Store 4 consecutive features (v = 4q .. 4q+3 of one accumulator) of one
+// token as one 8-byte (16-bit types) or 16-byte (fp32) write.
 template <int DT>
-__device__ __forceinline__ typename Raw8<DT>::T load_raw8(const TE<DT>* p) {
+__device__ __forceinline__ void store4(TE<DT>* p, float a, float b, float c, float d) {
   if constexpr (DT == DT_F32) {
-    const f4v* q = reinterpret_cast<const f4v*>(p);
-    f4v a = q[0], b = q[1];
-    f8 c;
-    c[0] = a[0]; c[1] = a[1]; c[2] = a[2]; c[3] = a[3];
-    c[4] = b[0]; c[5] = b[1]; c[6] = b[2]; c[7] = b[3];
-    return c;
+    f4v v = {a, b, c, d};
+    *reinterpret_cast<f4v*>(p) = v;
   } else {
-    return *reinterpret_cast<const u4v*>(p);
+    const uint32_t lo = static_cast<uint32_t>(from_f32<DT>(a)) | (static_cast<uint32_t>(from_f32<DT>(b)) << 16);
+    const uint32_t hi = static_cast<uint32_t>(from_f32<DT>(c)) | (static_cast<uint32_t>(from_f32<DT>(d)) << 16);
+    uint2 v;
+    v.x = lo;
+    v.y = hi;
+    *reinterpret_cast<uint2*>(p) = v;
   }
 }
 
-// Convert a raw chunk of type SRC to an MFMA chunk of type TY.
-template <int SRC, int TY>
-__device__ __forceinline__ typename Chunk<TY>::T convert8(const typename Raw8<SRC>::T& r) {
-  if constexpr (SRC == TY) {
-    return r;
-  } else if constexpr (SRC == DT_F32) {
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = r[i];
-    return chunk_from_f32<TY>(v);
-  } else {
-    static_assert(SRC == DT_BF16 && TY == DT_F16, "unsupported activation/MFMA type pair");
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint16_t b = static_cast<uint16_t>((r[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      v[i] = bf16_bits_to_f32(b);
-    }
-    return chunk_from_f32<TY>(v);
-  }
+template <int TY, int RT>
+constexpr size_t tbuf_bytes() {
+  return (size_t)2 * RT * 4 * 64 * sizeof(FragT<TY>);
 }
 
-// A-operand loader over rows of a [rows][ld] matrix of type SRC, staged to
-// LDS as type TY.  fetch() only issues the loads; store() converts, zeroes
-// rows past the tile's end and writes LDS, so no instruction waits on a
-// load until the stage's MFMAs have been issued.  GATHER: row r of the tile
-// is token garow[row0 + r] / kg of X (stride d); otherwise rows row0 + r of
-// base (stride ld).
-template <int SRC, int TY, int BM, int BK, bool GATHER>
-struct ALoader {
-  static constexpr int CPT = BM * BK / 8 / 256;
-  static constexpr int AST = BK + APAD;
-  using Raw = typename Raw8<SRC>::T;
-  const TE<SRC>* rowp[CPT];
-  int lofs[CPT];
-  bool ok[CPT];
-  __device__ void init(const TE<SRC>* base, long ld, const int* garow, int kg, int row0, int m0,
-                       int M) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      const int lr = c / (BK / 8);
-      const int kc = c % (BK / 8);
-      lofs[j] = lr * AST + kc * 8;
-      ok[j] = m0 + lr < M;
-      const int r = row0 + (ok[j] ? lr : 0);
-      const long src_row = GATHER ? (long)(garow[r] / kg) : (long)r;
-      rowp[j] = base + src_row * ld + kc * 8;
-    }
-  }
-  __device__ void fetch(int kt, Raw (&r)[CPT]) const {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) r[j] = load_raw8<SRC>(rowp[j] + kt * BK);
-  }
-  __device__ void store(const Raw (&r)[CPT], TE<TY>* buf) const {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const typename Chunk<TY>::T c = convert8<SRC, TY>(r[j]);
-      store_chunk<TY>(buf + lofs[j], ok[j] ? c : zero_chunk<TY>());
-    }
-  }
-};
-
-// ------------------------------------------------------ B-operand loaders --
-// Each loader has load(ks, cb) -> Raw (loads only) and decode(Raw) -> Frag.
-
-// Fragment-major matrix of type TY: block nb0 + cb, k-step ks.
-template <int TY>
-struct BFrag {
-  using Raw = typename Frag<TY>::T;
-  const TE<TY>* base;
-  int KS, nb0, lane;
-  __device__ Raw load(int ks, int cb) const {
-    return load_frag<TY>(base + ((long)((nb0 + cb) * KS + ks) * 64 + lane) * 8);
-  }
-  __device__ typename Frag<TY>::T decode(const Raw& r) const { return r; }
-};
-
-// INT4 fragment-major factor with one scale per lane (blocks along k):
-// scales [N/32][Kd/32][32].
-template <int TY>
-struct BInt4K {
-  struct Raw {
-    uint32_t word;
-    uint16_t sc;
-  };
-  const uint32_t* words;
-  const uint16_t* scales;
-  int KS, nb0, lane;
-  __device__ Raw load(int ks, int cb) const {
-    const int nb = nb0 + cb;
-    Raw r;
-    r.word = words[(long)(nb * KS + ks) * 64 + lane];
-    r.sc = scales[((long)nb * (KS / 2) + (ks >> 1)) * 32 + (lane & 31)];
-    return r;
-  }
-  __device__ typename Frag<TY>::T decode(const Raw& r) const {
-    return int4_frag_1scale<TY>(r.word, f16_bits_to_f32(r.sc));
-  }
-};
-
-// INT4 residual tail of the down projection (k-step kt = expert kt of the
-// group, blocks along n): 8 scales per lane, scales [E][d/32][16].
-template <int TY>
-struct BInt4Tail {
-  struct Raw {
-    uint32_t word;
-    u4v sc;
-  };
-  const uint32_t* words;
-  const uint16_t* scales;  // of expert g*K
-  int KS, nb0, lane, K, nd32;
-  __device__ Raw load(int kt, int cb) const {
-    const int nb = nb0 + cb;
-    const int je = kt < K ? kt : K - 1;  // padding steps hold zero codes
-    Raw r;
-    r.word = words[(long)(nb * KS + kt) * 64 + lane];
-    r.sc = *reinterpret_cast<const u4v*>(scales + ((long)je * nd32 + nb) * RPAD + 8 * (lane >> 5));
-    return r;
-  }
-  __device__ typename Frag<TY>::T decode(const Raw& r) const {
-    return int4_frag_8scale<TY>(r.word, r.sc);
-  }
-};
-
-// ------------------------------------------------------------- mainloop --
-// KS_total 16-deep k-steps (a multiple of BK / 16) in stages of BK.  Two
-// register sets for B and two LDS buffers for A alternate (the loop body is
-// unrolled by two so no set is copied): the loads of stage kt+1 are issued
-// before stage kt's MFMAs, and their conversion, decoding and LDS stores
-// come after, so the load latency overlaps the stage's MFMAs.
-template <int TY, int BM, int BK, class AL, class BL>
-__device__ __forceinline__ void mainloop_stage(int kt, int KT, const AL& al, const BL& bl,
-                                               f16v (&acc)[BM / 32][2], TE<TY>* As, int lane,
-                                               typename AL::Raw (&regs)[AL::CPT],
-                                               const typename BL::Raw (&bcur)[BK / 16][2],
-                                               typename BL::Raw (&bnext)[BK / 16][2]) {
-  constexpr int RB = BM / 32;
-  constexpr int KSS = BK / 16;
-  constexpr int AST = BK + APAD;
-  using Fr = typename Frag<TY>::T;
-  const int kn = (kt + 1 < KT) ? kt + 1 : kt;  // the last stage re-reads itself
-  al.fetch(kn, regs);
-#pragma unroll
-  for (int ks = 0; ks < KSS; ++ks)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) bnext[ks][cb] = bl.load(kn * KSS + ks, cb);
-  // keep the next stage's loads ahead of this stage's MFMAs (left alone,
-  // the scheduler sinks them next to their uses and the latency shows)
-  __builtin_amdgcn_sched_barrier(0);
-  const TE<TY>* buf = As + (kt & 1) * BM * AST;
-#pragma unroll
-  for (int ks = 0; ks < KSS; ++ks) {
-    Fr af[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      af[rb] = load_frag<TY>(buf + (rb * 32 + (lane & 31)) * AST + ks * 16 + 8 * (lane >> 5));
-    Fr bf[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) bf[cb] = bl.decode(bcur[ks][cb]);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma32<TY>(af[rb], bf[cb], acc[rb][cb]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  al.store(regs, As + ((kt + 1) & 1) * BM * AST);
-  __syncthreads();
-}
-
-template <int TY, int BM, int BK, class AL, class BL>
-__device__ __forceinline__ void mainloop(int KS_total, const AL& al, const BL& bl,
-                                         f16v (&acc)[BM / 32][2], TE<TY>* As, int lane) {
-  constexpr int KSS = BK / 16;
-  const int KT = KS_total / KSS;
-  typename AL::Raw regs[AL::CPT];
-  typename BL::Raw b0[KSS][2], b1[KSS][2];
-  al.fetch(0, regs);
-#pragma unroll
-  for (int ks = 0; ks < KSS; ++ks)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) b0[ks][cb] = bl.load(ks, cb);
-  al.store(regs, As);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    mainloop_stage<TY, BM, BK>(kt, KT, al, bl, acc, As, lane, regs, b0, b1);
-    mainloop_stage<TY, BM, BK>(kt + 1, KT, al, bl, acc, As, lane, regs, b1, b0);
-  }
-  if (kt < KT) mainloop_stage<TY, BM, BK>(kt, KT, al, bl, acc, As, lane, regs, b0, b1);
-}
-
-template <int BM>
-__device__ __forceinline__ void zero_acc(f16v (&acc)[BM / 32][2]) {
-#pragma unroll
-  for (int rb = 0; rb < BM / 32; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
+// Mainloop over the token operand TO (LDS-shared) and weight source WS
+// (direct), KT stages.
+template <int TY, int RT, class TO, class WS>
+__device__ __forceinline__ void run_tile(int KT, const TO& to, const WS& ws, int nb0, FragT<TY>* tl, int wave,
+                                         int lane, f16v (&acc)[RT][CB]) {
+  using WO = WDirect<WS, CB>;
+  WO wo;
+  wo.src = ws;
+  wo.nb0 = nb0;
+  using TSr = typename TO::Raw[TO::SEG][4];
+  using WRr = typename WO::Raw[CB][4];
+  Mainloop<TY, RT, CB, true, false, TO, WO> ml{to, wo, tl, nullptr, 0, wave, lane};
+  ml.template run<TSr, int, int, WRr>(KT, acc);
 }
 
 // ------------------------------------------------------------- U = X . A --
-template <int XT, int TY, int BM, int BK>
+template <int XT, int TY, int RT, bool INT4>
 __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
+  constexpr int BMT = 32 * RT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   TileCoord tc;
-  if (!map_tile(a.gcounts, a.G, BM, (a.NU + BN - 1) / BN, tc)) return;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.NU + BNF - 1) / BNF, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = tc.nt * BN + wave * 64;
-  const bool active = n0 < a.NU;
+  const int nbw = (tc.nt * BNF + wave * 64) / 32;
+  const bool active = nbw * 32 < a.NU;
+  const int nb0 = active ? nbw : a.NU / 32 - CB;  // idle wavefronts read a valid block
   const int row0 = a.goffsets[g] + m0;
-  TE<TY>* As = reinterpret_cast<TE<TY>*>(smem);
+  FragT<TY>* tl = reinterpret_cast<FragT<TY>*>(smem);
 
-  ALoader<XT, TY, BM, BK, true> al;
-  al.init(static_cast<const TE<XT>*>(a.X), a.d, a.garow, a.kg, row0, m0, M);
+  TShared<XT, TY, RT> to;
+  to.init(static_cast<const TE<XT>*>(a.X), a.d, [&](int blk, int r) -> long {
+    const int m = blk * 32 + r;
+    return m0 + m < M ? (long)(a.garow[row0 + m] / a.kg) : -1L;
+  });
+  f16v acc[RT][CB];
+  zero_acc<RT, CB>(acc);
   const int KS = a.d / 16;
-  const int nb0 = (active ? n0 : a.NU - 64) / 32;  // idle wavefronts read a valid block
-  f16v acc[BM / 32][2];
-  zero_acc<BM>(acc);
-  if (a.resid == RS_INT4) {
-    BInt4K<TY> bl{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride,
-                  KS, nb0, lane};
-    mainloop<TY, BM, BK>(KS, al, bl, acc, As, lane);
+  if constexpr (INT4) {
+    WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride, KS};
+    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);
   } else {
-    BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride, KS, nb0, lane};
-    mainloop<TY, BM, BK>(KS, al, bl, acc, As, lane);
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, KS};
+    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);
   }
   if (!active) return;
   TE<TY>* U = static_cast<TE<TY>*>(a.U);
 #pragma unroll
-  for (int rb = 0; rb < BM / 32; ++rb)
+  for (int t = 0; t < RT; ++t) {
+    const int m = t * 32 + (lane & 31);
+    if (m0 + m >= M) continue;
+    TE<TY>* urow = U + (long)(row0 + m) * a.NU + nb0 * 32 + 4 * (lane >> 5);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = rb * 32 + acc32_row(v, lane);
-        if (m0 + r < M) U[(long)(row0 + r) * a.NU + n0 + cb * 32 + (lane & 31)] = from_f32<TY>(acc[rb][cb][v]);
-      }
+      for (int q = 0; q < 4; ++q)
+        store4<TY>(urow + c * 32 + 8 * q, acc[t][c][4 * q], acc[t][c][4 * q + 1], acc[t][c][4 * q + 2],
+                   acc[t][c][4 * q + 3]);
+  }
 }
 
 // --------------------------------------------- G1: base GEMM + epilogue --
-// Per-expert operands of the G1 epilogue for one wavefront.
-template <int TY, int RB, int NF>
-struct ExpertOps {
-  typename Frag<TY>::T b[2];       // B_j fragments (gate, up) or (f-block 0, 1)
-  typename Frag<TY>::T u[RB][2];   // u_j = x A_j rows of this tile (gate, up)
-  typename Frag<TY>::T ad[NF];     // A_down,j fragments of this wavefront's f-blocks
-};
-
-template <int XT, int TY, int BM, int BK, int ACT>
+template <int XT, int TY, int RT, int ACT>
 __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
-  constexpr int RB = BM / 32;
-  constexpr int NF = (ACT == ACT_SWIGLU) ? 1 : 2;  // 32-column f-blocks per wavefront
+  constexpr int BMT = 32 * RT;
   constexpr int PIN = (ACT == ACT_SWIGLU) ? 2 : 1;
-  constexpr int HST = NF * 32 + 8;                  // LDS row stride of the h tile
-  constexpr int AST = BK + APAD;
-  using Fr = typename Frag<TY>::T;
+  constexpr int NFB = (ACT == ACT_SWIGLU) ? 1 : 2;  // f-blocks per wavefront
+  using F = FragT<TY>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int N = PIN * a.f;
   TileCoord tc;
-  if (!map_tile(a.gcounts, a.G, BM, (N + BN - 1) / BN, tc)) return;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (N + BNF - 1) / BNF, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n0 = tc.nt * BN + wave * 64;
-  const bool active = n0 < N;
+  const int nbw = (tc.nt * BNF + wave * 64) / 32;
+  const bool active = nbw * 32 < N;
+  const int nb0 = active ? nbw : N / 32 - CB;
+  // first f-block of this wavefront: SwiGLU interleaves gate and up blocks
+  const int fb0 = (ACT == ACT_SWIGLU) ? nb0 / 2 : nb0;
+  const int nfb = a.f / 32;
   const int row0 = a.goffsets[g] + m0;
-  const int K = a.K;
+  const int K = a.K, ke = a.ke;
+  const bool has_resid = a.resid != RS_NONE;
+  const bool int4 = a.resid == RS_INT4;
 
-  // LDS: [A tiles | h tiles] (aliased) | gate weights [BM][K] | slot of
-  // expert j in the row's chosen list [BM][K] | used flags [K] | partial
-  // V of the 4 wavefronts [4][BM][16]
-  const size_t abytes = sizeof(TE<TY>) * 2 * BM * AST;
-  const size_t hbytes = sizeof(TE<TY>) * 4 * BM * HST;
-  char* p = smem + (abytes > hbytes ? abytes : hbytes);
-  float* s_w = reinterpret_cast<float*>(p);
-  int* s_slot = reinterpret_cast<int*>(s_w + BM * K);
-  int* s_used = s_slot + BM * K;
-  float* s_red = reinterpret_cast<float*>(s_used + ((K + 3) & ~3));
-  TE<TY>* As = reinterpret_cast<TE<TY>*>(smem);
-  TE<TY>* Hs = reinterpret_cast<TE<TY>*>(smem) + wave * BM * HST;
+  // LDS: [token stages | V sums [BMT][ke][16] fp32] | gate weights [BMT][K] |
+  // slot of expert j in the row's chosen list [BMT][K] (int8) | used [K]
+  const size_t vbytes = (size_t)BMT * ke * RPAD * sizeof(float);
+  const size_t abytes = tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes;
+  float* s_v = reinterpret_cast<float*>(smem);
+  float* s_w = reinterpret_cast<float*>(smem + abytes);
+  int8_t* s_slot = reinterpret_cast<int8_t*>(s_w + BMT * K);
+  int* s_used = reinterpret_cast<int*>(s_slot + ((BMT * K + 15) & ~15));
+  F* tl = reinterpret_cast<F*>(smem);
 
-  for (int i = tid; i < BM * K; i += 256) {
+  for (int i = tid; i < BMT * K; i += 256) {
     s_w[i] = 0.f;
     s_slot[i] = -1;
   }
   for (int j = tid; j < K; j += 256) s_used[j] = 0;
   __syncthreads();
-  for (int i = tid; i < BM; i += 256) {
+  for (int i = tid; i < BMT; i += 256) {
     if (m0 + i < M) {
       const int aid = a.garow[row0 + i];
       const int t = aid / a.kg, ga = aid - t * a.kg;
-      for (int s = 0; s < a.ke; ++s) {
-        const int slot = t * a.k + ga * a.ke + s;
+      for (int s = 0; s < ke; ++s) {
+        const int slot = t * a.k + ga * ke + s;
         const int j = a.idx[slot] - g * K;
         s_w[i * K + j] = a.w[slot];
-        s_slot[i * K + j] = s;
+        s_slot[i * K + j] = static_cast<int8_t>(s);
         s_used[j] = 1;
       }
     }
   }
+  // (the main loop's first barrier publishes these tables)
 
-  ALoader<XT, TY, BM, BK, true> al;
-  al.init(static_cast<const TE<XT>*>(a.X), a.d, a.garow, a.kg, row0, m0, M);
-  const int KS = a.d / 16;
-  const int nb0 = (active ? n0 : N - 64) / 32;  // idle wavefronts read a valid block
-  BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride, KS, nb0, lane};
-  f16v acc[RB][2];
-  zero_acc<BM>(acc);
-  // first 32-column f-block of this wavefront
-  const int fb0 = (ACT == ACT_SWIGLU) ? n0 / 64 : n0 / 32;
-  const int nfb = a.f / 32;
-  f16v hbar[RB][NF];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < NF; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) hbar[rb][c][v] = 0.f;
+  TShared<XT, TY, RT> to;
+  to.init(static_cast<const TE<XT>*>(a.X), a.d, [&](int blk, int r) -> long {
+    const int m = blk * 32 + r;
+    return m0 + m < M ? (long)(a.garow[row0 + m] / a.kg) : -1L;
+  });
+  f16v acc[RT][CB];
+  zero_acc<RT, CB>(acc);
+  WPlain<TY> ws{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
+  run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);  // ends with a barrier
 
-  const bool has_resid = a.resid != RS_NONE;
-  const bool int4 = a.resid == RS_INT4;
+  if (has_resid) {
+    for (int i = tid; i < BMT * ke * RPAD; i += 256) s_v[i] = 0.f;
+    __syncthreads();
+  }
   const TE<TY>* Ub = static_cast<const TE<TY>*>(a.U);
+  TE<TY>* H = static_cast<TE<TY>*>(a.H);
+  const int h = lane >> 5;
 
-  // loads of expert j's epilogue operands (issued one expert ahead)
-  auto load_ops = [&](int j, ExpertOps<TY, RB, NF>& o) {
-    const int ex = g * K + j;
+  // (unrolled so the accumulators are indexed statically)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      // SwiGLU: c = projection (gate, up) of f-block fb0; GELU: f-block fb0 + c
-      const int pj = (ACT == ACT_SWIGLU) ? c : 0;
-      const int fb = (ACT == ACT_SWIGLU) ? fb0 : fb0 + c;
-      const long fr = (long)(ex * PIN + pj) * nfb + fb;
-      if (int4) {
-        const uint32_t word = static_cast<const uint32_t*>(a.B1)[fr * 64 + lane];
-        o.b[c] = int4_frag_8scale<TY>(word, *reinterpret_cast<const u4v*>(a.b1_scale + fr * RPAD + 8 * (lane >> 5)));
-      } else {
-        o.b[c] = load_frag<TY>(static_cast<const TE<TY>*>(a.B1) + (fr * 64 + lane) * 8);
-      }
-    }
+  for (int t = 0; t < RT; ++t) {
+    const int m = t * 32 + (lane & 31);  // this lane's token row in the tile
+    const bool valid = m0 + m < M;
+    const long urow = row0 + (valid ? m : 0);
+    float hbar[NFB][16];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r_lane = rb * 32 + (lane & 31);
-      const bool rv = m0 + r_lane < M;
-      const long urow = row0 + (rv ? r_lane : 0);
+    for (int c = 0; c < NFB; ++c)
 #pragma unroll
-      for (int c = 0; c < PIN; ++c) {
-        const Fr u = load_frag<TY>(Ub + urow * a.NU + (j * PIN + c) * RPAD + 8 * (lane >> 5));
-        o.u[rb][c] = rv ? u : zero_frag<TY>();
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < NF; ++c) {
-      const long fr = (long)ex * nfb + fb0 + c;
-      if (int4) {
-        const uint32_t word = static_cast<const uint32_t*>(a.Ad)[fr * 64 + lane];
-        o.ad[c] = int4_frag_1scale<TY>(word, f16_bits_to_f32(a.ad_scale[fr * RPAD + (lane & 15)]));
-      } else {
-        o.ad[c] = load_frag<TY>(static_cast<const TE<TY>*>(a.Ad) + (fr * 64 + lane) * 8);
-      }
-    }
-  };
-  auto next_used = [&](int j) {
-    while (j < K && !s_used[j]) ++j;
-    return j;
-  };
+      for (int v = 0; v < 16; ++v) hbar[c][v] = 0.f;
 
-  // the first expert's operands do not depend on the main loop: their
-  // loads are in flight during it
-  ExpertOps<TY, RB, NF> cur, nxt;
-  __syncthreads();  // s_used is complete
-  int j = next_used(0);
-  if (has_resid && active && j < K) load_ops(j, cur);
-  mainloop<TY, BM, BK>(KS, al, bl, acc, As, lane);  // ends with a barrier
-
-  while (j < K) {
-    const int jn = next_used(j + 1);
-    if (has_resid && active && jn < K) load_ops(jn, nxt);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this expert's work
-    if (active) {
+    for (int j = 0; j < K && active; ++j) {
+      if (!s_used[j]) continue;
+      const float wgt = s_w[m * K + j];
+      if (!__any(wgt != 0.f)) continue;  // no token of this block picked j
+      const int ex = g * K + j;
+      f16v z[CB];
+      if (has_resid) {
+        // z_j = Z + u_j B_j^T: one 16-deep MFMA step per feature block
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f16v z[2];
-        if (has_resid) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) z[c] = mfma32<TY>(cur.u[rb][(ACT == ACT_SWIGLU) ? c : 0], cur.b[c], acc[rb][c]);
-        } else {
-          z[0] = acc[rb][0];
-          z[1] = acc[rb][1];
+        for (int c = 0; c < CB; ++c) {
+          const int pj = (ACT == ACT_SWIGLU) ? c : 0;
+          const int fb = (ACT == ACT_SWIGLU) ? fb0 : fb0 + c;
+          const long fr = (long)(ex * PIN + pj) * nfb + fb;
+          F bfr;
+          if (int4) {
+            const uint32_t word = static_cast<const uint32_t*>(a.B1)[fr * 64 + lane];
+            bfr = int4_frag_8scale<TY>(word, *reinterpret_cast<const u4v*>(a.b1_scale + fr * RPAD + 8 * h));
+          } else {
+            bfr = static_cast<const F*>(a.B1)[fr * 64 + lane];
+          }
+          const F ufr = *reinterpret_cast<const F*>(Ub + urow * a.NU + (j * PIN + pj) * RPAD + 8 * h);
+          z[c] = mfma32<TY>(bfr, ufr, acc[t][c]);
         }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CB; ++c) z[c] = acc[t][c];
+      }
+      float hw[NFB][16];
+      if constexpr (ACT == ACT_SWIGLU) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = rb * 32 + acc32_row(v, lane);
-          const float wgt = s_w[r * K + j];
-          if constexpr (ACT == ACT_SWIGLU) {
-            float hw = 0.f;
-            // the two rows this register holds: skip when neither picked j
-            if (__any(wgt != 0.f)) {
-              const float h = silu_f(z[0][v]) * z[1][v];
-              hw = (wgt != 0.f) ? wgt * h : 0.f;
-            }
-            hbar[rb][0][v] += hw;
-            if (has_resid) Hs[r * HST + (lane & 31)] = from_f32<TY>(hw);
-          } else {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              float hw = 0.f;
-              if (wgt != 0.f) hw = wgt * gelu_tanh_f(z[c][v]);
-              hbar[rb][c][v] += hw;
-              if (has_resid) Hs[r * HST + c * 32 + (lane & 31)] = from_f32<TY>(hw);
-            }
-          }
+          hw[0][v] = wgt * (silu_f(z[0][v]) * z[1][v]);
+          hbar[0][v] += hw[0][v];
         }
-      }
-    }
-    if (has_resid) {
-      __syncthreads();
-      // (w_j h_j)[row, this wavefront's f] . A_down,j[f, :], summed over the
-      // 4 wavefronts in LDS: one partial per (column tile, row, slot)
+      } else {
 #pragma unroll
-      for (int mb = 0; mb < BM / 16; ++mb) {
-        f4v vacc = {0.f, 0.f, 0.f, 0.f};
-        if (active) {
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int c = 0; c < NF; ++c) {
-            const Fr hf = load_frag<TY>(Hs + (mb * 16 + (lane & 15)) * HST + c * 32 + 8 * (lane >> 4));
-            vacc = mfma16<TY>(hf, cur.ad[c], vacc);
+          for (int v = 0; v < 16; ++v) {
+            hw[c][v] = wgt * gelu_tanh_f(z[c][v]);
+            hbar[c][v] += hw[c][v];
           }
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          s_red[(wave * BM + mb * 16 + acc16_row(v, lane)) * RPAD + (lane & 15)] = vacc[v];
       }
-      __syncthreads();
-      for (int e = tid; e < BM * RPAD; e += 256) {
-        const int r = e / RPAD, rho = e % RPAD;
-        const int sl = s_slot[r * K + j];
+      if (has_resid) {
+        // V^T[rho, token] = sum over this wavefront's features of
+        // A_down[f, rho] (w h)[token, f]: the accumulator rows a lane holds
+        // are the k of the MFMA, in the order the A_down operand was packed
+        f16v vacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) vacc[v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NFB; ++c)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const long fr = ((long)ex * nfb + fb0 + c) * 2 + st;
+            F afr;
+            if (int4) {
+              const uint32_t word = static_cast<const uint32_t*>(a.Ad)[fr * 64 + lane];
+              const int rho = lane & 31;
+              const float sc = rho < RPAD ? f16_bits_to_f32(a.ad_scale[(fr >> 1) * RPAD + rho]) : 0.f;
+              afr = int4_frag_1scale<TY>(word, sc);
+            } else {
+              afr = static_cast<const F*>(a.Ad)[fr * 64 + lane];
+            }
+            const F hfr = to_frag<TY>(&hw[c][8 * st]);  // hw is a plain float array
+            vacc = mfma32<TY>(afr, hfr, vacc);
+          }
+        const int sl = s_slot[m * K + j];
         if (sl >= 0) {
-          const float sum = (s_red[e] + s_red[BM * RPAD + e]) +
-                            (s_red[2 * BM * RPAD + e] + s_red[3 * BM * RPAD + e]);
-          a.Vp[(((long)tc.nt * a.vp_rows + row0 + r) * a.ke + sl) * RPAD + rho] = sum;
+          float* dst = s_v + ((long)m * ke + sl) * RPAD;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) atomicAdd(dst + acc_feat(v, lane), vacc[v]);
         }
       }
-      __syncthreads();
     }
-    cur = nxt;
-    j = jn;
+    if (active && valid) {  // (idle wavefronts computed nothing above)
+      TE<TY>* hrow = H + (long)(row0 + m) * a.f + 4 * h;
+#pragma unroll
+      for (int c = 0; c < NFB; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store4<TY>(hrow + (fb0 + c) * 32 + 8 * q, hbar[c][4 * q], hbar[c][4 * q + 1], hbar[c][4 * q + 2],
+                     hbar[c][4 * q + 3]);
+    }
   }
-  if (!active) return;
-  TE<TY>* H = static_cast<TE<TY>*>(a.H);
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < NF; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = rb * 32 + acc32_row(v, lane);
-        if (m0 + r < M) H[(long)(row0 + r) * a.f + (fb0 + c) * 32 + (lane & 31)] = from_f32<TY>(hbar[rb][c][v]);
-      }
+  if (has_resid) {
+    __syncthreads();
+    // one partial per (column tile, row, slot), summed by vreduce
+    const int per_row = ke * RPAD;
+    for (int e = tid; e < BMT * per_row; e += 256) {
+      const int r = e / per_row;
+      if (m0 + r < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + r) * per_row + (e - r * per_row)] = s_v[e];
+    }
+  }
 }
 
 // ---------------------------------------------- G2: down projection ------
-template <int XT, int TY, int BM, int BK>
+// Grid: tiles x S k-splits (split s = logical workgroup % S takes stages
+// [s KT / S, (s+1) KT / S) of the base part; split 0 also runs the residual
+// tail).  One split and one group per token: Y is written directly;
+// otherwise fp32 partials ypart[s][t*kg + ga][d] for the combine kernel.
+template <int XT, int TY, int RT, bool INT4>
 __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
+  constexpr int BMT = 32 * RT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (blockIdx.x == 0 && a.zero_ptr) {
     for (int i = threadIdx.x; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
   }
+  const int S = a.ksplit;
+  const int split = blockIdx.x % S;
   TileCoord tc;
-  if (!map_tile(a.gcounts, a.G, BM, (a.d + BN - 1) / BN, tc)) return;
+  if (!map_tile(blockIdx.x / S, a.gcounts, a.G, BMT, (a.d + BNF - 1) / BNF, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = tc.nt * BN + wave * 64;
-  const bool active = n0 < a.d;
+  const int nbw = (tc.nt * BNF + wave * 64) / 32;
+  const bool active = nbw * 32 < a.d;
+  const int nb0 = active ? nbw : a.d / 32 - CB;
   const int row0 = a.goffsets[g] + m0;
-  TE<TY>* As = reinterpret_cast<TE<TY>*>(smem);
+  FragT<TY>* tl = reinterpret_cast<FragT<TY>*>(smem);
 
-  const int KSm = a.f / 16;       // k-steps of the base part
-  const int KSt = a.NV / 16;      // k-steps of the residual tail
-  const int nb0 = (active ? n0 : a.d - 64) / 32;  // idle wavefronts read a valid block
-  const int nd32 = a.d / 32;
-  f16v acc[BM / 32][2];
-  zero_acc<BM>(acc);
+  f16v acc[RT][CB];
+  zero_acc<RT, CB>(acc);
+  const int KT = a.f / KB;
+  const int k0 = split * KT / S, k1 = (split + 1) * KT / S;
+  auto rows = [&](int blk, int r) -> long {
+    const int m = blk * 32 + r;
+    return m0 + m < M ? (long)(row0 + m) : -1L;
+  };
   {
-    // hbar . W2_base^g
-    ALoader<TY, TY, BM, BK, false> al;
-    al.init(static_cast<const TE<TY>*>(a.H), a.f, nullptr, 1, row0, m0, M);
-    BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bw) + g * a.bw_gstride, KSm, nb0, lane};
-    mainloop<TY, BM, BK>(KSm, al, bl, acc, As, lane);
+    // hbar . W2_base^g over this split's stages
+    TShared<TY, TY, RT> to;
+    to.init(static_cast<const TE<TY>*>(a.H) + (long)k0 * KB, a.f, rows);
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8 + (long)k0 * 4 * 64, a.f / 16};
+    run_tile<TY, RT>(k1 - k0, to, ws, nb0, tl, wave, lane, acc);
   }
-  if (KSt > 0) {
-    // + V . [B_down,j^T]_j : one 16-deep k-step per expert of the group
-    ALoader<DT_F32, TY, BM, 64, false> al;
-    al.init(a.V, a.NV, nullptr, 1, row0, m0, M);
-    if (a.resid == RS_INT4) {
-      BInt4Tail<TY> bl{static_cast<const uint32_t*>(a.Bd) + g * a.bd_gstride,
-                       a.bd_scale + (long)g * a.K * nd32 * RPAD, KSt, nb0, lane, a.K, nd32};
-      mainloop<TY, BM, 64>(KSt, al, bl, acc, As, lane);
+  if (a.NV > 0 && split == 0) {
+    // + V . [B_down,j^T]_j : 16 residual k per expert of the group
+    TShared<TY, TY, RT> to;
+    to.init(static_cast<const TE<TY>*>(a.V), a.NV, rows);
+    const int KS = a.NV / 16;
+    if constexpr (INT4) {
+      WInt4Tail<TY> ws{static_cast<const uint32_t*>(a.Bd) + g * a.bd_gstride,
+                       a.bd_scale + (long)g * a.K * (a.d / 32) * RPAD, KS, a.K, a.d / 32};
+      run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, wave, lane, acc);
     } else {
-      BFrag<TY> bl{static_cast<const TE<TY>*>(a.Bd) + g * a.bd_gstride, KSt, nb0, lane};
-      mainloop<TY, BM, 64>(KSt, al, bl, acc, As, lane);
+      WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bd) + g * a.bd_gstride / 8, KS};
+      run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, wave, lane, acc);
     }
   }
   if (!active) return;
+  const bool direct = a.kg == 1 && S == 1;
 #pragma unroll
-  for (int rb = 0; rb < BM / 32; ++rb)
+  for (int t = 0; t < RT; ++t) {
+    const int m = t * 32 + (lane & 31);
+    if (m0 + m >= M) continue;
+    const long aid = a.garow[row0 + m];
+    const int n = nb0 * 32 + 4 * (lane >> 5);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = rb * 32 + acc32_row(v, lane);
-      if (m0 + r >= M) continue;
-      const int aid = a.garow[row0 + r];
+    for (int c = 0; c < CB; ++c)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int n = n0 + cb * 32 + (lane & 31);
-        if (a.kg == 1) {
-          static_cast<TE<XT>*>(a.Y)[(long)aid * a.d + n] = from_f32<XT>(acc[rb][cb][v]);
+      for (int q = 0; q < 4; ++q) {
+        const float v0 = acc[t][c][4 * q], v1 = acc[t][c][4 * q + 1];
+        const float v2 = acc[t][c][4 * q + 2], v3 = acc[t][c][4 * q + 3];
+        if (direct) {
+          store4<XT>(static_cast<TE<XT>*>(a.Y) + aid * a.d + n + c * 32 + 8 * q, v0, v1, v2, v3);
         } else {
-          a.ypart[(long)aid * a.d + n] = acc[rb][cb][v];
+          store4<DT_F32>(a.ypart + ((long)split * a.rows_total + aid) * a.d + n + c * 32 + 8 * q, v0, v1, v2, v3);
         }
       }
-    }
+  }
 }
 
 // ----------------------------------------------------------------- V sum --
 // V[row, j*16 + rho] = sum over G1 column tiles of the partial for the slot
 // of expert j in the row's chosen list; zero for experts the row did not
-// pick.  One block of 256 threads per 16 rows.
+// pick.  V is stored in the MFMA type: the down projection's residual tail
+// would round it to that type on load anyway.  One block of 256 threads per
+// 16 rows.
+template <int TY>
 __global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
+  TE<TY>* V = static_cast<TE<TY>*>(a.V);
   const int row_base = blockIdx.x * 16;
   const int nrow = min(16, a.rows - row_base);
   if (nrow <= 0) return;
-  for (int e = threadIdx.x; e < nrow * a.NV; e += 256) a.V[(long)row_base * a.NV + e] = 0.f;
+  for (int e = threadIdx.x; e < nrow * a.NV; e += 256) V[(long)row_base * a.NV + e] = from_f32<TY>(0.f);
   __syncthreads();
   const int per_row = a.ke * RPAD;
   for (int e = threadIdx.x; e < nrow * per_row; e += 256) {
@@ -675,90 +454,84 @@ __global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
     const int g = a.gidx[aid];
     const int j = a.idx[t * a.k + ga * a.ke + sl] - g * a.K;
     float sum = 0.f;
-    for (int nt = 0; nt < a.ntiles; ++nt)
-      sum += a.Vp[(((long)nt * a.vp_rows + row) * a.ke + sl) * RPAD + rho];
-    a.V[(long)row * a.NV + j * RPAD + rho] = sum;
+    for (int nt = 0; nt < a.ntiles; ++nt) sum += a.Vp[(((long)nt * a.vp_rows + row) * a.ke + sl) * RPAD + rho];
+    V[(long)row * a.NV + j * RPAD + rho] = from_f32<TY>(sum);
   }
 }
 
 // ---------------------------------------------------------------- combine --
+// Y[t] = sum over k splits s and chosen groups ga of ypart[s][t*kg + ga].
 template <int XT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const long n4 = (long)a.T * a.d / 4;
+  const long stride = (long)a.T * a.kg * a.d;
   for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
     const long t = (i * 4) / a.d, c = (i * 4) % a.d;
-    f4v s = *reinterpret_cast<const f4v*>(a.ypart + (t * a.kg) * a.d + c);
-    for (int ga = 1; ga < a.kg; ++ga) {
-      f4v v = *reinterpret_cast<const f4v*>(a.ypart + (t * a.kg + ga) * a.d + c);
-      s += v;
-    }
-    TE<XT>* Y = static_cast<TE<XT>*>(a.Y) + t * a.d + c;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) Y[q] = from_f32<XT>(s[q]);
+    f4v s = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < a.ksplit; ++sp)
+      for (int ga = 0; ga < a.kg; ++ga) {
+        const f4v v = *reinterpret_cast<const f4v*>(a.ypart + sp * stride + (t * a.kg + ga) * a.d + c);
+        s += v;
+      }
+    store4<XT>(static_cast<TE<XT>*>(a.Y) + t * a.d + c, s[0], s[1], s[2], s[3]);
   }
 }
 
 // ------------------------------------------------ debug: residual decode --
-// kind 0: fragment-major 32x16 blocks (N = n rows of the factor's column
-// space); kind 1: B1 / Bd layouts (8 scales per lane); kind 2: Ad layout.
-// Writes values [n][r] of one factor.
+// Decodes one stored factor [n][r] back to values, reading the layouts the
+// kernels use: kind 0 At (columns aux0 + rho, k = row permuted, KS = aux1),
+// kind 1 B1 (column = row, k = rho, plain 16-deep step), kind 2 Ad,
+// kind 3 Bd (column = row, k = aux0 * 16 + rho permuted, KS = aux1).
+__device__ __forceinline__ void perm_pos(int k, int& ks, int& h, int& e) {
+  ks = (k >> 6) * 4 + ((k & 31) >> 3);
+  h = (k & 63) >> 5;
+  e = k & 7;
+}
+
 template <int TY>
-__global__ void debug_decode_kernel(int resid, int kind, const void* src, const uint16_t* scales,
-                                    long base, long sbase, int n, int r, int aux0, int aux1,
-                                    float* out) {
+__global__ void debug_decode_kernel(int resid, int kind, const void* src, const uint16_t* scales, long base,
+                                    long sbase, int n, int r, int aux0, int aux1, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;  // entry index i = row * r + rho
   if (i >= n * r) return;
   const int row = i / r, rho = i % r;
+  const bool q4 = resid == RS_INT4;
   float val = 0.f;
+  long fo = 0;  // fragment (word) index
+  int e = 0;
+  float sc = 0.f;
   if (kind == 0) {
-    // At: column n_col = aux0 + rho, k = row; KS = aux1 (= d/16)
     const int ncol = aux0 + rho, k = row;
-    const int nb = ncol / 32, ks = k / 16, ln = (ncol % 32) + 32 * ((k % 16) / 8), e = k % 8;
-    const long fo = (long)(nb * aux1 + ks) * 64 + ln;
-    if (resid == RS_INT4) {
-      const uint32_t word = static_cast<const uint32_t*>(src)[base + fo];
-      const float sc = f16_bits_to_f32(scales[sbase + ((long)nb * (aux1 / 2) + ks / 2) * 32 + (ncol % 32)]);
-      val = int4_value(word, e, sc);
-    } else {
-      val = load_as_f32<TY>(static_cast<const TE<TY>*>(src), (base + fo) * 8 + e);
-    }
+    int ks, h;
+    perm_pos(k, ks, h, e);
+    fo = (long)((ncol / 32) * aux1 + ks) * 64 + (ncol % 32) + 32 * h;
+    if (q4) sc = f16_bits_to_f32(scales[sbase + ((long)(ncol / 32) * (aux1 / 2) + k / 32) * 32 + (ncol % 32)]);
   } else if (kind == 1) {
-    // B1/Bd: column = row (output index), k = aux0 * RPAD + rho; KS = aux1
-    const int ncol = row, k = aux0 * RPAD + rho;
-    const int nb = ncol / 32, ks = k / 16, ln = (ncol % 32) + 32 * ((k % 16) / 8), e = k % 8;
-    const long fo = (long)(nb * aux1 + ks) * 64 + ln;
-    if (resid == RS_INT4) {
-      const uint32_t word = static_cast<const uint32_t*>(src)[base + fo];
-      const float sc = f16_bits_to_f32(scales[sbase + (long)nb * RPAD + rho]);
-      val = int4_value(word, e, sc);
-    } else {
-      val = load_as_f32<TY>(static_cast<const TE<TY>*>(src), (base + fo) * 8 + e);
-    }
+    const int ncol = row, h = rho / 8;
+    e = rho % 8;
+    fo = (long)(ncol / 32) * 64 + (ncol % 32) + 32 * h;
+    if (q4) sc = f16_bits_to_f32(scales[sbase + (long)(ncol / 32) * RPAD + rho]);
+  } else if (kind == 2) {
+    const int fb = row / 32, w = row % 32, st = w / 16, rem = w % 16;
+    const int h = (rem >> 2) & 1;
+    e = (rem & 3) + 4 * (rem >> 3);
+    fo = ((long)fb * 2 + st) * 64 + rho + 32 * h;
+    if (q4) sc = f16_bits_to_f32(scales[sbase + (long)fb * RPAD + rho]);
   } else {
-    // Ad: k = row (f index), column rho
-    const int fb = row / 32, ln = rho + 16 * ((row % 32) / 8), e = row % 8;
-    const long fo = (long)fb * 64 + ln;
-    if (resid == RS_INT4) {
-      const uint32_t word = static_cast<const uint32_t*>(src)[base + fo];
-      const float sc = f16_bits_to_f32(scales[sbase + (long)fb * RPAD + rho]);
-      val = int4_value(word, e, sc);
-    } else {
-      val = load_as_f32<TY>(static_cast<const TE<TY>*>(src), (base + fo) * 8 + e);
-    }
+    const int ncol = row, k = aux0 * RPAD + rho;
+    int ks, h;
+    perm_pos(k, ks, h, e);
+    fo = (long)((ncol / 32) * aux1 + ks) * 64 + (ncol % 32) + 32 * h;
+    if (q4) sc = f16_bits_to_f32(scales[sbase + (long)(ncol / 32) * RPAD + rho]);
+  }
+  if (q4) {
+    val = int4_value(static_cast<const uint32_t*>(src)[base + fo], e, sc);
+  } else {
+    val = load_as_f32<TY>(static_cast<const TE<TY>*>(src), (base + fo) * 8 + e);
   }
   out[i] = val;
 }
 
 // ---------------------------------------------------------------- launch --
-size_t gemm_lds(int kind, int ty, int bm, int bk, int K) {
-  const size_t es = ty == DT_F32 ? 4 : 2;
-  const size_t abytes = es * 2 * bm * (bk + APAD);
-  if (kind != GK_G1) return abytes;
-  const size_t hbytes = es * 4 * bm * (2 * 32 + 8);
-  return (abytes > hbytes ? abytes : hbytes) + (sizeof(float) + sizeof(int)) * bm * K +
-         sizeof(int) * ((K + 3) & ~3) + sizeof(float) * 4 * bm * RPAD + 64;
-}
-
 template <class KF>
 hipError_t go(KF kfn, dim3 grid, size_t lds, const GemmArgs& a, hipStream_t st) {
   if (lds > 65536) {
@@ -770,63 +543,74 @@ hipError_t go(KF kfn, dim3 grid, size_t lds, const GemmArgs& a, hipStream_t st) 
   return hipGetLastError();
 }
 
-template <int XT, int TY, int BM, int BK>
-hipError_t launch_t(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
-  const size_t lds = gemm_lds(kind, TY, BM, BK, a.K);
+template <int XT, int TY, int RT>
+hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = gemm_lds(kind, TY, RT * 32, a.K, a.ke);
+  const bool int4 = a.resid == RS_INT4;
   switch (kind) {
-    case GK_U: return go(ugemm_kernel<XT, TY, BM, BK>, grid, lds, a, st);
+    case GK_U:
+      if (int4) return go(ugemm_kernel<XT, TY, RT, true>, grid, lds, a, st);
+      return go(ugemm_kernel<XT, TY, RT, false>, grid, lds, a, st);
     case GK_G1:
-      if (a.act == ACT_SWIGLU) return go(gemm1_kernel<XT, TY, BM, BK, ACT_SWIGLU>, grid, lds, a, st);
-      return go(gemm1_kernel<XT, TY, BM, BK, ACT_GELU>, grid, lds, a, st);
-    case GK_G2: return go(gemm2_kernel<XT, TY, BM, BK>, grid, lds, a, st);
+      if (a.act == ACT_SWIGLU) return go(gemm1_kernel<XT, TY, RT, ACT_SWIGLU>, grid, lds, a, st);
+      return go(gemm1_kernel<XT, TY, RT, ACT_GELU>, grid, lds, a, st);
+    case GK_G2:
+      if (int4) return go(gemm2_kernel<XT, TY, RT, true>, grid, lds, a, st);
+      return go(gemm2_kernel<XT, TY, RT, false>, grid, lds, a, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <int XT, int TY>
-hipError_t launch_bm(int kind, int bm, int bk, const GemmArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_types(int kind, int bm, const GemmArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (TY == DT_F32) {
     // fp32 fragments are twice as large: small tiles only
-    if (bk != 64) return hipErrorInvalidValue;
     switch (bm) {
-      case 32: return launch_t<XT, TY, 32, 64>(kind, a, grid, st);
-      case 64: return launch_t<XT, TY, 64, 64>(kind, a, grid, st);
+      case 32: return launch_rt<XT, TY, 1>(kind, a, grid, st);
+      case 64: return launch_rt<XT, TY, 2>(kind, a, grid, st);
     }
-    return hipErrorInvalidValue;
   } else {
-    if (bk == 64) {
-      switch (bm) {
-        case 32: return launch_t<XT, TY, 32, 64>(kind, a, grid, st);
-        case 64: return launch_t<XT, TY, 64, 64>(kind, a, grid, st);
-        case 128: return launch_t<XT, TY, 128, 64>(kind, a, grid, st);
-      }
-    } else if (bk == 128) {
-      switch (bm) {
-        case 32: return launch_t<XT, TY, 32, 128>(kind, a, grid, st);
-        case 64: return launch_t<XT, TY, 64, 128>(kind, a, grid, st);
-        case 128: return launch_t<XT, TY, 128, 128>(kind, a, grid, st);
-      }
+    switch (bm) {
+      case 32: return launch_rt<XT, TY, 1>(kind, a, grid, st);
+      case 64: return launch_rt<XT, TY, 2>(kind, a, grid, st);
+      case 128: return launch_rt<XT, TY, 4>(kind, a, grid, st);
+      case 256: return launch_rt<XT, TY, 8>(kind, a, grid, st);
     }
-    return hipErrorInvalidValue;
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, int bk, const GemmArgs& a,
-                       int max_mtiles, int ntiles, hipStream_t st) {
+size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
+  const size_t fb = ty == DT_F32 ? 32 : 16;
+  const size_t tbytes = 2 * (size_t)(bm / 32) * 4 * 64 * fb;
+  if (kind != GK_G1) return tbytes;
+  const size_t vbytes = (size_t)bm * ke * RPAD * sizeof(float);
+  return (tbytes > vbytes ? tbytes : vbytes) + sizeof(float) * bm * K + (((size_t)bm * K + 15) & ~(size_t)15) +
+         sizeof(int) * K + 64;
+}
+
+hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a, int max_mtiles,
+                       int ntiles, int splits, hipStream_t st) {
   if (max_mtiles <= 0 || ntiles <= 0) return hipSuccess;
-  dim3 grid((unsigned)max_mtiles * (unsigned)ntiles);
-  if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_bm<DT_F32, DT_F32>(kind, bm, bk, a, grid, st);
-  if (x_dtype == DT_F16 && mma_dtype == DT_F16) return launch_bm<DT_F16, DT_F16>(kind, bm, bk, a, grid, st);
-  if (x_dtype == DT_BF16 && mma_dtype == DT_BF16) return launch_bm<DT_BF16, DT_BF16>(kind, bm, bk, a, grid, st);
-  if (x_dtype == DT_BF16 && mma_dtype == DT_F16) return launch_bm<DT_BF16, DT_F16>(kind, bm, bk, a, grid, st);
+  dim3 grid((unsigned)max_mtiles * (unsigned)ntiles * (unsigned)splits);
+  if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_types<DT_F32, DT_F32>(kind, bm, a, grid, st);
+  if (x_dtype == DT_F16 && mma_dtype == DT_F16) return launch_types<DT_F16, DT_F16>(kind, bm, a, grid, st);
+  if (x_dtype == DT_BF16 && mma_dtype == DT_BF16) return launch_types<DT_BF16, DT_BF16>(kind, bm, a, grid, st);
+  if (x_dtype == DT_BF16 && mma_dtype == DT_F16) return launch_types<DT_BF16, DT_F16>(kind, bm, a, grid, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_vreduce(const VReduceArgs& a, hipStream_t st) {
+hipError_t launch_vreduce(int mma_dtype, const VReduceArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(vreduce_kernel, dim3((a.rows + 15) / 16), dim3(256), 0, st, a);
+  const dim3 grid((a.rows + 15) / 16);
+  switch (mma_dtype) {
+    case DT_F32: hipLaunchKernelGGL(vreduce_kernel<DT_F32>, grid, dim3(256), 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL(vreduce_kernel<DT_F16>, grid, dim3(256), 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL(vreduce_kernel<DT_BF16>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -844,9 +628,9 @@ hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_debug_decode(int mma_dtype, int resid, int kind, const void* src,
-                               const uint16_t* scales, long base, long sbase, int n, int r,
-                               int aux0, int aux1, float* out, hipStream_t st) {
+hipError_t launch_debug_decode(int mma_dtype, int resid, int kind, const void* src, const uint16_t* scales,
+                               long base, long sbase, int n, int r, int aux0, int aux1, float* out,
+                               hipStream_t st) {
   const int tot = n * r;
   dim3 grid((tot + 255) / 256), block(256);
   switch (mma_dtype) {

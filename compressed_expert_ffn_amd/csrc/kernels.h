@@ -1,11 +1,14 @@
 // Internal interface between the host layer (api.hip) and the kernels.
 //
-// Device weight layouts (built by pack.cpp at create time):
+// Device weight layouts (built by api.hip with pack.h at create time):
 //
 //  "fragment-major" for a matrix with N columns and depth Kd (the MFMA k):
-//     [N/32][Kd/16][64 lanes][8]   element (n, k) at lane (n%32) + 32*((k%16)/8),
-//     slot k%8 -- one 16-deep k-step of a 32-column block is 64 x 8 contiguous
-//     elements, so a wavefront reads it with one coalesced 16-byte load per lane.
+//     [N/32][Kd/16][64 lanes][8]: fragment (n/32, ks), lane (n%32) + 32h,
+//     slot e holds k = frag_k(ks, h, e) -- one 16-deep k-step of a 32-column
+//     block is 64 x 8 contiguous elements, one coalesced 16-byte load per
+//     lane.  Matrices whose depth is a multiple of 64 use the permuted k
+//     order of tile.h (lane half h covers 32 consecutive k of each 64-deep
+//     block); the 16-deep residual steps (B1) use the plain order.
 //  INT4 factors use the same order with 8 nibbles (q + 8, element e in bits
 //  4e..4e+3) in one 32-bit word per lane, plus fp16 scales.
 //
@@ -16,8 +19,9 @@
 //       A_{p, gK+j}[:, rho] (zero for rho >= r and for padding columns);
 //       INT4 scales [G][NU/32][d/32][32]
 //  B1   [E][P_in] x frag(N = f, Kd = RPAD)  B_p^T; INT4 scales [E][P_in][f/32][RPAD]
-//  Ad   [E] x [f/32][64][8]   16x16x32 B-operand of A_down: lane rho + 16*((k%32)/8),
-//       slot k%8 (k = row of A_down); INT4 scales [E][f/32][RPAD]
+//  Ad   [E][f/32][2][64][8]  A_down as the MFMA operand of the fused
+//       h . A_down product: lane rho + 32h, slot e of step s holds row
+//       fb*32 + ad_row(s, h, e) (pack.h); INT4 scales [E][f/32][RPAD]
 //  Bd   [G] x frag(N = d, Kd = NV)  row j*RPAD + rho of the k axis holds
 //       B_{down, gK+j}[:, rho]; INT4 scales [E][d/32][RPAD]
 #pragma once
@@ -85,20 +89,22 @@ struct GemmArgs {
   // workspace
   void* U;              // [rows][NU] MFMA type
   int NU;
-  float* V;             // [rows][NV] fp32 (G2 tail input)
+  void* V;              // [rows][NV] MFMA type (G2 tail input)
   int NV;
   float* Vp;            // [G1 column tiles][vp_rows][ke][16] partials of V
   long vp_rows;
   void* H;              // [rows][f] MFMA type
-  float* ypart;         // [T*kg][d] (kg > 1)
-  void* Y;              // [T][d] x dtype (kg == 1)
+  float* ypart;         // [ksplit][T*kg][d] fp32 partials (kg > 1 or ksplit > 1)
+  void* Y;              // [T][d] x dtype (kg == 1 and one k split)
+  int ksplit;           // G2: k splits of the base part (partials in ypart)
+  long rows_total;      // T * kg
   int* zero_ptr;        // cleared by the output GEMM's first block
   int zero_n;
 };
 
 struct VReduceArgs {
   const float* Vp;
-  float* V;
+  void* V;  // MFMA type
   const int* garow;
   const int* gidx;
   const int* idx;
@@ -109,7 +115,7 @@ struct VReduceArgs {
 struct CombineArgs {
   const float* ypart;
   void* Y;
-  int T, d, kg;
+  int T, d, kg, ksplit;
 };
 
 enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2 };
@@ -119,11 +125,14 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
 size_t scatter_lds_bytes(int E, int G);
 hipError_t launch_zero(int* p, int n, hipStream_t st);
 
-// bm x 256 tiles with bk-deep stages; max_mtiles: upper bound of
-// sum_g ceil(M_g / bm); ntiles: column tiles of 256.
-hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, int bk, const GemmArgs& a,
-                       int max_mtiles, int ntiles, hipStream_t st);
-hipError_t launch_vreduce(const VReduceArgs& a, hipStream_t st);
+// bm (32, 64, 128, 256; fp32: 32, 64) token rows x 256 columns per tile;
+// max_mtiles: upper bound of sum_g ceil(M_g / bm); ntiles: column tiles of
+// 256; splits: k splits (G2 only, 1 otherwise).
+hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a, int max_mtiles,
+                       int ntiles, int splits, hipStream_t st);
+// LDS bytes of one tile (K experts per group, ke chosen per group)
+size_t gemm_lds(int kind, int mma_dtype, int bm, int K, int ke);
+hipError_t launch_vreduce(int mma_dtype, const VReduceArgs& a, hipStream_t st);
 hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st);
 
 // Device-side decode of stored residual factors (test export).

@@ -1,0 +1,362 @@
+// MFMA tile engine shared by the grouped GEMMs.
+//
+// Orientation.  Every GEMM here multiplies token rows (activations, the "T"
+// side) by weight columns (the "W" side) over a depth k.  The accumulators
+// are held transposed: acc[t][c] is the 32x32 block of feature block c
+// (rows) by token block t (columns), produced by
+//   acc[t][c] = mfma(W fragment of block c, T fragment of block t, acc[t][c]).
+// In that layout lane l owns one token (l % 32) of the block and 16 of its
+// features, which is what the epilogues want: per-token gate weights are one
+// value per lane, and h can feed the next MFMA straight from registers.
+//
+// k order.  Inside every 64-deep k block, k-step s (0..3) of an MFMA
+// fragment gives lane half h (= lane / 32) element i the depth
+//   k = 64 * kb + 32 * h + 8 * s + i,
+// so over one 64-deep stage a lane reads 32 consecutive k of its row: 64
+// contiguous bytes of a 16-bit token row, one full 128-byte line per row
+// for the two lane halves.  Weights are packed with the same order (the
+// contraction does not care how k is enumerated as long as both sides agree).
+//
+// Workgroup = 4 wavefronts arranged WM (token direction) x WN (feature
+// direction); each wavefront computes RT token blocks x CB feature blocks.
+// An operand shared by several wavefronts (T when WN > 1, W when WM > 1) is
+// staged through LDS, double-buffered, one barrier per 64-deep stage; an
+// operand private to a wavefront is loaded straight into registers one stage
+// ahead.
+#pragma once
+#include "common.h"
+
+namespace cefn {
+
+constexpr int KB = 64;  // depth of one stage / one permuted k block
+
+template <int TY> using TE = typename Elem<TY>::T;
+template <int TY> using FragT = typename Frag<TY>::T;
+
+// ------------------------------------------------------------ raw chunks --
+// Raw16<SRC>: the 8 source elements of one fragment as loaded (16 bytes for
+// 16-bit types, 32 for fp32).
+template <int SRC> struct Raw16 { using T = u4v; };
+template <> struct Raw16<DT_F32> { using T = f8; };
+template <int SRC> using RawT = typename Raw16<SRC>::T;
+
+template <int SRC>
+__device__ __forceinline__ RawT<SRC> ld_raw(const TE<SRC>* p) {
+  if constexpr (SRC == DT_F32) {
+    const f4v* q = reinterpret_cast<const f4v*>(p);
+    const f4v a = q[0], b = q[1];
+    f8 c;
+    c[0] = a[0]; c[1] = a[1]; c[2] = a[2]; c[3] = a[3];
+    c[4] = b[0]; c[5] = b[1]; c[6] = b[2]; c[7] = b[3];
+    return c;
+  } else {
+    return *reinterpret_cast<const u4v*>(p);
+  }
+}
+
+template <int SRC>
+__device__ __forceinline__ RawT<SRC> zero_raw() {
+  RawT<SRC> c;
+  if constexpr (SRC == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = 0.f;
+  } else {
+    c[0] = c[1] = c[2] = c[3] = 0u;
+  }
+  return c;
+}
+
+// Raw chunk of type SRC -> MFMA fragment of type TY.
+template <int SRC, int TY>
+__device__ __forceinline__ FragT<TY> cvt_frag(const RawT<SRC>& r) {
+  if constexpr (SRC == TY) {
+    if constexpr (TY == DT_F32) return r;
+    else return __builtin_bit_cast(FragT<TY>, r);
+  } else if constexpr (SRC == DT_F32) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = r[i];
+    return to_frag<TY>(v);
+  } else {
+    static_assert(SRC == DT_BF16 && TY == DT_F16, "unsupported activation / MFMA type pair");
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t b = static_cast<uint16_t>((r[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      v[i] = bf16_bits_to_f32(b);
+    }
+    return to_frag<TY>(v);
+  }
+}
+
+template <int TY>
+__device__ __forceinline__ void st_frag(FragT<TY>* p, const FragT<TY>& f) { *p = f; }
+
+// ------------------------------------------------------ token operand (T) --
+// Rows of a row-major [rows][ld] matrix of type SRC, optionally gathered
+// (row r of the tile is source row map(r)).  Each lane owns one 64-byte
+// (or 128-byte for fp32) segment per stage: token row (lane % 32) of a
+// block, k half h = lane / 32.
+//
+// TDirect: a wavefront loads its own RT blocks into registers.
+// TShared: the workgroup copies all NB token blocks into LDS; each thread
+// handles (NB * 64) / 256 segments.
+template <int SRC, int TY, int RT>
+struct TDirect {
+  using Raw = RawT<SRC>;
+  const TE<SRC>* rowp[RT];
+  bool ok[RT];
+  // row_of(t): source row of token (block t, row lane % 32), or -1
+  template <class RowOf>
+  __device__ void init(const TE<SRC>* base, long ld, int lane, RowOf row_of) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const long r = row_of(t);
+      ok[t] = r >= 0;
+      rowp[t] = base + (ok[t] ? r : 0) * ld + 32 * (lane >> 5);
+    }
+  }
+  __device__ void fetch(int kt, Raw (&r)[RT][4]) const {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) r[t][s] = ld_raw<SRC>(rowp[t] + kt * KB + 8 * s);
+  }
+  __device__ FragT<TY> frag(const Raw (&r)[RT][4], int t, int s) const {
+    return ok[t] ? cvt_frag<SRC, TY>(r[t][s]) : zero_frag<TY>();
+  }
+};
+
+template <int SRC, int TY, int NB>
+struct TShared {
+  // segments per thread; with fewer than 4 blocks some threads hold a
+  // duplicate (clamped) segment that they load but do not write
+  static constexpr int NSEG = NB * 64;
+  static constexpr int SEG = (NSEG + 255) / 256;
+  using Raw = RawT<SRC>;
+  const TE<SRC>* rowp[SEG];
+  bool ok[SEG];
+  int lofs[SEG];  // fragment index (block * 4) * 64 + lane' of the segment, -1: none
+  template <class RowOf>
+  __device__ void init(const TE<SRC>* base, long ld, RowOf row_of) {
+#pragma unroll
+    for (int q = 0; q < SEG; ++q) {
+      const int seg0 = threadIdx.x + 256 * q;  // = block * 64 + lane'
+      const int seg = seg0 < NSEG ? seg0 : NSEG - 1;
+      const int blk = seg >> 6, ln = seg & 63;
+      const long r = row_of(blk, ln & 31);
+      ok[q] = r >= 0;
+      rowp[q] = base + (ok[q] ? r : 0) * ld + 32 * (ln >> 5);
+      lofs[q] = seg0 < NSEG ? blk * 4 * 64 + ln : -1;
+    }
+  }
+  __device__ void fetch(int kt, Raw (&r)[SEG][4]) const {
+#pragma unroll
+    for (int q = 0; q < SEG; ++q)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) r[q][s] = ld_raw<SRC>(rowp[q] + kt * KB + 8 * s);
+  }
+  // LDS image of one stage: [NB][4 k-steps][64 lanes] fragments of type TY
+  __device__ void commit(const Raw (&r)[SEG][4], FragT<TY>* buf) const {
+#pragma unroll
+    for (int q = 0; q < SEG; ++q) {
+      if (NSEG % 256 == 0 || lofs[q] >= 0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          st_frag<TY>(buf + lofs[q] + s * 64, ok[q] ? cvt_frag<SRC, TY>(r[q][s]) : zero_frag<TY>());
+      }
+    }
+  }
+  static constexpr int frags_per_stage = NB * 4 * 64;
+};
+
+// ----------------------------------------------------- weight operand (W) --
+// Fragment-major weights: [N/32][Kd/16][64 lanes] fragments (k permuted as
+// above), so 32 columns x one 64-deep stage is 4 consecutive fragments.
+// WFrag: plain TY fragments.  WInt4: 8 nibbles per lane plus scales, decoded
+// by a functor (scale layout differs by matrix).
+template <int TY>
+struct WPlain {
+  using Raw = FragT<TY>;
+  const FragT<TY>* base;  // block 0 of this matrix
+  int KS;                 // k-steps (Kd / 16)
+  __device__ Raw load(int nb, int kstep, int lane) const { return base[((long)nb * KS + kstep) * 64 + lane]; }
+  __device__ FragT<TY> decode(const Raw& r, int, int, int) const { return r; }
+};
+
+// INT4 with one scale per (column, 32 consecutive k): scales [N/32][Kd/32][32].
+// Over one 64-deep stage lane half h covers k 32h..32h+31 -- one scale.
+template <int TY>
+struct WInt4ColK {
+  struct Raw {
+    uint32_t w;
+    uint16_t s;
+  };
+  const uint32_t* words;
+  const uint16_t* scales;
+  int KS;
+  __device__ Raw load(int nb, int kstep, int lane) const {
+    Raw r;
+    r.w = words[((long)nb * KS + kstep) * 64 + lane];
+    r.s = scales[((long)nb * (KS / 2) + 2 * (kstep >> 2) + (lane >> 5)) * 32 + (lane & 31)];
+    return r;
+  }
+  __device__ FragT<TY> decode(const Raw& r, int, int, int) const {
+    return int4_frag_1scale<TY>(r.w, f16_bits_to_f32(r.s));
+  }
+};
+
+// INT4 stacked residual tail of the down projection: k = j*16 + rho (j the
+// expert of the group, permuted in 64-deep blocks like every k); 8 scales per
+// lane, scales [E][d/32][16] of expert gK + j.
+template <int TY>
+struct WInt4Tail {
+  struct Raw {
+    uint32_t w;
+    u4v s;
+  };
+  const uint32_t* words;
+  const uint16_t* scales;  // of expert gK
+  int KS, K, nd32;
+  __device__ Raw load(int nb, int kstep, int lane) const {
+    // k-step kstep = 4 kb + s covers, for lane half h, expert j = 4kb + 2h + s/2
+    // and rho = 8 (s % 2) + i
+    const int kb = kstep >> 2, s = kstep & 3;
+    int j = 4 * kb + 2 * (lane >> 5) + (s >> 1);
+    j = j < K ? j : K - 1;  // padding k holds zero codes
+    Raw r;
+    r.w = words[((long)nb * KS + kstep) * 64 + lane];
+    r.s = *reinterpret_cast<const u4v*>(scales + ((long)j * nd32 + nb) * RPAD + 8 * (s & 1));
+    return r;
+  }
+  __device__ FragT<TY> decode(const Raw& r, int, int, int) const { return int4_frag_8scale<TY>(r.w, r.s); }
+};
+
+// WDirect: a wavefront loads CB column blocks (nb0 .. nb0 + CB - 1) itself.
+template <class WS, int CB>
+struct WDirect {
+  using Raw = typename WS::Raw;
+  WS src;
+  int nb0;
+  __device__ void fetch(int kt, int lane, Raw (&r)[CB][4]) const {
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) r[c][s] = src.load(nb0 + c, kt * 4 + s, lane);
+  }
+};
+
+// WShared: the workgroup copies NBW column blocks x one stage into LDS,
+// decoded to TY: [NBW][4][64] fragments.
+template <int TY, class WS, int NBW>
+struct WShared {
+  static constexpr int PER = NBW * 4 * 64 / 256;  // fragments per thread
+  using Raw = typename WS::Raw;
+  WS src;
+  int nb0;
+  __device__ void fetch(int kt, Raw (&r)[PER]) const {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int fi = threadIdx.x + 256 * q;  // = (blk * 4 + s) * 64 + lane'
+      const int blk = fi >> 8, s = (fi >> 6) & 3, ln = fi & 63;
+      r[q] = src.load(nb0 + blk, kt * 4 + s, ln);
+    }
+  }
+  __device__ void commit(const Raw (&r)[PER], FragT<TY>* buf) const {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int fi = threadIdx.x + 256 * q;
+      st_frag<TY>(buf + fi, src.decode(r[q], 0, 0, 0));
+    }
+  }
+  static constexpr int frags_per_stage = NBW * 4 * 64;
+};
+
+
+// ---------------------------------------------------------------- mainloop --
+// KT stages of 64 k.  TSH / WSH: the token / weight operand is shared
+// through LDS (tl / wl point at two stage buffers each).  wm, wn: this
+// wavefront's position in the WM x WN arrangement.
+//
+// Per stage: the loads of stage kt+1 are issued first (the last stage
+// re-issues its own, harmlessly, so no load sits in a branch), then the
+// 4 k-steps of MFMAs with LDS fragments read one k-step ahead, then the
+// staged registers are converted and written to the other LDS buffer and
+// the workgroup synchronises once.
+template <int TY, int RT, int CB, bool TSH, bool WSH, class TO, class WO>
+struct Mainloop {
+  using F = FragT<TY>;
+  const TO& to;
+  const WO& wo;
+  F* tl;
+  F* wl;
+  int wm, wn, lane;
+
+  template <class TR, class WR>
+  __device__ __forceinline__ void frags(int b, int s, const TR& tr, const WR& wr, F (&tf)[RT], F (&wf)[CB]) const {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      if constexpr (TSH) tf[t] = tl[b * TO::frags_per_stage + ((wm * RT + t) * 4 + s) * 64 + lane];
+      else tf[t] = to.frag(tr, t, s);
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      if constexpr (WSH) wf[c] = wl[b * WO::frags_per_stage + ((wn * CB + c) * 4 + s) * 64 + lane];
+      else wf[c] = wo.src.decode(wr[c][s], 0, 0, 0);
+    }
+  }
+
+  template <class TS, class WS, class TR, class WR>
+  __device__ __forceinline__ void stage(int kt, int KT, f16v (&acc)[RT][CB], TS& ts, WS& ws, const TR& tcur,
+                                        TR& tnxt, const WR& wcur, WR& wnxt) const {
+    const int kn = (kt + 1 < KT) ? kt + 1 : kt;
+    if constexpr (TSH) to.fetch(kn, ts); else to.fetch(kn, tnxt);
+    if constexpr (WSH) wo.fetch(kn, ws); else wo.fetch(kn, lane, wnxt);
+    __builtin_amdgcn_sched_barrier(0);
+    const int b = kt & 1;
+    F tf[2][RT], wf[2][CB];
+    frags(b, 0, tcur, wcur, tf[0], wf[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) frags(b, s + 1, tcur, wcur, tf[(s + 1) & 1], wf[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int c = 0; c < CB; ++c) acc[t][c] = mfma32<TY>(wf[s & 1][c], tf[s & 1][t], acc[t][c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (TSH) to.commit(ts, tl + (b ^ 1) * TO::frags_per_stage);
+    if constexpr (WSH) wo.commit(ws, wl + (b ^ 1) * WO::frags_per_stage);
+    if constexpr (TSH || WSH) __syncthreads();
+  }
+
+  template <class TS, class WS, class TR, class WR>
+  __device__ void run(int KT, f16v (&acc)[RT][CB]) const {
+    TS ts;
+    WS ws;
+    TR t0, t1;
+    WR w0, w1;
+    if constexpr (TSH) { to.fetch(0, ts); to.commit(ts, tl); } else to.fetch(0, t0);
+    if constexpr (WSH) { wo.fetch(0, ws); wo.commit(ws, wl); } else wo.fetch(0, lane, w0);
+    if constexpr (TSH || WSH) __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      stage(kt, KT, acc, ts, ws, t0, t1, w0, w1);
+      stage(kt + 1, KT, acc, ts, ws, t1, t0, w1, w0);
+    }
+    if (kt < KT) stage(kt, KT, acc, ts, ws, t0, t1, w0, w1);
+  }
+};
+
+template <int RT, int CB>
+__device__ __forceinline__ void zero_acc(f16v (&acc)[RT][CB]) {
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][c][v] = 0.f;
+}
+
+}  // namespace cefn

@@ -197,16 +197,17 @@ def test_repeated_calls_and_different_T_on_one_handle():
 
 
 TILE_VARIANTS = [
-    {"CEFN_BM_G1": "128", "CEFN_BK_G1": "64", "CEFN_BM_G2": "128", "CEFN_BK_G2": "128", "CEFN_BM_U": "64"},
-    {"CEFN_BM_G1": "32", "CEFN_BK_G1": "128", "CEFN_BM_G2": "64", "CEFN_BK_G2": "64", "CEFN_BK_U": "64"},
-    {"CEFN_BM_G1": "64", "CEFN_BK_G1": "64", "CEFN_BM_G2": "32", "CEFN_BK_G2": "128", "CEFN_BM_U": "128"},
+    {"CEFN_BM_U": "256", "CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1"},
+    {"CEFN_BM_U": "64", "CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4"},
+    {"CEFN_BM_U": "32", "CEFN_BM_G1": "32", "CEFN_BM_G2": "128", "CEFN_KS_G2": "2"},
+    {"CEFN_BM_U": "128", "CEFN_BM_G1": "64", "CEFN_BM_G2": "64", "CEFN_KS_G2": "3"},
 ]
 
 
 @pytest.mark.parametrize("wi,T", [(1, 700), (3, 333), (4, 64), (2, 150)])
 @pytest.mark.parametrize("vi", range(len(TILE_VARIANTS)))
 def test_tile_variants_match_oracle(wi, T, vi, monkeypatch):
-    """Every tile shape and stage depth the library can pick gives the same
+    """Every tile height and k split the library can pick gives the same
     routing and outputs within tolerance (ragged tiles included)."""
     L = _lib()
     for k, v in TILE_VARIANTS[vi].items():
