@@ -175,7 +175,32 @@ __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
 }
 
 // --------------------------------------------- G1: base GEMM + epilogue --
-template <int XT, int TY, int RT, int ACT>
+// Residual storage of the epilogue operands: none, plain (stored in the MFMA
+// type), or INT4.
+enum { ER_NONE = 0, ER_PLAIN = 1, ER_INT4 = 2 };
+
+// Raw bits of one epilogue operand fragment: plain fragments use f; INT4
+// uses the 8 codes in w and its scales in x (8 fp16, or one in x[0]).  The
+// field a kernel does not use is dead and takes no registers.
+template <int TY>
+struct ORaw {
+  FragT<TY> f;
+  u4v x;
+  uint32_t w;
+};
+
+// Operands of one (token block, expert) step of the epilogue, loaded one
+// step ahead of their use.
+template <int TY, int PIN, int NFB>
+struct EOps {
+  ORaw<TY> b[2];      // B_j fragments of the wavefront's two feature blocks
+  FragT<TY> u[PIN];   // u_j = x A_j of this lane's token, per input projection
+  ORaw<TY> ad[NFB][2];  // A_down,j fragments of the wavefront's f-blocks, 2 k-steps
+  float wgt;          // gate weight of expert j for this lane's token (0: not chosen)
+  int slot;           // position of j in the token's chosen list (-1: not chosen)
+};
+
+template <int XT, int TY, int RT, int ACT, int RES>
 __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   constexpr int BMT = 32 * RT;
   constexpr int PIN = (ACT == ACT_SWIGLU) ? 2 : 1;
@@ -195,35 +220,45 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   const int nfb = a.f / 32;
   const int row0 = a.goffsets[g] + m0;
   const int K = a.K, ke = a.ke;
-  const bool has_resid = a.resid != RS_NONE;
-  const bool int4 = a.resid == RS_INT4;
 
-  // LDS: [token stages | V sums [BMT][ke][16] fp32] | gate weights [BMT][K] |
-  // slot of expert j in the row's chosen list [BMT][K] (int8) | used [K]
-  const size_t vbytes = (size_t)BMT * ke * RPAD * sizeof(float);
-  const size_t abytes = tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes;
+  // LDS: [token stages | V sums, row stride VS = ke*16 + 1 floats (odd, so
+  // the 32 tokens of an LDS add land in different banks)] | gate weights
+  // [BMT][K] | slot of expert j in the row's chosen list [BMT][K] (int8) |
+  // per token block, the bit set of experts picked by any of its tokens
+  const int VS = ke * RPAD + 1;
+  const size_t vbytes = (size_t)BMT * VS * sizeof(float);
+  const size_t abytes = (tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes + 15) & ~(size_t)15;
   float* s_v = reinterpret_cast<float*>(smem);
   float* s_w = reinterpret_cast<float*>(smem + abytes);
   int8_t* s_slot = reinterpret_cast<int8_t*>(s_w + BMT * K);
-  int* s_used = reinterpret_cast<int*>(s_slot + ((BMT * K + 15) & ~15));
+  uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_slot + ((BMT * K + 15) & ~15));
   F* tl = reinterpret_cast<F*>(smem);
 
   for (int i = tid; i < BMT * K; i += 256) {
     s_w[i] = 0.f;
     s_slot[i] = -1;
   }
-  for (int j = tid; j < K; j += 256) s_used[j] = 0;
+  for (int i = tid; i < 2 * RT; i += 256) s_bm[i] = 0u;
   __syncthreads();
   for (int i = tid; i < BMT; i += 256) {
     if (m0 + i < M) {
       const int aid = a.garow[row0 + i];
       const int t = aid / a.kg, ga = aid - t * a.kg;
-      for (int s = 0; s < ke; ++s) {
-        const int slot = t * a.k + ga * ke + s;
-        const int j = a.idx[slot] - g * K;
-        s_w[i * K + j] = a.w[slot];
-        s_slot[i * K + j] = static_cast<int8_t>(s);
-        s_used[j] = 1;
+      if constexpr (RES == ER_NONE) {
+        // without residuals every expert of the group is the base itself:
+        // sum_j w_j act(Z) = (sum_j w_j) act(Z), one step per token
+        float ws = 0.f;
+        for (int s = 0; s < ke; ++s) ws += a.w[t * a.k + ga * ke + s];
+        s_w[i * K] = ws;
+        atomicOr(&s_bm[(i >> 5) * 2], 1u);
+      } else {
+        for (int s = 0; s < ke; ++s) {
+          const int slot = t * a.k + ga * ke + s;
+          const int j = a.idx[slot] - g * K;
+          s_w[i * K + j] = a.w[slot];
+          s_slot[i * K + j] = static_cast<int8_t>(s);
+          atomicOr(&s_bm[(i >> 5) * 2 + (j >> 5)], 1u << (j & 31));
+        }
       }
     }
   }
@@ -239,53 +274,109 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   WPlain<TY> ws{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
   run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);  // ends with a barrier
 
-  if (has_resid) {
-    for (int i = tid; i < BMT * ke * RPAD; i += 256) s_v[i] = 0.f;
+  if constexpr (RES != ER_NONE) {
+    for (int i = tid; i < BMT * VS; i += 256) s_v[i] = 0.f;
     __syncthreads();
   }
   const TE<TY>* Ub = static_cast<const TE<TY>*>(a.U);
   TE<TY>* H = static_cast<TE<TY>*>(a.H);
   const int h = lane >> 5;
 
+  // expert bit sets of the token blocks (wave-uniform; idle wavefronts none)
+  uint32_t mlo[RT], mhi[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    mlo[t] = active ? __builtin_amdgcn_readfirstlane(s_bm[2 * t]) : 0u;
+    mhi[t] = active ? __builtin_amdgcn_readfirstlane(s_bm[2 * t + 1]) : 0u;
+  }
+  auto first_j = [](uint32_t lo, uint32_t hi) { return lo ? __builtin_ctz(lo) : 32 + __builtin_ctz(hi); };
+
+  // issue the loads of step (t, j)
+  auto load_ops = [&](int t, int j, EOps<TY, PIN, NFB>& o) {
+    const int m = t * 32 + (lane & 31);
+    const int ex = g * K + j;
+    o.wgt = s_w[m * K + j];
+    o.slot = s_slot[m * K + j];
+    if constexpr (RES != ER_NONE) {
+      const long urow = row0 + (m0 + m < M ? m : 0);
+#pragma unroll
+      for (int p = 0; p < PIN; ++p) o.u[p] = *reinterpret_cast<const F*>(Ub + urow * a.NU + (j * PIN + p) * RPAD + 8 * h);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int pj = (ACT == ACT_SWIGLU) ? c : 0;
+        const int fb = (ACT == ACT_SWIGLU) ? fb0 : fb0 + c;
+        const long fr = (long)(ex * PIN + pj) * nfb + fb;
+        if constexpr (RES == ER_INT4) {
+          o.b[c].w = static_cast<const uint32_t*>(a.B1)[fr * 64 + lane];
+          o.b[c].x = *reinterpret_cast<const u4v*>(a.b1_scale + fr * RPAD + 8 * h);
+        } else {
+          o.b[c].f = static_cast<const F*>(a.B1)[fr * 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NFB; ++c)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const long fr = ((long)ex * nfb + fb0 + c) * 2 + st;
+          if constexpr (RES == ER_INT4) {
+            const int rho = lane & 31;
+            o.ad[c][st].w = static_cast<const uint32_t*>(a.Ad)[fr * 64 + lane];
+            o.ad[c][st].x[0] = a.ad_scale[(fr >> 1) * RPAD + (rho < RPAD ? rho : RPAD - 1)];
+          } else {
+            o.ad[c][st].f = static_cast<const F*>(a.Ad)[fr * 64 + lane];
+          }
+        }
+    }
+  };
+
+  EOps<TY, PIN, NFB> cur, nxt;
+  bool have = false;  // cur already holds the first step of block t
   // (unrolled so the accumulators are indexed statically)
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int m = t * 32 + (lane & 31);  // this lane's token row in the tile
-    const bool valid = m0 + m < M;
-    const long urow = row0 + (valid ? m : 0);
     float hbar[NFB][16];
 #pragma unroll
     for (int c = 0; c < NFB; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) hbar[c][v] = 0.f;
-
-    for (int j = 0; j < K && active; ++j) {
-      if (!s_used[j]) continue;
-      const float wgt = s_w[m * K + j];
-      if (!__any(wgt != 0.f)) continue;  // no token of this block picked j
-      const int ex = g * K + j;
+    uint32_t lo = mlo[t], hi = mhi[t];
+    if ((lo | hi) && !have) load_ops(t, first_j(lo, hi), cur);
+    have = false;
+    while (lo | hi) {
+      const int j = first_j(lo, hi);
+      if (lo) lo &= lo - 1; else hi &= hi - 1;
+      // prefetch the next step: the next expert of this block, else the
+      // first of the next block (else reload this one, harmlessly)
+      {
+        int tn = t, jn = j;
+        if (lo | hi) {
+          jn = first_j(lo, hi);
+        } else if (t + 1 < RT) {
+          const int t1 = (t + 1 < RT) ? t + 1 : t;
+          if (mlo[t1] | mhi[t1]) {
+            tn = t1;
+            jn = first_j(mlo[t1], mhi[t1]);
+            have = true;
+          }
+        }
+        load_ops(tn, jn, nxt);
+      }
       f16v z[CB];
-      if (has_resid) {
+      if constexpr (RES != ER_NONE) {
         // z_j = Z + u_j B_j^T: one 16-deep MFMA step per feature block
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
-          const int pj = (ACT == ACT_SWIGLU) ? c : 0;
-          const int fb = (ACT == ACT_SWIGLU) ? fb0 : fb0 + c;
-          const long fr = (long)(ex * PIN + pj) * nfb + fb;
           F bfr;
-          if (int4) {
-            const uint32_t word = static_cast<const uint32_t*>(a.B1)[fr * 64 + lane];
-            bfr = int4_frag_8scale<TY>(word, *reinterpret_cast<const u4v*>(a.b1_scale + fr * RPAD + 8 * h));
-          } else {
-            bfr = static_cast<const F*>(a.B1)[fr * 64 + lane];
-          }
-          const F ufr = *reinterpret_cast<const F*>(Ub + urow * a.NU + (j * PIN + pj) * RPAD + 8 * h);
-          z[c] = mfma32<TY>(bfr, ufr, acc[t][c]);
+          if constexpr (RES == ER_INT4) bfr = int4_frag_8scale<TY>(cur.b[c].w, cur.b[c].x);
+          else bfr = cur.b[c].f;
+          z[c] = mfma32<TY>(bfr, cur.u[(ACT == ACT_SWIGLU) ? c : 0], acc[t][c]);
         }
       } else {
 #pragma unroll
         for (int c = 0; c < CB; ++c) z[c] = acc[t][c];
       }
+      const float wgt = cur.wgt;
       float hw[NFB][16];
       if constexpr (ACT == ACT_SWIGLU) {
 #pragma unroll
@@ -302,7 +393,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
             hbar[c][v] += hw[c][v];
           }
       }
-      if (has_resid) {
+      if constexpr (RES != ER_NONE) {
         // V^T[rho, token] = sum over this wavefront's features of
         // A_down[f, rho] (w h)[token, f]: the accumulator rows a lane holds
         // are the k of the MFMA, in the order the A_down operand was packed
@@ -313,28 +404,25 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
         for (int c = 0; c < NFB; ++c)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const long fr = ((long)ex * nfb + fb0 + c) * 2 + st;
             F afr;
-            if (int4) {
-              const uint32_t word = static_cast<const uint32_t*>(a.Ad)[fr * 64 + lane];
-              const int rho = lane & 31;
-              const float sc = rho < RPAD ? f16_bits_to_f32(a.ad_scale[(fr >> 1) * RPAD + rho]) : 0.f;
-              afr = int4_frag_1scale<TY>(word, sc);
+            if constexpr (RES == ER_INT4) {
+              const uint16_t sb = static_cast<uint16_t>(cur.ad[c][st].x[0] & 0xFFFFu);
+              afr = int4_frag_1scale<TY>(cur.ad[c][st].w, (lane & 31) < RPAD ? f16_bits_to_f32(sb) : 0.f);
             } else {
-              afr = static_cast<const F*>(a.Ad)[fr * 64 + lane];
+              afr = cur.ad[c][st].f;
             }
             const F hfr = to_frag<TY>(&hw[c][8 * st]);  // hw is a plain float array
             vacc = mfma32<TY>(afr, hfr, vacc);
           }
-        const int sl = s_slot[m * K + j];
-        if (sl >= 0) {
-          float* dst = s_v + ((long)m * ke + sl) * RPAD;
+        if (cur.slot >= 0) {
+          float* dst = s_v + m * VS + cur.slot * RPAD;
 #pragma unroll
           for (int v = 0; v < 8; ++v) atomicAdd(dst + acc_feat(v, lane), vacc[v]);
         }
       }
+      cur = nxt;
     }
-    if (active && valid) {  // (idle wavefronts computed nothing above)
+    if (active && m0 + m < M) {  // (idle wavefronts computed nothing above)
       TE<TY>* hrow = H + (long)(row0 + m) * a.f + 4 * h;
 #pragma unroll
       for (int c = 0; c < NFB; ++c)
@@ -344,13 +432,13 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
                      hbar[c][4 * q + 3]);
     }
   }
-  if (has_resid) {
+  if constexpr (RES != ER_NONE) {
     __syncthreads();
     // one partial per (column tile, row, slot), summed by vreduce
     const int per_row = ke * RPAD;
     for (int e = tid; e < BMT * per_row; e += 256) {
-      const int r = e / per_row;
-      if (m0 + r < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + r) * per_row + (e - r * per_row)] = s_v[e];
+      const int r = e / per_row, c = e - r * per_row;
+      if (m0 + r < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + r) * per_row + c] = s_v[r * VS + c];
     }
   }
 }
@@ -543,6 +631,30 @@ hipError_t go(KF kfn, dim3 grid, size_t lds, const GemmArgs& a, hipStream_t st) 
   return hipGetLastError();
 }
 
+// Residual storage kinds valid for a (activation type, MFMA type) pair:
+// plain residuals are stored in the MFMA type (F32 with an F32 base, F16 with
+// an F16 base), INT4 needs a 16-bit base.
+template <int XT, int TY, int RT, int ACT>
+hipError_t launch_g1_act(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (a.resid == RS_NONE) return go(gemm1_kernel<XT, TY, RT, ACT, ER_NONE>, grid, lds, a, st);
+  if constexpr (TY == DT_F32) {
+    if (a.resid == RS_F32) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN>, grid, lds, a, st);
+  } else {
+    if (a.resid == RS_INT4) return go(gemm1_kernel<XT, TY, RT, ACT, ER_INT4>, grid, lds, a, st);
+    if constexpr (TY == DT_F16) {
+      if (a.resid == RS_F16) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN>, grid, lds, a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int XT, int TY, int RT>
+hipError_t launch_g1(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (a.act == ACT_SWIGLU) return launch_g1_act<XT, TY, RT, ACT_SWIGLU>(a, grid, lds, st);
+  if constexpr (RT <= 4) return launch_g1_act<XT, TY, RT, ACT_GELU>(a, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
 template <int XT, int TY, int RT>
 hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
   const size_t lds = gemm_lds(kind, TY, RT * 32, a.K, a.ke);
@@ -552,8 +664,7 @@ hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
       if (int4) return go(ugemm_kernel<XT, TY, RT, true>, grid, lds, a, st);
       return go(ugemm_kernel<XT, TY, RT, false>, grid, lds, a, st);
     case GK_G1:
-      if (a.act == ACT_SWIGLU) return go(gemm1_kernel<XT, TY, RT, ACT_SWIGLU>, grid, lds, a, st);
-      return go(gemm1_kernel<XT, TY, RT, ACT_GELU>, grid, lds, a, st);
+      return launch_g1<XT, TY, RT>(a, grid, lds, st);
     case GK_G2:
       if (int4) return go(gemm2_kernel<XT, TY, RT, true>, grid, lds, a, st);
       return go(gemm2_kernel<XT, TY, RT, false>, grid, lds, a, st);
@@ -586,9 +697,10 @@ size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
   const size_t fb = ty == DT_F32 ? 32 : 16;
   const size_t tbytes = 2 * (size_t)(bm / 32) * 4 * 64 * fb;
   if (kind != GK_G1) return tbytes;
-  const size_t vbytes = (size_t)bm * ke * RPAD * sizeof(float);
-  return (tbytes > vbytes ? tbytes : vbytes) + sizeof(float) * bm * K + (((size_t)bm * K + 15) & ~(size_t)15) +
-         sizeof(int) * K + 64;
+  const size_t vbytes = (size_t)bm * (ke * RPAD + 1) * sizeof(float);
+  const size_t abytes = (tbytes > vbytes ? tbytes : vbytes + 15) & ~(size_t)15;
+  return abytes + sizeof(float) * bm * K + (((size_t)bm * K + 15) & ~(size_t)15) + sizeof(uint32_t) * 2 * (bm / 32) +
+         64;
 }
 
 hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a, int max_mtiles,
