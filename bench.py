@@ -80,6 +80,76 @@ def traffic_for(workload_name: str, kernel: str):
     return rec.get("bytes_per_launch") if rec.get("src_sha") == sha else None
 
 
+KERNEL_STAGE = (("router", "router"), ("scatter", "scatter"), ("ugemm", "ugemm"), ("gemm1", "gemm1"),
+                ("vreduce", "vreduce"), ("gemm2", "gemm2"), ("combine", "combine"), ("zero_kernel", "zero"))
+
+
+def stage_of(kernel_name: str):
+    for key, stage in KERNEL_STAGE:
+        if key in kernel_name:
+            return stage
+    return None
+
+
+def pmc_means(csv_path: str, counter: str) -> dict:
+    """Mean value of one counter per dispatch, by stage and for the copy."""
+    import csv
+    acc = {}
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = stage_of(name) or ("copy" if "copy" in name.lower() else None)
+            if key is None:
+                continue
+            acc.setdefault(key, []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_pmc(args) -> None:
+    """Turn two rocprofv3 counter runs of the benchmark (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) and the same two counters on a plain device
+    copy of --copy-mib MiB into HBM bytes per launch per kernel, scaled so the
+    copy reads and writes exactly its size; written to profiles/pmc_traffic.json
+    keyed by workload and stamped with the kernel source it was taken on."""
+    fetch = pmc_means(args.fetch_csv, "FETCH_SIZE")
+    write = pmc_means(args.write_csv, "WRITE_SIZE")
+    cf = pmc_means(args.copy_fetch_csv, "FETCH_SIZE")["copy"]
+    cw = pmc_means(args.copy_write_csv, "WRITE_SIZE")["copy"]
+    kib = args.copy_mib * 1024.0
+    f_scale, w_scale = kib / cf, kib / cw
+    src = os.path.join(ROOT, "compressed_expert_ffn_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    from compressed_expert_ffn_amd.workloads import WORKLOADS
+    w = WORKLOADS[args.workload]
+    rec = {}
+    for k in sorted(set(fetch) & set(write)):
+        if k == "copy":
+            continue
+        rec[k] = dict(fetch_kib=round(fetch[k], 1), write_kib=round(write[k], 1),
+                      bytes_per_launch=int((fetch[k] * f_scale + write[k] * w_scale) * 1024),
+                      src_sha=sha)
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    allrec = json.load(open(path)) if os.path.exists(path) else {}
+    allrec[w.name] = dict(rec, _calibration=dict(copy_mib=args.copy_mib, copy_fetch_kib=round(cf, 1),
+                                                 copy_write_kib=round(cw, 1), fetch_scale=round(f_scale, 4),
+                                                 write_scale=round(w_scale, 4)))
+    json.dump(allrec, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(allrec[w.name], indent=1))
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of a known size, for counter scaling."""
+    import torch
+    a = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB x5", flush=True)
+
+
 def cpu_baseline(w, inputs, budget_s: float) -> dict:
     """The CPU oracle as it stands, on the same workload (the sample is the
     whole batch, repeated while the time budget lasts)."""
@@ -121,7 +191,19 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="plain stream launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of --copy-mib MiB (counter scaling)")
+    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/pmc_traffic.json from rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        args.fetch_csv, args.write_csv, args.copy_fetch_csv, args.copy_write_csv = args.summarize_pmc
+        summarize_pmc(args)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this layer is built and measured on one GPU only; "
               "run with --gpus 1", file=sys.stderr)
