@@ -59,7 +59,9 @@ struct moe_handle {
   int device = 0;
   bool dirty = false;
   // weights
-  float *Wg = nullptr, *We = nullptr, *gbias = nullptr, *ebias = nullptr;
+  float *Wr = nullptr, *gbias = nullptr, *ebias = nullptr;
+  int NCp = 0;         // router score columns, padded to 32
+  float* L = nullptr;  // router scores (k-split partials)
   void *W1 = nullptr, *W2 = nullptr, *At = nullptr, *B1 = nullptr, *Ad = nullptr, *Bd = nullptr;
   uint16_t *At_s = nullptr, *B1_s = nullptr, *Ad_s = nullptr, *Bd_s = nullptr;
   long w1_gs = 0, w2_gs = 0, at_gs = 0, at_sgs = 0, bd_gs = 0;
@@ -466,7 +468,8 @@ int hip_fail(moe_handle* h, hipError_t e, const char* what) {
 }
 
 // router + scatter into the workspace (and the caller's buffers where given)
-int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, hipStream_t st, Prof& pf) {
+int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, bool need_experts, hipStream_t st,
+              Prof& pf) {
   const moe_config& c = h->cfg;
   hipError_t e;
   if (h->dirty) {
@@ -487,8 +490,10 @@ int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, hipS
   ra.ke = c.top_experts;
   ra.k = h->k;
   ra.E = h->E;
-  ra.Wg = h->Wg;
-  ra.We = h->We;
+  ra.Wr = h->Wr;
+  ra.NCp = h->NCp;
+  ra.L = h->L;
+  ra.nsplit = router_splits(T, c.d, h->NCp);
   ra.gbias = h->gbias;
   ra.ebias = h->ebias;
   ra.idx = idx;
@@ -496,6 +501,9 @@ int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, hipS
   ra.gidx = gidx;
   ra.ccount = h->cc;
   ra.cgcount = h->cc + (size_t)h->nch_e_max * h->E;
+  // the forward pass needs only the group lists; expert-level counts,
+  // offsets and perm are built when the caller asks for routing outputs
+  ra.count_experts = need_experts ? 1 : 0;
   pf.begin(0);
   e = launch_router(c.x_dtype, ra, st);
   if (e != hipSuccess) return hip_fail(h, e, "router launch");
@@ -519,6 +527,7 @@ int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, hipS
   sa.goffsets = (ro && ro->goffsets) ? ro->goffsets : h->goffsets;
   sa.gperm = (ro && ro->gperm) ? ro->gperm : nullptr;
   sa.garow = h->garow;
+  sa.do_experts = ra.count_experts;
   pf.begin(1);
   e = launch_scatter(sa, st);
   if (e != hipSuccess) return hip_fail(h, e, "scatter launch");
@@ -580,12 +589,23 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
 
   // router weights and biases
   {
-    std::vector<float> wg(w->W_grp, w->W_grp + (size_t)c.d * c.G);
-    TRY(upload(h.get(), &h->Wg, wg));
-    if (c.K > 1) {
-      std::vector<float> we(w->W_exp, w->W_exp + (size_t)c.G * c.d * c.K);
-      TRY(upload(h.get(), &h->We, we));
-    }
+    // one score matrix for both levels: [W_grp | W_exp^0 | ... | W_exp^{G-1}],
+    // sixteen k of a column contiguous (the order the score kernel reads)
+    const int NC = c.G + (c.K > 1 ? c.G * c.K : 0);
+    h->NCp = (int)roundup(NC, 32);
+    std::vector<float> wr((size_t)c.d * h->NCp, 0.f);
+    for (int k = 0; k < c.d; ++k)
+      for (int col = 0; col < NC; ++col) {
+        float v;
+        if (col < c.G) {
+          v = w->W_grp[(size_t)k * c.G + col];
+        } else {
+          const int g = (col - c.G) / c.K, j = (col - c.G) % c.K;
+          v = w->W_exp[((size_t)g * c.d + k) * c.K + j];
+        }
+        wr[((size_t)(k / 16) * h->NCp + col) * 16 + (k % 16)] = v;
+      }
+    TRY(upload(h.get(), &h->Wr, wr));
     if (w->group_bias) {
       std::vector<float> gb(w->group_bias, w->group_bias + c.G);
       TRY(upload(h.get(), &h->gbias, gb));
@@ -617,6 +637,15 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
     TRY(dalloc(h.get(), &h->goffsets, c.G + 1));
     TRY(dalloc(h.get(), &h->garow, T * kg + 1));
     TRY(dalloc(h.get(), &h->cc, (size_t)h->cc_n + 1));
+    {
+      // score buffer: the largest nsplit * T over the batch sizes up to T_max
+      long lmax = 0;
+      for (long t = 32; t < T + 32; t += 32) {
+        const long tt = std::min<long>(t, std::max<long>(T, 1));
+        lmax = std::max(lmax, router_splits((int)tt, c.d, h->NCp) * tt);
+      }
+      TRY(dalloc(h.get(), &h->L, (size_t)lmax * h->NCp + 4));
+    }
     char* tmp = nullptr;
     if (c.r > 0) {
       TRY(dalloc(h.get(), &tmp, T * kg * h->NU * es + 16));
@@ -659,7 +688,8 @@ int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out,
   if (T > 0 && !X) return fail(MOE_ERR_INVALID_ARG, "null X");
   hipStream_t st = static_cast<hipStream_t>(stream);
   Prof pf{h, st, -1};
-  TRY(run_route(h, X, T, out, st, pf));
+  if (h->prof && h->prof_calls < h->prof_max) pf.call = h->prof_calls++;
+  TRY(run_route(h, X, T, out, true, st, pf));
   hipError_t e = launch_zero(h->cc, h->cc_n, st);
   if (e != hipSuccess) return hip_fail(h, e, "clear counters");
   return MOE_OK;
@@ -676,7 +706,7 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   hipStream_t st = static_cast<hipStream_t>(stream);
   Prof pf{h, st, -1};
   if (h->prof && h->prof_calls < h->prof_max) pf.call = h->prof_calls++;
-  TRY(run_route(h, X, T, routing, st, pf));
+  TRY(run_route(h, X, T, routing, routing != nullptr, st, pf));
 
   const int kg = c.top_groups;
   const int rows = T * kg;
@@ -715,10 +745,8 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     u.bw_gstride = h->at_gs;
     u.bw_scale = h->At_s;
     u.bws_gstride = h->at_sgs;
-    const int nt = (h->NU + 255) / 256;
-    const int bm = pick_bm(h, GK_U, rows, nt, 1);
     pf.begin(2);
-    e = launch_gemm(GK_U, c.x_dtype, h->mma, bm, u, max_mtiles(T, kg, c.G, bm), nt, 1, st);
+    e = launch_gemm(GK_U, c.x_dtype, h->mma, 32, u, max_mtiles(T, kg, c.G, 32), 1, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "ugemm launch");
     pf.end(2);
   }

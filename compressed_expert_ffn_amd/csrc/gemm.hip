@@ -124,53 +124,77 @@ __device__ __forceinline__ void run_tile(int KT, const TO& to, const WS& ws, int
   wo.nb0 = nb0;
   using TSr = typename TO::Raw[TO::SEG][4];
   using WRr = typename WO::Raw[CB][4];
-  Mainloop<TY, RT, CB, true, false, TO, WO> ml{to, wo, tl, nullptr, 0, wave, lane};
+  // a 256-token stage keeps the MFMAs busy for longer than a load takes;
+  // shorter tiles keep two stages of loads in flight
+  constexpr int PD = (RT >= 8) ? 1 : 2;
+  Mainloop<TY, RT, CB, true, false, TO, WO, PD> ml{to, wo, tl, nullptr, 0, wave, lane};
   ml.template run<TSr, int, int, WRr>(KT, acc);
 }
 
 // ------------------------------------------------------------- U = X . A --
-template <int XT, int TY, int RT, bool INT4>
+// A thin GEMM (N = K*P_in*16 columns): a workgroup takes 32 token rows x
+// CB*32 columns, and its 4 wavefronts walk consecutive quarters of d for
+// that same tile (rows and weights read straight into registers, two stages
+// ahead), so each dependent chain is a quarter as long; the four partial
+// tiles meet in LDS and wavefront c writes column block c.
+template <int XT, int TY, int CB_, bool INT4>
 __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
-  constexpr int BMT = 32 * RT;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BW = CB_ * 32;
+  __shared__ __attribute__((aligned(16))) float red[4][CB_][16][64];
   TileCoord tc;
-  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.NU + BNF - 1) / BNF, tc)) return;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, 32, (a.NU + BW - 1) / BW, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nbw = (tc.nt * BNF + wave * 64) / 32;
-  const bool active = nbw * 32 < a.NU;
-  const int nb0 = active ? nbw : a.NU / 32 - CB;  // idle wavefronts read a valid block
   const int row0 = a.goffsets[g] + m0;
-  FragT<TY>* tl = reinterpret_cast<FragT<TY>*>(smem);
-
-  TShared<XT, TY, RT> to;
-  to.init(static_cast<const TE<XT>*>(a.X), a.d, [&](int blk, int r) -> long {
-    const int m = blk * 32 + r;
+  const int KT = a.d / KB;
+  const int k0 = wave * KT / 4, k1 = (wave + 1) * KT / 4;
+  TDirect<XT, TY, 1> to;
+  to.init(static_cast<const TE<XT>*>(a.X) + (long)k0 * KB, a.d, lane, [&](int) -> long {
+    const int m = lane & 31;
     return m0 + m < M ? (long)(a.garow[row0 + m] / a.kg) : -1L;
   });
-  f16v acc[RT][CB];
-  zero_acc<RT, CB>(acc);
+  f16v acc[1][CB_];
+  zero_acc<1, CB_>(acc);
+  const int nb0 = tc.nt * CB_;
+  auto run = [&](const auto& ws) {
+    using WS = std::decay_t<decltype(ws)>;
+    using WO = WDirect<WS, CB_>;
+    WO wo;
+    wo.src = ws;
+    wo.nb0 = nb0;
+    using TR = typename TDirect<XT, TY, 1>::Raw[1][4];
+    using WR = typename WO::Raw[CB_][4];
+    Mainloop<TY, 1, CB_, false, false, TDirect<XT, TY, 1>, WO, 2> ml{to, wo, nullptr, nullptr, 0, 0, lane};
+    if (k1 > k0) ml.template run<int, int, TR, WR>(k1 - k0, acc);
+  };
   const int KS = a.d / 16;
   if constexpr (INT4) {
     WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride, KS};
-    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);
+    ws.ks0 = k0 * 4;
+    run(ws);
   } else {
     WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, KS};
-    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);
+    ws.ks0 = k0 * 4;
+    run(ws);
   }
-  if (!active) return;
-  TE<TY>* U = static_cast<TE<TY>*>(a.U);
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int m = t * 32 + (lane & 31);
-    if (m0 + m >= M) continue;
-    TE<TY>* urow = U + (long)(row0 + m) * a.NU + nb0 * 32 + 4 * (lane >> 5);
+  for (int c = 0; c < CB_; ++c)
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
+    for (int v = 0; v < 16; ++v) red[wave][c][v][lane] = acc[0][c][v];
+  __syncthreads();
+  const int c = wave;
+  const int m = lane & 31;
+  if (c >= CB_ || m0 + m >= M || (nb0 + c) * 32 >= a.NU) return;
+  TE<TY>* urow = static_cast<TE<TY>*>(a.U) + (long)(row0 + m) * a.NU + (nb0 + c) * 32 + 4 * (lane >> 5);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store4<TY>(urow + c * 32 + 8 * q, acc[t][c][4 * q], acc[t][c][4 * q + 1], acc[t][c][4 * q + 2],
-                   acc[t][c][4 * q + 3]);
+  for (int q = 0; q < 4; ++q) {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = 4 * q + i;
+      o[i] = (red[0][c][v][lane] + red[1][c][v][lane]) + (red[2][c][v][lane] + red[3][c][v][lane]);
+    }
+    store4<TY>(urow + 8 * q, o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -523,28 +547,37 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
 // V[row, j*16 + rho] = sum over G1 column tiles of the partial for the slot
 // of expert j in the row's chosen list; zero for experts the row did not
 // pick.  V is stored in the MFMA type: the down projection's residual tail
-// would round it to that type on load anyway.  One block of 256 threads per
-// 16 rows.
+// would round it to that type on load anyway.  One thread per element of V;
+// the partial loads of a thread are issued four at a time.
 template <int TY>
 __global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
   TE<TY>* V = static_cast<TE<TY>*>(a.V);
-  const int row_base = blockIdx.x * 16;
-  const int nrow = min(16, a.rows - row_base);
-  if (nrow <= 0) return;
-  for (int e = threadIdx.x; e < nrow * a.NV; e += 256) V[(long)row_base * a.NV + e] = from_f32<TY>(0.f);
-  __syncthreads();
-  const int per_row = a.ke * RPAD;
-  for (int e = threadIdx.x; e < nrow * per_row; e += 256) {
-    const int r = e / per_row, rem = e % per_row, sl = rem / RPAD, rho = rem % RPAD;
-    const int row = row_base + r;
-    const int aid = a.garow[row];
-    const int t = aid / a.kg, ga = aid - t * a.kg;
-    const int g = a.gidx[aid];
-    const int j = a.idx[t * a.k + ga * a.ke + sl] - g * a.K;
-    float sum = 0.f;
-    for (int nt = 0; nt < a.ntiles; ++nt) sum += a.Vp[(((long)nt * a.vp_rows + row) * a.ke + sl) * RPAD + rho];
-    V[(long)row * a.NV + j * RPAD + rho] = from_f32<TY>(sum);
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long)a.rows * a.NV) return;
+  const int row = (int)(e / a.NV), col = (int)(e % a.NV);
+  const int j = col / RPAD, rho = col % RPAD;
+  const int aid = a.garow[row];
+  const int t = aid / a.kg, ga = aid - t * a.kg;
+  const int ex = a.gidx[aid] * a.K + j;
+  int sl = -1;
+  for (int s = 0; s < a.ke; ++s)
+    if (a.idx[t * a.k + ga * a.ke + s] == ex) sl = s;
+  float sum = 0.f;
+  if (sl >= 0) {
+    const float* p = a.Vp + ((long)row * a.ke + sl) * RPAD + rho;
+    const long step = a.vp_rows * a.ke * RPAD;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int nt = 0;
+    for (; nt + 4 <= a.ntiles; nt += 4) {
+      s0 += p[(nt + 0) * step];
+      s1 += p[(nt + 1) * step];
+      s2 += p[(nt + 2) * step];
+      s3 += p[(nt + 3) * step];
+    }
+    for (; nt < a.ntiles; ++nt) s0 += p[nt * step];
+    sum = (s0 + s1) + (s2 + s3);
   }
+  V[e] = from_f32<TY>(sum);
 }
 
 // ---------------------------------------------------------------- combine --
@@ -661,8 +694,7 @@ hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
   const bool int4 = a.resid == RS_INT4;
   switch (kind) {
     case GK_U:
-      if (int4) return go(ugemm_kernel<XT, TY, RT, true>, grid, lds, a, st);
-      return go(ugemm_kernel<XT, TY, RT, false>, grid, lds, a, st);
+      return hipErrorInvalidValue;  // launched by launch_ugemm
     case GK_G1:
       return launch_g1<XT, TY, RT>(a, grid, lds, st);
     case GK_G2:
@@ -703,9 +735,32 @@ size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
          64;
 }
 
+template <int XT, int TY>
+hipError_t launch_ugemm_t(const GemmArgs& a, int max_mtiles, hipStream_t st) {
+  const bool int4 = a.resid == RS_INT4;
+  // INT4 factors are decoded per use: narrower tiles keep two workgroups per
+  // compute unit to overlap the decode with the other's loads
+  if (a.NU <= 64 || int4) {
+    const dim3 grid((unsigned)max_mtiles * ((a.NU + 63) / 64));
+    if (int4) return go(ugemm_kernel<XT, TY, 2, true>, grid, 0, a, st);
+    return go(ugemm_kernel<XT, TY, 2, false>, grid, 0, a, st);
+  }
+  const dim3 grid((unsigned)max_mtiles * ((a.NU + 127) / 128));
+  if (int4) return go(ugemm_kernel<XT, TY, 4, true>, grid, 0, a, st);
+  return go(ugemm_kernel<XT, TY, 4, false>, grid, 0, a, st);
+}
+
 hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a, int max_mtiles,
                        int ntiles, int splits, hipStream_t st) {
   if (max_mtiles <= 0 || ntiles <= 0) return hipSuccess;
+  if (kind == GK_U) {
+    // 32-row tiles: max_mtiles must be counted for bm = 32
+    if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_ugemm_t<DT_F32, DT_F32>(a, max_mtiles, st);
+    if (x_dtype == DT_F16 && mma_dtype == DT_F16) return launch_ugemm_t<DT_F16, DT_F16>(a, max_mtiles, st);
+    if (x_dtype == DT_BF16 && mma_dtype == DT_BF16) return launch_ugemm_t<DT_BF16, DT_BF16>(a, max_mtiles, st);
+    if (x_dtype == DT_BF16 && mma_dtype == DT_F16) return launch_ugemm_t<DT_BF16, DT_F16>(a, max_mtiles, st);
+    return hipErrorInvalidValue;
+  }
   dim3 grid((unsigned)max_mtiles * (unsigned)ntiles * (unsigned)splits);
   if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_types<DT_F32, DT_F32>(kind, bm, a, grid, st);
   if (x_dtype == DT_F16 && mma_dtype == DT_F16) return launch_types<DT_F16, DT_F16>(kind, bm, a, grid, st);
@@ -716,7 +771,7 @@ hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmA
 
 hipError_t launch_vreduce(int mma_dtype, const VReduceArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
-  const dim3 grid((a.rows + 15) / 16);
+  const dim3 grid((unsigned)(((long)a.rows * a.NV + 255) / 256));
   switch (mma_dtype) {
     case DT_F32: hipLaunchKernelGGL(vreduce_kernel<DT_F32>, grid, dim3(256), 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL(vreduce_kernel<DT_F16>, grid, dim3(256), 0, st, a); break;

@@ -33,8 +33,12 @@ namespace cefn {
 struct RouteArgs {
   const void* X;
   int T, d, G, K, kg, ke, k, E;
-  const float* Wg;     // [d][G]
-  const float* We;     // [G][d][K]
+  const float* Wr;     // router matrix [d/16][NCp][16]: column c < G is W_grp[:, c],
+                       // column G + g*K + j is W_exp[g][:, j], the rest zero;
+                       // element (k, c) at ((k/16) * NCp + c) * 16 + k % 16
+  int NCp;             // score columns, G (+ G*K when K > 1), padded to 32
+  float* L;            // scores [nsplit][T][NCp] (partial sums over k splits)
+  int nsplit;          // k splits of the score GEMM (router_splits)
   const float* gbias;  // [G] or null
   const float* ebias;  // [E] or null
   int* idx;            // [T][k]
@@ -42,6 +46,7 @@ struct RouteArgs {
   int* gidx;           // [T][kg]
   int* ccount;         // [chunks of T*k][E], zero on entry
   int* cgcount;        // [chunks of T*kg][G], zero on entry
+  int count_experts;   // 0: skip the expert-level counters (group lists only)
 };
 
 struct ScatterArgs {
@@ -58,6 +63,7 @@ struct ScatterArgs {
   int* goffsets;  // [G+1]
   int* gperm;     // [T*kg] token ids, or null
   int* garow;     // [T*kg] group-list position -> t*kg + group rank
+  int do_experts; // 0: build the group lists only
 };
 
 // Common to the three grouped GEMMs.  Rows are group-list positions
@@ -121,6 +127,7 @@ struct CombineArgs {
 enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2 };
 
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st);
+int router_splits(int T, int d, int NCp);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
 size_t scatter_lds_bytes(int E, int G);
 hipError_t launch_zero(int* p, int n, hipStream_t st);

@@ -2,13 +2,22 @@
 //
 // Router ("Breaking the MoE LLM Trilemma", papernotes.org note, key design 3:
 // groups first, then experts inside the chosen groups; FP32 router as in the
-// MoE routing page "混合专家模型的路由机制与工程落地", section 3.1): 64-lane
-// wavefronts, each routing one to four tokens.  Lanes split the model width,
-// partial dot products are combined with cross-lane xor reductions, and the
-// top-k keeps the larger score, then the lower index.
+// MoE routing page "混合专家模型的路由机制与工程落地", section 3.1), in two
+// kernels:
+//   logits  every router score of every token, s = x . [W_grp | W_exp^0 ..
+//           W_exp^{G-1}], as one fp32 MFMA GEMM (32 x 32 x 2 steps; the
+//           products and sums are fp32), k split over the 4 wavefronts of
+//           a workgroup and, for small batches, over workgroups;
+//   select  one thread per token: the top groups of s_grp + c, then the top
+//           experts of each chosen group's scores + b, larger score first,
+//           ties to the lower index, NaN ranked last; gate weights are the
+//           product of the two softmaxes over the chosen scores.
+// Scoring the experts of every group (not only the chosen ones) costs
+// G*K extra columns of a small fp32 GEMM and removes a dependent second
+// pass over the weights.
 //
 // Token lists (dropless dispatch, tokens ascending within each bin): the
-// router counts assignments per (chunk of 256 assignments, bin) with
+// select kernel counts assignments per (chunk of 256 assignments, bin) with
 // atomics; the scatter kernel turns those counts into per-bin offsets with a
 // prefix sum and places each assignment at offset + (assignments of the same
 // bin in earlier chunks) + (its rank inside its own chunk), the rank coming
@@ -21,348 +30,265 @@ namespace cefn {
 
 namespace {
 
-__device__ __forceinline__ int next_pow2(int c) {
-  int p = 1;
-  while (p < c) p <<= 1;
-  return p;
-}
-
-// Logits x . W[:, c] for c < C (W row stride ldw).  Lane l ends up holding
-// column l + 64 q in out[q] (columns >= C hold garbage).
-template <int XT, int NQ>
-__device__ void wave_logits(const typename Elem<XT>::T* x, int d, const float* W, int ldw, int C,
-                            int lane, float (&out)[NQ]) {
-  if (C <= 64) {
-    const int Cp = next_pow2(C);
-    const int S = 64 / Cp;
-    const int col = lane & (Cp - 1);
-    const int sl = lane / Cp;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    if (col < C) {
-      int i = sl;
-      for (; i + 3 * S < d; i += 4 * S) {
-        a0 = fmaf(load_as_f32<XT>(x, i), W[(long)i * ldw + col], a0);
-        a1 = fmaf(load_as_f32<XT>(x, i + S), W[(long)(i + S) * ldw + col], a1);
-        a2 = fmaf(load_as_f32<XT>(x, i + 2 * S), W[(long)(i + 2 * S) * ldw + col], a2);
-        a3 = fmaf(load_as_f32<XT>(x, i + 3 * S), W[(long)(i + 3 * S) * ldw + col], a3);
-      }
-      for (; i < d; i += S) a0 = fmaf(load_as_f32<XT>(x, i), W[(long)i * ldw + col], a0);
-    }
-    float acc = (a0 + a1) + (a2 + a3);
-    for (int off = Cp; off < 64; off <<= 1) acc += __shfl_xor(acc, off);
-    out[0] = acc;
-#pragma unroll
-    for (int q = 1; q < NQ; ++q) out[q] = 0.f;
-  } else {
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int c = lane + 64 * q;
-      float a0 = 0.f, a1 = 0.f;
-      if (c < C) {
-        int i = 0;
-        for (; i + 1 < d; i += 2) {
-          a0 = fmaf(load_as_f32<XT>(x, i), W[(long)i * ldw + c], a0);
-          a1 = fmaf(load_as_f32<XT>(x, i + 1), W[(long)(i + 1) * ldw + c], a1);
-        }
-        for (; i < d; ++i) a0 = fmaf(load_as_f32<XT>(x, i), W[(long)i * ldw + c], a0);
-      }
-      out[q] = a0 + a1;
-    }
-  }
-}
-
-// k largest of the C values spread as in wave_logits; ties to the lower
-// column.  sel/val receive columns and values, best first (wave-uniform).
-template <int NQ, int KMAX>
-__device__ void wave_topk(const float (&v)[NQ], int C, int k, int lane, int (&sel)[KMAX],
-                          float (&val)[KMAX]) {
-  bool taken[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) taken[q] = false;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int c = lane + 64 * q;
-        // a NaN score ranks as -inf, so every untaken column stays a
-        // candidate and the result is always a valid column
-        const float vq = (v[q] == v[q]) ? v[q] : -INFINITY;
-        if (c < C && !taken[q] && (vq > bv || (vq == bv && c < bi))) {
-          bv = vq;
-          bi = c;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        float ov = __shfl_xor(bv, off);
-        int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      sel[j] = bi;
-      val[j] = bv;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        if (lane + 64 * q == bi) taken[q] = true;
-    } else {
-      sel[j] = 0;
-      val[j] = 0.f;
-    }
-  }
-}
-
-template <int KMAX>
-__device__ void softmax_sel(const float (&val)[KMAX], int k, float (&p)[KMAX]) {
-  float m = val[0];
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    p[j] = (j < k) ? expf(val[j] - m) : 0.f;
-    s += p[j];
-  }
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) p[j] = p[j] / s;
-}
-
+// ------------------------------------------------------------- logits --
+// Output blocks (32 score columns c, 32 tokens t) over depth k with
+// v_mfma_f32_32x32x2f32: A[c][k] from the router matrix, B[k][t] from X.
+// Sixteen k at a time: lane half h supplies k = base + 8h + s in step s, so
+// a lane reads 8 consecutive activations of its token (16 bytes, once for
+// every column block) and 8 consecutive (re-laid-out) weights of its column.
 template <int XT>
-__global__ __launch_bounds__(256) void router_generic_kernel(RouteArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  using XE = typename Elem<XT>::T;
-  const XE* x = static_cast<const XE*>(a.X) + (long)t * a.d;
-
-  // level 1: groups
-  float s[4];
-  wave_logits<XT, 4>(x, a.d, a.Wg, a.G, a.G, lane, s);
-  if (a.gbias) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int c = lane + 64 * q;
-      if (c < a.G) s[q] += a.gbias[c];
-    }
-  }
-  int gsel[MAX_KG];
-  float gval[MAX_KG], p[MAX_KG];
-  wave_topk<4, MAX_KG>(s, a.G, a.kg, lane, gsel, gval);
-  softmax_sel<MAX_KG>(gval, a.kg, p);
-
-  // level 2: experts inside each chosen group
-#pragma unroll
-  for (int ga = 0; ga < MAX_KG; ++ga) {
-    if (ga >= a.kg) break;
-    const int g = gsel[ga];
-    if (a.K == 1) {
-      if (lane == 0) {
-        const int slot = t * a.k + ga;
-        a.idx[slot] = g;
-        a.w[slot] = p[ga];
-        atomicAdd(&a.ccount[(slot / CHUNK) * a.E + g], 1);
-      }
-    } else {
-      float e[4];
-      wave_logits<XT, 4>(x, a.d, a.We + (long)g * a.d * a.K, a.K, a.K, lane, e);
-      if (a.ebias) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int c = lane + 64 * q;
-          if (c < a.K) e[q] += a.ebias[g * a.K + c];
-        }
-      }
-      int jsel[MAX_SLOTS];
-      float jval[MAX_SLOTS], q[MAX_SLOTS];
-      wave_topk<4, MAX_SLOTS>(e, a.K, a.ke, lane, jsel, jval);
-      softmax_sel<MAX_SLOTS>(jval, a.ke, q);
-      if (lane == 0) {
-#pragma unroll
-        for (int b = 0; b < MAX_SLOTS; ++b) {
-          if (b >= a.ke) break;
-          const int slot = t * a.k + ga * a.ke + b;
-          const int ex = g * a.K + jsel[b];
-          a.idx[slot] = ex;
-          a.w[slot] = p[ga] * q[b];
-          atomicAdd(&a.ccount[(slot / CHUNK) * a.E + ex], 1);
-        }
-      }
-    }
-    if (lane == 0) {
-      const int gslot = t * a.kg + ga;
-      a.gidx[gslot] = g;
-      atomicAdd(&a.cgcount[(gslot / CHUNK) * a.G + g], 1);
-    }
-  }
-}
-
-
-// ---------------------------------------------------------------------------
-// Router for the common shapes (G and K fixed at compile time, each a
-// multiple of 4 up to 16, or K = 1).  Wavefront w routes TPW tokens
-// together.  Lane l owns rows 4 (l + 64 m) .. +3 of d (m < d / 256) and
-// loads them as vectors: 4 activations per token and 4 rows of the router
-// matrix (row-major, so 4 * C consecutive floats, read as 16-byte vectors).
-// The group-level pass shares every weight load among the TPW tokens; the
-// expert-level pass runs once per (token, chosen group).  The loops carry no
-// branches, so the loads of a step are all in flight together.  One xor
-// butterfly per logit leaves every lane holding every logit, so the top-k
-// and the softmax run per lane without further cross-lane traffic.
-template <int XT>
-__device__ __forceinline__ void load4(const typename Elem<XT>::T* p, float (&v)[4]) {
+__device__ __forceinline__ void load8x(const typename Elem<XT>::T* p, float (&v)[8]) {
   if constexpr (XT == DT_F32) {
-    f4v q = *reinterpret_cast<const f4v*>(p);
-    v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+    const f4v q0 = *reinterpret_cast<const f4v*>(p);
+    const f4v q1 = *reinterpret_cast<const f4v*>(p + 4);
+    v[0] = q0[0]; v[1] = q0[1]; v[2] = q0[2]; v[3] = q0[3];
+    v[4] = q1[0]; v[5] = q1[1]; v[6] = q1[2]; v[7] = q1[3];
   } else {
-    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
-    u2v q = *reinterpret_cast<const u2v*>(p);
+    const u4v q = *reinterpret_cast<const u4v*>(p);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       const uint16_t b = static_cast<uint16_t>((q[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
       v[e] = (XT == DT_F16) ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
     }
   }
 }
 
-// acc[p][c] = sum over d of x_p[i] W[i][c] for NT token rows and the C
-// columns of W (row stride C); totals end up in every lane.
-template <int XT, int NT, int C>
-__device__ __forceinline__ void dot_pass(const typename Elem<XT>::T* const (&xs)[NT],
-                                         const float* W, int d, int lane, float (&acc)[NT][C]) {
-#pragma unroll
-  for (int p = 0; p < NT; ++p)
-#pragma unroll
-    for (int c = 0; c < C; ++c) acc[p][c] = 0.f;
-  const int steps = d / 256;
-#pragma unroll 2
-  for (int m = 0; m < steps; ++m) {
-    const int i0 = 4 * (lane + 64 * m);
-    float x[NT][4];
-#pragma unroll
-    for (int p = 0; p < NT; ++p) load4<XT>(xs[p] + i0, x[p]);
-    f4v wv[4][C / 4];
-    const float* w = W + (long)i0 * C;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int c4 = 0; c4 < C / 4; ++c4) wv[e][c4] = *reinterpret_cast<const f4v*>(w + e * C + 4 * c4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int c4 = 0; c4 < C / 4; ++c4)
-#pragma unroll
-        for (int p = 0; p < NT; ++p)
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) acc[p][4 * c4 + cc] = fmaf(x[p][e], wv[e][c4][cc], acc[p][4 * c4 + cc]);
-  }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1)
-#pragma unroll
-    for (int p = 0; p < NT; ++p)
-#pragma unroll
-      for (int c = 0; c < C; ++c) acc[p][c] += __shfl_xor(acc[p][c], off);
-}
-
-// k best of v[0..C) (descending, ties to the lower index), in every lane.
-template <int C, int KMAX>
-__device__ __forceinline__ void topk_local(const float (&v)[C], int k, int (&sel)[KMAX],
-                                           float (&val)[KMAX]) {
-  uint32_t taken = 0;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    float bv = -INFINITY;
-    int bi = -1;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const float x = (v[c] == v[c]) ? v[c] : -INFINITY;  // NaN ranks as -inf
-      if (!((taken >> c) & 1u) && (bi < 0 || x > bv)) {
-        bv = x;
-        bi = c;
-      }
-    }
-    if (j < k) {
-      sel[j] = bi;
-      val[j] = bv;
-      taken |= 1u << bi;
-    } else {
-      sel[j] = 0;
-      val[j] = 0.f;
-    }
-  }
-}
-
-template <int XT, int TPW, int CG, int CK>
-__global__ __launch_bounds__(256) void router_fast_kernel(RouteArgs a) {
+// Partial scores of one wavefront: token block tb, score-column blocks
+// cb0 .. cb0 + NCB - 1, depth [k0, k0 + kq) (kq a multiple of 16).  Lane l
+// ends with token tb*32 + l % 32 and columns cb*32 + 8 (v / 4) + 4 (l / 32)
+// + v % 4 in acc[cb - cb0][v].  The next 16 k are loaded before the
+// current 16 k's MFMAs (two register sets, loop unrolled by two).
+template <int XT, int NCB>
+__device__ __forceinline__ void score_tiles(const RouteArgs& a, int tb, int cb0, int k0, int kq, int lane,
+                                            f16v (&acc)[NCB]) {
   using XE = typename Elem<XT>::T;
-  const int lane = threadIdx.x & 63;
-  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
-  if (t0 >= a.T) return;
-  const int nt = min(TPW, a.T - t0);
-  const XE* X = static_cast<const XE*>(a.X);
-  const XE* xs[TPW];
+  const int h = lane >> 5;
+  int tok = tb * 32 + (lane & 31);
+  tok = tok < a.T ? tok : a.T - 1;  // rows past the batch repeat the last one
+  const XE* xp = static_cast<const XE*>(a.X) + (long)tok * a.d + k0 + 8 * h;
+  const float* wp = a.Wr + ((long)(k0 / 16) * a.NCp + cb0 * 32 + (lane & 31)) * 16 + 8 * h;
+  const long wstep = (long)a.NCp * 16;
 #pragma unroll
-  for (int p = 0; p < TPW; ++p) xs[p] = X + (long)(t0 + (p < nt ? p : 0)) * a.d;
-
-  // level 1: group logits, one weight load shared by the TPW tokens
-  float s[TPW][CG];
-  dot_pass<XT, TPW, CG>(xs, a.Wg, a.d, lane, s);
+  for (int c = 0; c < NCB; ++c)
 #pragma unroll
-  for (int p = 0; p < TPW; ++p) {
-    if (p >= nt) break;
-    const int t = t0 + p;
-    if (a.gbias) {
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+  const int n16 = kq / 16;
+  if (n16 == 0) return;
+  float xa[8], xb[8];
+  f4v wa[NCB][2], wb[NCB][2];
+  auto issue = [&](int i, float (&xv)[8], f4v (&wv)[NCB][2]) {
+    const int ic = i < n16 ? i : n16 - 1;  // the last group re-reads itself
+    load8x<XT>(xp + ic * 16, xv);
 #pragma unroll
-      for (int c = 0; c < CG; ++c) s[p][c] += a.gbias[c];
+    for (int c = 0; c < NCB; ++c) {
+      const float* q = wp + ic * wstep + c * 32 * 16;
+      wv[c][0] = *reinterpret_cast<const f4v*>(q);
+      wv[c][1] = *reinterpret_cast<const f4v*>(q + 4);
     }
-    int gsel[MAX_KG];
-    float gval[MAX_KG], pg[MAX_KG];
-    topk_local<CG, MAX_KG>(s[p], a.kg, gsel, gval);
-    softmax_sel<MAX_KG>(gval, a.kg, pg);
-    // level 2: expert logits of each chosen group
+  };
+  auto mma = [&](const float (&xv)[8], const f4v (&wv)[NCB][2]) {
 #pragma unroll
-    for (int ga = 0; ga < MAX_KG; ++ga) {
-      if (ga >= a.kg) break;
-      const int g = gsel[ga];
-      if constexpr (CK == 1) {
-        if (lane == 0) {
-          const int slot = t * a.k + ga;
-          a.idx[slot] = g;
-          a.w[slot] = pg[ga];
-          atomicAdd(&a.ccount[(slot / CHUNK) * a.E + g], 1);
-        }
-      } else {
-        const XE* x1[1] = {xs[p]};
-        float e[1][CK];
-        dot_pass<XT, 1, CK>(x1, a.We + (long)g * a.d * CK, a.d, lane, e);
-        if (a.ebias) {
+    for (int c = 0; c < NCB; ++c)
 #pragma unroll
-          for (int c = 0; c < CK; ++c) e[0][c] += a.ebias[g * CK + c];
-        }
-        int js[MAX_SLOTS];
-        float jv[MAX_SLOTS], qw[MAX_SLOTS];
-        topk_local<CK, MAX_SLOTS>(e[0], a.ke, js, jv);
-        softmax_sel<MAX_SLOTS>(jv, a.ke, qw);
-        if (lane == 0) {
-#pragma unroll
-          for (int b = 0; b < MAX_SLOTS; ++b) {
-            if (b >= a.ke) break;
-            const int slot = t * a.k + ga * a.ke + b;
-            const int ex = g * CK + js[b];
-            a.idx[slot] = ex;
-            a.w[slot] = pg[ga] * qw[b];
-            atomicAdd(&a.ccount[(slot / CHUNK) * a.E + ex], 1);
-          }
-        }
-      }
-      if (lane == 0) {
-        const int gslot = t * a.kg + ga;
-        a.gidx[gslot] = g;
-        atomicAdd(&a.cgcount[(gslot / CHUNK) * a.G + g], 1);
-      }
-    }
+      for (int st = 0; st < 8; ++st)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(wv[c][st >> 2][st & 3], xv[st], acc[c], 0, 0, 0);
+  };
+  issue(0, xa, wa);
+  int i = 0;
+  for (; i + 2 <= n16; i += 2) {
+    issue(i + 1, xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(i + 2, xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (i < n16) mma(xa, wa);
+}
+
+// grid: (token blocks of 32) x (score-column blocks of 32) x splits.  The 4
+// wavefronts take consecutive quarters of the split's k range; their sums
+// meet in LDS.  Output: L[split][t][NCp].
+template <int XT>
+__global__ __launch_bounds__(256) void logits_kernel(RouteArgs a) {
+  __shared__ __attribute__((aligned(16))) float red[4][16][64];
+  const int nct = a.NCp / 32;
+  const int tb = blockIdx.x % ((a.T + 31) / 32);
+  const int rest = blockIdx.x / ((a.T + 31) / 32);
+  const int cb = rest % nct, split = rest / nct;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int kq = a.d / (4 * a.nsplit);  // k per wavefront (multiple of 16)
+  f16v acc[1];
+  score_tiles<XT, 1>(a, tb, cb, (split * 4 + wave) * kq, kq, lane, acc);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[wave][v][lane] = acc[0][v];
+  __syncthreads();
+  // thread (vg, lane): rows 8 vg + 4 h .. +3 of the block for token lane % 32
+  const int vg = threadIdx.x >> 6;
+  const int t = tb * 32 + (lane & 31);
+  if (t < a.T) {
+    f4v o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = 4 * vg + q;
+      o[q] = (red[0][v][lane] + red[1][v][lane]) + (red[2][v][lane] + red[3][v][lane]);
+    }
+    *reinterpret_cast<f4v*>(a.L + ((long)split * a.T + t) * a.NCp + cb * 32 + 8 * vg + 4 * h) = o;
+  }
+}
+
+// ------------------------------------------------------------- select --
+// One thread per token walks its scores (biases included): the group
+// scores, then the chosen groups' expert scores, keeping the best n
+// (larger score first, ties to the lower index, NaN ranked last).  With
+// count_experts off the per-chunk expert counters are left alone (only the
+// group lists are built).
+template <int NMAX>
+__device__ __forceinline__ void keep_best(float v, int i, int n, float (&bv)[NMAX], int (&bi)[NMAX]) {
+  v = (v == v) ? v : -INFINITY;
+  if (bi[n - 1] >= 0 && !(v > bv[n - 1])) return;
+  int p = n - 1;
+  while (p > 0 && (bi[p - 1] < 0 || v > bv[p - 1])) {
+    bv[p] = bv[p - 1];
+    bi[p] = bi[p - 1];
+    --p;
+  }
+  bv[p] = v;
+  bi[p] = i;
+}
+
+// lcg / lce (optional): LDS counters [chunk - cg0][G] and [chunk - ce0][E]
+// that the caller flushes to the global per-chunk counters once per
+// workgroup (one global atomic per (chunk, bin) instead of one per token).
+__device__ void select_token(const RouteArgs& a, int t, const float* st, int* lcg = nullptr, int cg0 = 0,
+                             int* lce = nullptr, int ce0 = 0) {
+  // level 1: groups
+  float gv[MAX_KG];
+  int gi[MAX_KG];
+  for (int q = 0; q < MAX_KG; ++q) {
+    gv[q] = -INFINITY;
+    gi[q] = -1;
+  }
+  for (int g = 0; g < a.G; ++g) keep_best<MAX_KG>(st[g], g, a.kg, gv, gi);
+  float ps = 0.f;
+  for (int q = 0; q < a.kg; ++q) ps += expf(gv[q] - gv[0]);
+  // level 2: experts inside each chosen group, in selection order
+  for (int ga = 0; ga < a.kg; ++ga) {
+    const int g = gi[ga];
+    const float pg = expf(gv[ga] - gv[0]) / ps;
+    if (a.K == 1) {
+      const int slot = t * a.k + ga;
+      a.idx[slot] = g;
+      a.w[slot] = pg;
+      if (a.count_experts) {
+        if (lce) atomicAdd(&lce[(slot / CHUNK - ce0) * a.E + g], 1);
+        else atomicAdd(&a.ccount[(slot / CHUNK) * a.E + g], 1);
+      }
+    } else {
+      float ev[MAX_SLOTS];
+      int ei[MAX_SLOTS];
+      for (int q = 0; q < MAX_SLOTS; ++q) {
+        ev[q] = -INFINITY;
+        ei[q] = -1;
+      }
+      const float* se = st + a.G + g * a.K;
+      for (int j = 0; j < a.K; ++j) keep_best<MAX_SLOTS>(se[j], j, a.ke, ev, ei);
+      float qs = 0.f;
+      for (int b = 0; b < a.ke; ++b) qs += expf(ev[b] - ev[0]);
+      for (int b = 0; b < a.ke; ++b) {
+        const int slot = t * a.k + ga * a.ke + b;
+        const int ex = g * a.K + ei[b];
+        a.idx[slot] = ex;
+        a.w[slot] = pg * (expf(ev[b] - ev[0]) / qs);
+        if (a.count_experts) {
+          if (lce) atomicAdd(&lce[(slot / CHUNK - ce0) * a.E + ex], 1);
+          else atomicAdd(&a.ccount[(slot / CHUNK) * a.E + ex], 1);
+        }
+      }
+    }
+    const int gslot = t * a.kg + ga;
+    a.gidx[gslot] = g;
+    if (lcg) atomicAdd(&lcg[(gslot / CHUNK - cg0) * a.G + g], 1);
+    else atomicAdd(&a.cgcount[(gslot / CHUNK) * a.G + g], 1);
+  }
+}
+
+__device__ __forceinline__ float score_bias(const RouteArgs& a, int c) {
+  if (c < a.G) return a.gbias ? a.gbias[c] : 0.f;
+  return a.ebias ? a.ebias[c - a.G] : 0.f;
+}
+
+// A workgroup takes tpb consecutive tokens: its 256 threads first sum the
+// k-split partials of all their scores (plus the biases) into LDS, then one
+// thread per token selects.
+__global__ __launch_bounds__(256) void select_kernel(RouteArgs a, int tpb) {
+  extern __shared__ float sc[];  // [tpb][NC]
+  const int NC = a.G + (a.K > 1 ? a.G * a.K : 0);
+  const int t0 = blockIdx.x * tpb;
+  const int nt = min(tpb, a.T - t0);
+  const long stride = (long)a.T * a.NCp;
+  for (int e = threadIdx.x; e < nt * NC; e += 256) {
+    const int tk = e / NC, c = e - tk * NC;
+    const float* p = a.L + (long)(t0 + tk) * a.NCp + c;
+    float s0 = p[0], s1 = 0.f;
+    int sp = 1;
+    for (; sp + 1 < a.nsplit; sp += 2) {
+      s0 += p[sp * stride];
+      s1 += p[(sp + 1) * stride];
+    }
+    if (sp < a.nsplit) s0 += p[sp * stride];
+    sc[e] = (s0 + s1) + score_bias(a, c);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nt) select_token(a, t0 + threadIdx.x, sc + threadIdx.x * NC);
+}
+
+// Scores and selection in one kernel when a 32-token block's scores fit one
+// workgroup (at most 4 column blocks): wavefront w computes k quarter w of
+// every column block, the quarters meet in LDS, and 32 threads select.
+template <int XT, int NCB>
+__global__ __launch_bounds__(256) void route_fused_kernel(RouteArgs a) {
+  __shared__ __attribute__((aligned(16))) float red[4][NCB][16][64];
+  __shared__ float sc[32][NCB * 32 + 1];
+  // per-workgroup routing counts: 32 tokens span at most 2 group-list chunks
+  // and 3 expert-list chunks of 256 assignments
+  __shared__ int lcg[2 * 256];
+  __shared__ int lce[3 * 1024];
+  const int tb = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kq = a.d / 4;
+  for (int i = threadIdx.x; i < 2 * a.G; i += 256) lcg[i] = 0;
+  if (a.count_experts)
+    for (int i = threadIdx.x; i < 3 * a.E; i += 256) lce[i] = 0;
+  {
+    f16v acc[NCB];
+    score_tiles<XT, NCB>(a, tb, 0, wave * kq, kq, lane, acc);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[wave][cb][v][lane] = acc[cb][v];
+  }
+  __syncthreads();
+  const int NC = a.G + (a.K > 1 ? a.G * a.K : 0);
+  for (int e = threadIdx.x; e < NCB * 16 * 64; e += 256) {
+    const int cb = e / (16 * 64), v = (e / 64) % 16, l = e % 64;
+    const int c = cb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    if (c < NC)
+      sc[l & 31][c] = ((red[0][cb][v][l] + red[1][cb][v][l]) + (red[2][cb][v][l] + red[3][cb][v][l])) + score_bias(a, c);
+  }
+  __syncthreads();
+  const int t = tb * 32 + threadIdx.x;
+  const int t0 = tb * 32;
+  const int cg0 = t0 * a.kg / CHUNK, ce0 = t0 * a.k / CHUNK;
+  if (threadIdx.x < 32 && t < a.T) select_token(a, t, sc[threadIdx.x], lcg, cg0, lce, ce0);
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * a.G; i += 256)
+    if (lcg[i]) atomicAdd(&a.cgcount[(cg0 + i / a.G) * a.G + i % a.G], lcg[i]);
+  if (a.count_experts)
+    for (int i = threadIdx.x; i < 3 * a.E; i += 256)
+      if (lce[i]) atomicAdd(&a.ccount[(ce0 + i / a.E) * a.E + i % a.E], lce[i]);
 }
 
 // Exclusive scan of n (<= 1024) ints held in lds_in into lds_out[0..n];
@@ -460,7 +386,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   extern __shared__ int lds[];
   const int b = blockIdx.x;
   // with no assignments block 0 still publishes zero counts and offsets
-  if (b < (a.nch_e > 0 ? a.nch_e : 1))
+  if (a.do_experts && b < (a.nch_e > 0 ? a.nch_e : 1))
     bin_scatter(b, a.T * a.k, a.k, a.E, a.idx, a.ccount, a.nch_e, a.counts, a.offsets, a.perm,
                 nullptr, lds);
   if (b < (a.nch_g > 0 ? a.nch_g : 1))
@@ -474,47 +400,62 @@ __global__ void zero_kernel(int* p, int n) {
 
 }  // namespace
 
-template <int XT, int TPW, int CG, int CK>
-hipError_t launch_fast(const RouteArgs& a, hipStream_t st) {
-  const int waves = (a.T + TPW - 1) / TPW;
-  hipLaunchKernelGGL((router_fast_kernel<XT, TPW, CG, CK>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
+template <int XT>
+hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
+  const unsigned grid = (unsigned)((a.T + 31) / 32) * (a.NCp / 32) * a.nsplit;
+  hipLaunchKernelGGL(logits_kernel<XT>, dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int XT, int CG, int CK>
-hipError_t launch_tpw(const RouteArgs& a, hipStream_t st) {
-  // several tokens per wavefront once there are enough tokens to fill the chip
-  if (a.T >= 8192) return launch_fast<XT, 4, CG, CK>(a, st);
-  if (a.T >= 2048) return launch_fast<XT, 2, CG, CK>(a, st);
-  return launch_fast<XT, 1, CG, CK>(a, st);
-}
-
 template <int XT>
-hipError_t launch_router_t(const RouteArgs& a, hipStream_t st) {
-  if (a.d % 256 == 0) {
-    const int key = a.G * 100 + a.K;
-    switch (key) {
-      case 404: return launch_tpw<XT, 4, 4>(a, st);
-      case 808: return launch_tpw<XT, 8, 8>(a, st);
-      case 1616: return launch_tpw<XT, 16, 16>(a, st);
-      case 401: return launch_tpw<XT, 4, 1>(a, st);
-      case 801: return launch_tpw<XT, 8, 1>(a, st);
-      case 1601: return launch_tpw<XT, 16, 1>(a, st);
-      default: break;
-    }
+hipError_t launch_fused(const RouteArgs& a, int ncb, hipStream_t st) {
+  const dim3 grid((a.T + 31) / 32);
+  switch (ncb) {
+    case 1: hipLaunchKernelGGL((route_fused_kernel<XT, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((route_fused_kernel<XT, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((route_fused_kernel<XT, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((route_fused_kernel<XT, 4>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(router_generic_kernel<XT>, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
-  switch (x_dtype) {
-    case DT_F32: return launch_router_t<DT_F32>(a, st);
-    case DT_F16: return launch_router_t<DT_F16>(a, st);
-    case DT_BF16: return launch_router_t<DT_BF16>(a, st);
+  hipError_t e = hipErrorInvalidValue;
+  const int ncb = a.NCp / 32;
+  if (a.nsplit == 1 && ncb <= 4) {
+    switch (x_dtype) {
+      case DT_F32: return launch_fused<DT_F32>(a, ncb, st);
+      case DT_F16: return launch_fused<DT_F16>(a, ncb, st);
+      case DT_BF16: return launch_fused<DT_BF16>(a, ncb, st);
+    }
+    return e;
   }
-  return hipErrorInvalidValue;
+  switch (x_dtype) {
+    case DT_F32: e = launch_logits<DT_F32>(a, st); break;
+    case DT_F16: e = launch_logits<DT_F16>(a, st); break;
+    case DT_BF16: e = launch_logits<DT_BF16>(a, st); break;
+  }
+  if (e != hipSuccess) return e;
+  // tokens per selection workgroup: about 64 workgroups for small batches,
+  // at most 64 tokens and 64 KiB of scores each
+  const int NC = a.G + (a.K > 1 ? a.G * a.K : 0);
+  int tpb = 1;
+  while (tpb < 64 && (long)a.T >= 64L * 2 * tpb && (size_t)2 * tpb * NC * sizeof(float) <= 65536) tpb *= 2;
+  const size_t lds = (size_t)tpb * NC * sizeof(float);
+  hipLaunchKernelGGL(select_kernel, dim3((a.T + tpb - 1) / tpb), dim3(256), lds, st, a, tpb);
+  return hipGetLastError();
+}
+
+// k splits of the router GEMM: enough workgroups for the chip, each
+// wavefront keeping at least 64 of the d products.
+int router_splits(int T, int d, int NCp) {
+  if (NCp <= 128) return 1;  // scores and selection fused
+  const long blocks = (long)((T + 31) / 32) * (NCp / 32);
+  int s = 1;
+  while (blocks * s < 256 && d % (4 * 16 * 2 * s) == 0 && d / (4 * 2 * s) >= 64) s *= 2;
+  return s;
 }
 
 size_t scatter_lds_bytes(int E, int G) {
@@ -523,7 +464,7 @@ size_t scatter_lds_bytes(int E, int G) {
 }
 
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st) {
-  int nblk = a.nch_e > a.nch_g ? a.nch_e : a.nch_g;
+  int nblk = (a.do_experts && a.nch_e > a.nch_g) ? a.nch_e : a.nch_g;
   if (nblk <= 0) nblk = 1;  // T == 0 still publishes zero counts and offsets
   hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(256), scatter_lds_bytes(a.E, a.G), st, a);
   return hipGetLastError();

@@ -175,12 +175,16 @@ struct TShared {
 // above), so 32 columns x one 64-deep stage is 4 consecutive fragments.
 // WFrag: plain TY fragments.  WInt4: 8 nibbles per lane plus scales, decoded
 // by a functor (scale layout differs by matrix).
+// ks0: first k-step of the range a caller walks (k-split kernels).
 template <int TY>
 struct WPlain {
   using Raw = FragT<TY>;
   const FragT<TY>* base;  // block 0 of this matrix
   int KS;                 // k-steps (Kd / 16)
-  __device__ Raw load(int nb, int kstep, int lane) const { return base[((long)nb * KS + kstep) * 64 + lane]; }
+  int ks0 = 0;
+  __device__ Raw load(int nb, int kstep, int lane) const {
+    return base[((long)nb * KS + ks0 + kstep) * 64 + lane];
+  }
   __device__ FragT<TY> decode(const Raw& r, int, int, int) const { return r; }
 };
 
@@ -195,7 +199,9 @@ struct WInt4ColK {
   const uint32_t* words;
   const uint16_t* scales;
   int KS;
+  int ks0 = 0;
   __device__ Raw load(int nb, int kstep, int lane) const {
+    kstep += ks0;
     Raw r;
     r.w = words[((long)nb * KS + kstep) * 64 + lane];
     r.s = scales[((long)nb * (KS / 2) + 2 * (kstep >> 2) + (lane >> 5)) * 32 + (lane & 31)];
@@ -276,15 +282,21 @@ struct WShared {
 // ---------------------------------------------------------------- mainloop --
 // KT stages of 64 k.  TSH / WSH: the token / weight operand is shared
 // through LDS (tl / wl point at two stage buffers each).  wm, wn: this
-// wavefront's position in the WM x WN arrangement.
+// wavefront's position in the WM x WN arrangement.  PD: how many stages
+// ahead the global loads run (1 when a stage's MFMAs cover the memory
+// latency, 2 or 3 for short tiles).
 //
-// Per stage: the loads of stage kt+1 are issued first (the last stage
-// re-issues its own, harmlessly, so no load sits in a branch), then the
-// 4 k-steps of MFMAs with LDS fragments read one k-step ahead, then the
-// staged registers are converted and written to the other LDS buffer and
-// the workgroup synchronises once.
-template <int TY, int RT, int CB, bool TSH, bool WSH, class TO, class WO>
+// Per stage: the loads of stage kt + PD are issued first (stages past the
+// end re-issue the last one, harmlessly, so no load sits in a branch), then
+// the 4 k-steps of MFMAs with LDS fragments read one k-step ahead, then the
+// staged registers of stage kt + 1 are converted and written to the other
+// LDS buffer and the workgroup synchronises once.  Register sets rotate
+// through a ring of U = PD + 1 (the loop is unrolled U times so every index
+// is static); with PD = 1 the LDS staging needs a single set.
+template <int TY, int RT, int CB, bool TSH, bool WSH, class TO, class WO, int PD = 1>
 struct Mainloop {
+  static constexpr int U = PD + 1;
+  static constexpr int NTS = (PD == 1) ? 1 : U;  // LDS staging register sets
   using F = FragT<TY>;
   const TO& to;
   const WO& wo;
@@ -307,18 +319,27 @@ struct Mainloop {
   }
 
   template <class TS, class WS, class TR, class WR>
-  __device__ __forceinline__ void stage(int kt, int KT, f16v (&acc)[RT][CB], TS& ts, WS& ws, const TR& tcur,
-                                        TR& tnxt, const WR& wcur, WR& wnxt) const {
-    const int kn = (kt + 1 < KT) ? kt + 1 : kt;
-    if constexpr (TSH) to.fetch(kn, ts); else to.fetch(kn, tnxt);
-    if constexpr (WSH) wo.fetch(kn, ws); else wo.fetch(kn, lane, wnxt);
+  __device__ __forceinline__ void fetch(int kn, TS& ts, WS& ws, TR& tr, WR& wr) const {
+    if constexpr (TSH) to.fetch(kn, ts); else to.fetch(kn, tr);
+    if constexpr (WSH) wo.fetch(kn, ws); else wo.fetch(kn, lane, wr);
+  }
+
+  template <int u, class TS, class WS, class TR, class WR>
+  __device__ __forceinline__ void stage(int kt, int KT, f16v (&acc)[RT][CB], TS (&ts)[NTS], WS (&ws)[NTS],
+                                        TR (&tr)[U], WR (&wr)[U]) const {
+    constexpr int fs = (u + PD) % U;          // ring slot of stage kt + PD
+    constexpr int ns = (u + 1) % U;           // ring slot of stage kt + 1
+    constexpr int tf_ = (PD == 1) ? 0 : fs;   // staging set receiving stage kt + PD
+    constexpr int tc_ = (PD == 1) ? 0 : ns;   // staging set holding stage kt + 1
+    const int kn = (kt + PD < KT) ? kt + PD : KT - 1;
+    fetch(kn, ts[tf_], ws[tf_], tr[fs], wr[fs]);
     __builtin_amdgcn_sched_barrier(0);
     const int b = kt & 1;
     F tf[2][RT], wf[2][CB];
-    frags(b, 0, tcur, wcur, tf[0], wf[0]);
+    frags(b, 0, tr[u], wr[u], tf[0], wf[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) frags(b, s + 1, tcur, wcur, tf[(s + 1) & 1], wf[(s + 1) & 1]);
+      if (s + 1 < 4) frags(b, s + 1, tr[u], wr[u], tf[(s + 1) & 1], wf[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -326,26 +347,40 @@ struct Mainloop {
         for (int c = 0; c < CB; ++c) acc[t][c] = mfma32<TY>(wf[s & 1][c], tf[s & 1][t], acc[t][c]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (TSH) to.commit(ts, tl + (b ^ 1) * TO::frags_per_stage);
-    if constexpr (WSH) wo.commit(ws, wl + (b ^ 1) * WO::frags_per_stage);
+    if constexpr (TSH) to.commit(ts[tc_], tl + (b ^ 1) * TO::frags_per_stage);
+    if constexpr (WSH) wo.commit(ws[tc_], wl + (b ^ 1) * WO::frags_per_stage);
     if constexpr (TSH || WSH) __syncthreads();
   }
 
   template <class TS, class WS, class TR, class WR>
   __device__ void run(int KT, f16v (&acc)[RT][CB]) const {
-    TS ts;
-    WS ws;
-    TR t0, t1;
-    WR w0, w1;
-    if constexpr (TSH) { to.fetch(0, ts); to.commit(ts, tl); } else to.fetch(0, t0);
-    if constexpr (WSH) { wo.fetch(0, ws); wo.commit(ws, wl); } else wo.fetch(0, lane, w0);
+    TS ts[NTS];
+    WS ws[NTS];
+    TR tr[U];
+    WR wr[U];
+    // stages 0 .. PD-1 in flight, stage 0 in LDS
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+      const int kn = p < KT ? p : KT - 1;
+      fetch(kn, ts[(PD == 1) ? 0 : p], ws[(PD == 1) ? 0 : p], tr[p], wr[p]);
+    }
+    if constexpr (TSH) to.commit(ts[0], tl);
+    if constexpr (WSH) wo.commit(ws[0], wl);
     if constexpr (TSH || WSH) __syncthreads();
     int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-      stage(kt, KT, acc, ts, ws, t0, t1, w0, w1);
-      stage(kt + 1, KT, acc, ts, ws, t1, t0, w1, w0);
+    for (; kt + U <= KT; kt += U) {
+      stage<0>(kt, KT, acc, ts, ws, tr, wr);
+      stage<1>(kt + 1, KT, acc, ts, ws, tr, wr);
+      if constexpr (U > 2) stage<2>(kt + 2, KT, acc, ts, ws, tr, wr);
+      if constexpr (U > 3) stage<3>(kt + 3, KT, acc, ts, ws, tr, wr);
     }
-    if (kt < KT) stage(kt, KT, acc, ts, ws, t0, t1, w0, w1);
+    if (kt < KT) stage<0>(kt, KT, acc, ts, ws, tr, wr);
+    if constexpr (U > 2) {
+      if (kt + 1 < KT) stage<1>(kt + 1, KT, acc, ts, ws, tr, wr);
+    }
+    if constexpr (U > 3) {
+      if (kt + 2 < KT) stage<2>(kt + 2, KT, acc, ts, ws, tr, wr);
+    }
   }
 };
 

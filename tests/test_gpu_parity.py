@@ -1,7 +1,7 @@
 """HIP library vs the CPU oracle on seeded inputs, through the C ABI.
 
 Routing indices, permutations and INT4 codes must match bit for bit; gate
-weights to 1e-6; layer outputs to max|y - y_ref| / max|y_ref| <= 1e-5 (fp32)
+weights to 1e-6 * max(1, sqrt(d / 1024)) (FP32 scores); layer outputs to max|y - y_ref| / max|y_ref| <= 1e-5 (fp32)
 or 1e-2 (fp16 / bf16).  Inputs have every routing margin above 1e-3.
 """
 import dataclasses
@@ -22,11 +22,20 @@ def _lib():
     return L
 
 
+def gate_tol(d: int) -> float:
+    """Bound on |w_gpu - w_oracle|.  The router runs in FP32 (the MoE routing
+    page, section 3.1): a score is a sum of d FP32 products whose rounding
+    error grows like sqrt(d) ulps of the partial sums, and a gate weight
+    (a softmax of score differences) moves by at most half the score error.
+    1e-6 covers d = 1024 with room; it is scaled by sqrt(d / 1024)."""
+    return 1e-6 * max(1.0, (d / 1024) ** 0.5)
+
+
 def check_routing(got: dict, rt: dict, w, T: int):
     E, G, k, kg = w.E, w.G, w.k, w.top_groups
     assert np.array_equal(got["idx"], rt["idx"]), "expert indices differ"
     assert np.array_equal(got["gidx"], rt["gidx"]), "group indices differ"
-    assert np.abs(got["w"] - rt["w"]).max(initial=0.0) <= 1e-6
+    assert np.abs(got["w"] - rt["w"]).max(initial=0.0) <= gate_tol(w.d)
     counts, offsets, perm = O.permutation(rt["idx"], E)
     assert np.array_equal(got["counts"], counts)
     assert np.array_equal(got["offsets"], offsets)
