@@ -86,6 +86,7 @@ struct moe_handle {
   // tile overrides read from CEFN_BM_{U,G1,G2} (token rows per tile) and
   // CEFN_KS_G2 (k splits of the down projection) at create, for tuning
   int bm_env[3] = {0, 0, 0}, ks_env = 0;
+  int g2k_env = -1;  // CEFN_G2K: 1 / 0 forces the in-workgroup k split of G2 on / off
   // profiling
   bool prof = false;
   int prof_max = 0, prof_calls = 0, prof_mask = -1;
@@ -420,9 +421,12 @@ int pick_bm(const moe_handle* h, int which, int rows, int ntiles, int splits) {
     // GELU keeps two f-blocks of h per wavefront: up to 128 rows without spills
     if (which == GK_G1 && h->cfg.act != MOE_ACT_SWIGLU && bm > 128) continue;
     if (gemm_lds(which, h->mma, bm, h->cfg.K, h->cfg.top_experts) > 160 * 1024) continue;
-    const long tiles = ((long)(rows + bm - 1) / bm) * ntiles * splits;
-    const long rounds = (tiles + 255) / 256;
-    const float cost = rounds * bm / eff[i];
+    // row tiles: every group's last tile is partial (counted as half)
+    const long mt = (rows + bm - 1) / bm + h->cfg.G / 2;
+    const long tiles = mt * ntiles * splits;
+    const int occ = bm <= 64 ? 2 : 1;  // workgroups per compute unit
+    const long rounds = (tiles + 256L * occ - 1) / (256L * occ);
+    const float cost = rounds * (float)bm * occ / eff[i] / splits;
     if (cost < best_cost) {
       best_cost = cost;
       best = bm;
@@ -431,14 +435,39 @@ int pick_bm(const moe_handle* h, int which, int rows, int ntiles, int splits) {
   return best;
 }
 
-// k splits of the down projection: enough workgroups to cover the chip,
-// at least 8 stages of 64 per split.
-int pick_splits(const moe_handle* h, int rows, int ntiles) {
-  if (h->ks_env) return std::max(1, std::min(kMaxSplits, h->ks_env));
-  const int kt = h->cfg.f / 64;
-  int s = 1;
-  while (s < kMaxSplits && kt / (2 * s) >= 8 && ((long)(rows + 127) / 128) * ntiles * s < 256) s *= 2;
-  return s;
+// k splits of the down projection and its tile height together, from a
+// small time model: each round of workgroups costs one tile's MFMA work at
+// a third of the chip's per-unit peak (times the tile height's efficiency),
+// and any split (or more than one chosen group) adds the partial sums that
+// the combine kernel reads back, at 5 TB/s.  Each split keeps at least 8
+// stages of 64.
+void pick_g2(const moe_handle* h, int rows, int ntiles, int& bm, int& splits) {
+  const moe_config& c = h->cfg;
+  const int kt = c.f / 64;
+  const double unit_rate = 2.5e15 / 256 * 0.35;  // flop/s of one compute unit
+  double best = 1e30;
+  bm = 128;
+  splits = 1;
+  for (int s = 1; s <= kMaxSplits; ++s) {
+    if (h->ks_env && s != h->ks_env) continue;
+    if (s > 1 && kt / s < 8) break;
+    for (int b : {256, 128, 64, 32}) {
+      if (h->bm_env[GK_G2] && b != h->bm_env[GK_G2]) continue;
+      if (h->mma == MOE_F32 && b > 64) continue;
+      const long mt = (rows + b - 1) / b + c.G / 2;
+      const int occ = b <= 64 ? 2 : 1;
+      const long rounds = (mt * ntiles * s + 256L * occ - 1) / (256L * occ);
+      const double eff = b >= 256 ? 1.0 : b == 128 ? 0.95 : b == 64 ? 0.75 : 0.5;
+      const double wg = 2.0 * b * 256 * ((double)c.f / s) / (unit_rate * eff);
+      double t = rounds * occ * wg;
+      if (s > 1 || c.top_groups > 1) t += ((double)s * rows * c.d * 4 + (double)rows / c.top_groups * c.d * 2) / 5e12;
+      if (t < best) {
+        best = t;
+        bm = b;
+        splits = s;
+      }
+    }
+  }
 }
 
 int max_mtiles(int T, int kg, int G, int bm) {
@@ -585,6 +614,7 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
       if (const char* v = std::getenv(key)) h->bm_env[i] = std::atoi(v);
     }
     if (const char* v = std::getenv("CEFN_KS_G2")) h->ks_env = std::atoi(v);
+    if (const char* v = std::getenv("CEFN_G2K")) h->g2k_env = std::atoi(v);
   }
 
   // router weights and biases
@@ -795,11 +825,20 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     g2.zero_ptr = h->cc;
     g2.zero_n = h->cc_n;
     const int nt = (c.d + 255) / 256;
-    splits = pick_splits(h, rows, nt);
-    const int bm = pick_bm(h, GK_G2, rows, nt, splits);
-    g2.ksplit = splits;
+    // 256-column tiles with the rows staged through LDS and the k range split
+    // over workgroups; the variant that splits f inside each workgroup over
+    // 64 x 128 tiles is kept as an option (CEFN_G2K=1)
+    const bool ksplit_wg = h->g2k_env > 0;
     pf.begin(5);
-    e = launch_gemm(GK_G2, c.x_dtype, h->mma, bm, g2, max_mtiles(T, kg, c.G, bm), nt, splits, st);
+    if (ksplit_wg) {
+      splits = 1;
+      e = launch_gemm(GK_G2K, c.x_dtype, h->mma, 64, g2, max_mtiles(T, kg, c.G, 64), 1, 1, st);
+    } else {
+      int bm = 128;
+      pick_g2(h, rows, nt, bm, splits);
+      g2.ksplit = splits;
+      e = launch_gemm(GK_G2, c.x_dtype, h->mma, bm, g2, max_mtiles(T, kg, c.G, bm), nt, splits, st);
+    }
     if (e != hipSuccess) return hip_fail(h, e, "gemm2 launch");
     pf.end(5);
   }

@@ -543,6 +543,93 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
   }
 }
 
+// ------------------------------------ G2, k split inside the workgroup --
+// For down projections with few rows per group: a workgroup owns RT*32 rows
+// x CB_*32 columns and its 4 wavefronts walk consecutive quarters of f for
+// that same tile (rows of hbar and weights straight into registers); the
+// last wavefront also runs the residual tail.  The partial tiles are added
+// in LDS and written once: Y directly with one group per token, else the
+// per-(token, group) rows that the combine kernel sums.
+template <int XT, int TY, int RT, int CB_, bool INT4>
+__global__ __launch_bounds__(256) void gemm2k_kernel(GemmArgs a) {
+  constexpr int NV_ = RT * CB_ * 16;  // accumulator values per lane
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [4 waves][NV_][64]
+  if (blockIdx.x == 0 && a.zero_ptr) {
+    for (int i = threadIdx.x; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
+  }
+  TileCoord tc;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, 32 * RT, (a.d + CB_ * 32 - 1) / (CB_ * 32), tc)) return;
+  const int g = tc.g, m0 = tc.m0, M = tc.M;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = a.goffsets[g] + m0;
+  const int nb0 = tc.nt * CB_;
+  f16v acc[RT][CB_];
+  zero_acc<RT, CB_>(acc);
+  auto row_of = [&](int t) -> long {
+    const int m = t * 32 + (lane & 31);
+    return m0 + m < M ? (long)(row0 + m) : -1L;
+  };
+  auto run = [&](const TE<TY>* tbase, long ld, const auto& ws, int KT) {
+    using WS = std::decay_t<decltype(ws)>;
+    using TO = TDirect<TY, TY, RT>;
+    using WO = WDirect<WS, CB_>;
+    TO to;
+    to.init(tbase, ld, lane, row_of);
+    WO wo;
+    wo.src = ws;
+    wo.nb0 = nb0;
+    using TR = typename TO::Raw[RT][4];
+    using WR = typename WO::Raw[CB_][4];
+    Mainloop<TY, RT, CB_, false, false, TO, WO, 1> ml{to, wo, nullptr, nullptr, 0, 0, lane};
+    if (KT > 0) ml.template run<int, int, TR, WR>(KT, acc);
+  };
+  {
+    const int KT = a.f / KB;
+    const int k0 = wave * KT / 4, k1 = (wave + 1) * KT / 4;
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, a.f / 16};
+    ws.ks0 = k0 * 4;
+    run(static_cast<const TE<TY>*>(a.H) + (long)k0 * KB, a.f, ws, k1 - k0);
+  }
+  if (a.NV > 0 && wave == 3) {
+    const int KS = a.NV / 16;
+    if constexpr (INT4) {
+      WInt4Tail<TY> ws{static_cast<const uint32_t*>(a.Bd) + g * a.bd_gstride,
+                       a.bd_scale + (long)g * a.K * (a.d / 32) * RPAD, KS, a.K, a.d / 32};
+      run(static_cast<const TE<TY>*>(a.V), a.NV, ws, a.NV / KB);
+    } else {
+      WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bd) + g * a.bd_gstride / 8, KS};
+      run(static_cast<const TE<TY>*>(a.V), a.NV, ws, a.NV / KB);
+    }
+  }
+  // each wavefront parks its partial tile in its own LDS slice (plain
+  // stores: adds from several wavefronts to one LDS word serialise)
+  float* mine = red + (size_t)wave * NV_ * 64;
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int c = 0; c < CB_; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mine[((t * CB_ + c) * 16 + v) * 64 + lane] = acc[t][c][v];
+  __syncthreads();
+  // item (t, c, q) x lane: 4 consecutive features of one token
+  for (int it = threadIdx.x; it < RT * CB_ * 4 * 64; it += 256) {
+    const int l = it & 63, tcq = it >> 6;
+    const int q = tcq & 3, c = (tcq >> 2) % CB_, t = (tcq >> 2) / CB_;
+    const int m = t * 32 + (l & 31);
+    const int n = (nb0 + c) * 32 + 8 * q + 4 * (l >> 5);
+    if (m0 + m >= M || n >= a.d) continue;
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t e = ((size_t)(t * CB_ + c) * 16 + 4 * q + i) * 64 + l;
+      o[i] = (red[e] + red[e + NV_ * 64]) + (red[e + 2 * NV_ * 64] + red[e + 3 * NV_ * 64]);
+    }
+    const long aid = a.garow[row0 + m];
+    if (a.kg == 1) store4<XT>(static_cast<TE<XT>*>(a.Y) + aid * a.d + n, o[0], o[1], o[2], o[3]);
+    else store4<DT_F32>(a.ypart + aid * a.d + n, o[0], o[1], o[2], o[3]);
+  }
+}
+
 // ----------------------------------------------------------------- V sum --
 // V[row, j*16 + rho] = sum over G1 column tiles of the partial for the slot
 // of expert j in the row's chosen list; zero for experts the row did not
@@ -750,9 +837,26 @@ hipError_t launch_ugemm_t(const GemmArgs& a, int max_mtiles, hipStream_t st) {
   return go(ugemm_kernel<XT, TY, 4, false>, grid, 0, a, st);
 }
 
+template <int XT, int TY>
+hipError_t launch_g2k_t(const GemmArgs& a, int max_mtiles, hipStream_t st) {
+  const bool int4 = a.resid == RS_INT4;
+  const dim3 grid((unsigned)max_mtiles * ((a.d + 127) / 128));
+  const size_t lds = (size_t)4 * 2 * 4 * 16 * 64 * sizeof(float);
+  if (int4) return go(gemm2k_kernel<XT, TY, 2, 4, true>, grid, lds, a, st);
+  return go(gemm2k_kernel<XT, TY, 2, 4, false>, grid, lds, a, st);
+}
+
 hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmArgs& a, int max_mtiles,
                        int ntiles, int splits, hipStream_t st) {
   if (max_mtiles <= 0 || ntiles <= 0) return hipSuccess;
+  if (kind == GK_G2K) {
+    // 64-row tiles x 128 columns: max_mtiles must be counted for bm = 64
+    if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_g2k_t<DT_F32, DT_F32>(a, max_mtiles, st);
+    if (x_dtype == DT_F16 && mma_dtype == DT_F16) return launch_g2k_t<DT_F16, DT_F16>(a, max_mtiles, st);
+    if (x_dtype == DT_BF16 && mma_dtype == DT_BF16) return launch_g2k_t<DT_BF16, DT_BF16>(a, max_mtiles, st);
+    if (x_dtype == DT_BF16 && mma_dtype == DT_F16) return launch_g2k_t<DT_BF16, DT_F16>(a, max_mtiles, st);
+    return hipErrorInvalidValue;
+  }
   if (kind == GK_U) {
     // 32-row tiles: max_mtiles must be counted for bm = 32
     if (x_dtype == DT_F32 && mma_dtype == DT_F32) return launch_ugemm_t<DT_F32, DT_F32>(a, max_mtiles, st);

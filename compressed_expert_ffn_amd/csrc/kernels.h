@@ -124,7 +124,7 @@ struct CombineArgs {
   int T, d, kg, ksplit;
 };
 
-enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2 };
+enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2, GK_G2K = 3 };  // G2K: G2 with the k split inside a workgroup
 
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st);
 int router_splits(int T, int d, int NCp);

@@ -206,18 +206,19 @@ def test_repeated_calls_and_different_T_on_one_handle():
 
 
 TILE_VARIANTS = [
-    {"CEFN_BM_U": "256", "CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1"},
-    {"CEFN_BM_U": "64", "CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4"},
-    {"CEFN_BM_U": "32", "CEFN_BM_G1": "32", "CEFN_BM_G2": "128", "CEFN_KS_G2": "2"},
-    {"CEFN_BM_U": "128", "CEFN_BM_G1": "64", "CEFN_BM_G2": "64", "CEFN_KS_G2": "3"},
+    {"CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1", "CEFN_G2K": "0"},
+    {"CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4", "CEFN_G2K": "0"},
+    {"CEFN_BM_G1": "32", "CEFN_BM_G2": "128", "CEFN_KS_G2": "2", "CEFN_G2K": "1"},
+    {"CEFN_BM_G1": "64", "CEFN_BM_G2": "64", "CEFN_KS_G2": "3", "CEFN_G2K": "1"},
 ]
 
 
 @pytest.mark.parametrize("wi,T", [(1, 700), (3, 333), (4, 64), (2, 150)])
 @pytest.mark.parametrize("vi", range(len(TILE_VARIANTS)))
 def test_tile_variants_match_oracle(wi, T, vi, monkeypatch):
-    """Every tile height and k split the library can pick gives the same
-    routing and outputs within tolerance (ragged tiles included)."""
+    """Every tile height, k split and down-projection variant the library
+    can pick gives the same routing and outputs within tolerance (ragged
+    tiles included)."""
     L = _lib()
     for k, v in TILE_VARIANTS[vi].items():
         monkeypatch.setenv(k, v)
