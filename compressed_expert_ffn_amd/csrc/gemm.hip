@@ -245,12 +245,13 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   const int row0 = a.goffsets[g] + m0;
   const int K = a.K, ke = a.ke;
 
-  // LDS: [token stages | V sums, row stride VS = ke*16 + 1 floats (odd, so
-  // the 32 tokens of an LDS add land in different banks)] | gate weights
-  // [BMT][K] | slot of expert j in the row's chosen list [BMT][K] (int8) |
-  // per token block, the bit set of experts picked by any of its tokens
+  // LDS: [token stages | V sums of the current 32-token block, one slice per
+  // wavefront, row stride VS = ke*16 + 1 floats (odd, so the 32 tokens of
+  // one access land in different banks)] | gate weights [BMT][K] | slot of
+  // expert j in the row's chosen list [BMT][K] (int8) | per token block, the
+  // bit set of experts picked by any of its tokens
   const int VS = ke * RPAD + 1;
-  const size_t vbytes = (size_t)BMT * VS * sizeof(float);
+  const size_t vbytes = (size_t)4 * 32 * VS * sizeof(float);
   const size_t abytes = (tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes + 15) & ~(size_t)15;
   float* s_v = reinterpret_cast<float*>(smem);
   float* s_w = reinterpret_cast<float*>(smem + abytes);
@@ -299,9 +300,12 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);  // ends with a barrier
 
   if constexpr (RES != ER_NONE) {
-    for (int i = tid; i < BMT * VS; i += 256) s_v[i] = 0.f;
+    for (int i = tid; i < 4 * 32 * VS; i += 256) s_v[i] = 0.f;
     __syncthreads();
   }
+  // this wavefront's slice: within a wavefront every (token, slot, rho)
+  // belongs to one lane, so plain read-modify-writes need no atomics
+  float* s_vw = s_v + wave * 32 * VS;
   const TE<TY>* Ub = static_cast<const TE<TY>*>(a.U);
   TE<TY>* H = static_cast<TE<TY>*>(a.H);
   const int h = lane >> 5;
@@ -439,9 +443,9 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
             vacc = mfma32<TY>(afr, hfr, vacc);
           }
         if (cur.slot >= 0) {
-          float* dst = s_v + m * VS + cur.slot * RPAD;
+          float* dst = s_vw + (lane & 31) * VS + cur.slot * RPAD;
 #pragma unroll
-          for (int v = 0; v < 8; ++v) atomicAdd(dst + acc_feat(v, lane), vacc[v]);
+          for (int v = 0; v < 8; ++v) dst[acc_feat(v, lane)] += vacc[v];
         }
       }
       cur = nxt;
@@ -455,14 +459,20 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
           store4<TY>(hrow + (fb0 + c) * 32 + 8 * q, hbar[c][4 * q], hbar[c][4 * q + 1], hbar[c][4 * q + 2],
                      hbar[c][4 * q + 3]);
     }
-  }
-  if constexpr (RES != ER_NONE) {
-    __syncthreads();
-    // one partial per (column tile, row, slot), summed by vreduce
-    const int per_row = ke * RPAD;
-    for (int e = tid; e < BMT * per_row; e += 256) {
-      const int r = e / per_row, c = e - r * per_row;
-      if (m0 + r < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + r) * per_row + c] = s_v[r * VS + c];
+    if constexpr (RES != ER_NONE) {
+      // the four slices of this token block -> one partial per (column tile,
+      // row, slot), summed over column tiles by vreduce; slices cleared
+      __syncthreads();
+      const int per_row = ke * RPAD;
+      for (int e = tid; e < 32 * per_row; e += 256) {
+        const int r = e / per_row, c = e - r * per_row;
+        const int o = r * VS + c;
+        const float v = (s_v[o] + s_v[32 * VS + o]) + (s_v[2 * 32 * VS + o] + s_v[3 * 32 * VS + o]);
+        s_v[o] = s_v[32 * VS + o] = s_v[2 * 32 * VS + o] = s_v[3 * 32 * VS + o] = 0.f;
+        const int mr = t * 32 + r;
+        if (m0 + mr < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + mr) * per_row + c] = v;
+      }
+      __syncthreads();
     }
   }
 }
@@ -816,7 +826,7 @@ size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
   const size_t fb = ty == DT_F32 ? 32 : 16;
   const size_t tbytes = 2 * (size_t)(bm / 32) * 4 * 64 * fb;
   if (kind != GK_G1) return tbytes;
-  const size_t vbytes = (size_t)bm * (ke * RPAD + 1) * sizeof(float);
+  const size_t vbytes = (size_t)4 * 32 * (ke * RPAD + 1) * sizeof(float);
   const size_t abytes = (tbytes > vbytes ? tbytes : vbytes + 15) & ~(size_t)15;
   return abytes + sizeof(float) * bm * K + (((size_t)bm * K + 15) & ~(size_t)15) + sizeof(uint32_t) * 2 * (bm / 32) +
          64;
