@@ -113,22 +113,15 @@ constexpr size_t tbuf_bytes() {
   return (size_t)2 * RT * 4 * 64 * sizeof(FragT<TY>);
 }
 
-// Mainloop over the token operand TO (LDS-shared) and weight source WS
-// (direct), KT stages.
+// Main loop over the token operand TO (LDS-shared) and weight source WS
+// (direct), KT >= 1 stages (d and f are multiples of 64, a k split keeps at
+// least 8 stages, the residual tail is padded to 64); ends with a barrier.
+// (No early exit here: one made the compiler spill the 256-token tiles.)
 template <int TY, int RT, class TO, class WS>
-__device__ __forceinline__ void run_tile(int KT, const TO& to, const WS& ws, int nb0, FragT<TY>* tl, int wave,
-                                         int lane, f16v (&acc)[RT][CB]) {
-  using WO = WDirect<WS, CB>;
-  WO wo;
-  wo.src = ws;
-  wo.nb0 = nb0;
-  using TSr = typename TO::Raw[TO::SEG][4];
-  using WRr = typename WO::Raw[CB][4];
-  // a 256-token stage keeps the MFMAs busy for longer than a load takes;
-  // shorter tiles keep two stages of loads in flight
-  constexpr int PD = (RT >= 8) ? 1 : 2;
-  Mainloop<TY, RT, CB, true, false, TO, WO, PD> ml{to, wo, tl, nullptr, 0, wave, lane};
-  ml.template run<TSr, int, int, WRr>(KT, acc);
+__device__ __forceinline__ void run_tile(int KT, const TO& to, const WS& ws, int nb0, FragT<TY>* tl, int lane,
+                                         f16v (&acc)[RT][CB]) {
+  MainloopTW<TY, RT, CB, TO, WS> ml{to, ws, nb0, tl, lane};
+  ml.run(KT, acc);
 }
 
 // ------------------------------------------------------------- U = X . A --
@@ -297,7 +290,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   f16v acc[RT][CB];
   zero_acc<RT, CB>(acc);
   WPlain<TY> ws{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
-  run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, wave, lane, acc);  // ends with a barrier
+  run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);  // ends with a barrier
 
   if constexpr (RES != ER_NONE) {
     for (int i = tid; i < 4 * 32 * VS; i += 256) s_v[i] = 0.f;
@@ -514,7 +507,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
     TShared<TY, TY, RT> to;
     to.init(static_cast<const TE<TY>*>(a.H) + (long)k0 * KB, a.f, rows);
     WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8 + (long)k0 * 4 * 64, a.f / 16};
-    run_tile<TY, RT>(k1 - k0, to, ws, nb0, tl, wave, lane, acc);
+    run_tile<TY, RT>(k1 - k0, to, ws, nb0, tl, lane, acc);
   }
   if (a.NV > 0 && split == 0) {
     // + V . [B_down,j^T]_j : 16 residual k per expert of the group
@@ -524,10 +517,10 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
     if constexpr (INT4) {
       WInt4Tail<TY> ws{static_cast<const uint32_t*>(a.Bd) + g * a.bd_gstride,
                        a.bd_scale + (long)g * a.K * (a.d / 32) * RPAD, KS, a.K, a.d / 32};
-      run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, wave, lane, acc);
+      run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, lane, acc);
     } else {
       WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bd) + g * a.bd_gstride / 8, KS};
-      run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, wave, lane, acc);
+      run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, lane, acc);
     }
   }
   if (!active) return;

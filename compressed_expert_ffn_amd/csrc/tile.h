@@ -156,6 +156,14 @@ struct TShared {
 #pragma unroll
       for (int s = 0; s < 4; ++s) r[q][s] = ld_raw<SRC>(rowp[q] + kt * KB + 8 * s);
   }
+  // k-steps 2 h and 2 h + 1 only (the interleaved main loop splits a
+  // stage's loads in two)
+  __device__ void fetch_half(int kt, int h, Raw (&r)[SEG][4]) const {
+#pragma unroll
+    for (int q = 0; q < SEG; ++q)
+#pragma unroll
+      for (int s = 2 * h; s < 2 * h + 2; ++s) r[q][s] = ld_raw<SRC>(rowp[q] + kt * KB + 8 * s);
+  }
   // LDS image of one stage: [NB][4 k-steps][64 lanes] fragments of type TY
   __device__ void commit(const Raw (&r)[SEG][4], FragT<TY>* buf) const {
 #pragma unroll
@@ -381,6 +389,124 @@ struct Mainloop {
     if constexpr (U > 3) {
       if (kt + 2 < KT) stage<2>(kt + 2, KT, acc, ts, ws, tr, wr);
     }
+  }
+};
+
+// ------------------------------------------------- interleaved main loop --
+// Token rows staged through LDS (TShared, all 4 wavefronts share them) and
+// weights loaded straight into registers (each wavefront its own CB column
+// blocks).  One 64-deep stage is 4 k-steps of RT x CB MFMAs; around them:
+//   k-step 0: LDS reads of k-step 1, token loads of the next stage (k-steps
+//             0-1), weights of the next stage (k-step 0)
+//   k-step 1: LDS reads of k-step 2, token loads (k-steps 2-3), weights (1)
+//   k-step 2: LDS reads of k-step 3, weights (k-steps 2-3)
+//   then the token commit into the other LDS buffer and the barrier, after
+//   which k-step 3's MFMAs cover the LDS reads of the next stage's k-step 0.
+// Group scheduling barriers spread each k-step's loads between its MFMAs
+// rather than issuing them in one burst.  The barrier orders LDS only, so
+// global loads stay in flight across it.  Ends with a full barrier (callers
+// reuse the LDS).  KT >= 1.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int TY, int RT, int CB, class TO, class WS>
+struct MainloopTW {
+  using F = FragT<TY>;
+  using WR = typename WS::Raw;
+  static constexpr int FPS = TO::frags_per_stage;
+  static constexpr int M_MFMA = 0x008, M_VMEM = 0x020, M_DSR = 0x100;
+  const TO& to;
+  const WS& ws;
+  int nb0;
+  F* tl;
+  int lane;
+
+  __device__ __forceinline__ void mfmas(const WR (&wr)[CB][4], const F (&tf)[RT], int s, f16v (&acc)[RT][CB]) const {
+    F wf[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) wf[c] = ws.decode(wr[c][s], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < CB; ++c) acc[t][c] = mfma32<TY>(wf[c], tf[t], acc[t][c]);
+  }
+  __device__ __forceinline__ void dsr(int b, int s, F (&tf)[RT]) const {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) tf[t] = tl[b * FPS + (t * 4 + s) * 64 + lane];
+  }
+  __device__ __forceinline__ void wload(int kt, int s, WR (&wr)[CB][4]) const {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) wr[c][s] = ws.load(nb0 + c, kt * 4 + s, lane);
+  }
+  template <int NV>
+  __device__ __forceinline__ static void pattern() {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(M_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(M_DSR, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(M_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(M_VMEM, 1, 0);
+    }
+  }
+
+  // stage kt from LDS buffer kt & 1 with weights wc; loads stage kt + 1
+  // (clamped: the last stage reloads itself into the idle buffer) into wn
+  template <class TR>
+  __device__ __forceinline__ void stage(int kt, int KT, TR& tr, WR (&wc)[CB][4], WR (&wn)[CB][4], F (&tf)[2][RT],
+                                        f16v (&acc)[RT][CB]) const {
+    const int b = kt & 1;
+    const int kn = kt + 1 < KT ? kt + 1 : KT - 1;
+    dsr(b, 1, tf[1]);
+    to.fetch_half(kn, 0, tr);
+    wload(kn, 0, wn);
+    mfmas(wc, tf[0], 0, acc);
+    pattern<2 * TO::SEG + CB>();
+    __builtin_amdgcn_sched_barrier(0);
+    dsr(b, 2, tf[0]);
+    to.fetch_half(kn, 1, tr);
+    wload(kn, 1, wn);
+    mfmas(wc, tf[1], 1, acc);
+    pattern<2 * TO::SEG + CB>();
+    __builtin_amdgcn_sched_barrier(0);
+    dsr(b, 3, tf[1]);
+    wload(kn, 2, wn);
+    wload(kn, 3, wn);
+    mfmas(wc, tf[0], 2, acc);
+    pattern<2 * CB>();
+    __builtin_amdgcn_sched_barrier(0);
+    to.commit(tr, tl + (b ^ 1) * FPS);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    dsr(b ^ 1, 0, tf[0]);
+    mfmas(wc, tf[1], 3, acc);
+    pattern<0>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ void run(int KT, f16v (&acc)[RT][CB]) const {
+    typename TO::Raw tr[TO::SEG][4];
+    WR wr[2][CB][4];
+    F tf[2][RT];
+    to.fetch(0, tr);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) wload(0, s, wr[0]);
+    to.commit(tr, tl);
+    lds_barrier();
+    dsr(0, 0, tf[0]);
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+      stage(kt, KT, tr, wr[0], wr[1], tf, acc);
+      stage(kt + 1, KT, tr, wr[1], wr[0], tf, acc);
+    }
+    if (kt < KT) stage(kt, KT, tr, wr[0], wr[1], tf, acc);
+    __syncthreads();
   }
 };
 
