@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
     wo.nb0 = nb0;
     using TR = typename TDirect<XT, TY, 1>::Raw[1][4];
     using WR = typename WO::Raw[CB_][4];
-    Mainloop<TY, 1, CB_, false, false, TDirect<XT, TY, 1>, WO, 2> ml{to, wo, nullptr, nullptr, 0, 0, lane};
-    if (k1 > k0) ml.template run<int, int, TR, WR>(k1 - k0, acc);
+    Mainloop<TY, 1, CB_, TDirect<XT, TY, 1>, WO, 2> ml{to, wo, lane};
+    if (k1 > k0) ml.template run<TR, WR>(k1 - k0, acc);
   };
   const int KS = a.d / 16;
   if constexpr (INT4) {
@@ -583,8 +583,8 @@ __global__ __launch_bounds__(256) void gemm2k_kernel(GemmArgs a) {
     wo.nb0 = nb0;
     using TR = typename TO::Raw[RT][4];
     using WR = typename WO::Raw[CB_][4];
-    Mainloop<TY, RT, CB_, false, false, TO, WO, 1> ml{to, wo, nullptr, nullptr, 0, 0, lane};
-    if (KT > 0) ml.template run<int, int, TR, WR>(KT, acc);
+    Mainloop<TY, RT, CB_, TO, WO, 1> ml{to, wo, lane};
+    if (KT > 0) ml.template run<TR, WR>(KT, acc);
   };
   {
     const int KT = a.f / KB;

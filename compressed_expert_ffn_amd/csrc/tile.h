@@ -94,13 +94,19 @@ __device__ __forceinline__ void st_frag(FragT<TY>* p, const FragT<TY>& f) { *p =
 
 // ------------------------------------------------------ token operand (T) --
 // Rows of a row-major [rows][ld] matrix of type SRC, optionally gathered
-// (row r of the tile is source row map(r)).  Each lane owns one 64-byte
-// (or 128-byte for fp32) segment per stage: token row (lane % 32) of a
-// block, k half h = lane / 32.
+// (row r of the tile is source row map(r)).
 //
-// TDirect: a wavefront loads its own RT blocks into registers.
-// TShared: the workgroup copies all NB token blocks into LDS; each thread
-// handles (NB * 64) / 256 segments.
+// TDirect: a wavefront loads its own RT blocks into registers; lane l owns
+// one 64-byte (128-byte for fp32) segment per stage: token row l % 32 of a
+// block, k half l / 32.
+// TShared: the workgroup copies all NB token blocks of a stage into LDS.
+// Four consecutive lanes read the four 16-byte pieces of one 64-byte half
+// row, so a load instruction covers 8 whole 128-byte lines (one cache tag
+// per 64 bytes; the fragment-order mapping touched 64 tags per
+// instruction, and the vector L1 tag rate then bounded the main loop).
+// The LDS image is fragment-major with a swizzle: fragment (block, k-step s)
+// holds logical lane L in slot L ^ s, which keeps the four pieces a lane
+// quad writes in different banks; a reader of k-step s takes slot lane ^ s.
 template <int SRC, int TY, int RT>
 struct TDirect {
   using Raw = RawT<SRC>;
@@ -129,52 +135,44 @@ struct TDirect {
 
 template <int SRC, int TY, int NB>
 struct TShared {
-  // segments per thread; with fewer than 4 blocks some threads hold a
-  // duplicate (clamped) segment that they load but do not write
-  static constexpr int NSEG = NB * 64;
-  static constexpr int SEG = (NSEG + 255) / 256;
+  // load instructions per thread and stage (64 half rows each)
+  static constexpr int SEG = NB;
   using Raw = RawT<SRC>;
   const TE<SRC>* rowp[SEG];
   bool ok[SEG];
-  int lofs[SEG];  // fragment index (block * 4) * 64 + lane' of the segment, -1: none
+  int lofs[SEG];  // LDS fragment slot of the thread's piece
+  // row_of(blk, r): source row of token r of block blk, or -1 (zeros)
   template <class RowOf>
   __device__ void init(const TE<SRC>* base, long ld, RowOf row_of) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sq = lane & 3;
 #pragma unroll
     for (int q = 0; q < SEG; ++q) {
-      const int seg0 = threadIdx.x + 256 * q;  // = block * 64 + lane'
-      const int seg = seg0 < NSEG ? seg0 : NSEG - 1;
-      const int blk = seg >> 6, ln = seg & 63;
-      const long r = row_of(blk, ln & 31);
-      ok[q] = r >= 0;
-      rowp[q] = base + (ok[q] ? r : 0) * ld + 32 * (ln >> 5);
-      lofs[q] = seg0 < NSEG ? blk * 4 * 64 + ln : -1;
+      const int hr = (q * 4 + wave) * 16 + (lane >> 2);  // half row: 2 row + k half
+      const int row = hr >> 1, hh = hr & 1, blk = row >> 5, r = row & 31;
+      const long src = row_of(blk, r);
+      ok[q] = src >= 0;
+      rowp[q] = base + (ok[q] ? src : 0) * ld + 32 * hh + 8 * sq;
+      lofs[q] = (blk * 4 + sq) * 64 + ((32 * hh + r) ^ sq);
     }
   }
-  __device__ void fetch(int kt, Raw (&r)[SEG][4]) const {
+  __device__ void fetch(int kt, Raw (&r)[SEG]) const {
+#pragma unroll
+    for (int q = 0; q < SEG; ++q) r[q] = ld_raw<SRC>(rowp[q] + kt * KB);
+  }
+  // the first (h = 0) or second half of the instructions (the interleaved
+  // main loop spreads a stage's loads over two k-steps)
+  __device__ void fetch_half(int kt, int h, Raw (&r)[SEG]) const {
+    constexpr int H0 = (SEG + 1) / 2;
 #pragma unroll
     for (int q = 0; q < SEG; ++q)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) r[q][s] = ld_raw<SRC>(rowp[q] + kt * KB + 8 * s);
+      if ((q < H0) == (h == 0)) r[q] = ld_raw<SRC>(rowp[q] + kt * KB);
   }
-  // k-steps 2 h and 2 h + 1 only (the interleaved main loop splits a
-  // stage's loads in two)
-  __device__ void fetch_half(int kt, int h, Raw (&r)[SEG][4]) const {
+  __device__ void commit(const Raw (&r)[SEG], FragT<TY>* buf) const {
 #pragma unroll
-    for (int q = 0; q < SEG; ++q)
-#pragma unroll
-      for (int s = 2 * h; s < 2 * h + 2; ++s) r[q][s] = ld_raw<SRC>(rowp[q] + kt * KB + 8 * s);
+    for (int q = 0; q < SEG; ++q) st_frag<TY>(buf + lofs[q], ok[q] ? cvt_frag<SRC, TY>(r[q]) : zero_frag<TY>());
   }
-  // LDS image of one stage: [NB][4 k-steps][64 lanes] fragments of type TY
-  __device__ void commit(const Raw (&r)[SEG][4], FragT<TY>* buf) const {
-#pragma unroll
-    for (int q = 0; q < SEG; ++q) {
-      if (NSEG % 256 == 0 || lofs[q] >= 0) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          st_frag<TY>(buf + lofs[q] + s * 64, ok[q] ? cvt_frag<SRC, TY>(r[q][s]) : zero_frag<TY>());
-      }
-    }
-  }
+  // slot of logical lane `lane` in fragment (block, k-step s)
+  __device__ static int slot(int lane, int s) { return lane ^ s; }
   static constexpr int frags_per_stage = NB * 4 * 64;
 };
 
@@ -260,94 +258,42 @@ struct WDirect {
   }
 };
 
-// WShared: the workgroup copies NBW column blocks x one stage into LDS,
-// decoded to TY: [NBW][4][64] fragments.
-template <int TY, class WS, int NBW>
-struct WShared {
-  static constexpr int PER = NBW * 4 * 64 / 256;  // fragments per thread
-  using Raw = typename WS::Raw;
-  WS src;
-  int nb0;
-  __device__ void fetch(int kt, Raw (&r)[PER]) const {
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int fi = threadIdx.x + 256 * q;  // = (blk * 4 + s) * 64 + lane'
-      const int blk = fi >> 8, s = (fi >> 6) & 3, ln = fi & 63;
-      r[q] = src.load(nb0 + blk, kt * 4 + s, ln);
-    }
-  }
-  __device__ void commit(const Raw (&r)[PER], FragT<TY>* buf) const {
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int fi = threadIdx.x + 256 * q;
-      st_frag<TY>(buf + fi, src.decode(r[q], 0, 0, 0));
-    }
-  }
-  static constexpr int frags_per_stage = NBW * 4 * 64;
-};
-
 
 // ---------------------------------------------------------------- mainloop --
-// KT stages of 64 k.  TSH / WSH: the token / weight operand is shared
-// through LDS (tl / wl point at two stage buffers each).  wm, wn: this
-// wavefront's position in the WM x WN arrangement.  PD: how many stages
-// ahead the global loads run (1 when a stage's MFMAs cover the memory
-// latency, 2 or 3 for short tiles).
-//
-// Per stage: the loads of stage kt + PD are issued first (stages past the
-// end re-issue the last one, harmlessly, so no load sits in a branch), then
-// the 4 k-steps of MFMAs with LDS fragments read one k-step ahead, then the
-// staged registers of stage kt + 1 are converted and written to the other
-// LDS buffer and the workgroup synchronises once.  Register sets rotate
-// through a ring of U = PD + 1 (the loop is unrolled U times so every index
-// is static); with PD = 1 the LDS staging needs a single set.
-template <int TY, int RT, int CB, bool TSH, bool WSH, class TO, class WO, int PD = 1>
+// Both operands straight into registers (each wavefront its own token and
+// weight blocks), KT stages of 64 k.  PD: how many stages ahead the global
+// loads run.  Per stage: the loads of stage kt + PD are issued first (stages
+// past the end re-issue the last one, harmlessly, so no load sits in a
+// branch), then the 4 k-steps of MFMAs.  Register sets rotate through a ring
+// of U = PD + 1 (the loop is unrolled U times so every index is static).
+template <int TY, int RT, int CB, class TO, class WO, int PD = 1>
 struct Mainloop {
   static constexpr int U = PD + 1;
-  static constexpr int NTS = (PD == 1) ? 1 : U;  // LDS staging register sets
   using F = FragT<TY>;
   const TO& to;
   const WO& wo;
-  F* tl;
-  F* wl;
-  int wm, wn, lane;
+  int lane;
 
   template <class TR, class WR>
-  __device__ __forceinline__ void frags(int b, int s, const TR& tr, const WR& wr, F (&tf)[RT], F (&wf)[CB]) const {
+  __device__ __forceinline__ void frags(int s, const TR& tr, const WR& wr, F (&tf)[RT], F (&wf)[CB]) const {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      if constexpr (TSH) tf[t] = tl[b * TO::frags_per_stage + ((wm * RT + t) * 4 + s) * 64 + lane];
-      else tf[t] = to.frag(tr, t, s);
-    }
+    for (int t = 0; t < RT; ++t) tf[t] = to.frag(tr, t, s);
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      if constexpr (WSH) wf[c] = wl[b * WO::frags_per_stage + ((wn * CB + c) * 4 + s) * 64 + lane];
-      else wf[c] = wo.src.decode(wr[c][s], 0, 0, 0);
-    }
+    for (int c = 0; c < CB; ++c) wf[c] = wo.src.decode(wr[c][s], 0, 0, 0);
   }
 
-  template <class TS, class WS, class TR, class WR>
-  __device__ __forceinline__ void fetch(int kn, TS& ts, WS& ws, TR& tr, WR& wr) const {
-    if constexpr (TSH) to.fetch(kn, ts); else to.fetch(kn, tr);
-    if constexpr (WSH) wo.fetch(kn, ws); else wo.fetch(kn, lane, wr);
-  }
-
-  template <int u, class TS, class WS, class TR, class WR>
-  __device__ __forceinline__ void stage(int kt, int KT, f16v (&acc)[RT][CB], TS (&ts)[NTS], WS (&ws)[NTS],
-                                        TR (&tr)[U], WR (&wr)[U]) const {
-    constexpr int fs = (u + PD) % U;          // ring slot of stage kt + PD
-    constexpr int ns = (u + 1) % U;           // ring slot of stage kt + 1
-    constexpr int tf_ = (PD == 1) ? 0 : fs;   // staging set receiving stage kt + PD
-    constexpr int tc_ = (PD == 1) ? 0 : ns;   // staging set holding stage kt + 1
+  template <int u, class TR, class WR>
+  __device__ __forceinline__ void stage(int kt, int KT, f16v (&acc)[RT][CB], TR (&tr)[U], WR (&wr)[U]) const {
+    constexpr int fs = (u + PD) % U;  // ring slot of stage kt + PD
     const int kn = (kt + PD < KT) ? kt + PD : KT - 1;
-    fetch(kn, ts[tf_], ws[tf_], tr[fs], wr[fs]);
+    to.fetch(kn, tr[fs]);
+    wo.fetch(kn, lane, wr[fs]);
     __builtin_amdgcn_sched_barrier(0);
-    const int b = kt & 1;
     F tf[2][RT], wf[2][CB];
-    frags(b, 0, tr[u], wr[u], tf[0], wf[0]);
+    frags(0, tr[u], wr[u], tf[0], wf[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) frags(b, s + 1, tr[u], wr[u], tf[(s + 1) & 1], wf[(s + 1) & 1]);
+      if (s + 1 < 4) frags(s + 1, tr[u], wr[u], tf[(s + 1) & 1], wf[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -355,39 +301,31 @@ struct Mainloop {
         for (int c = 0; c < CB; ++c) acc[t][c] = mfma32<TY>(wf[s & 1][c], tf[s & 1][t], acc[t][c]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (TSH) to.commit(ts[tc_], tl + (b ^ 1) * TO::frags_per_stage);
-    if constexpr (WSH) wo.commit(ws[tc_], wl + (b ^ 1) * WO::frags_per_stage);
-    if constexpr (TSH || WSH) __syncthreads();
   }
 
-  template <class TS, class WS, class TR, class WR>
+  template <class TR, class WR>
   __device__ void run(int KT, f16v (&acc)[RT][CB]) const {
-    TS ts[NTS];
-    WS ws[NTS];
     TR tr[U];
     WR wr[U];
-    // stages 0 .. PD-1 in flight, stage 0 in LDS
 #pragma unroll
     for (int p = 0; p < PD; ++p) {
       const int kn = p < KT ? p : KT - 1;
-      fetch(kn, ts[(PD == 1) ? 0 : p], ws[(PD == 1) ? 0 : p], tr[p], wr[p]);
+      to.fetch(kn, tr[p]);
+      wo.fetch(kn, lane, wr[p]);
     }
-    if constexpr (TSH) to.commit(ts[0], tl);
-    if constexpr (WSH) wo.commit(ws[0], wl);
-    if constexpr (TSH || WSH) __syncthreads();
     int kt = 0;
     for (; kt + U <= KT; kt += U) {
-      stage<0>(kt, KT, acc, ts, ws, tr, wr);
-      stage<1>(kt + 1, KT, acc, ts, ws, tr, wr);
-      if constexpr (U > 2) stage<2>(kt + 2, KT, acc, ts, ws, tr, wr);
-      if constexpr (U > 3) stage<3>(kt + 3, KT, acc, ts, ws, tr, wr);
+      stage<0>(kt, KT, acc, tr, wr);
+      stage<1>(kt + 1, KT, acc, tr, wr);
+      if constexpr (U > 2) stage<2>(kt + 2, KT, acc, tr, wr);
+      if constexpr (U > 3) stage<3>(kt + 3, KT, acc, tr, wr);
     }
-    if (kt < KT) stage<0>(kt, KT, acc, ts, ws, tr, wr);
+    if (kt < KT) stage<0>(kt, KT, acc, tr, wr);
     if constexpr (U > 2) {
-      if (kt + 1 < KT) stage<1>(kt + 1, KT, acc, ts, ws, tr, wr);
+      if (kt + 1 < KT) stage<1>(kt + 1, KT, acc, tr, wr);
     }
     if constexpr (U > 3) {
-      if (kt + 2 < KT) stage<2>(kt + 2, KT, acc, ts, ws, tr, wr);
+      if (kt + 2 < KT) stage<2>(kt + 2, KT, acc, tr, wr);
     }
   }
 };
@@ -435,7 +373,7 @@ struct MainloopTW {
   }
   __device__ __forceinline__ void dsr(int b, int s, F (&tf)[RT]) const {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) tf[t] = tl[b * FPS + (t * 4 + s) * 64 + lane];
+    for (int t = 0; t < RT; ++t) tf[t] = tl[b * FPS + (t * 4 + s) * 64 + TO::slot(lane, s)];
   }
   __device__ __forceinline__ void wload(int kt, int s, WR (&wr)[CB][4]) const {
 #pragma unroll
@@ -466,13 +404,13 @@ struct MainloopTW {
     to.fetch_half(kn, 0, tr);
     wload(kn, 0, wn);
     mfmas(wc, tf[0], 0, acc);
-    pattern<2 * TO::SEG + CB>();
+    pattern<(TO::SEG + 1) / 2 + CB>();
     __builtin_amdgcn_sched_barrier(0);
     dsr(b, 2, tf[0]);
     to.fetch_half(kn, 1, tr);
     wload(kn, 1, wn);
     mfmas(wc, tf[1], 1, acc);
-    pattern<2 * TO::SEG + CB>();
+    pattern<TO::SEG / 2 + CB>();
     __builtin_amdgcn_sched_barrier(0);
     dsr(b, 3, tf[1]);
     wload(kn, 2, wn);
@@ -491,7 +429,7 @@ struct MainloopTW {
   }
 
   __device__ void run(int KT, f16v (&acc)[RT][CB]) const {
-    typename TO::Raw tr[TO::SEG][4];
+    typename TO::Raw tr[TO::SEG];
     WR wr[2][CB][4];
     F tf[2][RT];
     to.fetch(0, tr);
