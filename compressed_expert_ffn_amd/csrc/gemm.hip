@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   // wavefront, row stride VS = ke*16 + 1 floats (odd, so the 32 tokens of
   // one access land in different banks)] | gate weights [BMT][K] | slot of
   // expert j in the row's chosen list [BMT][K] (int8) | per token block, the
-  // bit set of experts picked by any of its tokens
+  // bit set of experts picked by any of its tokens | tile position -> row
+  // of the group tile [BMT] | expert-set histogram and offsets [2][256]
   const int VS = ke * RPAD + 1;
   const size_t vbytes = (size_t)4 * 32 * VS * sizeof(float);
   const size_t abytes = (tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes + 15) & ~(size_t)15;
@@ -250,6 +251,8 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   float* s_w = reinterpret_cast<float*>(smem + abytes);
   int8_t* s_slot = reinterpret_cast<int8_t*>(s_w + BMT * K);
   uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_slot + ((BMT * K + 15) & ~15));
+  int* s_perm = reinterpret_cast<int*>(s_bm + 2 * RT);
+  int* s_hist = s_perm + BMT;
   F* tl = reinterpret_cast<F*>(smem);
 
   for (int i = tid; i < BMT * K; i += 256) {
@@ -257,8 +260,51 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
     s_slot[i] = -1;
   }
   for (int i = tid; i < 2 * RT; i += 256) s_bm[i] = 0u;
+  s_hist[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < BMT; i += 256) {
+  // Row order inside the tile.  With residuals, the epilogue takes one step
+  // per expert picked by any token of a 32-token block, so the rows are
+  // counting-sorted by their expert set (folded to 8 bits; rows past the
+  // group's end last): blocks then see few distinct experts.  Each token's
+  // result depends only on its own column, so the order (including the
+  // arbitrary order inside one key) changes no value.
+  const bool mine = tid < BMT && m0 + tid < M;
+  if constexpr (RES != ER_NONE) {
+    int key = 255;
+    if (mine) {
+      const int t = a.garow[row0 + tid] / a.kg, ga = a.garow[row0 + tid] % a.kg;
+      uint64_t set = 0;
+      for (int s2 = 0; s2 < ke; ++s2) set |= 1ull << (a.idx[t * a.k + ga * ke + s2] - g * K);
+      uint32_t f = static_cast<uint32_t>(set) ^ static_cast<uint32_t>(set >> 32);
+      f ^= f >> 16;
+      f ^= f >> 8;
+      key = static_cast<int>(f & 255u) % 255;
+    }
+    int rk = 0;
+    if (tid < BMT) rk = atomicAdd(&s_hist[key], 1);
+    __syncthreads();
+    // exclusive scan of the 256 bins: per wavefront, then the wave totals
+    const int cnt = s_hist[tid];
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    __syncthreads();
+    if (lane == 63) s_hist[256 + wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int w2 = 0; w2 < wave; ++w2) base += s_hist[256 + w2];
+    s_hist[tid] = base + inc - cnt;
+    __syncthreads();
+    if (tid < BMT) s_perm[s_hist[key] + rk] = tid;
+  } else {
+    if (tid < BMT) s_perm[tid] = tid;
+  }
+  __syncthreads();
+  for (int p = tid; p < BMT; p += 256) {
+    const int i = s_perm[p];
     if (m0 + i < M) {
       const int aid = a.garow[row0 + i];
       const int t = aid / a.kg, ga = aid - t * a.kg;
@@ -267,15 +313,15 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
         // sum_j w_j act(Z) = (sum_j w_j) act(Z), one step per token
         float ws = 0.f;
         for (int s = 0; s < ke; ++s) ws += a.w[t * a.k + ga * ke + s];
-        s_w[i * K] = ws;
-        atomicOr(&s_bm[(i >> 5) * 2], 1u);
+        s_w[p * K] = ws;
+        atomicOr(&s_bm[(p >> 5) * 2], 1u);
       } else {
         for (int s = 0; s < ke; ++s) {
           const int slot = t * a.k + ga * ke + s;
           const int j = a.idx[slot] - g * K;
-          s_w[i * K + j] = a.w[slot];
-          s_slot[i * K + j] = static_cast<int8_t>(s);
-          atomicOr(&s_bm[(i >> 5) * 2 + (j >> 5)], 1u << (j & 31));
+          s_w[p * K + j] = a.w[slot];
+          s_slot[p * K + j] = static_cast<int8_t>(s);
+          atomicOr(&s_bm[(p >> 5) * 2 + (j >> 5)], 1u << (j & 31));
         }
       }
     }
@@ -285,7 +331,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   TShared<XT, TY, RT> to;
   to.init(static_cast<const TE<XT>*>(a.X), a.d, [&](int blk, int r) -> long {
     const int m = blk * 32 + r;
-    return m0 + m < M ? (long)(a.garow[row0 + m] / a.kg) : -1L;
+    return m0 + m < M ? (long)(a.garow[row0 + s_perm[m]] / a.kg) : -1L;
   });
   f16v acc[RT][CB];
   zero_acc<RT, CB>(acc);
@@ -319,7 +365,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
     o.wgt = s_w[m * K + j];
     o.slot = s_slot[m * K + j];
     if constexpr (RES != ER_NONE) {
-      const long urow = row0 + (m0 + m < M ? m : 0);
+      const long urow = row0 + (m0 + m < M ? s_perm[m] : 0);
 #pragma unroll
       for (int p = 0; p < PIN; ++p) o.u[p] = *reinterpret_cast<const F*>(Ub + urow * a.NU + (j * PIN + p) * RPAD + 8 * h);
 #pragma unroll
@@ -444,7 +490,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
       cur = nxt;
     }
     if (active && m0 + m < M) {  // (idle wavefronts computed nothing above)
-      TE<TY>* hrow = H + (long)(row0 + m) * a.f + 4 * h;
+      TE<TY>* hrow = H + (long)(row0 + s_perm[m]) * a.f + 4 * h;
 #pragma unroll
       for (int c = 0; c < NFB; ++c)
 #pragma unroll
@@ -463,7 +509,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
         const float v = (s_v[o] + s_v[32 * VS + o]) + (s_v[2 * 32 * VS + o] + s_v[3 * 32 * VS + o]);
         s_v[o] = s_v[32 * VS + o] = s_v[2 * 32 * VS + o] = s_v[3 * 32 * VS + o] = 0.f;
         const int mr = t * 32 + r;
-        if (m0 + mr < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + mr) * per_row + c] = v;
+        if (m0 + mr < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + s_perm[mr]) * per_row + c] = v;
       }
       __syncthreads();
     }
@@ -822,7 +868,7 @@ size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
   const size_t vbytes = (size_t)4 * 32 * (ke * RPAD + 1) * sizeof(float);
   const size_t abytes = (tbytes > vbytes ? tbytes : vbytes + 15) & ~(size_t)15;
   return abytes + sizeof(float) * bm * K + (((size_t)bm * K + 15) & ~(size_t)15) + sizeof(uint32_t) * 2 * (bm / 32) +
-         64;
+         sizeof(int) * ((size_t)bm + 256 + 4) + 64;
 }
 
 template <int XT, int TY>
