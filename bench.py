@@ -80,7 +80,8 @@ def traffic_for(workload_name: str, kernel: str):
     return rec.get("bytes_per_launch") if rec.get("src_sha") == sha else None
 
 
-KERNEL_STAGE = (("router", "router"), ("scatter", "scatter"), ("ugemm", "ugemm"), ("gemm1", "gemm1"),
+KERNEL_STAGE = (("route_fused", "router"), ("logits_kernel", "router"), ("select_kernel", "router"),
+                ("scatter", "scatter"), ("ugemm", "ugemm"), ("gemm1", "gemm1"),
                 ("vreduce", "vreduce"), ("gemm2", "gemm2"), ("combine", "combine"), ("zero_kernel", "zero"))
 
 
