@@ -220,9 +220,93 @@ __device__ __forceinline__ float score_bias(const RouteArgs& a, int c) {
   return a.ebias ? a.ebias[c - a.G] : 0.f;
 }
 
+// Wavefront top-k: the n candidates sv[0..n) are spread over the lanes
+// (candidate c on lane c % 64); each round takes the best remaining one by a
+// butterfly over the lanes -- higher score first, ties to the lower index,
+// NaN as -inf (the order keep_best gives).  Selection r ends up in lane r's
+// (myv, myi).  k <= n, k <= 64.
+__device__ void wave_topk(const float* sv, int n, int k, int lane, float& myv, int& myi) {
+  uint32_t used = 0;  // bit q: candidate lane + 64 q taken
+  myv = -INFINITY;
+  myi = -1;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    int bok = 0;
+    for (int q = 0; lane + 64 * q < n; ++q) {
+      if ((used >> q) & 1u) continue;
+      float v = sv[lane + 64 * q];
+      v = (v == v) ? v : -INFINITY;
+      if (!bok || v > bv) {
+        bv = v;
+        bi = lane + 64 * q;
+        bok = 1;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float ov = __shfl_xor(bv, m);
+      const int oi = __shfl_xor(bi, m);
+      const int ook = __shfl_xor(bok, m);
+      if (ook && (!bok || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+        bok = 1;
+      }
+    }
+    if (lane == r) {
+      myv = bv;
+      myi = bi;
+    }
+    if ((bi & 63) == lane) used |= 1u << (bi >> 6);
+  }
+}
+
+// One token's two-level selection by a wavefront; the gates are
+// select_token's arithmetic term by term (same sums in the same order).
+__device__ void select_token_wave(const RouteArgs& a, int t, const float* st, int lane) {
+  float gvl;
+  int gil;
+  wave_topk(st, a.G, a.kg, lane, gvl, gil);
+  const float g0 = __shfl(gvl, 0);
+  float ps = 0.f;
+  for (int q = 0; q < a.kg; ++q) ps += expf(__shfl(gvl, q) - g0);
+  for (int ga = 0; ga < a.kg; ++ga) {
+    const int g = __shfl(gil, ga);
+    const float pg = expf(__shfl(gvl, ga) - g0) / ps;
+    if (a.K == 1) {
+      const int slot = t * a.k + ga;
+      if (lane == 0) {
+        a.idx[slot] = g;
+        a.w[slot] = pg;
+        if (a.count_experts) atomicAdd(&a.ccount[(slot / CHUNK) * a.E + g], 1);
+      }
+    } else {
+      float evl;
+      int eil;
+      wave_topk(st + a.G + g * a.K, a.K, a.ke, lane, evl, eil);
+      const float e0 = __shfl(evl, 0);
+      float qs = 0.f;
+      for (int b = 0; b < a.ke; ++b) qs += expf(__shfl(evl, b) - e0);
+      if (lane < a.ke) {
+        const int slot = t * a.k + ga * a.ke + lane;
+        const int ex = g * a.K + eil;
+        a.idx[slot] = ex;
+        a.w[slot] = pg * (expf(evl - e0) / qs);
+        if (a.count_experts) atomicAdd(&a.ccount[(slot / CHUNK) * a.E + ex], 1);
+      }
+    }
+    if (lane == 0) {
+      const int gslot = t * a.kg + ga;
+      a.gidx[gslot] = g;
+      atomicAdd(&a.cgcount[(gslot / CHUNK) * a.G + g], 1);
+    }
+  }
+}
+
 // A workgroup takes tpb consecutive tokens: its 256 threads first sum the
-// k-split partials of all their scores (plus the biases) into LDS, then one
-// thread per token selects.
+// k-split partials of all their scores (plus the biases) into LDS, then
+// each wavefront selects for every fourth token.
 __global__ __launch_bounds__(256) void select_kernel(RouteArgs a, int tpb) {
   extern __shared__ float sc[];  // [tpb][NC]
   const int NC = a.G + (a.K > 1 ? a.G * a.K : 0);
@@ -242,7 +326,8 @@ __global__ __launch_bounds__(256) void select_kernel(RouteArgs a, int tpb) {
     sc[e] = (s0 + s1) + score_bias(a, c);
   }
   __syncthreads();
-  if ((int)threadIdx.x < nt) select_token(a, t0 + threadIdx.x, sc + threadIdx.x * NC);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int tk = wave; tk < nt; tk += 4) select_token_wave(a, t0 + tk, sc + tk * NC, lane);
 }
 
 // Scores and selection in one kernel when a 32-token block's scores fit one

@@ -205,6 +205,36 @@ def test_repeated_calls_and_different_T_on_one_handle():
         lay.close()
 
 
+@pytest.mark.parametrize("wi", [1, 2, 4])
+def test_routing_ties_go_to_the_lower_index(wi):
+    """Router weights zero and biases on a few levels: every score ties with
+    others, and the GPU must order them as the oracle does (higher score
+    first, equal scores by ascending index) on the fused path (fp16 and
+    flat layers) and on the separate logits + selection path (decode layer,
+    272 score columns)."""
+    from compressed_expert_ffn_amd import synth
+    from tests.layers import oracle_layer
+    L = _lib()
+    w = WORKLOADS[wi].with_T(96)
+    inputs = synth.make_layer(w)
+    wT = dataclasses.replace(w, T=inputs["X"].shape[0])
+    rng = np.random.default_rng(5)
+    inputs["W_grp"] = np.zeros_like(inputs["W_grp"])
+    if inputs["W_exp"] is not None:
+        inputs["W_exp"] = np.zeros_like(inputs["W_exp"])
+    inputs["group_bias"] = (rng.integers(0, 3, size=w.G) * 0.5).astype(np.float32)
+    if w.K > 1:
+        inputs["expert_bias"] = (rng.integers(0, 3, size=w.E) * 0.5).astype(np.float32)
+    layer = oracle_layer(wT, inputs)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        rt = O.route(layer)
+        got = route_to_host(lay.route(x_to_device(inputs["X"], w.x_dtype)))
+        check_routing(got, rt, wT, wT.T)
+    finally:
+        lay.close()
+
+
 TILE_VARIANTS = [
     {"CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1", "CEFN_G2K": "0"},
     {"CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4", "CEFN_G2K": "0"},
