@@ -87,6 +87,8 @@ struct moe_handle {
   // CEFN_KS_G2 (k splits of the down projection) at create, for tuning
   int bm_env[3] = {0, 0, 0}, ks_env = 0;
   int g2k_env = -1;  // CEFN_G2K: 1 / 0 forces the in-workgroup k split of G2 on / off
+  int g1k_env = -1;  // CEFN_G1K: 1 / 0 forces the k-split tiles of G1 on / off
+  int nt1k = 0;      // column tiles of the k-split G1 (0: its partials do not fit)
   // profiling
   bool prof = false;
   int prof_max = 0, prof_calls = 0, prof_mask = -1;
@@ -617,6 +619,7 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
     }
     if (const char* v = std::getenv("CEFN_KS_G2")) h->ks_env = std::atoi(v);
     if (const char* v = std::getenv("CEFN_G2K")) h->g2k_env = std::atoi(v);
+    if (const char* v = std::getenv("CEFN_G1K")) h->g1k_env = std::atoi(v);
   }
 
   // router weights and biases
@@ -684,7 +687,12 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
       h->U = tmp;
       TRY(dalloc(h.get(), &h->V, T * kg * h->NV + 4));
       h->nt1 = (h->P_in * c.f + 255) / 256;
-      TRY(dalloc(h.get(), &h->Vp, (size_t)h->nt1 * T * kg * c.top_experts * RPAD + 4));
+      // the k-split G1 writes one V partial per 64 columns: room for those
+      // when it stays under 256 MiB (the layouts that use it have few rows)
+      const int nt1k = h->P_in * c.f / 64;
+      const size_t per_tile = (size_t)T * kg * c.top_experts * RPAD;
+      h->nt1k = per_tile * nt1k * sizeof(float) <= ((size_t)256 << 20) ? nt1k : 0;
+      TRY(dalloc(h.get(), &h->Vp, (size_t)std::max(h->nt1, h->nt1k) * per_tile + 4));
     }
     TRY(dalloc(h.get(), &tmp, T * kg * (long)c.f * es + 16));
     h->H = tmp;
@@ -770,6 +778,7 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   ga.ksplit = 1;
   ga.rows_total = (long)rows;
   int splits = 1;
+  bool g1k = false;  // gemm1 ran with the k-split tiles
   hipError_t e;
   if (c.r > 0) {
     GemmArgs u = ga;
@@ -792,8 +801,18 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     g1.ad_scale = h->Ad_s;
     const int nt = (h->P_in * c.f + 255) / 256;
     const int bm = pick_bm(h, GK_G1, rows, nt, 1);
+    // very few tiles: 32-row x 64-column tiles with d split over the
+    // wavefronts, when the 256-column tiling at 32 rows has under half a
+    // round of workgroups (measured: tiny layers gain, the decode layer's
+    // 132 tiles do not)
+    const bool k_ok = c.r == 0 || h->nt1k > 0;
+    g1k = k_ok && (h->g1k_env == 1 || (h->g1k_env != 0 && h->bm_env[GK_G1] == 0 && bm == 32 &&
+                                        (long)max_mtiles(T, kg, c.G, 32) * nt < 128));
     pf.begin(3);
-    e = launch_gemm(GK_G1, c.x_dtype, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, 1, st);
+    if (g1k)
+      e = launch_gemm(GK_G1K, c.x_dtype, h->mma, 32, g1, max_mtiles(T, kg, c.G, 32), h->P_in * c.f / 64, 1, st);
+    else
+      e = launch_gemm(GK_G1, c.x_dtype, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "gemm1 launch");
     pf.end(3);
   }
@@ -806,7 +825,7 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     va.idx = h->idx_live;
     va.vp_rows = (long)c.T_max * kg;
     va.rows = rows;
-    va.ntiles = h->nt1;
+    va.ntiles = g1k ? h->nt1k : h->nt1;
     va.NV = h->NV;
     va.K = c.K;
     va.kg = kg;

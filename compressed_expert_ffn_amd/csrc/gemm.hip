@@ -120,7 +120,9 @@ constexpr size_t tbuf_bytes() {
 template <int TY, int RT, class TO, class WS>
 __device__ __forceinline__ void run_tile(int KT, const TO& to, const WS& ws, int nb0, FragT<TY>* tl, int lane,
                                          f16v (&acc)[RT][CB]) {
-  MainloopTW<TY, RT, CB, TO, WS> ml{to, ws, nb0, tl, lane};
+  // short tiles: weights two stages ahead (a stage of 32 or 64 rows has too
+  // few MFMAs to cover one load's latency)
+  MainloopTW<TY, RT, CB, TO, WS, (RT <= 2 ? 2 : 1)> ml{to, ws, nb0, tl, lane};
   ml.run(KT, acc);
 }
 
@@ -217,19 +219,28 @@ struct EOps {
   int slot;           // position of j in the token's chosen list (-1: not chosen)
 };
 
-template <int XT, int TY, int RT, int ACT, int RES>
-__global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
+// KS (with RT = 1): for few rows per group, a workgroup owns 32 rows x one
+// wavefront's 64 columns and its 4 wavefronts walk consecutive quarters of d
+// for that tile (rows and weights straight into registers); the partial
+// tiles meet in LDS and every wavefront takes their sum, then the expert
+// steps of the block are dealt round-robin to the wavefronts and their h
+// sums meet in LDS before the store.  Four times the workgroups of the
+// 256-column tiling, each with a quarter of the dependent chain.
+template <int XT, int TY, int RT, int ACT, int RES, bool KS = false>
+__global__ __launch_bounds__(256, (KS && TY != DT_F32) ? 2 : 1) void gemm1_kernel(GemmArgs a) {
+  static_assert(!KS || RT == 1, "the k-split tile is 32 rows");
   constexpr int BMT = 32 * RT;
+  constexpr int BNFT = KS ? CB * 32 : BNF;  // columns of a tile
   constexpr int PIN = (ACT == ACT_SWIGLU) ? 2 : 1;
   constexpr int NFB = (ACT == ACT_SWIGLU) ? 1 : 2;  // f-blocks per wavefront
   using F = FragT<TY>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int N = PIN * a.f;
   TileCoord tc;
-  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (N + BNF - 1) / BNF, tc)) return;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (N + BNFT - 1) / BNFT, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nbw = (tc.nt * BNF + wave * 64) / 32;
+  const int nbw = KS ? tc.nt * CB : (tc.nt * BNF + wave * 64) / 32;
   const bool active = nbw * 32 < N;
   const int nb0 = active ? nbw : N / 32 - CB;
   // first f-block of this wavefront: SwiGLU interleaves gate and up blocks
@@ -244,15 +255,21 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   // expert j in the row's chosen list [BMT][K] (int8) | per token block, the
   // bit set of experts picked by any of its tokens | tile position -> row
   // of the group tile [BMT] | expert-set histogram and offsets [2][256]
+  // (KS: the first region also holds the four partial tiles [4][CB][16][64]
+  // floats before the V sums, and h sums [4][NFB][16][64] follow the
+  // histogram)
   const int VS = ke * RPAD + 1;
   const size_t vbytes = (size_t)4 * 32 * VS * sizeof(float);
-  const size_t abytes = (tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes + 15) & ~(size_t)15;
+  size_t abytes = tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes;
+  if (KS && abytes < (size_t)4 * CB * 16 * 64 * sizeof(float)) abytes = (size_t)4 * CB * 16 * 64 * sizeof(float);
+  abytes = (abytes + 15) & ~(size_t)15;
   float* s_v = reinterpret_cast<float*>(smem);
   float* s_w = reinterpret_cast<float*>(smem + abytes);
   int8_t* s_slot = reinterpret_cast<int8_t*>(s_w + BMT * K);
   uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_slot + ((BMT * K + 15) & ~15));
   int* s_perm = reinterpret_cast<int*>(s_bm + 2 * RT);
   int* s_hist = s_perm + BMT;
+  float* s_h = reinterpret_cast<float*>(s_hist + 260);
   F* tl = reinterpret_cast<F*>(smem);
 
   for (int i = tid; i < BMT * K; i += 256) {
@@ -328,15 +345,48 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
   }
   // (the main loop's first barrier publishes these tables)
 
-  TShared<XT, TY, RT> to;
-  to.init(static_cast<const TE<XT>*>(a.X), a.d, [&](int blk, int r) -> long {
-    const int m = blk * 32 + r;
-    return m0 + m < M ? (long)(a.garow[row0 + s_perm[m]] / a.kg) : -1L;
-  });
   f16v acc[RT][CB];
   zero_acc<RT, CB>(acc);
-  WPlain<TY> ws{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
-  run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);  // ends with a barrier
+  if constexpr (KS) {
+    const int KT = a.d / KB;
+    const int k0 = wave * KT / 4, k1 = (wave + 1) * KT / 4;
+    using TD = TDirect<XT, TY, 1>;
+    TD td;
+    td.init(static_cast<const TE<XT>*>(a.X) + (long)k0 * KB, a.d, lane, [&](int) -> long {
+      const int m = lane & 31;
+      return m0 + m < M ? (long)(a.garow[row0 + s_perm[m]] / a.kg) : -1L;
+    });
+    using WO = WDirect<WPlain<TY>, CB>;
+    WO wo;
+    wo.src = WPlain<TY>{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
+    wo.src.ks0 = k0 * 4;
+    wo.nb0 = nb0;
+    Mainloop<TY, 1, CB, TD, WO, 2> ml{td, wo, lane};
+    if (k1 > k0) ml.template run<typename TD::Raw[1][4], typename WO::Raw[CB][4]>(k1 - k0, acc);
+    // the four partial tiles meet in LDS; every wavefront takes the sum
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[((wave * CB + c) * 16 + v) * 64 + lane] = acc[0][c][v];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float* q = red + (c * 16 + v) * 64 + lane;
+        acc[0][c][v] = (q[0] + q[CB * 16 * 64]) + (q[2 * CB * 16 * 64] + q[3 * CB * 16 * 64]);
+      }
+    __syncthreads();
+  } else {
+    TShared<XT, TY, RT> to;
+    to.init(static_cast<const TE<XT>*>(a.X), a.d, [&](int blk, int r) -> long {
+      const int m = blk * 32 + r;
+      return m0 + m < M ? (long)(a.garow[row0 + s_perm[m]] / a.kg) : -1L;
+    });
+    WPlain<TY> ws{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
+    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);  // ends with a barrier
+  }
 
   if constexpr (RES != ER_NONE) {
     for (int i = tid; i < 4 * 32 * VS; i += 256) s_v[i] = 0.f;
@@ -357,6 +407,20 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
     mhi[t] = active ? __builtin_amdgcn_readfirstlane(s_bm[2 * t + 1]) : 0u;
   }
   auto first_j = [](uint32_t lo, uint32_t hi) { return lo ? __builtin_ctz(lo) : 32 + __builtin_ctz(hi); };
+  if constexpr (KS) {
+    // expert steps of the block dealt round-robin: the r-th set bit to
+    // wavefront r % 4
+    uint32_t lo = mlo[0], hi = mhi[0], flo = 0u, fhi = 0u;
+    for (int r = 0; lo | hi; ++r) {
+      const int j = first_j(lo, hi);
+      if (lo) lo &= lo - 1; else hi &= hi - 1;
+      if ((r & 3) == wave) {
+        if (j < 32) flo |= 1u << j; else fhi |= 1u << (j - 32);
+      }
+    }
+    mlo[0] = flo;
+    mhi[0] = fhi;
+  }
 
   // issue the loads of step (t, j)
   auto load_ops = [&](int t, int j, EOps<TY, PIN, NFB>& o) {
@@ -489,7 +553,24 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
       }
       cur = nxt;
     }
-    if (active && m0 + m < M) {  // (idle wavefronts computed nothing above)
+    if constexpr (KS) {
+      // h sums of the four wavefronts' expert steps meet in LDS
+#pragma unroll
+      for (int c = 0; c < NFB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s_h[((wave * NFB + c) * 16 + v) * 64 + lane] = hbar[c][v];
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int c = 0; c < NFB; ++c)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float* q = s_h + (c * 16 + v) * 64 + lane;
+            hbar[c][v] = (q[0] + q[NFB * 16 * 64]) + (q[2 * NFB * 16 * 64] + q[3 * NFB * 16 * 64]);
+          }
+      }
+    }
+    if (active && m0 + m < M && (!KS || wave == 0)) {  // (idle wavefronts computed nothing above)
       TE<TY>* hrow = H + (long)(row0 + s_perm[m]) * a.f + 4 * h;
 #pragma unroll
       for (int c = 0; c < NFB; ++c)
@@ -803,24 +884,24 @@ hipError_t go(KF kfn, dim3 grid, size_t lds, const GemmArgs& a, hipStream_t st) 
 // Residual storage kinds valid for a (activation type, MFMA type) pair:
 // plain residuals are stored in the MFMA type (F32 with an F32 base, F16 with
 // an F16 base), INT4 needs a 16-bit base.
-template <int XT, int TY, int RT, int ACT>
+template <int XT, int TY, int RT, int ACT, bool KS>
 hipError_t launch_g1_act(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (a.resid == RS_NONE) return go(gemm1_kernel<XT, TY, RT, ACT, ER_NONE>, grid, lds, a, st);
+  if (a.resid == RS_NONE) return go(gemm1_kernel<XT, TY, RT, ACT, ER_NONE, KS>, grid, lds, a, st);
   if constexpr (TY == DT_F32) {
-    if (a.resid == RS_F32) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN>, grid, lds, a, st);
+    if (a.resid == RS_F32) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN, KS>, grid, lds, a, st);
   } else {
-    if (a.resid == RS_INT4) return go(gemm1_kernel<XT, TY, RT, ACT, ER_INT4>, grid, lds, a, st);
+    if (a.resid == RS_INT4) return go(gemm1_kernel<XT, TY, RT, ACT, ER_INT4, KS>, grid, lds, a, st);
     if constexpr (TY == DT_F16) {
-      if (a.resid == RS_F16) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN>, grid, lds, a, st);
+      if (a.resid == RS_F16) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN, KS>, grid, lds, a, st);
     }
   }
   return hipErrorInvalidValue;
 }
 
-template <int XT, int TY, int RT>
+template <int XT, int TY, int RT, bool KS = false>
 hipError_t launch_g1(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (a.act == ACT_SWIGLU) return launch_g1_act<XT, TY, RT, ACT_SWIGLU>(a, grid, lds, st);
-  if constexpr (RT <= 4) return launch_g1_act<XT, TY, RT, ACT_GELU>(a, grid, lds, st);
+  if (a.act == ACT_SWIGLU) return launch_g1_act<XT, TY, RT, ACT_SWIGLU, KS>(a, grid, lds, st);
+  if constexpr (RT <= 4) return launch_g1_act<XT, TY, RT, ACT_GELU, KS>(a, grid, lds, st);
   return hipErrorInvalidValue;
 }
 
@@ -833,6 +914,9 @@ hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
       return hipErrorInvalidValue;  // launched by launch_ugemm
     case GK_G1:
       return launch_g1<XT, TY, RT>(a, grid, lds, st);
+    case GK_G1K:
+      if constexpr (RT == 1) return launch_g1<XT, TY, 1, true>(a, grid, lds, st);
+      return hipErrorInvalidValue;
     case GK_G2:
       if (int4) return go(gemm2_kernel<XT, TY, RT, true>, grid, lds, a, st);
       return go(gemm2_kernel<XT, TY, RT, false>, grid, lds, a, st);
@@ -864,11 +948,14 @@ hipError_t launch_types(int kind, int bm, const GemmArgs& a, dim3 grid, hipStrea
 size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
   const size_t fb = ty == DT_F32 ? 32 : 16;
   const size_t tbytes = 2 * (size_t)(bm / 32) * 4 * 64 * fb;
-  if (kind != GK_G1) return tbytes;
+  if (kind != GK_G1 && kind != GK_G1K) return tbytes;
   const size_t vbytes = (size_t)4 * 32 * (ke * RPAD + 1) * sizeof(float);
-  const size_t abytes = (tbytes > vbytes ? tbytes : vbytes + 15) & ~(size_t)15;
+  size_t abytes = tbytes > vbytes ? tbytes : vbytes;
+  if (kind == GK_G1K && abytes < (size_t)4 * CB * 16 * 64 * sizeof(float)) abytes = (size_t)4 * CB * 16 * 64 * sizeof(float);
+  abytes = (abytes + 15) & ~(size_t)15;
+  const size_t hsum = kind == GK_G1K ? (size_t)4 * 2 * 16 * 64 * sizeof(float) : 0;  // NFB <= 2
   return abytes + sizeof(float) * bm * K + (((size_t)bm * K + 15) & ~(size_t)15) + sizeof(uint32_t) * 2 * (bm / 32) +
-         sizeof(int) * ((size_t)bm + 256 + 4) + 64;
+         sizeof(int) * ((size_t)bm + 260) + hsum + 64;
 }
 
 template <int XT, int TY>

@@ -350,7 +350,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int TY, int RT, int CB, class TO, class WS>
+// WPD: how many stages ahead the weights are loaded (2 for short tiles, whose
+// stage of MFMAs is too short to cover the memory latency).
+template <int TY, int RT, int CB, class TO, class WS, int WPD = 1>
 struct MainloopTW {
   using F = FragT<TY>;
   using WR = typename WS::Raw;
@@ -393,28 +395,30 @@ struct MainloopTW {
     }
   }
 
-  // stage kt from LDS buffer kt & 1 with weights wc; loads stage kt + 1
-  // (clamped: the last stage reloads itself into the idle buffer) into wn
+  // stage kt from LDS buffer kt & 1 with weights wc; loads the tokens of
+  // stage kt + 1 (clamped: the last stage reloads itself into the idle
+  // buffer) and the weights of stage kt + WPD (clamped) into wn
   template <class TR>
   __device__ __forceinline__ void stage(int kt, int KT, TR& tr, WR (&wc)[CB][4], WR (&wn)[CB][4], F (&tf)[2][RT],
                                         f16v (&acc)[RT][CB]) const {
     const int b = kt & 1;
     const int kn = kt + 1 < KT ? kt + 1 : KT - 1;
+    const int kw = kt + WPD < KT ? kt + WPD : KT - 1;
     dsr(b, 1, tf[1]);
     to.fetch_half(kn, 0, tr);
-    wload(kn, 0, wn);
+    wload(kw, 0, wn);
     mfmas(wc, tf[0], 0, acc);
     pattern<(TO::SEG + 1) / 2 + CB>();
     __builtin_amdgcn_sched_barrier(0);
     dsr(b, 2, tf[0]);
     to.fetch_half(kn, 1, tr);
-    wload(kn, 1, wn);
+    wload(kw, 1, wn);
     mfmas(wc, tf[1], 1, acc);
     pattern<TO::SEG / 2 + CB>();
     __builtin_amdgcn_sched_barrier(0);
     dsr(b, 3, tf[1]);
-    wload(kn, 2, wn);
-    wload(kn, 3, wn);
+    wload(kw, 2, wn);
+    wload(kw, 3, wn);
     mfmas(wc, tf[0], 2, acc);
     pattern<2 * CB>();
     __builtin_amdgcn_sched_barrier(0);
@@ -429,21 +433,29 @@ struct MainloopTW {
   }
 
   __device__ void run(int KT, f16v (&acc)[RT][CB]) const {
+    static_assert(WPD == 1 || WPD == 2, "weights one or two stages ahead");
+    constexpr int U = WPD + 1;  // weight register sets in the ring
     typename TO::Raw tr[TO::SEG];
-    WR wr[2][CB][4];
+    WR wr[U][CB][4];
     F tf[2][RT];
     to.fetch(0, tr);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wload(0, s, wr[0]);
+    for (int p = 0; p < WPD; ++p)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wload(p < KT ? p : KT - 1, s, wr[p]);
     to.commit(tr, tl);
     lds_barrier();
     dsr(0, 0, tf[0]);
     int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-      stage(kt, KT, tr, wr[0], wr[1], tf, acc);
-      stage(kt + 1, KT, tr, wr[1], wr[0], tf, acc);
+    for (; kt + U <= KT; kt += U) {
+      stage(kt, KT, tr, wr[0], wr[WPD % U], tf, acc);
+      stage(kt + 1, KT, tr, wr[1], wr[(1 + WPD) % U], tf, acc);
+      if constexpr (U > 2) stage(kt + 2, KT, tr, wr[2 % U], wr[(2 + WPD) % U], tf, acc);
     }
-    if (kt < KT) stage(kt, KT, tr, wr[0], wr[1], tf, acc);
+    if (kt < KT) stage(kt, KT, tr, wr[0], wr[WPD % U], tf, acc);
+    if constexpr (U > 2) {
+      if (kt + 1 < KT) stage(kt + 1, KT, tr, wr[1], wr[(1 + WPD) % U], tf, acc);
+    }
     __syncthreads();
   }
 };
