@@ -428,9 +428,17 @@ int pick_bm(const moe_handle* h, int which, int rows, int ntiles, int splits) {
     // row tiles: every group's last tile is partial (counted as half)
     const long mt = (rows + bm - 1) / bm + h->cfg.G / 2;
     const long tiles = mt * ntiles * splits;
-    const int occ = bm <= 64 ? 2 : 1;  // workgroups per compute unit
+    int occ = bm <= 64 ? 2 : 1;  // workgroups per compute unit
+    float e = eff[i];
+    if (which == GK_G1 && bm == 128 && !f32 && h->cfg.act == MOE_ACT_SWIGLU) {
+      // the SwiGLU gemm1 at 128 rows fits two workgroups per compute unit,
+      // so one's epilogue overlaps the other's main loop: measured 6-18%
+      // faster than 256-row tiles on the fp16, flat bf16 and INT4 layers
+      occ = 2;
+      e = 1.1f;
+    }
     const long rounds = (tiles + 256L * occ - 1) / (256L * occ);
-    const float cost = rounds * (float)bm * occ / eff[i] / splits;
+    const float cost = rounds * (float)bm * occ / e / splits;
     if (cost < best_cost) {
       best_cost = cost;
       best = bm;

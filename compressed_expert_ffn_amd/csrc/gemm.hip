@@ -227,7 +227,7 @@ struct EOps {
 // sums meet in LDS before the store.  Four times the workgroups of the
 // 256-column tiling, each with a quarter of the dependent chain.
 template <int XT, int TY, int RT, int ACT, int RES, bool KS = false>
-__global__ __launch_bounds__(256, (KS && TY != DT_F32) ? 2 : 1) void gemm1_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT_SWIGLU))) ? 2 : 1) void gemm1_kernel(GemmArgs a) {
   static_assert(!KS || RT == 1, "the k-split tile is 32 rows");
   constexpr int BMT = 32 * RT;
   constexpr int BNFT = KS ? CB * 32 : BNF;  // columns of a tile
