@@ -603,7 +603,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
 // tail).  One split and one group per token: Y is written directly;
 // otherwise fp32 partials ypart[s][t*kg + ga][d] for the combine kernel.
 template <int XT, int TY, int RT, bool INT4>
-__global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_kernel(GemmArgs a) {
   constexpr int BMT = 32 * RT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (blockIdx.x == 0 && a.zero_ptr) {
