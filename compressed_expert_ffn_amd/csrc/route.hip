@@ -331,11 +331,14 @@ __global__ __launch_bounds__(256) void select_kernel(RouteArgs a, int tpb) {
 }
 
 // Scores and selection in one kernel when a 32-token block's scores fit one
-// workgroup (at most 4 column blocks): wavefront w computes k quarter w of
-// every column block, the quarters meet in LDS, and 32 threads select.
-template <int XT, int NCB>
-__global__ __launch_bounds__(256) void route_fused_kernel(RouteArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[4][NCB][16][64];
+// workgroup (at most 4 column blocks): wavefront w of NW (4 or 8) computes k
+// range w of every column block, the NW partial blocks meet in LDS
+// (dynamic, summed pairwise in a fixed order), and 32 threads select.  More
+// wavefronts shorten the dependent MFMA chain of the few workgroups a small
+// batch has.
+template <int XT, int NCB, int NW>
+__global__ __launch_bounds__(64 * NW) void route_fused_kernel(RouteArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [NW][NCB][16][64]
   __shared__ float sc[32][NCB * 32 + 1];
   // per-workgroup routing counts: 32 tokens span at most 2 group-list chunks
   // and 3 expert-list chunks of 256 assignments
@@ -343,25 +346,35 @@ __global__ __launch_bounds__(256) void route_fused_kernel(RouteArgs a) {
   __shared__ int lce[3 * 1024];
   const int tb = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kq = a.d / 4;
-  for (int i = threadIdx.x; i < 2 * a.G; i += 256) lcg[i] = 0;
+  constexpr int NT = 64 * NW;
+  const int kq = a.d / NW;
+  for (int i = threadIdx.x; i < 2 * a.G; i += NT) lcg[i] = 0;
   if (a.count_experts)
-    for (int i = threadIdx.x; i < 3 * a.E; i += 256) lce[i] = 0;
+    for (int i = threadIdx.x; i < 3 * a.E; i += NT) lce[i] = 0;
   {
     f16v acc[NCB];
     score_tiles<XT, NCB>(a, tb, 0, wave * kq, kq, lane, acc);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) red[wave][cb][v][lane] = acc[cb][v];
+      for (int v = 0; v < 16; ++v) red[((wave * NCB + cb) * 16 + v) * 64 + lane] = acc[cb][v];
   }
   __syncthreads();
   const int NC = a.G + (a.K > 1 ? a.G * a.K : 0);
-  for (int e = threadIdx.x; e < NCB * 16 * 64; e += 256) {
+  for (int e = threadIdx.x; e < NCB * 16 * 64; e += NT) {
     const int cb = e / (16 * 64), v = (e / 64) % 16, l = e % 64;
     const int c = cb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-    if (c < NC)
-      sc[l & 31][c] = ((red[0][cb][v][l] + red[1][cb][v][l]) + (red[2][cb][v][l] + red[3][cb][v][l])) + score_bias(a, c);
+    if (c < NC) {
+      // pairwise over the wavefronts' partials
+      float p[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) p[w] = red[w * NCB * 16 * 64 + e];
+#pragma unroll
+      for (int st = 1; st < NW; st <<= 1)
+#pragma unroll
+        for (int w = 0; w + st < NW; w += 2 * st) p[w] += p[w + st];
+      sc[l & 31][c] = p[0] + score_bias(a, c);
+    }
   }
   __syncthreads();
   const int t = tb * 32 + threadIdx.x;
@@ -369,10 +382,10 @@ __global__ __launch_bounds__(256) void route_fused_kernel(RouteArgs a) {
   const int cg0 = t0 * a.kg / CHUNK, ce0 = t0 * a.k / CHUNK;
   if (threadIdx.x < 32 && t < a.T) select_token(a, t, sc[threadIdx.x], lcg, cg0, lce, ce0);
   __syncthreads();
-  for (int i = threadIdx.x; i < 2 * a.G; i += 256)
+  for (int i = threadIdx.x; i < 2 * a.G; i += NT)
     if (lcg[i]) atomicAdd(&a.cgcount[(cg0 + i / a.G) * a.G + i % a.G], lcg[i]);
   if (a.count_experts)
-    for (int i = threadIdx.x; i < 3 * a.E; i += 256)
+    for (int i = threadIdx.x; i < 3 * a.E; i += NT)
       if (lce[i]) atomicAdd(&a.ccount[(ce0 + i / a.E) * a.E + i % a.E], lce[i]);
 }
 
@@ -492,17 +505,42 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int XT, int NCB, int NW>
+hipError_t launch_fused_nw(const RouteArgs& a, hipStream_t st) {
+  auto k = route_fused_kernel<XT, NCB, NW>;
+  const size_t lds = (size_t)NW * NCB * 16 * 64 * sizeof(float);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, dim3((a.T + 31) / 32), dim3(64 * NW), lds, st, a);
+  return hipGetLastError();
+}
+
+// Wavefronts per workgroup: 8 when the batch has fewer 32-token blocks than
+// the chip has compute units (the chain length then decides) and each
+// wavefront still keeps at least 128 of the d products; else 4, which
+// leaves more LDS for other workgroups on the same compute unit.
+inline int fused_waves(int T, int d) {
+  return ((T + 31) / 32 < 256 && d % (16 * 8) == 0 && d / 8 >= 128) ? 8 : 4;
+}
+
+template <int XT, int NCB>
+hipError_t launch_fused_ncb(const RouteArgs& a, hipStream_t st) {
+  if (fused_waves(a.T, a.d) == 8) return launch_fused_nw<XT, NCB, 8>(a, st);
+  return launch_fused_nw<XT, NCB, 4>(a, st);
+}
+
 template <int XT>
 hipError_t launch_fused(const RouteArgs& a, int ncb, hipStream_t st) {
-  const dim3 grid((a.T + 31) / 32);
   switch (ncb) {
-    case 1: hipLaunchKernelGGL((route_fused_kernel<XT, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((route_fused_kernel<XT, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((route_fused_kernel<XT, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((route_fused_kernel<XT, 4>), grid, dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
+    case 1: return launch_fused_ncb<XT, 1>(a, st);
+    case 2: return launch_fused_ncb<XT, 2>(a, st);
+    case 3: return launch_fused_ncb<XT, 3>(a, st);
+    case 4: return launch_fused_ncb<XT, 4>(a, st);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st) {
