@@ -88,6 +88,7 @@ struct moe_handle {
   int bm_env[3] = {0, 0, 0}, ks_env = 0;
   int g2k_env = -1;  // CEFN_G2K: 1 / 0 forces the in-workgroup k split of G2 on / off
   int g1k_env = -1;  // CEFN_G1K: 1 / 0 forces the k-split tiles of G1 on / off
+  int ut_env = -1;   // CEFN_UT: 1 / 0 forces the tile-engine U GEMM on / off
   int nt1k = 0;      // column tiles of the k-split G1 (0: its partials do not fit)
   // profiling
   bool prof = false;
@@ -631,6 +632,7 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
     if (const char* v = std::getenv("CEFN_KS_G2")) h->ks_env = std::atoi(v);
     if (const char* v = std::getenv("CEFN_G2K")) h->g2k_env = std::atoi(v);
     if (const char* v = std::getenv("CEFN_G1K")) h->g1k_env = std::atoi(v);
+    if (const char* v = std::getenv("CEFN_UT")) h->ut_env = std::atoi(v);
   }
 
   // router weights and biases
@@ -797,8 +799,18 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     u.bw_gstride = h->at_gs;
     u.bw_scale = h->At_s;
     u.bws_gstride = h->at_sgs;
+    // many rows: the tile engine over 64- or 128-row x 256-column tiles
+    // once there are a chip's worth of them (each row of X read once per 256
+    // columns of U); otherwise 32-row tiles with d split over the wavefronts
+    const int nut = (h->NU + 255) / 256;
+    const int ubm = (long)max_mtiles(T, kg, c.G, 128) * nut >= 256 ? 128 : 64;
+    const bool ut = h->ut_env == 1 || (h->ut_env != 0 && (long)max_mtiles(T, kg, c.G, 64) * nut >= 256);
     pf.begin(2);
-    e = launch_gemm(GK_U, c.x_dtype, h->mma, 32, u, max_mtiles(T, kg, c.G, 32), 1, 1, st);
+    if (ut)
+      e = launch_gemm(GK_UT, c.x_dtype, h->mma, h->mma == MOE_F32 ? 64 : ubm, u,
+                      max_mtiles(T, kg, c.G, h->mma == MOE_F32 ? 64 : ubm), nut, 1, st);
+    else
+      e = launch_gemm(GK_U, c.x_dtype, h->mma, 32, u, max_mtiles(T, kg, c.G, 32), 1, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "ugemm launch");
     pf.end(2);
   }

@@ -193,6 +193,53 @@ __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
   }
 }
 
+// U = X . A for many rows: the tile engine (gathered rows staged through
+// LDS, A straight into registers, INT4 decoded per use) on BM-row x
+// 256-column tiles, so a row of X is read once per 256 columns of U rather
+// than once per 64 and the INT4 factors are decoded once per BM rows.
+template <int XT, int TY, int RT, bool INT4>
+__global__ __launch_bounds__(256, (TY != DT_F32 && RT <= 4) ? 2 : 1) void ugemm_tile_kernel(GemmArgs a) {
+  constexpr int BMT = 32 * RT;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  TileCoord tc;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.NU + BNF - 1) / BNF, tc)) return;
+  const int g = tc.g, m0 = tc.m0, M = tc.M;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nbw = (tc.nt * BNF + wave * 64) / 32;
+  const bool active = nbw * 32 < a.NU;
+  const int nb0 = active ? nbw : a.NU / 32 - CB;
+  const int row0 = a.goffsets[g] + m0;
+  FragT<TY>* tl = reinterpret_cast<FragT<TY>*>(smem);
+  TShared<XT, TY, RT> to;
+  to.init(static_cast<const TE<XT>*>(a.X), a.d, [&](int blk, int r) -> long {
+    const int m = blk * 32 + r;
+    return m0 + m < M ? (long)(a.garow[row0 + m] / a.kg) : -1L;
+  });
+  f16v acc[RT][CB];
+  zero_acc<RT, CB>(acc);
+  const int KS = a.d / 16;
+  if constexpr (INT4) {
+    WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride, KS};
+    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);
+  } else {
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, KS};
+    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);
+  }
+  if (!active) return;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int m = t * 32 + (lane & 31);
+    if (m0 + m >= M) continue;
+    TE<TY>* urow = static_cast<TE<TY>*>(a.U) + (long)(row0 + m) * a.NU + nb0 * 32 + 4 * (lane >> 5);
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store4<TY>(urow + c * 32 + 8 * q, acc[t][c][4 * q], acc[t][c][4 * q + 1], acc[t][c][4 * q + 2],
+                   acc[t][c][4 * q + 3]);
+  }
+}
+
 // --------------------------------------------- G1: base GEMM + epilogue --
 // Residual storage of the epilogue operands: none, plain (stored in the MFMA
 // type), or INT4.
@@ -912,6 +959,9 @@ hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
   switch (kind) {
     case GK_U:
       return hipErrorInvalidValue;  // launched by launch_ugemm
+    case GK_UT:
+      if (int4) return go(ugemm_tile_kernel<XT, TY, RT, true>, grid, lds, a, st);
+      return go(ugemm_tile_kernel<XT, TY, RT, false>, grid, lds, a, st);
     case GK_G1:
       return launch_g1<XT, TY, RT>(a, grid, lds, st);
     case GK_G1K:

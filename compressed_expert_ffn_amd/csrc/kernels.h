@@ -126,8 +126,9 @@ struct CombineArgs {
 
 // G2K: G2 with the k split inside a workgroup.  G1K: G1 with 32-row x
 // 64-column tiles and d split over the four wavefronts (few rows per group;
-// bm = 32, ntiles counted for 64 columns).
-enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2, GK_G2K = 3, GK_G1K = 4 };
+// bm = 32, ntiles counted for 64 columns).  UT: U on the tile engine
+// (BM-row x 256-column tiles; many rows).
+enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2, GK_G2K = 3, GK_G1K = 4, GK_UT = 5 };
 
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st);
 int router_splits(int T, int d, int NCp);
