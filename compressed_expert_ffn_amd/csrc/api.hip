@@ -60,6 +60,7 @@ struct moe_handle {
   bool dirty = false;
   // weights
   float *Wr = nullptr, *gbias = nullptr, *ebias = nullptr;
+  uint16_t* Wb = nullptr;  // bf16 parts of Wr (16-bit activations)
   int NCp = 0;         // router score columns, padded to 32
   float* L = nullptr;  // router scores (k-split partials)
   void *W1 = nullptr, *W2 = nullptr, *At = nullptr, *B1 = nullptr, *Ad = nullptr, *Bd = nullptr;
@@ -536,6 +537,7 @@ int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, bool
   ra.k = h->k;
   ra.E = h->E;
   ra.Wr = h->Wr;
+  ra.Wb = h->Wb;
   ra.NCp = h->NCp;
   ra.L = h->L;
   ra.nsplit = router_splits(T, c.d, h->NCp);
@@ -654,6 +656,24 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
         wr[((size_t)(k / 16) * h->NCp + col) * 16 + (k % 16)] = v;
       }
     TRY(upload(h.get(), &h->Wr, wr));
+    if (c.x_dtype != MOE_F32) {
+      // three bf16 parts, each the nearest bf16 to what the previous parts
+      // leave (every subtraction exact in fp32)
+      const size_t n = wr.size();
+      std::vector<uint16_t> wb(3 * n);
+      for (size_t i = 0; i < n; ++i) {
+        float rest = wr[i];
+        for (int p = 0; p < 3; ++p) {
+          const uint16_t b = host_f32_to_bf16(rest);
+          uint32_t u = static_cast<uint32_t>(b) << 16;
+          float bv;
+          std::memcpy(&bv, &u, 4);
+          wb[p * n + i] = b;
+          rest -= bv;
+        }
+      }
+      TRY(upload(h.get(), &h->Wb, wb));
+    }
     if (w->group_bias) {
       std::vector<float> gb(w->group_bias, w->group_bias + c.G);
       TRY(upload(h.get(), &h->gbias, gb));

@@ -33,6 +33,9 @@ namespace cefn {
 struct RouteArgs {
   const void* X;
   int T, d, G, K, kg, ke, k, E;
+  const uint16_t* Wb;  // 16-bit activations: the same matrix as three bf16 parts
+                       // [3][d/16][NCp][16], W = part 0 + part 1 + part 2 to
+                       // within 2^-24 relative (split on the host)
   const float* Wr;     // router matrix [d/16][NCp][16]: column c < G is W_grp[:, c],
                        // column G + g*K + j is W_exp[g][:, j], the rest zero;
                        // element (k, c) at ((k/16) * NCp + c) * 16 + k % 16

@@ -53,14 +53,94 @@ __device__ __forceinline__ void load8x(const typename Elem<XT>::T* p, float (&v)
   }
 }
 
+// 16-bit activations: the same partial scores from bf16 MFMAs.  The FP32
+// router matrix is held as three bf16 parts (W = p0 + p1 + p2 to within
+// 2^-24 relative); bf16 activations enter as they are, fp16 ones as two
+// exact bf16 parts (an fp16 significand has 11 bits: the nearest bf16 and
+// the at most 4-bit remainder).  A product of two bf16 is exact in FP32,
+// so the FP32 accumulation of x.p0 + x.p1 + x.p2 (+ xr.p0 + xr.p1 for fp16)
+// differs from an FP32 dot product only by the order of the additions and
+// by terms below 2^-24 of the score, as the FP32 router requires, at a
+// fraction of the FP32 MFMA time.
+template <int XT, int NCB>
+__device__ __forceinline__ void score_tiles_bf(const RouteArgs& a, int tb, int cb0, int k0, int kq, int lane,
+                                               f16v (&acc)[NCB]) {
+  using XE = typename Elem<XT>::T;
+  using B8 = typename Frag<DT_BF16>::T;
+  const int h = lane >> 5;
+  int tok = tb * 32 + (lane & 31);
+  tok = tok < a.T ? tok : a.T - 1;  // rows past the batch repeat the last one
+  const XE* xp = static_cast<const XE*>(a.X) + (long)tok * a.d + k0 + 8 * h;
+  const long pstride = (long)(a.d / 16) * a.NCp * 16;
+  const uint16_t* wp = a.Wb + ((long)(k0 / 16) * a.NCp + cb0 * 32 + (lane & 31)) * 16 + 8 * h;
+  const long wstep = (long)a.NCp * 16;
+#pragma unroll
+  for (int c = 0; c < NCB; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+  const int n16 = kq / 16;
+  if (n16 == 0) return;
+  u4v xa, xb;
+  u4v wa[NCB][3], wb[NCB][3];
+  auto issue = [&](int i, u4v& xv, u4v (&wv)[NCB][3]) {
+    const int ic = i < n16 ? i : n16 - 1;  // the last group re-reads itself
+    xv = *reinterpret_cast<const u4v*>(xp + ic * 16);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) wv[c][p] = *reinterpret_cast<const u4v*>(wp + p * pstride + ic * wstep + c * 32 * 16);
+  };
+  auto mma = [&](const u4v& xv, const u4v (&wv)[NCB][3]) {
+    B8 xh, xl;
+    if constexpr (XT == DT_BF16) {
+      xh = __builtin_bit_cast(B8, xv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = f16_bits_to_f32(static_cast<uint16_t>((xv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+        const uint16_t hb = f32_to_bf16_bits(f);
+        xh[e] = __builtin_bit_cast(__bf16, hb);
+        xl[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(f - bf16_bits_to_f32(hb)));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p) acc[c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xh, acc[c]);
+      if constexpr (XT != DT_BF16) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) acc[c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xl, acc[c]);
+      }
+    }
+  };
+  issue(0, xa, wa);
+  int i = 0;
+  for (; i + 2 <= n16; i += 2) {
+    issue(i + 1, xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(i + 2, xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (i < n16) mma(xa, wa);
+}
+
 // Partial scores of one wavefront: token block tb, score-column blocks
 // cb0 .. cb0 + NCB - 1, depth [k0, k0 + kq) (kq a multiple of 16).  Lane l
 // ends with token tb*32 + l % 32 and columns cb*32 + 8 (v / 4) + 4 (l / 32)
 // + v % 4 in acc[cb - cb0][v].  The next 16 k are loaded before the
-// current 16 k's MFMAs (two register sets, loop unrolled by two).
+// current 16 k's MFMAs (two register sets, loop unrolled by two).  FP32
+// MFMAs for fp32 activations; the bf16 form above for 16-bit ones.
 template <int XT, int NCB>
 __device__ __forceinline__ void score_tiles(const RouteArgs& a, int tb, int cb0, int k0, int kq, int lane,
                                             f16v (&acc)[NCB]) {
+  if constexpr (XT != DT_F32) {
+    score_tiles_bf<XT, NCB>(a, tb, cb0, k0, kq, lane, acc);
+    return;
+  }
   using XE = typename Elem<XT>::T;
   const int h = lane >> 5;
   int tok = tb * 32 + (lane & 31);
