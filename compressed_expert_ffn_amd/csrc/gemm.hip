@@ -132,17 +132,17 @@ __device__ __forceinline__ void run_tile(int KT, const TO& to, const WS& ws, int
 // that same tile (rows and weights read straight into registers, two stages
 // ahead), so each dependent chain is a quarter as long; the four partial
 // tiles meet in LDS and wavefront c writes column block c.
-template <int XT, int TY, int CB_, bool INT4>
-__global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
+template <int XT, int TY, int CB_, bool INT4, int NWU = 4>
+__global__ __launch_bounds__(64 * NWU) void ugemm_kernel(GemmArgs a) {
   constexpr int BW = CB_ * 32;
-  __shared__ __attribute__((aligned(16))) float red[4][CB_][16][64];
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [NWU][CB_][16][64]
   TileCoord tc;
   if (!map_tile(blockIdx.x, a.gcounts, a.G, 32, (a.NU + BW - 1) / BW, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = a.goffsets[g] + m0;
   const int KT = a.d / KB;
-  const int k0 = wave * KT / 4, k1 = (wave + 1) * KT / 4;
+  const int k0 = wave * KT / NWU, k1 = (wave + 1) * KT / NWU;
   TDirect<XT, TY, 1> to;
   to.init(static_cast<const TE<XT>*>(a.X) + (long)k0 * KB, a.d, lane, [&](int) -> long {
     const int m = lane & 31;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int c = 0; c < CB_; ++c)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) red[wave][c][v][lane] = acc[0][c][v];
+    for (int v = 0; v < 16; ++v) red[((wave * CB_ + c) * 16 + v) * 64 + lane] = acc[0][c][v];
   __syncthreads();
   const int c = wave;
   const int m = lane & 31;
@@ -187,7 +187,15 @@ __global__ __launch_bounds__(256) void ugemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = 4 * q + i;
-      o[i] = (red[0][c][v][lane] + red[1][c][v][lane]) + (red[2][c][v][lane] + red[3][c][v][lane]);
+      // pairwise over the wavefronts' partial tiles
+      float pr[NWU];
+#pragma unroll
+      for (int w = 0; w < NWU; ++w) pr[w] = red[((w * CB_ + c) * 16 + v) * 64 + lane];
+#pragma unroll
+      for (int st = 1; st < NWU; st <<= 1)
+#pragma unroll
+        for (int w = 0; w + st < NWU; w += 2 * st) pr[w] += pr[w + st];
+      o[i] = pr[0];
     }
     store4<TY>(urow + 8 * q, o[0], o[1], o[2], o[3]);
   }
@@ -1008,6 +1016,30 @@ size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
          sizeof(int) * ((size_t)bm + 260) + hsum + 64;
 }
 
+template <class KF>
+hipError_t go_nw(KF kfn, dim3 grid, int nw, size_t lds, const GemmArgs& a, hipStream_t st) {
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kfn, grid, dim3(64 * nw), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int XT, int TY, int CB_, bool INT4>
+hipError_t launch_ugemm_cb(const GemmArgs& a, dim3 grid, hipStream_t st) {
+  // 8 wavefronts (a dependent chain half as long) when there are fewer
+  // workgroups than compute units and every wavefront keeps at least 2
+  // stages of d; 64-column 16-bit tiles only (the others would spill at two
+  // wavefronts per SIMD)
+  if constexpr (CB_ == 2 && TY != DT_F32) {
+    if (grid.x < 256 && a.d / KB >= 16)
+      return go_nw(ugemm_kernel<XT, TY, CB_, INT4, 8>, grid, 8, (size_t)8 * CB_ * 16 * 64 * sizeof(float), a, st);
+  }
+  return go_nw(ugemm_kernel<XT, TY, CB_, INT4, 4>, grid, 4, (size_t)4 * CB_ * 16 * 64 * sizeof(float), a, st);
+}
+
 template <int XT, int TY>
 hipError_t launch_ugemm_t(const GemmArgs& a, int max_mtiles, hipStream_t st) {
   const bool int4 = a.resid == RS_INT4;
@@ -1015,12 +1047,12 @@ hipError_t launch_ugemm_t(const GemmArgs& a, int max_mtiles, hipStream_t st) {
   // compute unit to overlap the decode with the other's loads
   if (a.NU <= 64 || int4) {
     const dim3 grid((unsigned)max_mtiles * ((a.NU + 63) / 64));
-    if (int4) return go(ugemm_kernel<XT, TY, 2, true>, grid, 0, a, st);
-    return go(ugemm_kernel<XT, TY, 2, false>, grid, 0, a, st);
+    if (int4) return launch_ugemm_cb<XT, TY, 2, true>(a, grid, st);
+    return launch_ugemm_cb<XT, TY, 2, false>(a, grid, st);
   }
   const dim3 grid((unsigned)max_mtiles * ((a.NU + 127) / 128));
-  if (int4) return go(ugemm_kernel<XT, TY, 4, true>, grid, 0, a, st);
-  return go(ugemm_kernel<XT, TY, 4, false>, grid, 0, a, st);
+  if (int4) return launch_ugemm_cb<XT, TY, 4, true>(a, grid, st);
+  return launch_ugemm_cb<XT, TY, 4, false>(a, grid, st);
 }
 
 template <int XT, int TY>

@@ -133,6 +133,9 @@ struct CombineArgs {
 // (BM-row x 256-column tiles; many rows).
 enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2, GK_G2K = 3, GK_G1K = 4, GK_UT = 5 };
 
+// most k splits of the router score GEMM (the selection sums that many
+// partial score sets)
+constexpr int kMaxRouterSplits = 16;
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st);
 int router_splits(int T, int d, int NCp);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);

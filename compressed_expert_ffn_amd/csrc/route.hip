@@ -396,14 +396,17 @@ __global__ __launch_bounds__(256) void select_kernel(RouteArgs a, int tpb) {
   for (int e = threadIdx.x; e < nt * NC; e += 256) {
     const int tk = e / NC, c = e - tk * NC;
     const float* p = a.L + (long)(t0 + tk) * a.NCp + c;
-    float s0 = p[0], s1 = 0.f;
-    int sp = 1;
-    for (; sp + 1 < a.nsplit; sp += 2) {
-      s0 += p[sp * stride];
-      s1 += p[(sp + 1) * stride];
-    }
-    if (sp < a.nsplit) s0 += p[sp * stride];
-    sc[e] = (s0 + s1) + score_bias(a, c);
+    // every partial in flight at once (they were written by other
+    // workgroups, often on other XCDs: one latency, not nsplit of them),
+    // then summed pairwise
+    float q[kMaxRouterSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxRouterSplits; ++sp) q[sp] = sp < a.nsplit ? p[sp * stride] : 0.f;
+#pragma unroll
+    for (int st = 1; st < kMaxRouterSplits; st <<= 1)
+#pragma unroll
+      for (int sp = 0; sp + st < kMaxRouterSplits; sp += 2 * st) q[sp] += q[sp + st];
+    sc[e] = q[0] + score_bias(a, c);
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -657,7 +660,7 @@ int router_splits(int T, int d, int NCp) {
   if (NCp <= 128) return 1;  // scores and selection fused
   const long blocks = (long)((T + 31) / 32) * (NCp / 32);
   int s = 1;
-  while (blocks * s < 256 && d % (4 * 16 * 2 * s) == 0 && d / (4 * 2 * s) >= 64) s *= 2;
+  while (s < kMaxRouterSplits && blocks * s < 256 && d % (4 * 16 * 2 * s) == 0 && d / (4 * 2 * s) >= 64) s *= 2;
   return s;
 }
 
