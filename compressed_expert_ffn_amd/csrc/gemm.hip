@@ -1044,8 +1044,9 @@ template <int XT, int TY>
 hipError_t launch_ugemm_t(const GemmArgs& a, int max_mtiles, hipStream_t st) {
   const bool int4 = a.resid == RS_INT4;
   // INT4 factors are decoded per use: narrower tiles keep two workgroups per
-  // compute unit to overlap the decode with the other's loads
-  if (a.NU <= 64 || int4) {
+  // compute unit to overlap the decode with the other's loads; narrower
+  // tiles also when the wider ones would leave most compute units idle
+  if (a.NU <= 64 || int4 || (long)max_mtiles * ((a.NU + 63) / 64) < 256) {
     const dim3 grid((unsigned)max_mtiles * ((a.NU + 63) / 64));
     if (int4) return launch_ugemm_cb<XT, TY, 2, true>(a, grid, st);
     return launch_ugemm_cb<XT, TY, 2, false>(a, grid, st);
