@@ -831,7 +831,10 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     // once there are a chip's worth of them (each row of X read once per 256
     // columns of U); otherwise 32-row tiles with d split over the wavefronts
     const int nut = (h->NU + 255) / 256;
-    const int ubm = (long)max_mtiles(T, kg, c.G, 128) * nut >= 256 ? 128 : 64;
+    // 128 rows halve the INT4 decode per row and measured faster than 64
+    // rows even with half the compute units busy
+    int ubm = (long)max_mtiles(T, kg, c.G, 128) * nut >= 128 ? 128 : 64;
+    if (h->bm_env[GK_U] >= 64) ubm = h->bm_env[GK_U];
     const bool ut = h->ut_env == 1 || (h->ut_env != 0 && (long)max_mtiles(T, kg, c.G, 64) * nut >= 256);
     pf.begin(2);
     if (ut)
