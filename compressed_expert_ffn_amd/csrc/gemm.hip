@@ -838,16 +838,17 @@ __global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
   if (sl >= 0) {
     const float* p = a.Vp + ((long)row * a.ke + sl) * RPAD + rho;
     const long step = a.vp_rows * a.ke * RPAD;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    int nt = 0;
-    for (; nt + 4 <= a.ntiles; nt += 4) {
-      s0 += p[(nt + 0) * step];
-      s1 += p[(nt + 1) * step];
-      s2 += p[(nt + 2) * step];
-      s3 += p[(nt + 3) * step];
+    // eight partials in flight per round (the loads are independent), the
+    // eight running sums added pairwise at the end
+    float q[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < a.ntiles; nt += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = nt + u < a.ntiles ? p[(long)(nt + u) * step] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) q[u] += v[u];
     }
-    for (; nt < a.ntiles; ++nt) s0 += p[nt * step];
-    sum = (s0 + s1) + (s2 + s3);
+    sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
   }
   V[e] = from_f32<TY>(sum);
 }
