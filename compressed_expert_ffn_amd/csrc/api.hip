@@ -480,11 +480,13 @@ void pick_g2(const moe_handle* h, int rows, int ntiles, int& bm, int& splits) {
       // 128-row tiles of 16-bit types run two workgroups per compute unit
       // (measured 5-15% faster than 256-row tiles on the large layers)
       const bool two = b <= 64 || (b == 128 && h->mma != MOE_F32);
-      const int occ = two ? 2 : 1;
-      const long rounds = (mt * ntiles * s + 256L * occ - 1) / (256L * occ);
+      const long tiles = mt * ntiles * s;
       const double eff = b >= 256 ? 1.0 : b == 128 ? (two ? 1.05 : 0.88) : b == 64 ? 0.75 : 0.5;
-      const double wg = 2.0 * b * 256 * ((double)c.f / s) / (unit_rate * eff);
-      double t = rounds * occ * wg;
+      const double wg = 2.0 * b * 256 * ((double)c.f / s) / (unit_rate * eff);  // one workgroup alone
+      // the busiest compute unit's share of workgroups: two resident ones
+      // share its MFMA pipe, so residency hides latency (in eff) but does
+      // not add throughput
+      double t = (double)((tiles + 255) / 256) * wg;
       if (s > 1 || c.top_groups > 1) t += ((double)s * rows * c.d * 4 + (double)rows / c.top_groups * c.d * 2) / 5e12;
       if (t < best) {
         best = t;
