@@ -105,9 +105,9 @@ def resid_bytes_per_factor(w: Workload, n_in: int) -> float:
 
 
 # The five layers.  Shapes, dtypes and routing fan-out follow the workload
-# list this library is measured on; config 2 is the uncompressed flat top-2
-# of 8 (Llama-3 FFN shape d=4096, d_ff=14336 from the MoE routing survey page,
-# section 1.2), the degenerate case G=E, K=1, r=0.
+# list this library is measured on; layer 2 is the uncompressed flat top-2
+# of 8 (the Llama-3 FFN shape d=4096, d_ff=14336 the MoE routing and
+# engineering page gives in section 1.2), the degenerate case G=E, K=1, r=0.
 WORKLOADS = [
     Workload("tiny_fp32_gelu", 0, T=64, d=64, f=128, G=2, K=4, top_groups=1,
              top_experts=2, r=4, act=ACT_GELU_TANH, x_dtype=F32,
