@@ -69,6 +69,17 @@ struct ScatterArgs {
   int do_experts; // 0: build the group lists only
 };
 
+// Rows of each group list reordered by the expert set of the row (forward
+// pass only; the internal row map, not the routing outputs): one
+// workgroup per group, counting sort on the set folded to 8 bits.
+struct GroupSortArgs {
+  const int* garow_in;   // [T*kg] group-list position -> t*kg + group rank
+  int* garow_out;        // [T*kg] the same rows, sorted inside each group
+  const int* goffsets;   // [G+1]
+  const int* idx;        // [T*k]
+  int G, K, kg, ke, k;
+};
+
 // Common to the three grouped GEMMs.  Rows are group-list positions
 // (goffsets[g] <= row < goffsets[g+1]); a tile is (group, BM rows) x (256 cols).
 struct GemmArgs {
@@ -138,6 +149,8 @@ enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2, GK_G2K = 3, GK_G1K = 4, GK_UT = 
 constexpr int kMaxRouterSplits = 16;
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st);
 int router_splits(int T, int d, int NCp);
+// max_rows: an upper bound on any group's row count (sizes the key cache)
+hipError_t launch_group_sort(const GroupSortArgs& a, int max_rows, hipStream_t st);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
 size_t scatter_lds_bytes(int E, int G);
 hipError_t launch_zero(int* p, int n, hipStream_t st);

@@ -664,6 +664,81 @@ int router_splits(int T, int d, int NCp) {
   return s;
 }
 
+// Counting sort of group g's rows by the 8-bit fold of their expert set
+// (the same fold the input projection's tile sort uses).  Rows of equal key
+// keep no particular order: each token's results depend only on its own
+// row, so the order changes no value, and a 32-row block of the sorted list
+// then sees few distinct experts.  Keys are computed once, eight rows per
+// thread at a time (their loads in flight together), and kept in LDS when
+// the group fits (kcap bytes), else recomputed.
+__device__ __forceinline__ int group_row_key(const GroupSortArgs& a, int g, int aid) {
+  const int t = aid / a.kg, ga = aid - t * a.kg;
+  const int* ip = a.idx + t * a.k + ga * a.ke;
+  uint64_t set = 0;
+#pragma unroll
+  for (int s = 0; s < MAX_SLOTS; ++s)
+    if (s < a.ke) set |= 1ull << (ip[s] - g * a.K);
+  uint32_t f = static_cast<uint32_t>(set) ^ static_cast<uint32_t>(set >> 32);
+  f ^= f >> 16;
+  f ^= f >> 8;
+  return static_cast<int>(f & 255u);
+}
+
+__global__ __launch_bounds__(256) void group_sort_kernel(GroupSortArgs a, int kcap) {
+  extern __shared__ uint8_t skey[];  // [kcap]
+  __shared__ int hist[256];
+  __shared__ int cur[256];
+  __shared__ int wsum[4];
+  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = a.goffsets[g], n = a.goffsets[g + 1] - r0;
+  const bool keep = n <= kcap;
+  hist[tid] = 0;
+  __syncthreads();
+  constexpr int B = 8;
+  for (int i0 = 0; i0 < n; i0 += 256 * B) {
+    int aid[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int i = i0 + b * 256 + tid;
+      aid[b] = i < n ? a.garow_in[r0 + i] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (aid[b] < 0) continue;
+      const int key = group_row_key(a, g, aid[b]);
+      atomicAdd(&hist[key], 1);
+      if (keep) skey[i0 + b * 256 + tid] = static_cast<uint8_t>(key);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the 256 bins
+  const int cnt = hist[tid];
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  cur[tid] = base + inc - cnt;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) {
+    const int aid = a.garow_in[r0 + i];
+    const int key = keep ? static_cast<int>(skey[i]) : group_row_key(a, g, aid);
+    a.garow_out[r0 + atomicAdd(&cur[key], 1)] = aid;
+  }
+}
+
+hipError_t launch_group_sort(const GroupSortArgs& a, int max_rows, hipStream_t st) {
+  if (a.G <= 0) return hipSuccess;
+  const int kcap = max_rows < 32768 ? max_rows : 32768;
+  hipLaunchKernelGGL(group_sort_kernel, dim3(a.G), dim3(256), (size_t)kcap, st, a, kcap);
+  return hipGetLastError();
+}
+
 size_t scatter_lds_bytes(int E, int G) {
   int nb = E > G ? E : G;
   return sizeof(int) * (7 * (size_t)nb + 257 + 8);

@@ -236,8 +236,8 @@ def test_routing_ties_go_to_the_lower_index(wi):
 
 
 TILE_VARIANTS = [
-    {"CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1", "CEFN_G2K": "0", "CEFN_UT": "1"},
-    {"CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4", "CEFN_G2K": "0", "CEFN_UT": "0"},
+    {"CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1", "CEFN_G2K": "0", "CEFN_UT": "1", "CEFN_GSORT": "1"},
+    {"CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4", "CEFN_G2K": "0", "CEFN_UT": "0", "CEFN_GSORT": "0"},
     {"CEFN_BM_G1": "32", "CEFN_BM_G2": "128", "CEFN_KS_G2": "2", "CEFN_G2K": "1", "CEFN_G1K": "1"},
     {"CEFN_BM_G1": "64", "CEFN_BM_G2": "64", "CEFN_KS_G2": "3", "CEFN_G2K": "1", "CEFN_G1K": "0"},
 ]
