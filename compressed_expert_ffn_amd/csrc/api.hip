@@ -70,6 +70,7 @@ struct moe_handle {
   int *idx = nullptr, *gidx = nullptr, *counts = nullptr, *offsets = nullptr, *perm = nullptr;
   int *gcounts = nullptr, *goffsets = nullptr, *gperm = nullptr, *garow = nullptr, *cc = nullptr;
   int* garow_sorted = nullptr;  // garow with each group's rows sorted by expert set
+  uint16_t* X16 = nullptr;      // fp16 copy of bf16 activations (fp16 MFMAs)
   float* w = nullptr;
   int cc_n = 0;
   // where the last routing pass left the lists the GEMMs read
@@ -717,6 +718,7 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
     TRY(dalloc(h.get(), &h->gcounts, c.G));
     TRY(dalloc(h.get(), &h->goffsets, c.G + 1));
     TRY(dalloc(h.get(), &h->garow, T * kg + 1));
+    if (c.x_dtype == MOE_BF16 && h->mma == MOE_F16) TRY(dalloc(h.get(), &h->X16, T * (long)c.d + 8));
     if (c.r > 0 && c.K > 1 && c.top_experts < c.K) TRY(dalloc(h.get(), &h->garow_sorted, T * kg + 1));
     TRY(dalloc(h.get(), &h->cc, (size_t)h->cc_n + 1));
     {
@@ -841,8 +843,19 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   int splits = 1;
   bool g1k = false;  // gemm1 ran with the k-split tiles
   hipError_t e;
+  // bf16 activations with fp16 MFMAs: the row GEMMs read an fp16 copy made
+  // in one pass, instead of converting every staged row in their loaders
+  const void* xg = X;
+  int xt = c.x_dtype;
+  if (h->X16) {
+    e = launch_cvt_x(X, h->X16, (long)T * c.d, st);
+    if (e != hipSuccess) return hip_fail(h, e, "activation conversion launch");
+    xg = h->X16;
+    xt = MOE_F16;
+  }
   if (c.r > 0) {
     GemmArgs u = ga;
+    u.X = xg;
     u.Bw = h->At;
     u.bw_gstride = h->at_gs;
     u.bw_scale = h->At_s;
@@ -858,15 +871,16 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     const bool ut = h->ut_env == 1 || (h->ut_env != 0 && (long)max_mtiles(T, kg, c.G, 64) * nut >= 256);
     pf.begin(2);
     if (ut)
-      e = launch_gemm(GK_UT, c.x_dtype, h->mma, h->mma == MOE_F32 ? 64 : ubm, u,
+      e = launch_gemm(GK_UT, xt, h->mma, h->mma == MOE_F32 ? 64 : ubm, u,
                       max_mtiles(T, kg, c.G, h->mma == MOE_F32 ? 64 : ubm), nut, 1, st);
     else
-      e = launch_gemm(GK_U, c.x_dtype, h->mma, 32, u, max_mtiles(T, kg, c.G, 32), 1, 1, st);
+      e = launch_gemm(GK_U, xt, h->mma, 32, u, max_mtiles(T, kg, c.G, 32), 1, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "ugemm launch");
     pf.end(2);
   }
   {
     GemmArgs g1 = ga;
+    g1.X = xg;
     g1.Bw = h->W1;
     g1.bw_gstride = h->w1_gs;
     g1.B1 = h->B1;
@@ -884,9 +898,9 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
                                         (long)max_mtiles(T, kg, c.G, 32) * nt < 128));
     pf.begin(3);
     if (g1k)
-      e = launch_gemm(GK_G1K, c.x_dtype, h->mma, 32, g1, max_mtiles(T, kg, c.G, 32), h->P_in * c.f / 64, 1, st);
+      e = launch_gemm(GK_G1K, xt, h->mma, 32, g1, max_mtiles(T, kg, c.G, 32), h->P_in * c.f / 64, 1, st);
     else
-      e = launch_gemm(GK_G1, c.x_dtype, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, 1, st);
+      e = launch_gemm(GK_G1, xt, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "gemm1 launch");
     pf.end(3);
   }

@@ -853,6 +853,27 @@ __global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
   V[e] = from_f32<TY>(sum);
 }
 
+// ------------------------------------------------ bf16 -> fp16 activations --
+// For bf16 activations with fp16 MFMAs, one pass converting X to fp16 (exact
+// for the activations' range, the same conversion the tile loaders would
+// otherwise do per stage on the path between the loads and the LDS
+// commit), eight elements per thread.
+__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const u4v* in, u4v* out, long n8) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const u4v v = in[i];
+  u4v o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = bf16_bits_to_f32(static_cast<uint16_t>(v[q] & 0xFFFFu));
+    const float hi = bf16_bits_to_f32(static_cast<uint16_t>(v[q] >> 16));
+    const uint32_t l16 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(lo));
+    const uint32_t h16 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hi));
+    o[q] = l16 | (h16 << 16);
+  }
+  out[i] = o;
+}
+
 // ---------------------------------------------------------------- combine --
 // Y[t] = sum over k splits s and chosen groups ga of ypart[s][t*kg + ga].
 template <int XT>
@@ -1091,6 +1112,14 @@ hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmA
   if (x_dtype == DT_BF16 && mma_dtype == DT_BF16) return launch_types<DT_BF16, DT_BF16>(kind, bm, a, grid, st);
   if (x_dtype == DT_BF16 && mma_dtype == DT_F16) return launch_types<DT_BF16, DT_F16>(kind, bm, a, grid, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_cvt_x(const void* X, void* X16, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long n8 = n / 8;  // n = T * d, d a multiple of 64
+  hipLaunchKernelGGL(cvt_bf16_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const u4v*>(X), static_cast<u4v*>(X16), n8);
+  return hipGetLastError();
 }
 
 hipError_t launch_vreduce(int mma_dtype, const VReduceArgs& a, hipStream_t st) {

@@ -150,6 +150,8 @@ constexpr int kMaxRouterSplits = 16;
 hipError_t launch_router(int x_dtype, const RouteArgs& a, hipStream_t st);
 int router_splits(int T, int d, int NCp);
 // max_rows: an upper bound on any group's row count (sizes the key cache)
+// bf16 X -> fp16 copy (n elements, a multiple of 8)
+hipError_t launch_cvt_x(const void* X, void* X16, long n, hipStream_t st);
 hipError_t launch_group_sort(const GroupSortArgs& a, int max_rows, hipStream_t st);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t st);
 size_t scatter_lds_bytes(int E, int G);
