@@ -5,13 +5,16 @@
 // MoE routing page "混合专家模型的路由机制与工程落地", section 3.1), in two
 // kernels:
 //   logits  every router score of every token, s = x . [W_grp | W_exp^0 ..
-//           W_exp^{G-1}], as one fp32 MFMA GEMM (32 x 32 x 2 steps; the
-//           products and sums are fp32), k split over the 4 wavefronts of
-//           a workgroup and, for small batches, over workgroups;
-//   select  one thread per token: the top groups of s_grp + c, then the top
-//           experts of each chosen group's scores + b, larger score first,
-//           ties to the lower index, NaN ranked last; gate weights are the
-//           product of the two softmaxes over the chosen scores.
+//           W_exp^{G-1}], as one MFMA GEMM with FP32 accuracy (fp32 MFMAs
+//           for fp32 activations, split-bf16 MFMAs with FP32 accumulation
+//           for 16-bit ones), k split over the wavefronts of a workgroup
+//           and, for small batches, over workgroups;
+//   select  the top groups of s_grp + c, then the top experts of each
+//           chosen group's scores + b, larger score first, ties to the
+//           lower index, NaN ranked last; gate weights are the product of
+//           the two softmaxes over the chosen scores.  A wavefront per
+//           token (butterfly top-k over the lanes) in the select kernel, a
+//           thread per token where scores and selection share one kernel.
 // Scoring the experts of every group (not only the chosen ones) costs
 // G*K extra columns of a small fp32 GEMM and removes a dependent second
 // pass over the weights.
@@ -220,8 +223,9 @@ __global__ __launch_bounds__(256) void logits_kernel(RouteArgs a) {
 }
 
 // ------------------------------------------------------------- select --
-// One thread per token walks its scores (biases included): the group
-// scores, then the chosen groups' expert scores, keeping the best n
+// Thread-per-token form (used by the fused kernel): one thread walks its
+// scores (biases included): the group scores, then the chosen groups'
+// expert scores, keeping the best n
 // (larger score first, ties to the lower index, NaN ranked last).  With
 // count_experts off the per-chunk expert counters are left alone (only the
 // group lists are built).
