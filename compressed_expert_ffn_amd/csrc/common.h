@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace cefn {
 
 enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
@@ -24,6 +26,16 @@ typedef float f8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile
+// time (register arrays indexed by i stay in registers).
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 // ---------------------------------------------------------------- scalars --
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -149,25 +161,67 @@ __device__ __forceinline__ float int4_value(uint32_t word, int e, float scale) {
   return static_cast<float>(nib - 8) * scale;
 }
 
-// Decode 8 INT4 codes that share one scale.
-template <int TY>
-__device__ __forceinline__ typename Frag<TY>::T int4_frag_1scale(uint32_t word, float scale) {
-  float v[8];
+// fp16 fragments decode with packed fp16 arithmetic: byte permutes put
+// codes 2i and 2i+1 in the two halves of dword i (fragment order); a code c
+// (= q + 8) placed in the low mantissa bits of the fp16 1024.0 is the fp16
+// number 1024 + c, subtracting 1032 leaves q exactly, and one fp16 multiply
+// by the scale pair rounds the exact product q * scale once -- the same
+// value as the (exact) fp32 product converted to fp16.
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h8 int4_frag_f16_pairs(uint32_t word, u4v sc) {
+  const uint32_t odd = word >> 4;
+  u4v d;
+  // bytes of {word, odd}: word byte b holds codes 2b, 2b+1; odd byte b holds
+  // code 2b+1 in its low nibble; selector 0x0c gives a zero byte
+  d[0] = __builtin_amdgcn_perm(word, odd, 0x0c000c04u);
+  d[1] = __builtin_amdgcn_perm(word, odd, 0x0c010c05u);
+  d[2] = __builtin_amdgcn_perm(word, odd, 0x0c020c06u);
+  d[3] = __builtin_amdgcn_perm(word, odd, 0x0c030c07u);
+  const h2v off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+  u4v r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = int4_value(word, e, scale);
-  return to_frag<TY>(v);
+  for (int i = 0; i < 4; ++i) {
+    // (vector elements go through plain scalars: a bit cast applied
+    // directly to an element of a vector read element 0 in this compiler)
+    const uint32_t code = (d[i] & 0x000F000Fu) | 0x64006400u;
+    const uint32_t scale = sc[i];
+    const h2v q = __builtin_bit_cast(h2v, code) - off;
+    const h2v p = q * __builtin_bit_cast(h2v, scale);
+    r[i] = __builtin_bit_cast(uint32_t, p);
+  }
+  return __builtin_bit_cast(h8, r);
+}
+
+// Decode 8 INT4 codes that share one scale (fp16 bits).
+template <int TY>
+__device__ __forceinline__ typename Frag<TY>::T int4_frag_1scale(uint32_t word, uint16_t scale_bits) {
+  if constexpr (TY == DT_F16) {
+    const uint32_t p = static_cast<uint32_t>(scale_bits) * 0x00010001u;
+    const u4v sc = {p, p, p, p};
+    return int4_frag_f16_pairs(word, sc);
+  } else {
+    const float scale = f16_bits_to_f32(scale_bits);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = int4_value(word, e, scale);
+    return to_frag<TY>(v);
+  }
 }
 // Decode 8 INT4 codes with one scale each (8 consecutive fp16 scales held
 // in a 16-byte vector).
 template <int TY>
 __device__ __forceinline__ typename Frag<TY>::T int4_frag_8scale(uint32_t word, u4v s) {
-  float v[8];
+  if constexpr (TY == DT_F16) {
+    return int4_frag_f16_pairs(word, s);
+  } else {
+    float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint16_t bits = static_cast<uint16_t>((s[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    v[e] = int4_value(word, e, f16_bits_to_f32(bits));
+    for (int e = 0; e < 8; ++e) {
+      uint16_t bits = static_cast<uint16_t>((s[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      v[e] = int4_value(word, e, f16_bits_to_f32(bits));
+    }
+    return to_frag<TY>(v);
   }
-  return to_frag<TY>(v);
 }
 
 // ----------------------------------------------------------- fast math ---

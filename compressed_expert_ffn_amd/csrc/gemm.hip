@@ -478,7 +478,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   }
 
   // issue the loads of step (t, j)
-  auto load_ops = [&](int t, int j, EOps<TY, PIN, NFB>& o) {
+  auto load_ops = [&](int t, int j, EOps<TY, PIN, NFB>& o) __attribute__((always_inline)) {
     const int m = t * 32 + (lane & 31);
     const int ex = g * K + j;
     o.wgt = s_w[m * K + j];
@@ -515,11 +515,95 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     }
   };
 
+  // One expert step of token block t: takes the next expert from (lo, hi),
+  // prefetches the step after it into nxt (the next expert of this block,
+  // else the first of the next block, else this one again, harmlessly) and
+  // computes with cur.  With INT4 operands the caller alternates the two
+  // operand sets, so no operand registers are copied between steps.
+  auto step = [&](auto tc_, uint32_t& lo, uint32_t& hi, const EOps<TY, PIN, NFB>& cur,
+                  EOps<TY, PIN, NFB>& nxt, float (&hbar)[NFB][16], bool& have) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc_)::value;
+    const int j = first_j(lo, hi);
+    if (lo) lo &= lo - 1; else hi &= hi - 1;
+    {
+      int tn = t, jn = j;
+      if (lo | hi) {
+        jn = first_j(lo, hi);
+      } else if (t + 1 < RT) {
+        const int t1 = (t + 1 < RT) ? t + 1 : t;
+        if (mlo[t1] | mhi[t1]) {
+          tn = t1;
+          jn = first_j(mlo[t1], mhi[t1]);
+          have = true;
+        }
+      }
+      load_ops(tn, jn, nxt);
+    }
+    f16v z[CB];
+    if constexpr (RES != ER_NONE) {
+      // z_j = Z + u_j B_j^T: one 16-deep MFMA step per feature block
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        F bfr;
+        if constexpr (RES == ER_INT4) bfr = int4_frag_8scale<TY>(cur.b[c].w, cur.b[c].x);
+        else bfr = cur.b[c].f;
+        z[c] = mfma32<TY>(bfr, cur.u[(ACT == ACT_SWIGLU) ? c : 0], acc[t][c]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CB; ++c) z[c] = acc[t][c];
+    }
+    const float wgt = cur.wgt;
+    float hw[NFB][16];
+    if constexpr (ACT == ACT_SWIGLU) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        hw[0][v] = wgt * (silu_f(z[0][v]) * z[1][v]);
+        hbar[0][v] += hw[0][v];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          hw[c][v] = wgt * gelu_tanh_f(z[c][v]);
+          hbar[c][v] += hw[c][v];
+        }
+    }
+    if constexpr (RES != ER_NONE) {
+      // V^T[rho, token] = sum over this wavefront's features of
+      // A_down[f, rho] (w h)[token, f]: the accumulator rows a lane holds
+      // are the k of the MFMA, in the order the A_down operand was packed
+      f16v vacc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) vacc[v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NFB; ++c)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          F afr;
+          if constexpr (RES == ER_INT4) {
+            const uint16_t sb = static_cast<uint16_t>(cur.ad[c][st].x[0] & 0xFFFFu);
+            afr = int4_frag_1scale<TY>(cur.ad[c][st].w, (lane & 31) < RPAD ? sb : uint16_t{0});
+          } else {
+            afr = cur.ad[c][st].f;
+          }
+          const F hfr = to_frag<TY>(&hw[c][8 * st]);  // hw is a plain float array
+          vacc = mfma32<TY>(afr, hfr, vacc);
+        }
+      if (cur.slot >= 0) {
+        float* dst = s_vw + (lane & 31) * VS + cur.slot * RPAD;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) dst[acc_feat(v, lane)] += vacc[v];
+      }
+    }
+  };
+
   EOps<TY, PIN, NFB> cur, nxt;
   bool have = false;  // cur already holds the first step of block t
   // (unrolled so the accumulators are indexed statically)
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
+  static_for<RT>([&](auto tc_) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc_)::value;
     const int m = t * 32 + (lane & 31);  // this lane's token row in the tile
     float hbar[NFB][16];
 #pragma unroll
@@ -530,83 +614,17 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     if ((lo | hi) && !have) load_ops(t, first_j(lo, hi), cur);
     have = false;
     while (lo | hi) {
-      const int j = first_j(lo, hi);
-      if (lo) lo &= lo - 1; else hi &= hi - 1;
-      // prefetch the next step: the next expert of this block, else the
-      // first of the next block (else reload this one, harmlessly)
-      {
-        int tn = t, jn = j;
-        if (lo | hi) {
-          jn = first_j(lo, hi);
-        } else if (t + 1 < RT) {
-          const int t1 = (t + 1 < RT) ? t + 1 : t;
-          if (mlo[t1] | mhi[t1]) {
-            tn = t1;
-            jn = first_j(mlo[t1], mhi[t1]);
-            have = true;
-          }
-        }
-        load_ops(tn, jn, nxt);
-      }
-      f16v z[CB];
-      if constexpr (RES != ER_NONE) {
-        // z_j = Z + u_j B_j^T: one 16-deep MFMA step per feature block
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-          F bfr;
-          if constexpr (RES == ER_INT4) bfr = int4_frag_8scale<TY>(cur.b[c].w, cur.b[c].x);
-          else bfr = cur.b[c].f;
-          z[c] = mfma32<TY>(bfr, cur.u[(ACT == ACT_SWIGLU) ? c : 0], acc[t][c]);
-        }
+      step(tc_, lo, hi, cur, nxt, hbar, have);
+      if constexpr (RES != ER_INT4) {
+        // (plain operands: the alternating form costs spills here)
+        cur = nxt;
       } else {
-#pragma unroll
-        for (int c = 0; c < CB; ++c) z[c] = acc[t][c];
-      }
-      const float wgt = cur.wgt;
-      float hw[NFB][16];
-      if constexpr (ACT == ACT_SWIGLU) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          hw[0][v] = wgt * (silu_f(z[0][v]) * z[1][v]);
-          hbar[0][v] += hw[0][v];
+        if (!(lo | hi)) {
+          cur = nxt;  // once per block, when it took an odd number of steps
+          break;
         }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            hw[c][v] = wgt * gelu_tanh_f(z[c][v]);
-            hbar[c][v] += hw[c][v];
-          }
+        step(tc_, lo, hi, nxt, cur, hbar, have);
       }
-      if constexpr (RES != ER_NONE) {
-        // V^T[rho, token] = sum over this wavefront's features of
-        // A_down[f, rho] (w h)[token, f]: the accumulator rows a lane holds
-        // are the k of the MFMA, in the order the A_down operand was packed
-        f16v vacc;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) vacc[v] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NFB; ++c)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            F afr;
-            if constexpr (RES == ER_INT4) {
-              const uint16_t sb = static_cast<uint16_t>(cur.ad[c][st].x[0] & 0xFFFFu);
-              afr = int4_frag_1scale<TY>(cur.ad[c][st].w, (lane & 31) < RPAD ? f16_bits_to_f32(sb) : 0.f);
-            } else {
-              afr = cur.ad[c][st].f;
-            }
-            const F hfr = to_frag<TY>(&hw[c][8 * st]);  // hw is a plain float array
-            vacc = mfma32<TY>(afr, hfr, vacc);
-          }
-        if (cur.slot >= 0) {
-          float* dst = s_vw + (lane & 31) * VS + cur.slot * RPAD;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) dst[acc_feat(v, lane)] += vacc[v];
-        }
-      }
-      cur = nxt;
     }
     if constexpr (KS) {
       // h sums of the four wavefronts' expert steps meet in LDS
@@ -649,7 +667,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
       }
       __syncthreads();
     }
-  }
+  });
 }
 
 // ---------------------------------------------- G2: down projection ------
@@ -897,6 +915,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // kernels use: kind 0 At (columns aux0 + rho, k = row permuted, KS = aux1),
 // kind 1 B1 (column = row, k = rho, plain 16-deep step), kind 2 Ad,
 // kind 3 Bd (column = row, k = aux0 * 16 + rho permuted, KS = aux1).
+// INT4 entries are also decoded the way the GEMMs decode their operands
+// (the whole 8-code fragment, in the MFMA type); an entry whose operand value
+// is not its exact value rounded once to that type comes back as NaN.
 __device__ __forceinline__ void perm_pos(int k, int& ks, int& h, int& e) {
   ks = (k >> 6) * 4 + ((k & 31) >> 3);
   h = (k & 63) >> 5;
@@ -913,33 +934,51 @@ __global__ void debug_decode_kernel(int resid, int kind, const void* src, const 
   float val = 0.f;
   long fo = 0;  // fragment (word) index
   int e = 0;
-  float sc = 0.f;
+  long si = 0;  // scale of this entry
   if (kind == 0) {
     const int ncol = aux0 + rho, k = row;
     int ks, h;
     perm_pos(k, ks, h, e);
     fo = (long)((ncol / 32) * aux1 + ks) * 64 + (ncol % 32) + 32 * h;
-    if (q4) sc = f16_bits_to_f32(scales[sbase + ((long)(ncol / 32) * (aux1 / 2) + k / 32) * 32 + (ncol % 32)]);
+    si = sbase + ((long)(ncol / 32) * (aux1 / 2) + k / 32) * 32 + (ncol % 32);
   } else if (kind == 1) {
     const int ncol = row, h = rho / 8;
     e = rho % 8;
     fo = (long)(ncol / 32) * 64 + (ncol % 32) + 32 * h;
-    if (q4) sc = f16_bits_to_f32(scales[sbase + (long)(ncol / 32) * RPAD + rho]);
+    si = sbase + (long)(ncol / 32) * RPAD + rho;
   } else if (kind == 2) {
     const int fb = row / 32, w = row % 32, st = w / 16, rem = w % 16;
     const int h = (rem >> 2) & 1;
     e = (rem & 3) + 4 * (rem >> 3);
     fo = ((long)fb * 2 + st) * 64 + rho + 32 * h;
-    if (q4) sc = f16_bits_to_f32(scales[sbase + (long)fb * RPAD + rho]);
+    si = sbase + (long)fb * RPAD + rho;
   } else {
     const int ncol = row, k = aux0 * RPAD + rho;
     int ks, h;
     perm_pos(k, ks, h, e);
     fo = (long)((ncol / 32) * aux1 + ks) * 64 + (ncol % 32) + 32 * h;
-    if (q4) sc = f16_bits_to_f32(scales[sbase + (long)(ncol / 32) * RPAD + rho]);
+    si = sbase + (long)(ncol / 32) * RPAD + rho;
   }
   if (q4) {
-    val = int4_value(static_cast<const uint32_t*>(src)[base + fo], e, sc);
+    const uint32_t word = static_cast<const uint32_t*>(src)[base + fo];
+    val = int4_value(word, e, f16_bits_to_f32(scales[si]));
+    if constexpr (TY != DT_F32) {
+      // B1 and Bd fragments carry 8 scales (entries e' of the fragment at
+      // scale index si - e + e'), At and Ad one
+      FragT<TY> fr;
+      if (kind == 1 || kind == 3) {
+        u4v s8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          s8[q] = static_cast<uint32_t>(scales[si - e + 2 * q]) | (static_cast<uint32_t>(scales[si - e + 2 * q + 1]) << 16);
+        fr = int4_frag_8scale<TY>(word, s8);
+      } else {
+        fr = int4_frag_1scale<TY>(word, scales[si]);
+      }
+      const u4v fb = __builtin_bit_cast(u4v, fr);
+      const uint32_t got = (fb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      if (got != from_f32<TY>(val)) val = __builtin_nanf("");
+    }
   } else {
     val = load_as_f32<TY>(static_cast<const TE<TY>*>(src), (base + fo) * 8 + e);
   }

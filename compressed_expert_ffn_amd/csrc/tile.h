@@ -214,7 +214,7 @@ struct WInt4ColK {
     return r;
   }
   __device__ FragT<TY> decode(const Raw& r, int, int, int) const {
-    return int4_frag_1scale<TY>(r.w, f16_bits_to_f32(r.s));
+    return int4_frag_1scale<TY>(r.w, r.s);
   }
 };
 
