@@ -224,6 +224,18 @@ __device__ __forceinline__ typename Frag<TY>::T int4_frag_8scale(uint32_t word, 
   }
 }
 
+// Position of the 8-bit word g in the binary reflected Gray code sequence
+// (prefix XOR from the top bit down).  Among words with the same number of
+// set bits, consecutive ones in that order differ by moving one bit, so
+// rows sorted by the rank of their expert set see, within a block of
+// neighbours, sets that differ by one expert.
+__device__ __forceinline__ uint32_t gray_rank8(uint32_t g) {
+  g ^= g >> 1;
+  g ^= g >> 2;
+  g ^= g >> 4;
+  return g & 255u;
+}
+
 // ----------------------------------------------------------- fast math ---
 // SiLU z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp
 // each) instead of an IEEE division sequence.

@@ -336,8 +336,9 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   __syncthreads();
   // Row order inside the tile.  With residuals, the epilogue takes one step
   // per expert picked by any token of a 32-token block, so the rows are
-  // counting-sorted by their expert set (folded to 8 bits; rows past the
-  // group's end last): blocks then see few distinct experts.  Each token's
+  // counting-sorted by the Gray-code rank of their expert set (folded to 8
+  // bits; rows past the group's end last): blocks then see few distinct
+  // experts.  Each token's
   // result depends only on its own column, so the order (including the
   // arbitrary order inside one key) changes no value.
   const bool mine = tid < BMT && m0 + tid < M;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
       uint32_t f = static_cast<uint32_t>(set) ^ static_cast<uint32_t>(set >> 32);
       f ^= f >> 16;
       f ^= f >> 8;
-      key = static_cast<int>(f & 255u) % 255;
+      key = static_cast<int>(gray_rank8(f & 255u)) % 255;
     }
     int rk = 0;
     if (tid < BMT) rk = atomicAdd(&s_hist[key], 1);
@@ -443,12 +444,21 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);  // ends with a barrier
   }
 
+  // V slices, one per wavefront.  Every (token, slot) of a valid row is
+  // written by exactly one expert step of each wavefront (the step of the
+  // token's expert in that slot), so the steps store instead of accumulate
+  // and the slices need no clearing, except an idle wavefront's (it takes
+  // no steps).  With KS the steps are dealt across the wavefronts: slices
+  // start at zero and accumulate (a lane owns its (token, slot, rho)
+  // entries, so plain read-modify-writes need no atomics).
   if constexpr (RES != ER_NONE) {
-    for (int i = tid; i < 4 * 32 * VS; i += 256) s_v[i] = 0.f;
-    __syncthreads();
+    if constexpr (KS) {
+      for (int i = tid; i < 4 * 32 * VS; i += 256) s_v[i] = 0.f;
+      __syncthreads();
+    } else if (!active) {
+      for (int i = lane; i < 32 * VS; i += 64) s_v[wave * 32 * VS + i] = 0.f;
+    }
   }
-  // this wavefront's slice: within a wavefront every (token, slot, rho)
-  // belongs to one lane, so plain read-modify-writes need no atomics
   float* s_vw = s_v + wave * 32 * VS;
   const TE<TY>* Ub = static_cast<const TE<TY>*>(a.U);
   TE<TY>* H = static_cast<TE<TY>*>(a.H);
@@ -594,7 +604,10 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
       if (cur.slot >= 0) {
         float* dst = s_vw + (lane & 31) * VS + cur.slot * RPAD;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) dst[acc_feat(v, lane)] += vacc[v];
+        for (int v = 0; v < 8; ++v) {
+          if constexpr (KS) dst[acc_feat(v, lane)] += vacc[v];
+          else dst[acc_feat(v, lane)] = vacc[v];
+        }
       }
     }
   };
@@ -654,14 +667,14 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     }
     if constexpr (RES != ER_NONE) {
       // the four slices of this token block -> one partial per (column tile,
-      // row, slot), summed over column tiles by vreduce; slices cleared
+      // row, slot), summed over column tiles by vreduce (KS: slices cleared)
       __syncthreads();
       const int per_row = ke * RPAD;
       for (int e = tid; e < 32 * per_row; e += 256) {
         const int r = e / per_row, c = e - r * per_row;
         const int o = r * VS + c;
         const float v = (s_v[o] + s_v[32 * VS + o]) + (s_v[2 * 32 * VS + o] + s_v[3 * 32 * VS + o]);
-        s_v[o] = s_v[32 * VS + o] = s_v[2 * 32 * VS + o] = s_v[3 * 32 * VS + o] = 0.f;
+        if constexpr (KS) s_v[o] = s_v[32 * VS + o] = s_v[2 * 32 * VS + o] = s_v[3 * 32 * VS + o] = 0.f;
         const int mr = t * 32 + r;
         if (m0 + mr < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + s_perm[mr]) * per_row + c] = v;
       }

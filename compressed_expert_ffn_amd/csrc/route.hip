@@ -668,8 +668,10 @@ int router_splits(int T, int d, int NCp) {
   return s;
 }
 
-// Counting sort of group g's rows by the 8-bit fold of their expert set
-// (the same fold the input projection's tile sort uses).  Rows of equal key
+// Counting sort of group g's rows by the Gray-code rank of the 8-bit fold
+// of their expert set (the same key the input projection's tile sort uses;
+// for groups of at most 8 experts the fold is the set itself, and
+// neighbouring keys are sets that differ by one expert).  Rows of equal key
 // keep no particular order: each token's results depend only on its own
 // row, so the order changes no value, and a 32-row block of the sorted list
 // then sees few distinct experts.  Keys are computed once, eight rows per
@@ -685,7 +687,7 @@ __device__ __forceinline__ int group_row_key(const GroupSortArgs& a, int g, int 
   uint32_t f = static_cast<uint32_t>(set) ^ static_cast<uint32_t>(set >> 32);
   f ^= f >> 16;
   f ^= f >> 8;
-  return static_cast<int>(f & 255u);
+  return static_cast<int>(gray_rank8(f & 255u));
 }
 
 __global__ __launch_bounds__(256) void group_sort_kernel(GroupSortArgs a, int kcap) {
