@@ -108,11 +108,6 @@ __device__ __forceinline__ void store4(TE<DT>* p, float a, float b, float c, flo
   }
 }
 
-template <int TY, int RT>
-constexpr size_t tbuf_bytes() {
-  return (size_t)2 * RT * 4 * 64 * sizeof(FragT<TY>);
-}
-
 // Main loop over the token operand TO (LDS-shared) and weight source WS
 // (direct), KT >= 1 stages (d and f are multiples of 64, a k split keeps at
 // least 8 stages, the residual tail is padded to 64); ends with a barrier.
@@ -314,12 +309,10 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   // floats before the V sums, and h sums [4][NFB][16][64] follow the
   // histogram)
   const int VS = ke * RPAD + 1;
-  const size_t vbytes = (size_t)4 * 32 * VS * sizeof(float);
-  size_t abytes = tbuf_bytes<TY, RT>() > vbytes ? tbuf_bytes<TY, RT>() : vbytes;
-  if (KS && abytes < (size_t)4 * CB * 16 * 64 * sizeof(float)) abytes = (size_t)4 * CB * 16 * 64 * sizeof(float);
-  abytes = (abytes + 15) & ~(size_t)15;
+  const G1Lds lay = g1_lds(KS, TY, BMT, K, ke);
+  static_assert(CB == 2, "the layout counts two feature blocks per wavefront");
   float* s_v = reinterpret_cast<float*>(smem);
-  float* s_w = reinterpret_cast<float*>(smem + abytes);
+  float* s_w = reinterpret_cast<float*>(smem + lay.abytes);
   int8_t* s_slot = reinterpret_cast<int8_t*>(s_w + BMT * K);
   uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_slot + ((BMT * K + 15) & ~15));
   int* s_perm = reinterpret_cast<int*>(s_bm + 2 * RT);
@@ -451,15 +444,19 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   // no steps).  With KS the steps are dealt across the wavefronts: slices
   // start at zero and accumulate (a lane owns its (token, slot, rho)
   // entries, so plain read-modify-writes need no atomics).
+  // Token block t uses V set t & 1 when there are two (lay.vdb).
   if constexpr (RES != ER_NONE) {
     if constexpr (KS) {
       for (int i = tid; i < 4 * 32 * VS; i += 256) s_v[i] = 0.f;
       __syncthreads();
     } else if (!active) {
-      for (int i = lane; i < 32 * VS; i += 64) s_v[wave * 32 * VS + i] = 0.f;
+      for (int i = lane; i < 32 * VS; i += 64) {
+        s_v[wave * 32 * VS + i] = 0.f;
+        if (lay.vdb) s_v[(4 + wave) * 32 * VS + i] = 0.f;
+      }
     }
   }
-  float* s_vw = s_v + wave * 32 * VS;
+  auto vset = [&](int t) { return s_v + (lay.vdb ? (t & 1) * 4 * 32 * VS : 0); };
   const TE<TY>* Ub = static_cast<const TE<TY>*>(a.U);
   TE<TY>* H = static_cast<TE<TY>*>(a.H);
   const int h = lane >> 5;
@@ -602,7 +599,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
           vacc = mfma32<TY>(afr, hfr, vacc);
         }
       if (cur.slot >= 0) {
-        float* dst = s_vw + (lane & 31) * VS + cur.slot * RPAD;
+        float* dst = vset(t) + (wave * 32 + (lane & 31)) * VS + cur.slot * RPAD;
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           if constexpr (KS) dst[acc_feat(v, lane)] += vacc[v];
@@ -668,17 +665,21 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     if constexpr (RES != ER_NONE) {
       // the four slices of this token block -> one partial per (column tile,
       // row, slot), summed over column tiles by vreduce (KS: slices cleared)
+      // (with two V sets no barrier follows: block t + 1 writes the other
+      // set, and block t + 2, which writes this one, starts only after
+      // every thread has passed block t + 1's barrier)
       __syncthreads();
       const int per_row = ke * RPAD;
+      float* sv = vset(t);
       for (int e = tid; e < 32 * per_row; e += 256) {
         const int r = e / per_row, c = e - r * per_row;
         const int o = r * VS + c;
-        const float v = (s_v[o] + s_v[32 * VS + o]) + (s_v[2 * 32 * VS + o] + s_v[3 * 32 * VS + o]);
-        if constexpr (KS) s_v[o] = s_v[32 * VS + o] = s_v[2 * 32 * VS + o] = s_v[3 * 32 * VS + o] = 0.f;
+        const float v = (sv[o] + sv[32 * VS + o]) + (sv[2 * 32 * VS + o] + sv[3 * 32 * VS + o]);
+        if constexpr (KS) sv[o] = sv[32 * VS + o] = sv[2 * 32 * VS + o] = sv[3 * 32 * VS + o] = 0.f;
         const int mr = t * 32 + r;
         if (m0 + mr < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + s_perm[mr]) * per_row + c] = v;
       }
-      __syncthreads();
+      if (!lay.vdb) __syncthreads();
     }
   });
 }
@@ -1081,13 +1082,7 @@ size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
   const size_t fb = ty == DT_F32 ? 32 : 16;
   const size_t tbytes = 2 * (size_t)(bm / 32) * 4 * 64 * fb;
   if (kind != GK_G1 && kind != GK_G1K) return tbytes;
-  const size_t vbytes = (size_t)4 * 32 * (ke * RPAD + 1) * sizeof(float);
-  size_t abytes = tbytes > vbytes ? tbytes : vbytes;
-  if (kind == GK_G1K && abytes < (size_t)4 * CB * 16 * 64 * sizeof(float)) abytes = (size_t)4 * CB * 16 * 64 * sizeof(float);
-  abytes = (abytes + 15) & ~(size_t)15;
-  const size_t hsum = kind == GK_G1K ? (size_t)4 * 2 * 16 * 64 * sizeof(float) : 0;  // NFB <= 2
-  return abytes + sizeof(float) * bm * K + (((size_t)bm * K + 15) & ~(size_t)15) + sizeof(uint32_t) * 2 * (bm / 32) +
-         sizeof(int) * ((size_t)bm + 260) + hsum + 64;
+  return g1_lds(kind == GK_G1K, ty, bm, K, ke).total;
 }
 
 template <class KF>

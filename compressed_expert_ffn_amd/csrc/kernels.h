@@ -164,6 +164,39 @@ hipError_t launch_gemm(int kind, int x_dtype, int mma_dtype, int bm, const GemmA
                        int ntiles, int splits, hipStream_t st);
 // LDS bytes of one tile (K experts per group, ke chosen per group)
 size_t gemm_lds(int kind, int mma_dtype, int bm, int K, int ke);
+
+// LDS layout of an input-projection workgroup of bm rows (the kernel and
+// gemm_lds both use it).  Region A holds the token stages during the main
+// loop, then the V slices (one per wavefront: 32 rows x (ke*RPAD + 1)
+// floats), two sets of them when the whole layout still fits two
+// workgroups per compute unit (80 KB; 160 KB at 256 rows), so consecutive
+// token blocks alternate sets and need one barrier each; the k-split form
+// (ks) keeps one set and also puts its four partial tiles there.  Then
+// gate weights [bm][K] floats, slots [bm][K] int8, the token blocks' expert
+// bit sets, the row order and key histogram [bm + 260] ints, and (ks) the h
+// sums [4][2][16][64] floats.
+struct G1Lds {
+  size_t vbytes;  // one set of V slices
+  bool vdb;       // two sets
+  size_t abytes;  // region A
+  size_t total;
+};
+__host__ __device__ inline G1Lds g1_lds(bool ks, int mma_dtype, int bm, int K, int ke) {
+  auto al16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
+  const size_t fb = mma_dtype == 0 ? 32 : 16;  // fragment bytes (fp32, dtype 0: 32)
+  const size_t tbytes = 2 * (size_t)(bm / 32) * 4 * 64 * fb;
+  G1Lds L;
+  L.vbytes = (size_t)4 * 32 * (ke * 16 + 1) * sizeof(float);
+  const size_t rest = sizeof(float) * bm * K + al16((size_t)bm * K) + sizeof(uint32_t) * 2 * (bm / 32) +
+                      sizeof(int) * ((size_t)bm + 260) + (ks ? (size_t)4 * 2 * 16 * 64 * sizeof(float) : 0) + 64;
+  const size_t a2 = al16(tbytes > 2 * L.vbytes ? tbytes : 2 * L.vbytes);
+  L.vdb = !ks && a2 + rest <= (bm >= 256 ? 160 * 1024 : 80 * 1024);
+  size_t a = tbytes > L.vbytes ? tbytes : L.vbytes;
+  if (ks && a < (size_t)4 * 2 * 16 * 64 * sizeof(float)) a = (size_t)4 * 2 * 16 * 64 * sizeof(float);
+  L.abytes = L.vdb ? a2 : al16(a);
+  L.total = L.abytes + rest;
+  return L;
+}
 hipError_t launch_vreduce(int mma_dtype, const VReduceArgs& a, hipStream_t st);
 hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st);
 
