@@ -671,13 +671,23 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
       __syncthreads();
       const int per_row = ke * RPAD;
       float* sv = vset(t);
+      float* vp = a.Vp + ((long)tc.nt * a.vp_rows + row0) * per_row;
+      // element e = tid + 256 i is (row r, column c) of the block; (r, c)
+      // advance by a fixed step instead of a division per element
+      const int rstep = 256 / per_row, cstep = 256 - rstep * per_row;
+      int r = tid / per_row, c = tid - r * per_row;
       for (int e = tid; e < 32 * per_row; e += 256) {
-        const int r = e / per_row, c = e - r * per_row;
         const int o = r * VS + c;
         const float v = (sv[o] + sv[32 * VS + o]) + (sv[2 * 32 * VS + o] + sv[3 * 32 * VS + o]);
         if constexpr (KS) sv[o] = sv[32 * VS + o] = sv[2 * 32 * VS + o] = sv[3 * 32 * VS + o] = 0.f;
         const int mr = t * 32 + r;
-        if (m0 + mr < M) a.Vp[((long)tc.nt * a.vp_rows + row0 + s_perm[mr]) * per_row + c] = v;
+        if (m0 + mr < M) vp[(long)s_perm[mr] * per_row + c] = v;
+        r += rstep;
+        c += cstep;
+        if (c >= per_row) {
+          c -= per_row;
+          ++r;
+        }
       }
       if (!lay.vdb) __syncthreads();
     }
