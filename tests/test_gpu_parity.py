@@ -235,6 +235,33 @@ def test_routing_ties_go_to_the_lower_index(wi):
         lay.close()
 
 
+# Column counts that leave the last 256-column tile partly empty (idle
+# wavefronts in the input projection: P_in * f not a multiple of 256; in the
+# down projection: d not a multiple of 256).
+PARTIAL_TILE_SHAPES = [(1, 700, 960, 2752), (3, 500, 2048, 1344), (4, 64, 4096, 1472)]
+
+
+@pytest.mark.parametrize("wi,T,d,f", PARTIAL_TILE_SHAPES)
+def test_partial_column_tiles_match_oracle(wi, T, d, f):
+    """Layers whose feature counts end inside a tile give the oracle's
+    routing and outputs (the idle wavefronts of the last tile write
+    nothing but must not disturb the others' sums)."""
+    L = _lib()
+    w = dataclasses.replace(WORKLOADS[wi], d=d, f=f).with_T(T)
+    wT, inputs, layer = make_parity_layer(w)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        X = x_to_device(inputs["X"], w.x_dtype)
+        rt = O.route(layer)
+        check_routing(route_to_host(lay.route(X)), rt, wT, wT.T)
+        y = y_to_host(lay.forward(X))
+        err = rel_err(y, O.forward(layer, routing=rt))
+        say(f"[partial tiles] {w.name} T={T} d={d} f={f}: rel err {err:.3e}")
+        assert err <= TOL[w.x_dtype]
+    finally:
+        lay.close()
+
+
 TILE_VARIANTS = [
     {"CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1", "CEFN_G2K": "0", "CEFN_UT": "1", "CEFN_GSORT": "1"},
     {"CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4", "CEFN_G2K": "0", "CEFN_UT": "0", "CEFN_GSORT": "0"},
