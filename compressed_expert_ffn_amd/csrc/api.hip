@@ -807,7 +807,9 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   // average); measured: large INT4 layer gemm1 395 -> 355 us, while on the
   // 4-expert fp16 layer the tile sort already suffices.
   const int* garow = h->garow;
-  if (h->garow_sorted && (h->gsort_env == 1 || (h->gsort_env != 0 && c.K >= 8 && rows >= 64L * c.G))) {
+  const bool gsorted =
+      h->garow_sorted && (h->gsort_env == 1 || (h->gsort_env != 0 && c.K >= 8 && rows >= 64L * c.G));
+  if (gsorted) {
     GroupSortArgs gs{h->garow, h->garow_sorted, h->goffsets_live, h->idx_live, c.G, c.K, kg, c.top_experts, h->k};
     hipError_t es = launch_group_sort(gs, rows, st);
     if (es != hipSuccess) return hip_fail(h, es, "group sort launch");
@@ -827,6 +829,7 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   ga.d = c.d;
   ga.f = c.f;
   ga.garow = garow;
+  ga.rows_sorted = gsorted ? 1 : 0;
   ga.idx = h->idx_live;
   ga.w = h->w_live;
   ga.U = h->U;

@@ -335,7 +335,8 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   // result depends only on its own column, so the order (including the
   // arbitrary order inside one key) changes no value.
   const bool mine = tid < BMT && m0 + tid < M;
-  if constexpr (RES != ER_NONE) {
+  // (rows that the group sort already ordered keep their order)
+  if (RES != ER_NONE && !a.rows_sorted) {
     int key = 255;
     if (mine) {
       const int t = a.garow[row0 + tid] / a.kg, ga = a.garow[row0 + tid] % a.kg;

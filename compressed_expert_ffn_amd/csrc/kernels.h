@@ -120,6 +120,7 @@ struct GemmArgs {
   long rows_total;      // T * kg
   int* zero_ptr;        // cleared by the output GEMM's first block
   int zero_n;
+  int rows_sorted;      // G1: group lists already ordered by expert set (tiles keep that order)
 };
 
 struct VReduceArgs {
