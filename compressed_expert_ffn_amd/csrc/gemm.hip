@@ -112,12 +112,12 @@ __device__ __forceinline__ void store4(TE<DT>* p, float a, float b, float c, flo
 // (direct), KT >= 1 stages (d and f are multiples of 64, a k split keeps at
 // least 8 stages, the residual tail is padded to 64); ends with a barrier.
 // (No early exit here: one made the compiler spill the 256-token tiles.)
-template <int TY, int RT, class TO, class WS>
+template <int TY, int RT, int CBT = CB, class TO, class WS>
 __device__ __forceinline__ void run_tile(int KT, const TO& to, const WS& ws, int nb0, FragT<TY>* tl, int lane,
-                                         f16v (&acc)[RT][CB]) {
+                                         f16v (&acc)[RT][CBT]) {
   // short tiles: weights two stages ahead (a stage of 32 or 64 rows has too
   // few MFMAs to cover one load's latency)
-  MainloopTW<TY, RT, CB, TO, WS, (RT <= 2 ? 2 : 1)> ml{to, ws, nb0, tl, lane};
+  MainloopTW<TY, RT, CBT, TO, WS, (RT <= 2 ? 2 : 1)> ml{to, ws, nb0, tl, lane};
   ml.run(KT, acc);
 }
 
@@ -198,19 +198,22 @@ __global__ __launch_bounds__(64 * NWU) void ugemm_kernel(GemmArgs a) {
 
 // U = X . A for many rows: the tile engine (gathered rows staged through
 // LDS, A straight into registers, INT4 decoded per use) on BM-row x
-// 256-column tiles, so a row of X is read once per 256 columns of U rather
-// than once per 64 and the INT4 factors are decoded once per BM rows.
-template <int XT, int TY, int RT, bool INT4>
+// CBT*128-column tiles, so a row of X is read once per 256 (CBT = 2) or 128
+// (CBT = 1: twice the workgroups, for layers with under one 256-column tile
+// per compute unit) columns of U rather than once per 64, and the INT4
+// factors are decoded once per BM rows.
+template <int XT, int TY, int RT, bool INT4, int CBT = CB>
 __global__ __launch_bounds__(256, (TY != DT_F32 && RT <= 4) ? 2 : 1) void ugemm_tile_kernel(GemmArgs a) {
   constexpr int BMT = 32 * RT;
+  constexpr int BNT = 4 * 32 * CBT;  // columns per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   TileCoord tc;
-  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.NU + BNF - 1) / BNF, tc)) return;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.NU + BNT - 1) / BNT, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nbw = (tc.nt * BNF + wave * 64) / 32;
+  const int nbw = (tc.nt * BNT + wave * 32 * CBT) / 32;
   const bool active = nbw * 32 < a.NU;
-  const int nb0 = active ? nbw : a.NU / 32 - CB;
+  const int nb0 = active ? nbw : a.NU / 32 - CBT;
   const int row0 = a.goffsets[g] + m0;
   FragT<TY>* tl = reinterpret_cast<FragT<TY>*>(smem);
   TShared<XT, TY, RT> to;
@@ -218,15 +221,15 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT <= 4) ? 2 : 1) void ugemm_
     const int m = blk * 32 + r;
     return m0 + m < M ? (long)(a.garow[row0 + m] / a.kg) : -1L;
   });
-  f16v acc[RT][CB];
-  zero_acc<RT, CB>(acc);
+  f16v acc[RT][CBT];
+  zero_acc<RT, CBT>(acc);
   const int KS = a.d / 16;
   if constexpr (INT4) {
     WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride, KS};
-    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);
+    run_tile<TY, RT, CBT>(a.d / KB, to, ws, nb0, tl, lane, acc);
   } else {
     WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, KS};
-    run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);
+    run_tile<TY, RT, CBT>(a.d / KB, to, ws, nb0, tl, lane, acc);
   }
   if (!active) return;
 #pragma unroll
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT <= 4) ? 2 : 1) void ugemm_
     if (m0 + m >= M) continue;
     TE<TY>* urow = static_cast<TE<TY>*>(a.U) + (long)(row0 + m) * a.NU + nb0 * 32 + 4 * (lane >> 5);
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
+    for (int c = 0; c < CBT; ++c)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         store4<TY>(urow + c * 32 + 8 * q, acc[t][c][4 * q], acc[t][c][4 * q + 1], acc[t][c][4 * q + 2],
@@ -1054,6 +1057,16 @@ hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
     case GK_U:
       return hipErrorInvalidValue;  // launched by launch_ugemm
     case GK_UT:
+      if constexpr (TY != DT_F32) {
+        // under one 256-column tile per compute unit: 128-column tiles
+        // (twice the workgroups; each row of X read twice)
+        const unsigned nt2 = (unsigned)(a.NU + BNF - 1) / BNF, nt1 = (unsigned)(a.NU + 127) / 128;
+        if (grid.x < 256 && nt1 > nt2) {
+          const dim3 g1(grid.x / nt2 * nt1);
+          if (int4) return go(ugemm_tile_kernel<XT, TY, RT, true, 1>, g1, lds, a, st);
+          return go(ugemm_tile_kernel<XT, TY, RT, false, 1>, g1, lds, a, st);
+        }
+      }
       if (int4) return go(ugemm_tile_kernel<XT, TY, RT, true>, grid, lds, a, st);
       return go(ugemm_tile_kernel<XT, TY, RT, false>, grid, lds, a, st);
     case GK_G1:
