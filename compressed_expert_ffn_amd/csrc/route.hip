@@ -65,70 +65,94 @@ __device__ __forceinline__ void load8x(const typename Elem<XT>::T* p, float (&v)
 // differs from an FP32 dot product only by the order of the additions and
 // by terms below 2^-24 of the score, as the FP32 router requires, at a
 // fraction of the FP32 MFMA time.
-template <int XT, int NCB>
+// TBN consecutive token blocks (tb .. tb + TBN - 1) share each load of the
+// router matrix parts: for large batches the parts, re-read once per token
+// block, are most of the bytes a compute unit loads.  Each block's MFMA
+// sequence is the same as with TBN = 1, so its scores are bit for bit the
+// same.
+template <int XT, int NCB, int TBN = 1>
 __device__ __forceinline__ void score_tiles_bf(const RouteArgs& a, int tb, int cb0, int k0, int kq, int lane,
-                                               f16v (&acc)[NCB]) {
+                                               f16v (&acc)[TBN][NCB]) {
   using XE = typename Elem<XT>::T;
   using B8 = typename Frag<DT_BF16>::T;
   const int h = lane >> 5;
-  int tok = tb * 32 + (lane & 31);
-  tok = tok < a.T ? tok : a.T - 1;  // rows past the batch repeat the last one
-  const XE* xp = static_cast<const XE*>(a.X) + (long)tok * a.d + k0 + 8 * h;
+  const XE* xp[TBN];
+#pragma unroll
+  for (int b = 0; b < TBN; ++b) {
+    int tok = (tb + b) * 32 + (lane & 31);
+    tok = tok < a.T ? tok : a.T - 1;  // rows past the batch repeat the last one
+    xp[b] = static_cast<const XE*>(a.X) + (long)tok * a.d + k0 + 8 * h;
+  }
   const long pstride = (long)(a.d / 16) * a.NCp * 16;
   const uint16_t* wp = a.Wb + ((long)(k0 / 16) * a.NCp + cb0 * 32 + (lane & 31)) * 16 + 8 * h;
   const long wstep = (long)a.NCp * 16;
 #pragma unroll
-  for (int c = 0; c < NCB; ++c)
+  for (int b = 0; b < TBN; ++b)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][c][v] = 0.f;
   const int n16 = kq / 16;
   if (n16 == 0) return;
-  u4v xa, xb;
-  u4v wa[NCB][3], wb[NCB][3];
-  auto issue = [&](int i, u4v& xv, u4v (&wv)[NCB][3]) {
+  auto issue = [&](int i, u4v (&xv)[TBN], u4v (&wv)[NCB][3]) {
     const int ic = i < n16 ? i : n16 - 1;  // the last group re-reads itself
-    xv = *reinterpret_cast<const u4v*>(xp + ic * 16);
+#pragma unroll
+    for (int b = 0; b < TBN; ++b) xv[b] = *reinterpret_cast<const u4v*>(xp[b] + ic * 16);
 #pragma unroll
     for (int c = 0; c < NCB; ++c)
 #pragma unroll
       for (int p = 0; p < 3; ++p) wv[c][p] = *reinterpret_cast<const u4v*>(wp + p * pstride + ic * wstep + c * 32 * 16);
   };
-  auto mma = [&](const u4v& xv, const u4v (&wv)[NCB][3]) {
-    B8 xh, xl;
-    if constexpr (XT == DT_BF16) {
-      xh = __builtin_bit_cast(B8, xv);
-    } else {
+  auto mma = [&](const u4v (&xv)[TBN], const u4v (&wv)[NCB][3]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = f16_bits_to_f32(static_cast<uint16_t>((xv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
-        const uint16_t hb = f32_to_bf16_bits(f);
-        xh[e] = __builtin_bit_cast(__bf16, hb);
-        xl[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(f - bf16_bits_to_f32(hb)));
+    for (int b = 0; b < TBN; ++b) {
+      B8 xh, xl;
+      if constexpr (XT == DT_BF16) {
+        xh = __builtin_bit_cast(B8, xv[b]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t pr = xv[b][e >> 1];
+          const float f = f16_bits_to_f32(static_cast<uint16_t>((pr >> (16 * (e & 1))) & 0xFFFFu));
+          const uint16_t hb = f32_to_bf16_bits(f);
+          xh[e] = __builtin_bit_cast(__bf16, hb);
+          xl[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(f - bf16_bits_to_f32(hb)));
+        }
       }
-    }
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
+      for (int c = 0; c < NCB; ++c) {
 #pragma unroll
-      for (int p = 0; p < 3; ++p) acc[c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xh, acc[c]);
-      if constexpr (XT != DT_BF16) {
+        for (int p = 0; p < 3; ++p) acc[b][c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xh, acc[b][c]);
+        if constexpr (XT != DT_BF16) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) acc[c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xl, acc[c]);
+          for (int p = 0; p < 2; ++p) acc[b][c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xl, acc[b][c]);
+        }
       }
     }
   };
-  issue(0, xa, wa);
+  // loads run PD groups of 16 k ahead of the MFMAs (a ring of PD + 1
+  // register sets): two for one token block, whose group has few MFMAs; one
+  // for two blocks (twice the MFMAs per group, and two workgroups per
+  // compute unit fit only then)
+  constexpr int PD = TBN > 1 ? 1 : 2, R = PD + 1;
+  u4v xr[R][TBN];
+  u4v wr[R][NCB][3];
+#pragma unroll
+  for (int p = 0; p < PD; ++p) issue(p, xr[p], wr[p]);
   int i = 0;
-  for (; i + 2 <= n16; i += 2) {
-    issue(i + 1, xb, wb);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(xa, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(i + 2, xa, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(xb, wb);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; i + R <= n16; i += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      issue(i + u + PD, xr[(u + PD) % R], wr[(u + PD) % R]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(xr[u], wr[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (i < n16) mma(xa, wa);
+  // fewer than R groups left, already loaded into sets 0 .. PD - 1
+#pragma unroll
+  for (int u = 0; u < PD; ++u)
+    if (i + u < n16) mma(xr[u], wr[u]);
 }
 
 // Partial scores of one wavefront: token block tb, score-column blocks
@@ -141,7 +165,10 @@ template <int XT, int NCB>
 __device__ __forceinline__ void score_tiles(const RouteArgs& a, int tb, int cb0, int k0, int kq, int lane,
                                             f16v (&acc)[NCB]) {
   if constexpr (XT != DT_F32) {
-    score_tiles_bf<XT, NCB>(a, tb, cb0, k0, kq, lane, acc);
+    f16v acc1[1][NCB];
+    score_tiles_bf<XT, NCB, 1>(a, tb, cb0, k0, kq, lane, acc1);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) acc[c] = acc1[0][c];
     return;
   }
   using XE = typename Elem<XT>::T;
@@ -157,8 +184,6 @@ __device__ __forceinline__ void score_tiles(const RouteArgs& a, int tb, int cb0,
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
   const int n16 = kq / 16;
   if (n16 == 0) return;
-  float xa[8], xb[8];
-  f4v wa[NCB][2], wb[NCB][2];
   auto issue = [&](int i, float (&xv)[8], f4v (&wv)[NCB][2]) {
     const int ic = i < n16 ? i : n16 - 1;  // the last group re-reads itself
     load8x<XT>(xp + ic * 16, xv);
@@ -176,19 +201,27 @@ __device__ __forceinline__ void score_tiles(const RouteArgs& a, int tb, int cb0,
       for (int st = 0; st < 8; ++st)
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(wv[c][st >> 2][st & 3], xv[st], acc[c], 0, 0, 0);
   };
-  issue(0, xa, wa);
+  // loads run PD = 2 groups of 16 k ahead of the MFMAs (a ring of three
+  // register sets): one group's MFMAs are too few to cover a load's latency
+  constexpr int PD = 2, R = PD + 1;
+  float xr[R][8];
+  f4v wr[R][NCB][2];
+#pragma unroll
+  for (int p = 0; p < PD; ++p) issue(p, xr[p], wr[p]);
   int i = 0;
-  for (; i + 2 <= n16; i += 2) {
-    issue(i + 1, xb, wb);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(xa, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(i + 2, xa, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(xb, wb);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; i + R <= n16; i += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      issue(i + u + PD, xr[(u + PD) % R], wr[(u + PD) % R]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(xr[u], wr[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (i < n16) mma(xa, wa);
+  // fewer than R groups left, already loaded into sets 0 .. PD - 1
+#pragma unroll
+  for (int u = 0; u < PD; ++u)
+    if (i + u < n16) mma(xr[u], wr[u]);
 }
 
 // grid: (token blocks of 32) x (score-column blocks of 32) x splits.  The 4
@@ -420,59 +453,69 @@ __global__ __launch_bounds__(256) void select_kernel(RouteArgs a, int tpb) {
 // Scores and selection in one kernel when a 32-token block's scores fit one
 // workgroup (at most 4 column blocks): wavefront w of NW (4 or 8) computes k
 // range w of every column block, the NW partial blocks meet in LDS
-// (dynamic, summed pairwise in a fixed order), and 32 threads select.  More
-// wavefronts shorten the dependent MFMA chain of the few workgroups a small
-// batch has.
-template <int XT, int NCB, int NW>
+// (dynamic, summed pairwise in a fixed order), and one thread per token
+// selects.  More wavefronts shorten the dependent MFMA chain of the few
+// workgroups a small batch has.  For large batches of 16-bit activations a
+// workgroup takes TBN = 2 token blocks, which share the loads of the router
+// matrix parts (their partial blocks go through LDS one block at a time).
+template <int XT, int NCB, int NW, int TBN = 1>
 __global__ __launch_bounds__(64 * NW) void route_fused_kernel(RouteArgs a) {
+  static_assert(TBN == 1 || XT != DT_F32, "several token blocks: 16-bit activations only");
   extern __shared__ __attribute__((aligned(16))) float red[];  // [NW][NCB][16][64]
-  __shared__ float sc[32][NCB * 32 + 1];
-  // per-workgroup routing counts: 32 tokens span at most 2 group-list chunks
-  // and 3 expert-list chunks of 256 assignments
-  __shared__ int lcg[2 * 256];
-  __shared__ int lce[3 * 1024];
-  const int tb = blockIdx.x;
+  __shared__ float sc[32 * TBN][NCB * 32 + 1];
+  // per-workgroup routing counts: 32 TBN tokens span at most TBN + 1
+  // group-list chunks and 2 TBN + 1 expert-list chunks of 256 assignments
+  // (at most 8 groups and 16 experts per token)
+  __shared__ int lcg[(TBN + 1) * 256];
+  __shared__ int lce[(2 * TBN + 1) * 1024];
+  const int tb = blockIdx.x * TBN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int NT = 64 * NW;
   const int kq = a.d / NW;
-  for (int i = threadIdx.x; i < 2 * a.G; i += NT) lcg[i] = 0;
+  for (int i = threadIdx.x; i < (TBN + 1) * a.G; i += NT) lcg[i] = 0;
   if (a.count_experts)
-    for (int i = threadIdx.x; i < 3 * a.E; i += NT) lce[i] = 0;
-  {
-    f16v acc[NCB];
-    score_tiles<XT, NCB>(a, tb, 0, wave * kq, kq, lane, acc);
+    for (int i = threadIdx.x; i < (2 * TBN + 1) * a.E; i += NT) lce[i] = 0;
+  const int NC = a.G + (a.K > 1 ? a.G * a.K : 0);
+  f16v acc[TBN][NCB];
+  if constexpr (XT != DT_F32) {
+    score_tiles_bf<XT, NCB, TBN>(a, tb, 0, wave * kq, kq, lane, acc);
+  } else {
+    score_tiles<XT, NCB>(a, tb, 0, wave * kq, kq, lane, acc[0]);
+  }
+#pragma unroll
+  for (int b = 0; b < TBN; ++b) {
+    if (b > 0) __syncthreads();  // the previous block's partials are summed
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) red[((wave * NCB + cb) * 16 + v) * 64 + lane] = acc[cb][v];
-  }
-  __syncthreads();
-  const int NC = a.G + (a.K > 1 ? a.G * a.K : 0);
-  for (int e = threadIdx.x; e < NCB * 16 * 64; e += NT) {
-    const int cb = e / (16 * 64), v = (e / 64) % 16, l = e % 64;
-    const int c = cb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-    if (c < NC) {
-      // pairwise over the wavefronts' partials
-      float p[NW];
+      for (int v = 0; v < 16; ++v) red[((wave * NCB + cb) * 16 + v) * 64 + lane] = acc[b][cb][v];
+    __syncthreads();
+    for (int e = threadIdx.x; e < NCB * 16 * 64; e += NT) {
+      const int cb = e / (16 * 64), v = (e / 64) % 16, l = e % 64;
+      const int c = cb * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+      if (c < NC) {
+        // pairwise over the wavefronts' partials
+        float p[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) p[w] = red[w * NCB * 16 * 64 + e];
+        for (int w = 0; w < NW; ++w) p[w] = red[w * NCB * 16 * 64 + e];
 #pragma unroll
-      for (int st = 1; st < NW; st <<= 1)
+        for (int st = 1; st < NW; st <<= 1)
 #pragma unroll
-        for (int w = 0; w + st < NW; w += 2 * st) p[w] += p[w + st];
-      sc[l & 31][c] = p[0] + score_bias(a, c);
+          for (int w = 0; w + st < NW; w += 2 * st) p[w] += p[w + st];
+        sc[b * 32 + (l & 31)][c] = p[0] + score_bias(a, c);
+      }
     }
   }
   __syncthreads();
   const int t = tb * 32 + threadIdx.x;
   const int t0 = tb * 32;
   const int cg0 = t0 * a.kg / CHUNK, ce0 = t0 * a.k / CHUNK;
-  if (threadIdx.x < 32 && t < a.T) select_token(a, t, sc[threadIdx.x], lcg, cg0, lce, ce0);
+  if (threadIdx.x < 32 * TBN && t < a.T) select_token(a, t, sc[threadIdx.x], lcg, cg0, lce, ce0);
   __syncthreads();
-  for (int i = threadIdx.x; i < 2 * a.G; i += NT)
+  for (int i = threadIdx.x; i < (TBN + 1) * a.G; i += NT)
     if (lcg[i]) atomicAdd(&a.cgcount[(cg0 + i / a.G) * a.G + i % a.G], lcg[i]);
   if (a.count_experts)
-    for (int i = threadIdx.x; i < 3 * a.E; i += NT)
+    for (int i = threadIdx.x; i < (2 * TBN + 1) * a.E; i += NT)
       if (lce[i]) atomicAdd(&a.ccount[(ce0 + i / a.E) * a.E + i % a.E], lce[i]);
 }
 
@@ -592,16 +635,16 @@ hipError_t launch_logits(const RouteArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int XT, int NCB, int NW>
+template <int XT, int NCB, int NW, int TBN = 1>
 hipError_t launch_fused_nw(const RouteArgs& a, hipStream_t st) {
-  auto k = route_fused_kernel<XT, NCB, NW>;
+  auto k = route_fused_kernel<XT, NCB, NW, TBN>;
   const size_t lds = (size_t)NW * NCB * 16 * 64 * sizeof(float);
-  if (lds > 65536) {
+  if (lds > 65536 || TBN > 1) {  // (TBN > 1: over 64 KB with the static arrays)
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k, dim3((a.T + 31) / 32), dim3(64 * NW), lds, st, a);
+  hipLaunchKernelGGL(k, dim3((a.T + 32 * TBN - 1) / (32 * TBN)), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
 
@@ -616,6 +659,11 @@ inline int fused_waves(int T, int d) {
 template <int XT, int NCB>
 hipError_t launch_fused_ncb(const RouteArgs& a, hipStream_t st) {
   if (fused_waves(a.T, a.d) == 8) return launch_fused_nw<XT, NCB, 8>(a, st);
+  // two token blocks per workgroup once that still gives a workgroup per
+  // compute unit (up to 3 column blocks: 4 would spill)
+  if constexpr (XT != DT_F32 && NCB <= 3) {
+    if ((a.T + 63) / 64 >= 256) return launch_fused_nw<XT, NCB, 4, 2>(a, st);
+  }
   return launch_fused_nw<XT, NCB, 4>(a, st);
 }
 

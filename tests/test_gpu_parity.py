@@ -59,6 +59,7 @@ CASES = [
     (3, 777, None),
     (2, 200, None),
     (3, None, 96),
+    (3, 16400, 64),  # two token blocks per router workgroup, the last one partly past the batch
 ]
 
 
