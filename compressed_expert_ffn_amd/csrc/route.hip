@@ -103,31 +103,40 @@ __device__ __forceinline__ void score_tiles_bf(const RouteArgs& a, int tb, int c
 #pragma unroll
       for (int p = 0; p < 3; ++p) wv[c][p] = *reinterpret_cast<const u4v*>(wp + p * pstride + ic * wstep + c * 32 * 16);
   };
+  // Each accumulator takes x.p0, x.p1, x.p2 (then xr.p0, xr.p1) in that
+  // order; the loops run the parts outermost so that consecutive MFMAs
+  // update different accumulators (back-to-back MFMAs on one accumulator
+  // wait for each other's results).
   auto mma = [&](const u4v (&xv)[TBN], const u4v (&wv)[NCB][3]) {
+    B8 xh[TBN], xl[TBN];
 #pragma unroll
     for (int b = 0; b < TBN; ++b) {
-      B8 xh, xl;
       if constexpr (XT == DT_BF16) {
-        xh = __builtin_bit_cast(B8, xv[b]);
+        xh[b] = __builtin_bit_cast(B8, xv[b]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t pr = xv[b][e >> 1];
           const float f = f16_bits_to_f32(static_cast<uint16_t>((pr >> (16 * (e & 1))) & 0xFFFFu));
           const uint16_t hb = f32_to_bf16_bits(f);
-          xh[e] = __builtin_bit_cast(__bf16, hb);
-          xl[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(f - bf16_bits_to_f32(hb)));
+          xh[b][e] = __builtin_bit_cast(__bf16, hb);
+          xl[b][e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(f - bf16_bits_to_f32(hb)));
         }
       }
+    }
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
+    for (int p = 0; p < 3; ++p)
 #pragma unroll
-        for (int p = 0; p < 3; ++p) acc[b][c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xh, acc[b][c]);
-        if constexpr (XT != DT_BF16) {
+      for (int b = 0; b < TBN; ++b)
 #pragma unroll
-          for (int p = 0; p < 2; ++p) acc[b][c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xl, acc[b][c]);
-        }
-      }
+        for (int c = 0; c < NCB; ++c) acc[b][c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xh[b], acc[b][c]);
+    if constexpr (XT != DT_BF16) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int b = 0; b < TBN; ++b)
+#pragma unroll
+          for (int c = 0; c < NCB; ++c) acc[b][c] = mfma32<DT_BF16>(__builtin_bit_cast(B8, wv[c][p]), xl[b], acc[b][c]);
     }
   };
   // loads run PD groups of 16 k ahead of the MFMAs (a ring of PD + 1
@@ -195,10 +204,11 @@ __device__ __forceinline__ void score_tiles(const RouteArgs& a, int tb, int cb0,
     }
   };
   auto mma = [&](const float (&xv)[8], const f4v (&wv)[NCB][2]) {
+    // k steps outermost: consecutive MFMAs update different accumulators
 #pragma unroll
-    for (int c = 0; c < NCB; ++c)
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
+      for (int c = 0; c < NCB; ++c)
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(wv[c][st >> 2][st & 3], xv[st], acc[c], 0, 0, 0);
   };
   // loads run PD = 2 groups of 16 k ahead of the MFMAs (a ring of three
