@@ -734,7 +734,8 @@ int router_splits(int T, int d, int NCp) {
 // row, so the order changes no value, and a 32-row block of the sorted list
 // then sees few distinct experts.  Keys are computed once, eight rows per
 // thread at a time (their loads in flight together), and kept in LDS when
-// the group fits (kcap bytes), else recomputed.
+// the group fits (kcap bytes), else recomputed; both passes take B rows per
+// thread at a time with all their global loads issued before any LDS update.
 __device__ __forceinline__ int group_row_key(const GroupSortArgs& a, int g, int aid) {
   const int t = aid / a.kg, ga = aid - t * a.kg;
   const int* ip = a.idx + t * a.k + ga * a.ke;
@@ -766,12 +767,15 @@ __global__ __launch_bounds__(256) void group_sort_kernel(GroupSortArgs a, int kc
       const int i = i0 + b * 256 + tid;
       aid[b] = i < n ? a.garow_in[r0 + i] : -1;
     }
+    // all B rows' expert loads in flight before any LDS update
+    int key[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) key[b] = aid[b] < 0 ? -1 : group_row_key(a, g, aid[b]);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      if (aid[b] < 0) continue;
-      const int key = group_row_key(a, g, aid[b]);
-      atomicAdd(&hist[key], 1);
-      if (keep) skey[i0 + b * 256 + tid] = static_cast<uint8_t>(key);
+      if (key[b] < 0) continue;
+      atomicAdd(&hist[key[b]], 1);
+      if (keep) skey[i0 + b * 256 + tid] = static_cast<uint8_t>(key[b]);
     }
   }
   __syncthreads();
@@ -789,10 +793,19 @@ __global__ __launch_bounds__(256) void group_sort_kernel(GroupSortArgs a, int kc
   for (int w = 0; w < wave; ++w) base += wsum[w];
   cur[tid] = base + inc - cnt;
   __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    const int aid = a.garow_in[r0 + i];
-    const int key = keep ? static_cast<int>(skey[i]) : group_row_key(a, g, aid);
-    a.garow_out[r0 + atomicAdd(&cur[key], 1)] = aid;
+  for (int i0 = 0; i0 < n; i0 += 256 * B) {
+    int aid[B], key[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int i = i0 + b * 256 + tid;
+      aid[b] = i < n ? a.garow_in[r0 + i] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      key[b] = aid[b] < 0 ? -1 : (keep ? static_cast<int>(skey[i0 + b * 256 + tid]) : group_row_key(a, g, aid[b]));
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      if (key[b] >= 0) a.garow_out[r0 + atomicAdd(&cur[key[b]], 1)] = aid[b];
   }
 }
 
