@@ -866,7 +866,8 @@ __global__ __launch_bounds__(256) void gemm2k_kernel(GemmArgs a) {
 // of expert j in the row's chosen list; zero for experts the row did not
 // pick.  V is stored in the MFMA type: the down projection's residual tail
 // would round it to that type on load anyway.  One thread per element of V;
-// the partial loads of a thread are issued four at a time.
+// eight partials of a thread in flight at a time (small layers: the most
+// threads, the shortest chains).
 template <int TY>
 __global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
   TE<TY>* V = static_cast<TE<TY>*>(a.V);
@@ -897,6 +898,62 @@ __global__ __launch_bounds__(256) void vreduce_kernel(VReduceArgs a) {
     sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
   }
   V[e] = from_f32<TY>(sum);
+}
+
+// The same sum for many rows: one thread per (row, 16-column block j; j < K
+// an expert of the group, the others padding, written as zeros).  The
+// row's lookups are done once for its 16 values, whose partials are 64
+// contiguous bytes per column tile; four tiles' loads are in flight at a
+// time, tile nt summed into running sum nt % 4, the four sums added
+// pairwise at the end (large INT4 layer: 21 -> 13.5 us; on small layers
+// the longer per-thread chain measured slower).
+template <int TY>
+__global__ __launch_bounds__(256) void vreduce_rows_kernel(VReduceArgs a) {
+  TE<TY>* V = static_cast<TE<TY>*>(a.V);
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const int NJ = a.NV / RPAD;
+  if (e >= (long)a.rows * NJ) return;
+  const int row = (int)(e / NJ), j = (int)(e % NJ);
+  const int aid = a.garow[row];
+  const int t = aid / a.kg, ga = aid - t * a.kg;
+  const int ex = a.gidx[aid] * a.K + j;
+  int sl = -1;
+  if (j < a.K)
+    for (int s = 0; s < a.ke; ++s)
+      if (a.idx[t * a.k + ga * a.ke + s] == ex) sl = s;
+  float sum[RPAD];
+#pragma unroll
+  for (int r = 0; r < RPAD; ++r) sum[r] = 0.f;
+  if (sl >= 0) {
+    const f4v* p = reinterpret_cast<const f4v*>(a.Vp + ((long)row * a.ke + sl) * RPAD);
+    const long step = a.vp_rows * a.ke * RPAD / 4;  // in f4v
+    f4v q[4][RPAD / 4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w = 0; w < RPAD / 4; ++w) q[u][w] = f4v{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < a.ntiles; nt += 4) {
+      f4v v[4][RPAD / 4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < RPAD / 4; ++w)
+          v[u][w] = nt + u < a.ntiles ? p[(long)(nt + u) * step + w] : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < RPAD / 4; ++w) q[u][w] += v[u][w];
+    }
+#pragma unroll
+    for (int w = 0; w < RPAD / 4; ++w) {
+      const f4v s4 = (q[0][w] + q[1][w]) + (q[2][w] + q[3][w]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[4 * w + i] = s4[i];
+    }
+  }
+  TE<TY>* out = V + (long)row * a.NV + j * RPAD;
+#pragma unroll
+  for (int q = 0; q < RPAD / 4; ++q) store4<TY>(out + 4 * q, sum[4 * q], sum[4 * q + 1], sum[4 * q + 2], sum[4 * q + 3]);
 }
 
 // ------------------------------------------------ bf16 -> fp16 activations --
@@ -1195,6 +1252,19 @@ hipError_t launch_cvt_x(const void* X, void* X16, long n, hipStream_t st) {
 
 hipError_t launch_vreduce(int mma_dtype, const VReduceArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
+  // many rows (the per-element form would take several rounds of the
+  // chip): a thread per 16 values; otherwise a thread per value
+  const long nblk = (long)a.rows * (a.NV / RPAD);
+  if (nblk >= 65536) {
+    const dim3 grid((unsigned)((nblk + 255) / 256));
+    switch (mma_dtype) {
+      case DT_F32: hipLaunchKernelGGL(vreduce_rows_kernel<DT_F32>, grid, dim3(256), 0, st, a); break;
+      case DT_F16: hipLaunchKernelGGL(vreduce_rows_kernel<DT_F16>, grid, dim3(256), 0, st, a); break;
+      case DT_BF16: hipLaunchKernelGGL(vreduce_rows_kernel<DT_BF16>, grid, dim3(256), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(((long)a.rows * a.NV + 255) / 256));
   switch (mma_dtype) {
     case DT_F32: hipLaunchKernelGGL(vreduce_kernel<DT_F32>, grid, dim3(256), 0, st, a); break;
