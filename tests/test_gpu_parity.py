@@ -263,6 +263,29 @@ def test_partial_column_tiles_match_oracle(wi, T, d, f):
         lay.close()
 
 
+def test_v_sum_padding_columns_many_rows():
+    """Two experts per group leave V with padding columns past K*16; with
+    16384 rows the V sum takes its per-(row, 16-value block) form, which
+    must write those columns as zeros (the down projection's tail reads
+    them)."""
+    L = _lib()
+    w = dataclasses.replace(WORKLOADS[3], K=2, top_experts=1).with_T(16384)
+    wT, inputs, layer = make_parity_layer(w)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        X = x_to_device(inputs["X"], w.x_dtype)
+        rt = O.route(layer)
+        check_routing(route_to_host(lay.route(X)), rt, wT, wT.T)
+        y = y_to_host(lay.forward(X))
+        assert np.isfinite(y).all()
+        toks = np.sort(np.random.default_rng(5).choice(wT.T, size=48, replace=False))
+        err = rel_err(y[toks], O.forward(layer, tokens=toks))
+        say(f"[v sum padding] {w.name} K=2 T={wT.T}: rel err {err:.3e}")
+        assert err <= TOL[w.x_dtype]
+    finally:
+        lay.close()
+
+
 TILE_VARIANTS = [
     {"CEFN_BM_G1": "256", "CEFN_BM_G2": "256", "CEFN_KS_G2": "1", "CEFN_G2K": "0", "CEFN_UT": "1", "CEFN_GSORT": "1"},
     {"CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4", "CEFN_G2K": "0", "CEFN_UT": "0", "CEFN_GSORT": "0"},
