@@ -3,9 +3,12 @@
 
 A step is one moe_forward over one batch of T synthetic tokens already
 resident in HBM (router, token lists, the grouped GEMMs, combine).  The
-default workload is the compressed fp16 SwiGLU layer (T = 2048, d = 1024,
-f = 2816, 4 groups of 4 experts, top-1 group then top-2 experts, rank 16);
-``--workload N`` selects another of the five shapes.
+default workload is the largest layer that fits one GPU: the flat top-2 of
+8 bf16 SwiGLU layer (T = 4096, d = 4096, f = 14336, 8 experts);
+``--workload N`` selects another of the five shapes.  The decode-shaped
+layer is timed cold: steps alternate between two copies of its weights
+whose total exceeds the 256 MB last-level cache, so every step streams
+its weights from HBM.
 
 Prints one JSON line: routed tokens/s (T per forward), the roofline of the
 dominant kernel (algorithmic work per launch over its average duration,
@@ -151,6 +154,18 @@ def copy_calibration(mib: int) -> None:
     print(f"copied {mib} MiB x5", flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, inputs, budget_s: float) -> dict:
     """The CPU oracle as it stands, on the same workload (the sample is the
     whole batch, repeated while the time budget lasts)."""
@@ -180,7 +195,8 @@ def cpu_baseline(w, inputs, budget_s: float) -> dict:
     med = times[len(times) // 2]
     return dict(value=n_tok / med, unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=f"{n_tok} of {T} tokens of the {w.name} layer, float64 NumPy oracle, "
-                       f"median of {len(times)} run(s) of {med:.2f} s")
+                       f"median of {len(times)} run(s) of {med:.2f} s",
+                cpu_model=cpu_model(), nproc=os.cpu_count())
 
 
 def main():
@@ -188,7 +204,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="weight copies rotated between steps (0: 2 for the decode layer, else 1)")
     ap.add_argument("--no-graph", action="store_true", help="plain stream launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -218,7 +236,10 @@ def main():
 
     w = WORKLOADS[args.workload]
     inputs = synth.make_layer(w)
-    lay = L.Layer(L.config_from_workload(w), inputs)
+    copies = args.copies or (2 if w.index == 4 else 1)
+    lays = [L.Layer(L.config_from_workload(w), inputs) for _ in range(copies)]
+    lay = lays[0]
+    weight_mb = lay.stats()["stored_bytes"] / 1e6
     xt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.x_dtype]
     Xh = inputs["X"]
     if w.x_dtype == "bf16":
@@ -234,47 +255,58 @@ def main():
     tg, te = int((gcounts > 0).sum()), int((counts > 0).sum())
     work = kernel_work(w, w.T, tg, te)
 
+    def step(i):
+        lays[i % copies].forward(X, Y)
+
     # warm-up, with every stage timed to find the dominant kernel (the first
-    # call loads code objects and is left out)
-    lay.forward(X, Y)
+    # call of each copy loads code objects and is left out)
+    for i in range(copies):
+        step(i)
     torch.cuda.synchronize()
-    lay.profile_begin(max(1, args.warmup))
-    for _ in range(max(1, args.warmup)):
-        lay.forward(X, Y)
-    stage_warm = lay.profile_end()
-    calls = max(1, stage_warm["calls"])
-    stage_ms = {s: stage_warm["stage_ms"].get(s, 0.0) / calls for s in STAGES}
+    nw = max(copies, args.warmup)
+    for lw in lays:
+        lw.profile_begin(nw)
+    for i in range(nw):
+        step(i)
+    warm = [lw.profile_end() for lw in lays]
+    calls = max(1, sum(x["calls"] for x in warm))
+    stage_ms = {s: sum(x["stage_ms"].get(s, 0.0) for x in warm) / calls for s in STAGES}
     dominant = max(STAGES, key=lambda s: stage_ms[s])
 
     # timed region: plain stream launches, HIP events around the dominant kernel
     torch.cuda.synchronize()
-    lay.profile_begin(args.steps, stages=[dominant])
+    for lw in lays:
+        lw.profile_begin(args.steps, stages=[dominant])
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        lay.forward(X, Y)
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prof = lay.profile_end()
+    profs = [lw.profile_end() for lw in lays]
     ms_stream = (t1 - t0) * 1e3 / args.steps
-    dom_ms = prof["stage_ms"][dominant] / max(1, prof["calls"])
+    dom_ms = sum(p["stage_ms"][dominant] for p in profs) / max(1, sum(p["calls"] for p in profs))
 
-    # the same step replayed from a captured HIP graph
+    # the same steps replayed from captured HIP graphs (one per weight copy)
     ms_graph = None
     if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
+        graphs = []
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            lay.forward(X, Y)
+            for i in range(copies):
+                step(i)
         torch.cuda.current_stream().wait_stream(s)
-        with torch.cuda.graph(g):
-            lay.forward(X, Y)
-        for _ in range(args.warmup):
-            g.replay()
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
+        for i in range(args.steps):
+            graphs[i % copies].replay()
         torch.cuda.synchronize()
         ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
 
@@ -304,7 +336,9 @@ def main():
         vs_baseline=None, dtype=w.base_dtype, data="synthetic",
         config=dict(workload=w.name, T=w.T, d=w.d, f=w.f, G=w.G, K=w.K,
                     top_groups=w.top_groups, top_experts=w.top_experts, r=w.r,
-                    residual=w.resid, act=w.act, x_dtype=w.x_dtype, launch=launch),
+                    residual=w.resid, act=w.act, x_dtype=w.x_dtype, launch=launch,
+                    weight_copies=copies, weight_mb_per_copy=round(weight_mb, 1),
+                    cache="cold" if copies * weight_mb > 256 else "warm"),
         roofline=roof,
         assignments_per_s=round(w.T * w.k / (ms * 1e-3), 1),
         layer_tflops=round(total_flops / (ms * 1e-3) / 1e12, 2),
@@ -318,7 +352,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
     else:
         out["cpu_baseline"] = None
-    lay.close()
+    for lw in lays:
+        lw.close()
     print(json.dumps(out), flush=True)
 
 

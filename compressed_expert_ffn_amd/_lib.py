@@ -29,7 +29,8 @@ class moe_config(C.Structure):
 class moe_weights(C.Structure):
     _fields_ = [("W_grp", C.c_void_p), ("W_exp", C.c_void_p),
                 ("group_bias", C.c_void_p), ("expert_bias", C.c_void_p),
-                ("base", C.c_void_p * 3), ("A", C.c_void_p * 3), ("B", C.c_void_p * 3)]
+                ("base", C.c_void_p * 3), ("A", C.c_void_p * 3), ("B", C.c_void_p * 3),
+                ("on_device", C.c_int32)]
 
 
 class moe_route_out(C.Structure):
@@ -66,7 +67,10 @@ def _load():
         "moe_destroy": ([P], C.c_int),
         "moe_last_error": ([], C.c_char_p),
         "moe_config_stats": ([C.POINTER(moe_config), C.POINTER(moe_stats)], C.c_int),
+        "moe_stats": ([P, C.POINTER(moe_stats)], C.c_int),
         "moe_debug_residual": ([P, C.c_int32, C.c_int32, C.c_int32, P, P, P], C.c_int),
+        "moe_debug_dequant": ([P, C.c_int32, C.c_int32, C.c_int32, P], C.c_int),
+        "moe_debug_q": ([P, C.c_int32, C.c_int32, C.c_int32, P, P], C.c_int),
         "moe_profile_begin": ([P, C.c_int32, C.c_int32], C.c_int),
         "moe_profile_end": ([P, P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                              C.c_char_p, C.c_int32], C.c_int),
@@ -112,6 +116,17 @@ def _host_ptr(a, keep):
     return a.ctypes.data
 
 
+def _device_ptr(a, keep):
+    """Copy a host array to a new device buffer (kept alive in ``keep``)."""
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.uint8).reshape(-1).copy()).cuda()
+    keep.append(t)
+    return t.data_ptr()
+
+
 def _stream_ptr(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -123,24 +138,27 @@ class Layer:
 
     inputs: the host arrays of one layer (X is not needed), in the layout
     include/moe.h documents; fp16 arrays as numpy float16, bf16 as uint16 bits.
+    on_device: hand the weights over as device buffers (copied there first).
     """
 
-    def __init__(self, cfg: moe_config, inputs: dict):
+    def __init__(self, cfg: moe_config, inputs: dict, on_device: bool = False):
         keep = []
+        ptr = _device_ptr if on_device else _host_ptr
         w = moe_weights()
-        w.W_grp = _host_ptr(np.asarray(inputs["W_grp"], dtype=np.float32), keep)
-        w.W_exp = _host_ptr(None if inputs.get("W_exp") is None
-                            else np.asarray(inputs["W_exp"], dtype=np.float32), keep)
-        w.group_bias = _host_ptr(None if inputs.get("group_bias") is None
-                                 else np.asarray(inputs["group_bias"], dtype=np.float32), keep)
-        w.expert_bias = _host_ptr(None if inputs.get("expert_bias") is None
-                                  else np.asarray(inputs["expert_bias"], dtype=np.float32), keep)
+        w.on_device = 1 if on_device else 0
+        w.W_grp = ptr(np.asarray(inputs["W_grp"], dtype=np.float32), keep)
+        w.W_exp = ptr(None if inputs.get("W_exp") is None
+                      else np.asarray(inputs["W_exp"], dtype=np.float32), keep)
+        w.group_bias = ptr(None if inputs.get("group_bias") is None
+                           else np.asarray(inputs["group_bias"], dtype=np.float32), keep)
+        w.expert_bias = ptr(None if inputs.get("expert_bias") is None
+                            else np.asarray(inputs["expert_bias"], dtype=np.float32), keep)
         for p, b in enumerate(inputs["base"]):
-            w.base[p] = _host_ptr(b, keep)
+            w.base[p] = ptr(b, keep)
         for p, a in enumerate(inputs.get("A") or []):
-            w.A[p] = _host_ptr(a, keep)
+            w.A[p] = ptr(a, keep)
         for p, b in enumerate(inputs.get("B") or []):
-            w.B[p] = _host_ptr(b, keep)
+            w.B[p] = ptr(b, keep)
         self.cfg = cfg
         self.E = cfg.G * cfg.K
         self.k = cfg.top_groups * cfg.top_experts
@@ -190,6 +208,30 @@ class Layer:
         check(lib.moe_forward(self.h, C.c_void_p(X.data_ptr()), T, C.c_void_p(Y.data_ptr()),
                               rop, _stream_ptr(stream)))
         return Y
+
+    def stats(self) -> dict:
+        st = moe_stats()
+        check(lib.moe_stats(self.h, C.byref(st)))
+        return dict(stored_params=st.stored_params, stored_bytes=st.stored_bytes,
+                    dense_equiv_params=st.dense_equiv_params)
+
+    def _factor_rows(self, proj: int, which: int) -> int:
+        d, f = self.cfg.d, self.cfg.f
+        P = 3 if self.cfg.act == ACT["swiglu"] else 2
+        din, dout = (d, f) if proj < P - 1 else (f, d)
+        return din if which == 0 else dout
+
+    def debug_dequant(self, proj: int, which: int, expert: int) -> np.ndarray:
+        vals = np.zeros((self._factor_rows(proj, which), self.cfg.r), dtype=np.float32)
+        check(lib.moe_debug_dequant(self.h, proj, which, expert, vals.ctypes.data))
+        return vals
+
+    def debug_q(self, proj: int, which: int, expert: int):
+        n, r = self._factor_rows(proj, which), self.cfg.r
+        q = np.zeros((n, r), dtype=np.int8)
+        sc = np.zeros((n // 32, r), dtype=np.uint16)
+        check(lib.moe_debug_q(self.h, proj, which, expert, q.ctypes.data, sc.ctypes.data))
+        return q, sc
 
     def debug_residual(self, proj: int, which: int, expert: int):
         """(values float32 [n, r], q int8 [n, r], scale fp16 bits [n/32, r])."""

@@ -52,10 +52,31 @@ constexpr int kStages = 7;
 
 }  // namespace
 
+
+// Workspace of one forward pass, carved out of one device buffer for a
+// capacity of T_cap tokens (the handle's own buffer is carved once for
+// T_max).  Only the per-chunk counters cc must be zero when
+// a pass starts; every other piece is written before it is read.
+struct Workspace {
+  long T_cap = 0;
+  int *idx = nullptr, *gidx = nullptr, *counts = nullptr, *offsets = nullptr;
+  int *gcounts = nullptr, *goffsets = nullptr, *garow = nullptr, *garow_sorted = nullptr;
+  int* cc = nullptr;  // per-chunk counters: [nch_e_max][E] then [nch_g_max][G]
+  int nch_e_max = 0, nch_g_max = 0, cc_n = 0;
+  uint16_t* X16 = nullptr;  // fp16 copy of bf16 activations (fp16 MFMAs)
+  float* w = nullptr;
+  float* L = nullptr;   // router scores (k-split partials)
+  void* U = nullptr;    // [T*kg][NU]
+  float* V = nullptr;   // [T*kg][NV]
+  float* Vp = nullptr;  // [G1 column tiles][T_cap*kg][ke][16]
+  int nt1k = 0;         // column tiles of the k-split G1 (0: its partials do not fit)
+  void* H = nullptr;    // [T*kg][f]
+  float* ypart = nullptr;
+};
+
 struct moe_handle {
   moe_config cfg{};
   int E = 0, k = 0, P = 0, P_in = 0, mma = 0, NU = 0, NV = 0;
-  int nch_e_max = 0, nch_g_max = 0;
   int device = 0;
   bool dirty = false;
   // weights
@@ -66,23 +87,8 @@ struct moe_handle {
   void *W1 = nullptr, *W2 = nullptr, *At = nullptr, *B1 = nullptr, *Ad = nullptr, *Bd = nullptr;
   uint16_t *At_s = nullptr, *B1_s = nullptr, *Ad_s = nullptr, *Bd_s = nullptr;
   long w1_gs = 0, w2_gs = 0, at_gs = 0, at_sgs = 0, bd_gs = 0;
-  // workspace
-  int *idx = nullptr, *gidx = nullptr, *counts = nullptr, *offsets = nullptr, *perm = nullptr;
-  int *gcounts = nullptr, *goffsets = nullptr, *gperm = nullptr, *garow = nullptr, *cc = nullptr;
-  int* garow_sorted = nullptr;  // garow with each group's rows sorted by expert set
-  uint16_t* X16 = nullptr;      // fp16 copy of bf16 activations (fp16 MFMAs)
-  float* w = nullptr;
-  int cc_n = 0;
-  // where the last routing pass left the lists the GEMMs read
-  int *gcounts_live = nullptr, *goffsets_live = nullptr, *idx_live = nullptr;
-  float* w_live = nullptr;
-  void* U = nullptr;
-  float* V = nullptr;
-  float* Vp = nullptr;
+  Workspace ws;         // the handle's own workspace, carved for T_max
   int nt1 = 0;          // column tiles of gemm1 (partials of V per row)
-  int* gidx_live = nullptr;
-  void* H = nullptr;
-  float* ypart = nullptr;
   std::vector<void*> allocs;
   int64_t weight_bytes = 0;
   // tile rows and stage depth per GEMM (0 = chosen per call); set from the
@@ -93,7 +99,6 @@ struct moe_handle {
   int g1k_env = -1;  // CEFN_G1K: 1 / 0 forces the k-split tiles of G1 on / off
   int ut_env = -1;   // CEFN_UT: 1 / 0 forces the tile-engine U GEMM on / off
   int gsort_env = -1;  // CEFN_GSORT: 1 / 0 forces the per-group row sort on / off
-  int nt1k = 0;      // column tiles of the k-split G1 (0: its partials do not fit)
   // profiling
   bool prof = false;
   int prof_max = 0, prof_calls = 0, prof_mask = -1;
@@ -150,7 +155,7 @@ void dims(const moe_config& c, int p, int& din, int& dout) {
   }
 }
 
-void compute_stats(const moe_config& c, moe_stats* s) {
+void compute_stats(const moe_config& c, moe_stats_t* s) {
   const int P = c.act == MOE_ACT_SWIGLU ? 3 : 2;
   const long E = (long)c.G * c.K;
   int64_t params = 0, dense = 0, bytes = 0;
@@ -168,6 +173,60 @@ void compute_stats(const moe_config& c, moe_stats* s) {
   s->stored_params = params;
   s->dense_equiv_params = dense;
   s->stored_bytes = bytes;
+}
+
+constexpr int kMaxSplits = 4;  // k splits of the down projection (ypart holds this many)
+
+// Lay the workspace for T tokens out from `base` (256-byte aligned pieces);
+// returns the bytes it spans.  base == nullptr only measures.
+size_t carve_workspace(const moe_handle* h, long T, char* base, Workspace* ws) {
+  const moe_config& c = h->cfg;
+  const long k = h->k, kg = c.top_groups;
+  const size_t es = elem_bytes(h->mma);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  *ws = Workspace{};
+  ws->T_cap = T;
+  ws->nch_e_max = (int)((T * k + CHUNK - 1) / CHUNK);
+  ws->nch_g_max = (int)((T * kg + CHUNK - 1) / CHUNK);
+  ws->cc_n = ws->nch_e_max * h->E + ws->nch_g_max * c.G;
+  ws->idx = reinterpret_cast<int*>(take(sizeof(int) * (T * k + 1)));
+  ws->w = reinterpret_cast<float*>(take(sizeof(float) * (T * k + 1)));
+  ws->gidx = reinterpret_cast<int*>(take(sizeof(int) * (T * kg + 1)));
+  ws->counts = reinterpret_cast<int*>(take(sizeof(int) * h->E));
+  ws->offsets = reinterpret_cast<int*>(take(sizeof(int) * (h->E + 1)));
+  ws->gcounts = reinterpret_cast<int*>(take(sizeof(int) * c.G));
+  ws->goffsets = reinterpret_cast<int*>(take(sizeof(int) * (c.G + 1)));
+  ws->garow = reinterpret_cast<int*>(take(sizeof(int) * (T * kg + 1)));
+  if (c.x_dtype == MOE_BF16 && h->mma == MOE_F16) ws->X16 = reinterpret_cast<uint16_t*>(take(2 * (T * c.d + 8)));
+  if (c.r > 0 && c.K > 1 && c.top_experts < c.K) ws->garow_sorted = reinterpret_cast<int*>(take(sizeof(int) * (T * kg + 1)));
+  ws->cc = reinterpret_cast<int*>(take(sizeof(int) * ((size_t)ws->cc_n + 1)));
+  {
+    // score buffer: the largest nsplit * T over the batch sizes up to T
+    long lmax = 0;
+    for (long t = 32; t < T + 32; t += 32) {
+      const long tt = std::min<long>(t, std::max<long>(T, 1));
+      lmax = std::max(lmax, router_splits((int)tt, c.d, h->NCp) * tt);
+    }
+    ws->L = reinterpret_cast<float*>(take(sizeof(float) * ((size_t)lmax * h->NCp + 4)));
+  }
+  if (c.r > 0) {
+    ws->U = take(T * kg * h->NU * es + 16);
+    ws->V = reinterpret_cast<float*>(take(sizeof(float) * (T * kg * h->NV + 4)));
+    // the k-split G1 writes one V partial per 64 columns: room for those
+    // when it stays under 256 MiB (the layouts that use it have few rows)
+    const int nt1k = h->P_in * c.f / 64;
+    const size_t per_tile = (size_t)T * kg * c.top_experts * RPAD;
+    ws->nt1k = per_tile * nt1k * sizeof(float) <= ((size_t)256 << 20) ? nt1k : 0;
+    ws->Vp = reinterpret_cast<float*>(take(sizeof(float) * ((size_t)std::max(h->nt1, ws->nt1k) * per_tile + 4)));
+  }
+  ws->H = take(T * kg * (long)c.f * es + 16);
+  ws->ypart = reinterpret_cast<float*>(take(sizeof(float) * ((size_t)kMaxSplits * T * kg * c.d + 4)));
+  return off;
 }
 
 template <class T>
@@ -407,8 +466,6 @@ int build_weights(moe_handle* h, const moe_weights* w) {
   return MOE_OK;
 }
 
-constexpr int kMaxSplits = 4;  // k splits of the down projection (ypart holds this many)
-
 // Token rows per tile for a grouped GEMM with `rows` rows and `ntiles`
 // column tiles of 256.  Bigger tiles reuse each weight fragment over more
 // tokens (fewer bytes per MFMA) but give fewer workgroups; the estimate
@@ -526,19 +583,71 @@ int hip_fail(moe_handle* h, hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Weights handed over as device pointers: read every array back into host
+// buffers (owned by `store`) and point a host-side copy of the struct at them,
+// so the packing below has one source form.
+int weights_to_host(const moe_config& c, const moe_weights* w, moe_weights* hw,
+                    std::vector<std::vector<char>>& store) {
+  *hw = *w;
+  hw->on_device = 0;
+  const int P = c.act == MOE_ACT_SWIGLU ? 3 : 2;
+  const long E = (long)c.G * c.K;
+  auto pull = [&](const void* src, size_t bytes, const void** dst) -> int {
+    if (!src) {
+      *dst = nullptr;
+      return MOE_OK;
+    }
+    store.emplace_back(bytes);
+    if (hipMemcpy(store.back().data(), src, bytes, hipMemcpyDeviceToHost) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MOE_ERR_INVALID_ARG, "on_device weights: copy from device failed (not a device pointer?)");
+    }
+    *dst = store.back().data();
+    return MOE_OK;
+  };
+  const void* t = nullptr;
+  TRY(pull(w->W_grp, sizeof(float) * c.d * c.G, &t));
+  hw->W_grp = static_cast<const float*>(t);
+  TRY(pull(c.K > 1 ? w->W_exp : nullptr, sizeof(float) * c.G * (size_t)c.d * c.K, &t));
+  hw->W_exp = static_cast<const float*>(t);
+  TRY(pull(w->group_bias, sizeof(float) * c.G, &t));
+  hw->group_bias = static_cast<const float*>(t);
+  TRY(pull(c.K > 1 ? w->expert_bias : nullptr, sizeof(float) * E, &t));
+  hw->expert_bias = static_cast<const float*>(t);
+  const size_t rb = c.resid == MOE_RESID_F16 ? 2 : 4;
+  for (int p = 0; p < P; ++p) {
+    int di, dn;
+    dims(c, p, di, dn);
+    TRY(pull(w->base[p], (size_t)c.G * di * dn * elem_bytes(c.base_dtype), &hw->base[p]));
+    if (c.r > 0) {
+      TRY(pull(w->A[p], (size_t)E * di * c.r * rb, &hw->A[p]));
+      TRY(pull(w->B[p], (size_t)E * dn * c.r * rb, &hw->B[p]));
+    } else {
+      hw->A[p] = hw->B[p] = nullptr;
+    }
+  }
+  return MOE_OK;
+}
+
 // router + scatter into the workspace (and the caller's buffers where given)
-int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, bool need_experts, hipStream_t st,
-              Prof& pf) {
+// Where the routing pass left the lists the GEMMs read.
+struct RouteLive {
+  int *gcounts, *goffsets, *idx, *gidx;
+  float* w;
+};
+
+int run_route(moe_handle* h, Workspace& ws, const void* X, int T, const moe_route_out* ro, bool need_experts,
+              hipStream_t st, Prof& pf, RouteLive& live) {
   const moe_config& c = h->cfg;
   hipError_t e;
-  if (h->dirty) {
-    e = launch_zero(h->cc, h->cc_n, st);
+  if (h->dirty && &ws == &h->ws) {
+    e = launch_zero(ws.cc, ws.cc_n, st);
     if (e != hipSuccess) return hip_fail(h, e, "clear counters");
     h->dirty = false;
   }
-  int* idx = (ro && ro->idx) ? ro->idx : h->idx;
-  float* wts = (ro && ro->w) ? ro->w : h->w;
-  int* gidx = (ro && ro->gidx) ? ro->gidx : h->gidx;
+  int* idx = (ro && ro->idx) ? ro->idx : ws.idx;
+  float* wts = (ro && ro->w) ? ro->w : ws.w;
+  int* gidx = (ro && ro->gidx) ? ro->gidx : ws.gidx;
   RouteArgs ra{};
   ra.X = X;
   ra.T = T;
@@ -552,15 +661,15 @@ int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, bool
   ra.Wr = h->Wr;
   ra.Wb = h->Wb;
   ra.NCp = h->NCp;
-  ra.L = h->L;
+  ra.L = ws.L;
   ra.nsplit = router_splits(T, c.d, h->NCp);
   ra.gbias = h->gbias;
   ra.ebias = h->ebias;
   ra.idx = idx;
   ra.w = wts;
   ra.gidx = gidx;
-  ra.ccount = h->cc;
-  ra.cgcount = h->cc + (size_t)h->nch_e_max * h->E;
+  ra.ccount = ws.cc;
+  ra.cgcount = ws.cc + (size_t)ws.nch_e_max * h->E;
   // the forward pass needs only the group lists; expert-level counts,
   // offsets and perm are built when the caller asks for routing outputs
   ra.count_experts = need_experts ? 1 : 0;
@@ -580,24 +689,24 @@ int run_route(moe_handle* h, const void* X, int T, const moe_route_out* ro, bool
   sa.cgcount = ra.cgcount;
   sa.nch_e = (int)(((long)T * h->k + CHUNK - 1) / CHUNK);
   sa.nch_g = (int)(((long)T * c.top_groups + CHUNK - 1) / CHUNK);
-  sa.counts = (ro && ro->counts) ? ro->counts : h->counts;
-  sa.offsets = (ro && ro->offsets) ? ro->offsets : h->offsets;
+  sa.counts = (ro && ro->counts) ? ro->counts : ws.counts;
+  sa.offsets = (ro && ro->offsets) ? ro->offsets : ws.offsets;
   sa.perm = (ro && ro->perm) ? ro->perm : nullptr;
-  sa.gcounts = (ro && ro->gcounts) ? ro->gcounts : h->gcounts;
-  sa.goffsets = (ro && ro->goffsets) ? ro->goffsets : h->goffsets;
+  sa.gcounts = (ro && ro->gcounts) ? ro->gcounts : ws.gcounts;
+  sa.goffsets = (ro && ro->goffsets) ? ro->goffsets : ws.goffsets;
   sa.gperm = (ro && ro->gperm) ? ro->gperm : nullptr;
-  sa.garow = h->garow;
+  sa.garow = ws.garow;
   sa.do_experts = ra.count_experts;
   pf.begin(1);
   e = launch_scatter(sa, st);
   if (e != hipSuccess) return hip_fail(h, e, "scatter launch");
   pf.end(1);
   // the GEMMs read the group lists from wherever the scatter put them
-  h->gcounts_live = sa.gcounts;
-  h->goffsets_live = sa.goffsets;
-  h->idx_live = idx;
-  h->w_live = wts;
-  h->gidx_live = gidx;
+  live.gcounts = sa.gcounts;
+  live.goffsets = sa.goffsets;
+  live.idx = idx;
+  live.w = wts;
+  live.gidx = gidx;
   return MOE_OK;
 }
 
@@ -607,19 +716,26 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
 
-int moe_config_stats(const moe_config* cfg, moe_stats* out) {
+int moe_config_stats(const moe_config* cfg, moe_stats_t* out) {
   TRY(validate(cfg));
   if (!out) return fail(MOE_ERR_INVALID_ARG, "null stats");
   compute_stats(*cfg, out);
   return MOE_OK;
 }
 
-int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_handle** out) {
+int moe_create(const moe_config* cfg, const moe_weights* wts, void* stream, moe_handle** out) {
   (void)stream;
   TRY(validate(cfg));
-  if (!w || !out) return fail(MOE_ERR_INVALID_ARG, "null weights or output handle");
+  if (!wts || !out) return fail(MOE_ERR_INVALID_ARG, "null weights or output handle");
   *out = nullptr;
   const moe_config& c = *cfg;
+  moe_weights host_w;
+  std::vector<std::vector<char>> host_store;
+  const moe_weights* w = wts;
+  if (wts->on_device) {
+    TRY(weights_to_host(c, wts, &host_w, host_store));
+    w = &host_w;
+  }
   const int P = c.act == MOE_ACT_SWIGLU ? 3 : 2;
   if (!w->W_grp) return fail(MOE_ERR_INVALID_ARG, "W_grp is required");
   if (c.K > 1 && !w->W_exp) return fail(MOE_ERR_INVALID_ARG, "W_exp is required when K > 1");
@@ -703,57 +819,18 @@ int moe_create(const moe_config* cfg, const moe_weights* w, void* stream, moe_ha
     return rc;
   }
 
-  // workspace
-  const long T = c.T_max, k = h->k, kg = c.top_groups;
-  const size_t es = elem_bytes(h->mma);
-  h->nch_e_max = (int)((T * k + CHUNK - 1) / CHUNK);
-  h->nch_g_max = (int)((T * kg + CHUNK - 1) / CHUNK);
-  h->cc_n = h->nch_e_max * h->E + h->nch_g_max * c.G;
-  auto ws = [&]() -> int {
-    TRY(dalloc(h.get(), &h->idx, T * k + 1));
-    TRY(dalloc(h.get(), &h->w, T * k + 1));
-    TRY(dalloc(h.get(), &h->gidx, T * kg + 1));
-    TRY(dalloc(h.get(), &h->counts, h->E));
-    TRY(dalloc(h.get(), &h->offsets, h->E + 1));
-    TRY(dalloc(h.get(), &h->gcounts, c.G));
-    TRY(dalloc(h.get(), &h->goffsets, c.G + 1));
-    TRY(dalloc(h.get(), &h->garow, T * kg + 1));
-    if (c.x_dtype == MOE_BF16 && h->mma == MOE_F16) TRY(dalloc(h.get(), &h->X16, T * (long)c.d + 8));
-    if (c.r > 0 && c.K > 1 && c.top_experts < c.K) TRY(dalloc(h.get(), &h->garow_sorted, T * kg + 1));
-    TRY(dalloc(h.get(), &h->cc, (size_t)h->cc_n + 1));
-    {
-      // score buffer: the largest nsplit * T over the batch sizes up to T_max
-      long lmax = 0;
-      for (long t = 32; t < T + 32; t += 32) {
-        const long tt = std::min<long>(t, std::max<long>(T, 1));
-        lmax = std::max(lmax, router_splits((int)tt, c.d, h->NCp) * tt);
-      }
-      TRY(dalloc(h.get(), &h->L, (size_t)lmax * h->NCp + 4));
+  // workspace, one buffer carved for T_max tokens
+  h->nt1 = (h->P_in * c.f + 255) / 256;
+  {
+    char* buf = nullptr;
+    rc = dalloc(h.get(), &buf, carve_workspace(h.get(), c.T_max, nullptr, &h->ws));
+    if (rc) {
+      moe_destroy(h.release());
+      return rc;
     }
-    char* tmp = nullptr;
-    if (c.r > 0) {
-      TRY(dalloc(h.get(), &tmp, T * kg * h->NU * es + 16));
-      h->U = tmp;
-      TRY(dalloc(h.get(), &h->V, T * kg * h->NV + 4));
-      h->nt1 = (h->P_in * c.f + 255) / 256;
-      // the k-split G1 writes one V partial per 64 columns: room for those
-      // when it stays under 256 MiB (the layouts that use it have few rows)
-      const int nt1k = h->P_in * c.f / 64;
-      const size_t per_tile = (size_t)T * kg * c.top_experts * RPAD;
-      h->nt1k = per_tile * nt1k * sizeof(float) <= ((size_t)256 << 20) ? nt1k : 0;
-      TRY(dalloc(h.get(), &h->Vp, (size_t)std::max(h->nt1, h->nt1k) * per_tile + 4));
-    }
-    TRY(dalloc(h.get(), &tmp, T * kg * (long)c.f * es + 16));
-    h->H = tmp;
-    TRY(dalloc(h.get(), &h->ypart, (size_t)kMaxSplits * T * kg * c.d + 4));
-    return MOE_OK;
-  };
-  rc = ws();
-  if (rc) {
-    moe_destroy(h.release());
-    return rc;
+    carve_workspace(h.get(), c.T_max, buf, &h->ws);
   }
-  if (hipMemset(h->cc, 0, sizeof(int) * ((size_t)h->cc_n + 1)) != hipSuccess ||
+  if (hipMemset(h->ws.cc, 0, sizeof(int) * ((size_t)h->ws.cc_n + 1)) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     moe_destroy(h.release());
     return fail(MOE_ERR_HIP, "initialising the workspace failed");
@@ -778,24 +855,26 @@ int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out,
   hipStream_t st = static_cast<hipStream_t>(stream);
   Prof pf{h, st, -1};
   if (h->prof && h->prof_calls < h->prof_max) pf.call = h->prof_calls++;
-  TRY(run_route(h, X, T, out, true, st, pf));
-  hipError_t e = launch_zero(h->cc, h->cc_n, st);
+  RouteLive live{};
+  TRY(run_route(h, h->ws, X, T, out, true, st, pf, live));
+  hipError_t e = launch_zero(h->ws.cc, h->ws.cc_n, st);
   if (e != hipSuccess) return hip_fail(h, e, "clear counters");
   return MOE_OK;
 }
 
-int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_route_out* routing,
-                void* stream) {
-  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
+}  // extern "C"
+
+namespace {
+
+// The whole layer on workspace ws (T >= 1, arguments checked by the caller).
+// The last GEMM clears ws's counters again for the next pass.
+int forward_impl(moe_handle* h, Workspace& ws, const void* X, int T, void* Y, const moe_route_out* routing,
+                 hipStream_t st) {
   const moe_config& c = h->cfg;
-  if (T < 0 || T > c.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, c.T_max);
-  if (T == 0) return MOE_OK;
-  if (!X || !Y) return fail(MOE_ERR_INVALID_ARG, "null X or Y");
-  if (X == Y) return fail(MOE_ERR_INVALID_ARG, "X and Y may not alias");
-  hipStream_t st = static_cast<hipStream_t>(stream);
   Prof pf{h, st, -1};
   if (h->prof && h->prof_calls < h->prof_max) pf.call = h->prof_calls++;
-  TRY(run_route(h, X, T, routing, routing != nullptr, st, pf));
+  RouteLive live{};
+  TRY(run_route(h, ws, X, T, routing, routing != nullptr, st, pf, live));
 
   const int kg = c.top_groups;
   const int rows = T * kg;
@@ -806,18 +885,18 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   // more experts per group) and many rows (64 or more per group on
   // average); measured: large INT4 layer gemm1 395 -> 355 us, while on the
   // 4-expert fp16 layer the tile sort already suffices.
-  const int* garow = h->garow;
+  const int* garow = ws.garow;
   const bool gsorted =
-      h->garow_sorted && (h->gsort_env == 1 || (h->gsort_env != 0 && c.K >= 8 && rows >= 64L * c.G));
+      ws.garow_sorted && (h->gsort_env == 1 || (h->gsort_env != 0 && c.K >= 8 && rows >= 64L * c.G));
   if (gsorted) {
-    GroupSortArgs gs{h->garow, h->garow_sorted, h->goffsets_live, h->idx_live, c.G, c.K, kg, c.top_experts, h->k};
+    GroupSortArgs gs{ws.garow, ws.garow_sorted, live.goffsets, live.idx, c.G, c.K, kg, c.top_experts, h->k};
     hipError_t es = launch_group_sort(gs, rows, st);
     if (es != hipSuccess) return hip_fail(h, es, "group sort launch");
-    garow = h->garow_sorted;
+    garow = ws.garow_sorted;
   }
   GemmArgs ga{};
-  ga.gcounts = h->gcounts_live;
-  ga.goffsets = h->goffsets_live;
+  ga.gcounts = live.gcounts;
+  ga.goffsets = live.goffsets;
   ga.G = c.G;
   ga.K = c.K;
   ga.kg = kg;
@@ -830,16 +909,16 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   ga.f = c.f;
   ga.garow = garow;
   ga.rows_sorted = gsorted ? 1 : 0;
-  ga.idx = h->idx_live;
-  ga.w = h->w_live;
-  ga.U = h->U;
+  ga.idx = live.idx;
+  ga.w = live.w;
+  ga.U = ws.U;
   ga.NU = h->NU;
-  ga.V = h->V;
+  ga.V = ws.V;
   ga.NV = h->NV;
-  ga.Vp = h->Vp;
-  ga.vp_rows = (long)c.T_max * kg;
-  ga.H = h->H;
-  ga.ypart = h->ypart;
+  ga.Vp = ws.Vp;
+  ga.vp_rows = ws.T_cap * kg;
+  ga.H = ws.H;
+  ga.ypart = ws.ypart;
   ga.Y = Y;
   ga.ksplit = 1;
   ga.rows_total = (long)rows;
@@ -850,10 +929,10 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   // in one pass, instead of converting every staged row in their loaders
   const void* xg = X;
   int xt = c.x_dtype;
-  if (h->X16) {
-    e = launch_cvt_x(X, h->X16, (long)T * c.d, st);
+  if (ws.X16) {
+    e = launch_cvt_x(X, ws.X16, (long)T * c.d, st);
     if (e != hipSuccess) return hip_fail(h, e, "activation conversion launch");
-    xg = h->X16;
+    xg = ws.X16;
     xt = MOE_F16;
   }
   if (c.r > 0) {
@@ -896,7 +975,7 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     // wavefronts, when the 256-column tiling at 32 rows has under half a
     // round of workgroups (measured: tiny layers gain, the decode layer's
     // 132 tiles do not)
-    const bool k_ok = c.r == 0 || h->nt1k > 0;
+    const bool k_ok = c.r == 0 || ws.nt1k > 0;
     g1k = k_ok && (h->g1k_env == 1 || (h->g1k_env != 0 && h->bm_env[GK_G1] == 0 && bm == 32 &&
                                         (long)max_mtiles(T, kg, c.G, 32) * nt < 128));
     pf.begin(3);
@@ -909,14 +988,14 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   }
   if (c.r > 0) {
     VReduceArgs va{};
-    va.Vp = h->Vp;
-    va.V = h->V;
+    va.Vp = ws.Vp;
+    va.V = ws.V;
     va.garow = garow;
-    va.gidx = h->gidx_live;
-    va.idx = h->idx_live;
-    va.vp_rows = (long)c.T_max * kg;
+    va.gidx = live.gidx;
+    va.idx = live.idx;
+    va.vp_rows = ws.T_cap * kg;
     va.rows = rows;
-    va.ntiles = g1k ? h->nt1k : h->nt1;
+    va.ntiles = g1k ? ws.nt1k : h->nt1;
     va.NV = h->NV;
     va.K = c.K;
     va.kg = kg;
@@ -934,8 +1013,8 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     g2.Bd = h->Bd;
     g2.bd_gstride = h->bd_gs;
     g2.bd_scale = h->Bd_s;
-    g2.zero_ptr = h->cc;
-    g2.zero_n = h->cc_n;
+    g2.zero_ptr = ws.cc;
+    g2.zero_n = ws.cc_n;
     const int nt = (c.d + 255) / 256;
     // 256-column tiles with the rows staged through LDS and the k range split
     // over workgroups; the variant that splits f inside each workgroup over
@@ -955,7 +1034,7 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
     pf.end(5);
   }
   if (kg > 1 || splits > 1) {
-    CombineArgs ca{h->ypart, Y, T, c.d, kg, splits};
+    CombineArgs ca{ws.ypart, Y, T, c.d, kg, splits};
     pf.begin(6);
     e = launch_combine(c.x_dtype, ca, st);
     if (e != hipSuccess) return hip_fail(h, e, "combine launch");
@@ -963,6 +1042,24 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   }
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_route_out* routing,
+                void* stream) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
+  const moe_config& c = h->cfg;
+  if (T < 0 || T > c.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, c.T_max);
+  // no tokens: nothing to compute, but the routing outputs still say so
+  if (T == 0) return routing ? moe_route(h, X, 0, routing, stream) : MOE_OK;
+  if (!X || !Y) return fail(MOE_ERR_INVALID_ARG, "null X or Y");
+  if (X == Y) return fail(MOE_ERR_INVALID_ARG, "X and Y may not alias");
+  return forward_impl(h, h->ws, X, T, Y, routing, static_cast<hipStream_t>(stream));
+}
+
+
 
 int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t expert, float* values,
                        int8_t* q, uint16_t* scale_bits) {
@@ -1047,6 +1144,26 @@ int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t exper
     }
   }
   return MOE_OK;
+}
+
+int moe_stats(const moe_handle* h, moe_stats_t* out) {
+  if (!h || !out) return fail(MOE_ERR_INVALID_ARG, "null handle or stats");
+  compute_stats(h->cfg, out);
+  return MOE_OK;
+}
+
+int moe_debug_dequant(moe_handle* h, int32_t proj, int32_t which, int32_t expert, float* host_out) {
+  return moe_debug_residual(h, proj, which, expert, host_out, nullptr, nullptr);
+}
+
+int moe_debug_q(moe_handle* h, int32_t proj, int32_t which, int32_t expert, int8_t* q, uint16_t* scale_bits) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
+  if (h->cfg.resid != MOE_RESID_INT4_G32) return fail(MOE_ERR_INVALID_ARG, "layer residual is not INT4");
+  if (proj < 0 || proj >= h->P) return fail(MOE_ERR_INVALID_ARG, "bad residual selector");
+  int di, dn;
+  dims(h->cfg, proj, di, dn);
+  std::vector<float> vals((size_t)(which == 0 ? di : dn) * h->cfg.r);
+  return moe_debug_residual(h, proj, which, expert, vals.data(), q, scale_bits);
 }
 
 int moe_profile_begin(moe_handle* h, int32_t max_calls, int32_t stage_mask) {

@@ -72,9 +72,10 @@ typedef enum {
 
 typedef enum { MOE_ACT_GELU_TANH = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 
-/* Layer shape.  Supported: 1 <= G, 1 <= K, G*K <= 1024; 1 <= top_groups <=
- * min(G, 8); 1 <= top_experts <= K; top_groups*top_experts <= 16; d and f
- * multiples of 64; r in {0} or 1..16 (r = 0 iff resid == MOE_RESID_NONE);
+/* Layer shape.  Supported: 1 <= G <= 256, 1 <= K <= 256, G*K <= 1024, and
+ * K <= 64 when r > 0; 1 <= top_groups <= min(G, 8); 1 <= top_experts <= K;
+ * top_groups*top_experts <= 16; d and f multiples of 64; r in {0} or 1..16
+ * (r = 0 iff resid == MOE_RESID_NONE);
  * dtype mixes (x, base): (F32, F32), (F16, F16), (BF16, BF16), (BF16, F16)
  * -- bf16 activations are converted to fp16 for an fp16 base; residual F32
  * needs an F32 base, F16 an F16 base, INT4_G32 an F16 or BF16 base. */
@@ -93,10 +94,13 @@ typedef struct {
   int32_t resid;       /* moe_resid */
 } moe_config;
 
-/* Weights, all HOST pointers, row-major, read only during moe_create (the
- * caller keeps ownership).  Projections in order (gate, up, down) for
- * SwiGLU, (w1, w2) for GELU; d_in x d_out is d x f for the input
- * projections and f x d for the output projection.
+/* Weights, row-major, read only during moe_create (the caller keeps
+ * ownership).  on_device = 0: every pointer is a HOST pointer; on_device = 1:
+ * every pointer is a DEVICE pointer on the current HIP device (moe_create
+ * reads them back before packing, so they may be freed once it returns).
+ * Projections in order (gate, up, down) for SwiGLU, (w1, w2) for GELU;
+ * d_in x d_out is d x f for the input projections and f x d for the output
+ * projection.
  *   W_grp       float32 [d][G]
  *   W_exp       float32 [G][d][K]     (ignored, may be NULL, when K == 1)
  *   group_bias  float32 [G]           (NULL = zeros)
@@ -114,6 +118,7 @@ typedef struct {
   const void* base[3];
   const void* A[3];
   const void* B[3];
+  int32_t on_device;
 } moe_weights;
 
 /* Routing outputs, caller-owned DEVICE buffers (any may be NULL to skip it):
@@ -143,7 +148,7 @@ typedef struct {
   int64_t stored_params;      /* G*sum_p d_in*d_out + E*r*sum_p (d_in + d_out) */
   int64_t stored_bytes;       /* expert weights as stored on the device */
   int64_t dense_equiv_params; /* E*sum_p d_in*d_out */
-} moe_stats;
+} moe_stats_t;
 
 typedef struct moe_handle moe_handle;
 
@@ -163,8 +168,9 @@ int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out,
 /* The whole layer: Y = sum over the selected experts of gate weight times
  * expert FFN.  X, Y: device [T][d] in x_dtype (may not alias).  routing may
  * be NULL; otherwise its non-NULL fields receive the routing as in
- * moe_route.  Enqueue only: no allocation, no host synchronisation.  One
- * handle is not re-entrant: calls on it must be ordered (one stream). */
+ * moe_route (T = 0 included: zero counts and offsets).  Enqueue only: no
+ * allocation, no host synchronisation.  One handle is not re-entrant: calls
+ * on it must be ordered (one stream). */
 int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y,
                 const moe_route_out* routing, void* stream);
 
@@ -178,11 +184,29 @@ const char* moe_last_error(void);
 /* Stored parameter and byte counts for a configuration; touches no device.
  * The count follows the compressed-expert form: one base per group and
  * projection, rank-r factors per expert. */
-int moe_config_stats(const moe_config* cfg, moe_stats* out);
+int moe_config_stats(const moe_config* cfg, moe_stats_t* out);
+
+/* The same counts for a created layer. */
+int moe_stats(const moe_handle* h, moe_stats_t* out);
 
 /* ---- test and measurement exports -------------------------------------- */
 
-/* Read back one residual factor as stored on the device: projection p,
+/* Dequantised values of one residual factor as the kernels use them:
+ * projection p, which = 0 for A (d_in x r) or 1 for B (d_out x r), expert
+ * i; host_out (host, [n][r] float32, n = d_in or d_out).  For INT4 each
+ * value is float(q) * float(scale), exact in FP32, decoded on the device by
+ * the routine the GEMM kernels call (the GEMMs round it once more to their
+ * 16-bit MFMA type).  Synchronous. */
+int moe_debug_dequant(moe_handle* h, int32_t proj, int32_t which, int32_t expert, float* host_out);
+
+/* INT4 codes and scales of the same factor as stored: q (host int8 [n][r],
+ * values in [-8, 7]) and scale_bits (host uint16 [n/32][r], fp16 bits); either
+ * may be NULL.  MOE_ERR_INVALID_ARG for a layer whose residual is not INT4.
+ * Synchronous. */
+int moe_debug_q(moe_handle* h, int32_t proj, int32_t which, int32_t expert, int8_t* q,
+                uint16_t* scale_bits);
+
+/* Both of the above in one call: projection p,
  * which = 0 for A (d_in x r) or 1 for B (d_out x r), expert i.  values
  * (host, [n][r] float32) receives the value the kernels use, decoded on
  * the device by the same routine the GEMM kernels call.  For INT4, q (host

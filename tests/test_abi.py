@@ -97,3 +97,14 @@ def test_null_arguments():
     cfg = L.make_config(8, 64, 128, 2, 4, 1, 2, 4, "swiglu", "f16", "f16", "f16")
     h = C.c_void_p()
     assert L.lib.moe_create(C.byref(cfg), None, None, C.byref(h)) == L.MOE_ERR_INVALID_ARG
+
+
+def test_handle_calls_reject_null():
+    assert L.lib.moe_stats(None, None) == L.MOE_ERR_INVALID_ARG
+    assert L.lib.moe_debug_dequant(None, 0, 0, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert L.lib.moe_debug_q(None, 0, 0, 0, None, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_weights_struct_matches_header_layout():
+    # nine pointers of weights, then the on_device flag
+    assert L.moe_weights.on_device.offset == 4 * 8 + 9 * 8

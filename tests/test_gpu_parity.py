@@ -36,6 +36,8 @@ def check_routing(got: dict, rt: dict, w, T: int):
     assert np.array_equal(got["idx"], rt["idx"]), "expert indices differ"
     assert np.array_equal(got["gidx"], rt["gidx"]), "group indices differ"
     assert np.abs(got["w"] - rt["w"]).max(initial=0.0) <= gate_tol(w.d)
+    # the FP32 gate weights of a token sum to 1 to FP32 accuracy
+    assert np.abs(got["w"].astype(np.float64).sum(axis=1) - 1.0).max(initial=0.0) <= 1e-6
     counts, offsets, perm = O.permutation(rt["idx"], E)
     assert np.array_equal(got["counts"], counts)
     assert np.array_equal(got["offsets"], offsets)
@@ -194,14 +196,10 @@ def test_repeated_calls_and_different_T_on_one_handle():
             check_routing(route_to_host(bufs), sub, dataclasses.replace(wT, T=T), T)
             assert rel_err(y, ref[:T]) <= TOL[w.x_dtype]
             ys.append(y)
-        # same input twice: identical routing (checked above); outputs may
-        # differ by the order of the fp32 atomics that accumulate h A_down:
-        # an absolute reordering error far below the output scale, which can
-        # move a value across one rounding boundary of the bf16 output
-        a, b = ys[0], ys[2]
-        scale = np.abs(ref).max()
-        bound = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-5 * scale
-        assert (np.abs(a - b) <= bound).all(), float((np.abs(a - b) - bound).max())
+        # same input twice: identical routing (checked above) and identical
+        # outputs, bit for bit (every sum runs in a fixed order: no float
+        # atomics anywhere on the path)
+        assert np.array_equal(ys[0].view(np.uint64), ys[2].view(np.uint64))
     finally:
         lay.close()
 

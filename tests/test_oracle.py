@@ -31,6 +31,55 @@ def small_layer(seed=1, **kw):
     return w, oracle_layer(w, synth.make_layer(w, seed=seed))
 
 
+# ------------------------------------------------------------- decoding
+def _bf16_value(bits: int) -> float:
+    """bf16 value from its 16 bits by the format's definition (1 sign bit,
+    8 exponent bits with bias 127, 7 fraction bits), in pure Python."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e, m = (bits >> 7) & 0xFF, bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if m == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(m, -126 - 7)
+    return sign * math.ldexp(128 + m, e - 127 - 7)
+
+
+def test_bf16_decode_hand_values():
+    """Stored bf16 bit patterns decode to the values the format fixes."""
+    cases = {
+        0x3F80: 1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x3E80: 0.25,
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,    # largest finite
+        0x0080: 2.0 ** -126,                          # smallest normal
+        0x0001: 2.0 ** -133,                          # smallest subnormal
+        0x807F: -(127 * 2.0 ** -133),                 # largest negative subnormal
+        0x0000: 0.0, 0xFF80: -math.inf,
+    }
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = O.as_f64(bits, "bf16")
+    assert got.dtype == np.float64
+    for b, v, g in zip(cases, cases.values(), got):
+        assert g == v and _bf16_value(b) == v, hex(b)
+    # every finite pattern against the format definition
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = ((allb >> 7) & 0xFF) != 0xFF
+    ref = np.array([_bf16_value(int(b)) for b in allb[fin][::97]])
+    assert (O.as_f64(allb[fin][::97], "bf16") == ref).all()
+    # storing rounds to nearest, ties to even: 1 + 2^-8 lies halfway between
+    # 1 and 1 + 2^-7 (even fraction wins), 1 + 3*2^-8 halfway between
+    # 1 + 2^-7 and 1 + 2^-6 (the latter has the even fraction)
+    f = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -(1 + 2.0 ** -8)],
+                 dtype=np.float32)
+    st = synth.f32_to_bf16_bits(f)
+    assert list(O.as_f64(st, "bf16")) == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0]
+
+
+def test_fp16_and_fp32_decode_hand_values():
+    h = np.array([0x3C00, 0xC000, 0x7BFF, 0x0001, 0x0400], dtype=np.uint16).view(np.float16)
+    assert list(O.as_f64(h, "f16")) == [1.0, -2.0, 65504.0, 2.0 ** -24, 2.0 ** -14]
+    f = np.array([0x3F800000, 0x00000001], dtype=np.uint32).view(np.float32)
+    assert list(O.as_f64(f, "f32")) == [1.0, 2.0 ** -149]
+
+
 # ------------------------------------------------------------------ routing
 @pytest.mark.parametrize("G,K,kg,ke", [(2, 4, 1, 2), (4, 4, 2, 3), (8, 1, 2, 1), (3, 5, 3, 5), (16, 16, 2, 4)])
 def test_gate_weights_sum_to_one(G, K, kg, ke):
@@ -334,6 +383,56 @@ def test_scalar_bruteforce_tiny(act, kg):
                 z = vecmat(x, wt(0, i))
                 h = [0.5 * v * (1 + math.tanh(math.sqrt(2 / math.pi) * (v + 0.044715 * v ** 3))) for v in z]
                 o = vecmat(h, wt(1, i))
+            y = [y[c] + gw * o[c] for c in range(w.d)]
+        assert np.allclose(Y[t], y, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("x_dtype,base_dtype", [("bf16", "bf16"), ("bf16", "f16"), ("f16", "f16")])
+def test_scalar_bruteforce_16bit_storage(x_dtype, base_dtype):
+    """The layer on 16-bit stored X and base, every stored value decoded by
+    the format definition in pure Python (bf16 bits above, fp16 through the
+    IEEE half layout), then scalar loops in float64."""
+    w = small_workload(G=2, K=3, kg=1, ke=2, r=2, d=6, f=5, T=5, act="swiglu", bias=0.3,
+                       x_dtype=x_dtype, base_dtype=base_dtype, resid="f16")
+    inputs = synth.make_layer(w, seed=12)
+    L = oracle_layer(w, inputs)
+    rt = O.route(L)
+    Y = O.forward(L, routing=rt)
+
+    def half_value(v) -> float:
+        b = int(np.asarray(v, dtype=np.float16).view(np.uint16))
+        sign = -1.0 if b >> 15 else 1.0
+        e, m = (b >> 10) & 0x1F, b & 0x3FF
+        return sign * (math.ldexp(m, -24) if e == 0 else math.ldexp(1024 + m, e - 25))
+
+    def dec(v, dt):
+        return _bf16_value(int(v)) if dt == "bf16" else half_value(v)
+
+    def wt(p, i):
+        bse, A, B = inputs["base"][p][i // w.K], inputs["A"][p][i], inputs["B"][p][i]
+        din, dout = bse.shape
+        return [[dec(bse[a][c], base_dtype) + sum(half_value(A[a][q]) * half_value(B[c][q])
+                                                  for q in range(w.r))
+                 for c in range(dout)] for a in range(din)]
+
+    def vecmat(v, M):
+        return [sum(v[a] * M[a][c] for a in range(len(v))) for c in range(len(M[0]))]
+
+    # routing from the decoded X with scalar loops: the chosen set must agree
+    Wg, We = inputs["W_grp"], inputs["W_exp"]
+    for t in range(w.T):
+        x = [dec(v, x_dtype) for v in inputs["X"][t]]
+        s = [sum(x[a] * float(Wg[a][g]) for a in range(w.d)) for g in range(w.G)]
+        g = max(range(w.G), key=lambda c: (s[c], -c))
+        e = [sum(x[a] * float(We[g][a][j]) for a in range(w.d)) for j in range(w.K)]
+        top = sorted(range(w.K), key=lambda j: (-e[j], j))[:w.top_experts]
+        assert [g * w.K + j for j in top] == list(rt["idx"][t])
+        y = [0.0] * w.d
+        for sl in range(w.k):
+            i, gw = int(rt["idx"][t, sl]), float(rt["w"][t, sl])
+            zg, zu = vecmat(x, wt(0, i)), vecmat(x, wt(1, i))
+            h = [zg[c] / (1 + math.exp(-zg[c])) * zu[c] for c in range(w.f)]
+            o = vecmat(h, wt(2, i))
             y = [y[c] + gw * o[c] for c in range(w.d)]
         assert np.allclose(Y[t], y, rtol=1e-12, atol=1e-12)
 

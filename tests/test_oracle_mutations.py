@@ -29,6 +29,8 @@ def _pins():
         (P.test_int4_layer_uses_dequantised_factors, ()),
         (P.test_int4_nearest_code_range_and_exact_dequant, ()),
         (P.test_int4_half_even_ties_hand_example, ()),
+        (P.test_bf16_decode_hand_values, ()),
+        (P.test_scalar_bruteforce_16bit_storage, ("bf16", "bf16")),
     ]
 
 
@@ -41,7 +43,21 @@ MUTATIONS = {
     "ties_to_higher_index": ("_desc_order", lambda s: (s.shape[-1] - 1) - np.argsort(-s[..., ::-1], axis=-1, kind="stable")),
     "softmax_without_max_shift_and_wrong_norm": ("_softmax", lambda v: np.exp(v) / np.exp(v).sum(axis=-1, keepdims=True) ** 0.5),
     "int4_round_half_away": ("quantize_int4_g32", None),
+    "bf16_scaled": ("as_f64", None),
+    "bf16_truncated_to_fp16_grid": ("as_f64", None),
 }
+
+_as_f64 = O.as_f64
+
+
+def _bf16_scaled(a, dtype):
+    v = _as_f64(a, dtype)
+    return v * 1.01 if dtype == "bf16" else v
+
+
+def _bf16_via_fp16(a, dtype):
+    v = _as_f64(a, dtype)
+    return v.astype(np.float16).astype(np.float64) if dtype == "bf16" else v
 
 
 def _int4_half_away(M):
@@ -62,6 +78,10 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     if name == "int4_round_half_away":
         fn = _int4_half_away
+    elif name == "bf16_scaled":
+        fn = _bf16_scaled
+    elif name == "bf16_truncated_to_fp16_grid":
+        fn = _bf16_via_fp16
     monkeypatch.setattr(O, attr, fn)
     caught = [p.__name__ for p, args in _pins() if _fails(p, *args)]
     assert caught, f"no pin caught the planted mistake {name}"
