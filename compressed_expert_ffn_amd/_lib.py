@@ -64,6 +64,7 @@ def _load():
         "moe_create": ([C.POINTER(moe_config), C.POINTER(moe_weights), P, C.POINTER(P)], C.c_int),
         "moe_route": ([P, P, C.c_int32, C.POINTER(moe_route_out), P], C.c_int),
         "moe_forward": ([P, P, C.c_int32, P, C.POINTER(moe_route_out), P], C.c_int),
+        "moe_forward_noalloc": ([P, P, C.c_int32, P, C.POINTER(moe_route_out), P], C.c_int),
         "moe_destroy": ([P], C.c_int),
         "moe_last_error": ([], C.c_char_p),
         "moe_config_stats": ([C.POINTER(moe_config), C.POINTER(moe_stats)], C.c_int),
@@ -232,6 +233,15 @@ class Layer:
         sc = np.zeros((n // 32, r), dtype=np.uint16)
         check(lib.moe_debug_q(self.h, proj, which, expert, q.ctypes.data, sc.ctypes.data))
         return q, sc
+
+    def forward_noalloc(self, X, Y, route_bufs=None, stream=None):
+        """moe_forward_noalloc: the workspace is the library's static device
+        array; Y must be given (nothing is allocated on this path)."""
+        ro = self._route_struct(route_bufs)
+        rop = C.byref(ro) if route_bufs is not None else None
+        check(lib.moe_forward_noalloc(self.h, C.c_void_p(X.data_ptr()), X.shape[0],
+                                      C.c_void_p(Y.data_ptr()), rop, _stream_ptr(stream)))
+        return Y
 
     def debug_residual(self, proj: int, which: int, expert: int):
         """(values float32 [n, r], q int8 [n, r], scale fp16 bits [n/32, r])."""

@@ -21,6 +21,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -52,10 +53,43 @@ constexpr int kStages = 7;
 
 }  // namespace
 
+// Workspace of the no-allocation forward pass (moe_forward_noalloc): one
+// array in every device's memory, held until the process ends.  Host code
+// never uses the name itself: on each device the array's address comes from
+// hipGetSymbolAddress (with that device current) and is kept per device.
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of this device's scratch array (looked up once per device, with
+// that device current).
+int scratch_for_device(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
 
 // Workspace of one forward pass, carved out of one device buffer for a
-// capacity of T_cap tokens (the handle's own buffer is carved once for
-// T_max).  Only the per-chunk counters cc must be zero when
+// capacity of T_cap tokens: the handle's own buffer (carved once for T_max)
+// or the static scratch array of the no-allocation entry point (carved per
+// call for that call's T).  Only the per-chunk counters cc must be zero when
 // a pass starts; every other piece is written before it is read.
 struct Workspace {
   long T_cap = 0;
@@ -754,6 +788,11 @@ int moe_create(const moe_config* cfg, const moe_weights* wts, void* stream, moe_
   h->NV = c.r > 0 ? (int)roundup((long)c.K * RPAD, 64) : 0;
   if (hipGetDevice(&h->device) != hipSuccess) return fail(MOE_ERR_HIP, "no HIP device");
   {
+    // set-up of the no-allocation entry point on this device
+    char* sp = nullptr;
+    TRY(scratch_for_device(h->device, &sp));
+  }
+  {
     const char* names[3] = {"U", "G1", "G2"};
     for (int i = 0; i < 3; ++i) {
       char key[32];
@@ -1059,6 +1098,31 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y, const moe_rout
   return forward_impl(h, h->ws, X, T, Y, routing, static_cast<hipStream_t>(stream));
 }
 
+int moe_forward_noalloc(moe_handle* h, const void* X, int32_t T, void* Y, const moe_route_out* routing,
+                        void* stream) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
+  const moe_config& c = h->cfg;
+  if (T < 0 || T > c.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, c.T_max);
+  if (T == 0) return routing ? moe_route(h, X, 0, routing, stream) : MOE_OK;
+  if (!X || !Y) return fail(MOE_ERR_INVALID_ARG, "null X or Y");
+  if (X == Y) return fail(MOE_ERR_INVALID_ARG, "X and Y may not alias");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "no HIP device");
+  if (dev != h->device) return fail(MOE_ERR_INVALID_ARG, "handle lives on device %d, device %d is current", h->device, dev);
+  char* base = nullptr;
+  TRY(scratch_for_device(dev, &base));
+  Workspace ws;
+  const size_t need = carve_workspace(h, T, nullptr, &ws);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_INVALID_ARG, "T=%d needs %zu bytes of workspace, more than the %zu of the static scratch",
+                T, need, kScratchBytes);
+  carve_workspace(h, T, base, &ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the array keeps whatever the last call left: the counters must start at zero
+  const hipError_t e = launch_zero(ws.cc, ws.cc_n, st);
+  if (e != hipSuccess) return hip_fail(h, e, "clear counters");
+  return forward_impl(h, ws, X, T, Y, routing, st);
+}
 
 
 int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t expert, float* values,

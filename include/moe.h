@@ -174,6 +174,22 @@ int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out,
 int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y,
                 const moe_route_out* routing, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, but the workspace is a static
+ * device array of 96 MiB per device (held until the process ends) instead
+ * of the handle's own, carved per call for this T.  It calls no hipMalloc,
+ * hipFree or other allocating routine.  A T whose workspace exceeds 96 MiB
+ * is rejected with MOE_ERR_INVALID_ARG (the message gives the bytes it
+ * needs); for scale, a d = 1024, f = 2816, top-2 layer needs about 66 MiB
+ * at T = 2048.  The handle's device must be current.  All calls on one
+ * device share the array: calls that overlap in time on one device (two
+ * streams, two threads, two handles) race and give wrong results; order
+ * them.  The counters it needs zeroed are cleared at the start of every
+ * call. */
+int moe_forward_noalloc(moe_handle* h, const void* X, int32_t T, void* Y,
+                        const moe_route_out* routing, void* stream);
+
 /* Free everything the handle owns (synchronises the device first).  NULL is
  * a no-op. */
 int moe_destroy(moe_handle* h);
