@@ -167,3 +167,57 @@ def make_layer(w: Workload, seed: int = DEFAULT_SEED, T: int | None = None,
         B.append(_normal_slices(seed, [(w.index, ID_B + p, e) for e in range(E)], (dout, r), 0.05, rdt))
     out["base"], out["A"], out["B"] = base, A, B
     return out
+
+
+# ------------------------------------------------- dense expert banks ----
+def make_expert_bank(E: int, G: int, proj_dims, rank: int, resid_scale: float = 0.3,
+                     noise_scale: float = 0.005, seed: int = DEFAULT_SEED, key: int = 0) -> dict:
+    """Dense experts with a planted group structure, standing in for the
+    trained experts a clustering pass would see (no trained weights here).
+
+    Expert i belongs to planted group c_i (E / G experts per group, in a
+    seeded random order of the indices).  Per projection of shape
+    (d_in, d_out): W_i = C_c + s_r U_c M_i V_c^T + s_n N_i, with the group
+    centre C_c, the group's rank-``rank`` subspaces U_c [d_in, rank] and
+    V_c [d_out, rank], the expert's mixing matrix M_i [rank, rank] and the
+    noise N_i all drawn N(0, 1); C is scaled to variance 1/d_in per entry,
+    the subspace part to about ``resid_scale`` and the noise to about
+    ``noise_scale`` of C's Frobenius norm.
+
+    Returns W (list over projections of float32 [E, d_in, d_out]) and
+    planted (int [E]).
+    """
+    rng = _rng(seed, 900 + key)
+    planted = rng.permutation(np.repeat(np.arange(G), E // G))
+    Ws = []
+    for p, (din, dout) in enumerate(proj_dims):
+        r = _rng(seed, 900 + key, p)
+        sd = 1.0 / math.sqrt(din)
+        C = r.standard_normal((G, din, dout)) * sd
+        U = r.standard_normal((G, din, rank))
+        V = r.standard_normal((G, dout, rank))
+        M = r.standard_normal((E, rank, rank))
+        N = r.standard_normal((E, din, dout))
+        s_r = resid_scale * sd / rank if rank else 0.0
+        s_n = noise_scale * sd
+        W = np.empty((E, din, dout))
+        for i in range(E):
+            c = planted[i]
+            W[i] = C[c] + s_r * (U[c] @ M[i] @ V[c].T) + s_n * N[i]
+        Ws.append(W.astype(np.float32))
+    return dict(W=Ws, planted=planted)
+
+
+def draw_group_tokens(planted, G: int, d: int, T: int, k: int, spread: float = 0.5,
+                      seed: int = DEFAULT_SEED, key: int = 0):
+    """Tokens and a routing that sends each token to k experts of one
+    planted group: x = g_c + spread * n for a random group c (g_c a random
+    direction per group, n ~ N(0, 1)).  Returns X float32 [T, d] and idx
+    int32 [T, k]."""
+    rng = _rng(seed, 950 + key)
+    dirs = rng.standard_normal((G, d))
+    c = rng.integers(0, G, size=T)
+    X = dirs[c] + spread * rng.standard_normal((T, d))
+    members = [np.nonzero(np.asarray(planted) == g)[0] for g in range(G)]
+    idx = np.stack([rng.choice(members[ci], size=k, replace=False) for ci in c])
+    return X.astype(np.float32), idx.astype(np.int32)
