@@ -43,6 +43,12 @@ class moe_stats(C.Structure):
                 ("dense_equiv_params", C.c_int64)]
 
 
+class moe_cluster_config(C.Structure):
+    _fields_ = [("E", C.c_int32), ("G", C.c_int32), ("d", C.c_int32), ("n_param", C.c_int64),
+                ("alpha", C.c_double), ("beta", C.c_double), ("tau", C.c_double), ("eps", C.c_double),
+                ("cache_life", C.c_int32)]
+
+
 class MoEError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"moe error {code}: {msg}")
@@ -72,6 +78,14 @@ def _load():
         "moe_debug_residual": ([P, C.c_int32, C.c_int32, C.c_int32, P, P, P], C.c_int),
         "moe_debug_dequant": ([P, C.c_int32, C.c_int32, C.c_int32, P], C.c_int),
         "moe_debug_q": ([P, C.c_int32, C.c_int32, C.c_int32, P, P], C.c_int),
+        "moe_cluster_create": ([C.POINTER(moe_cluster_config), C.POINTER(P)], C.c_int),
+        "moe_cluster_destroy": ([P], C.c_int),
+        "moe_cluster_get_centroids": ([P, P], C.c_int),
+        "moe_cluster_set_centroids": ([P, P], C.c_int),
+        "moe_cluster_observe": ([P, P, C.c_int32, P, C.c_int32], C.c_int),
+        "moe_cluster_regroup": ([P, P, P, P, P, P, P], C.c_int),
+        "moe_compress_projection": ([C.c_int32, C.c_int32, P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P, P,
+                                     C.c_int32], C.c_int),
         "moe_profile_begin": ([P, C.c_int32, C.c_int32], C.c_int),
         "moe_profile_end": ([P, P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                              C.c_char_p, C.c_int32], C.c_int),
@@ -280,3 +294,74 @@ class Layer:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------- clustering and compression --
+class Cluster:
+    """The host clustering state of include/moe_cluster.h (marshalling only)."""
+
+    def __init__(self, E, G, d, n_param, alpha=0.7, beta=0.05, tau=0.1, eps=1e-3, cache_life=4):
+        self.cfg = moe_cluster_config(E, G, d, n_param, alpha, beta, tau, eps, cache_life)
+        h = C.c_void_p()
+        check(lib.moe_cluster_create(C.byref(self.cfg), C.byref(h)))
+        self.h = h
+
+    def observe(self, X, idx):
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        check(lib.moe_cluster_observe(self.h, X.ctypes.data, X.shape[0], idx.ctypes.data, idx.shape[1]))
+
+    def centroids(self) -> np.ndarray:
+        mu = np.zeros((self.cfg.E, self.cfg.d), dtype=np.float64)
+        check(lib.moe_cluster_get_centroids(self.h, mu.ctypes.data))
+        return mu
+
+    def set_centroids(self, mu):
+        mu = np.ascontiguousarray(mu, dtype=np.float64)
+        check(lib.moe_cluster_set_centroids(self.h, mu.ctypes.data))
+
+    def regroup(self, vecs, u):
+        """vecs: E float32 arrays of n_param values; u: G uniforms.
+        Returns (group_of [E], members [G, K], S [E, E], fresh [E])."""
+        E, G = self.cfg.E, self.cfg.G
+        keep = [np.ascontiguousarray(v, dtype=np.float32).reshape(-1) for v in vecs]
+        assert all(v.size == self.cfg.n_param for v in keep)
+        ptrs = (C.c_void_p * E)(*[v.ctypes.data for v in keep])
+        u = np.ascontiguousarray(u, dtype=np.float64)
+        group_of = np.zeros(E, dtype=np.int32)
+        members = np.zeros((G, E // G), dtype=np.int32)
+        S = np.zeros((E, E), dtype=np.float64)
+        fresh = np.zeros(E, dtype=np.int32)
+        check(lib.moe_cluster_regroup(self.h, ptrs, u.ctypes.data, group_of.ctypes.data,
+                                      members.ctypes.data, S.ctypes.data, fresh.ctypes.data))
+        return group_of, members, S, fresh
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib.moe_cluster_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def compress_projection(W, members, r: int, n_threads: int = 0):
+    """W: float32 [E, d_in, d_out] (or a list of E such arrays); members
+    [G, K].  Returns base [G, d_in, d_out], A [E, d_in, r], B [E, d_out, r]
+    (float32, regrouped order) and the relative errors [E] (float64)."""
+    keep = [np.ascontiguousarray(w, dtype=np.float32) for w in W]
+    E = len(keep)
+    din, dout = keep[0].shape
+    members = np.ascontiguousarray(members, dtype=np.int32)
+    G = members.shape[0]
+    ptrs = (C.c_void_p * E)(*[w.ctypes.data for w in keep])
+    base = np.zeros((G, din, dout), dtype=np.float32)
+    A = np.zeros((E, din, r), dtype=np.float32)
+    B = np.zeros((E, dout, r), dtype=np.float32)
+    err = np.zeros(E, dtype=np.float64)
+    check(lib.moe_compress_projection(E, G, members.ctypes.data, din, dout, r, ptrs, base.ctypes.data,
+                                      A.ctypes.data, B.ctypes.data, err.ctypes.data, n_threads))
+    return base, A, B, err

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcefn.so")
-SOURCES = ["route.hip", "gemm.hip", "api.hip", "pack.cpp"]
+SOURCES = ["route.hip", "gemm.hip", "api.hip", "pack.cpp", "cluster.cpp"]
 ARCH = "gfx950"
 
 
@@ -41,7 +41,8 @@ def compile_one(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [hipcc(), "-O2", "-fPIC", "-std=c++17", "-I", CSRC, "-c",
+        cmd = [hipcc(), "-O3", "-fPIC", "-std=c++17", "-I", CSRC, "-I",
+               os.path.join(os.path.dirname(HERE), "include"), "-c",
                os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

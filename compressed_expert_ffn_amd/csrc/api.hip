@@ -53,6 +53,18 @@ constexpr int kStages = 7;
 
 }  // namespace
 
+namespace cefn {
+int report_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+}  // namespace cefn
+
 // Workspace of the no-allocation forward pass (moe_forward_noalloc): one
 // array in every device's memory, held until the process ends.  Host code
 // never uses the name itself: on each device the array's address comes from

@@ -24,6 +24,9 @@ Q4 quantize_g32(const float* M, int n, int r);
 
 void parallel_for(int n, const std::function<void(int)>& fn);
 
+// Record an error for moe_last_error() (printf-style) and return code.
+int report_error(int code, const char* fmt, ...);
+
 // Depth k held by element e of lane half h in k-step ks of a fragment-major
 // matrix.  Permuted order (Kd a multiple of 64): inside every 64-deep block,
 // lane half h covers 32 consecutive k across the block's 4 k-steps, so a
