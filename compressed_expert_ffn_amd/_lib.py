@@ -43,6 +43,12 @@ class moe_stats(C.Structure):
                 ("dense_equiv_params", C.c_int64)]
 
 
+class moe_grads(C.Structure):
+    _fields_ = [("dW_grp", C.c_void_p), ("dW_exp", C.c_void_p), ("d_group_bias", C.c_void_p),
+                ("d_expert_bias", C.c_void_p), ("dbase", C.c_void_p * 3), ("dA", C.c_void_p * 3),
+                ("dB", C.c_void_p * 3)]
+
+
 class moe_cluster_config(C.Structure):
     _fields_ = [("E", C.c_int32), ("G", C.c_int32), ("d", C.c_int32), ("n_param", C.c_int64),
                 ("alpha", C.c_double), ("beta", C.c_double), ("tau", C.c_double), ("eps", C.c_double),
@@ -72,6 +78,7 @@ def _load():
         "moe_forward": ([P, P, C.c_int32, P, C.POINTER(moe_route_out), P], C.c_int),
         "moe_forward_noalloc": ([P, P, C.c_int32, P, C.POINTER(moe_route_out), P], C.c_int),
         "moe_destroy": ([P], C.c_int),
+        "moe_backward": ([P, P, C.c_int32, P, P, C.POINTER(moe_grads), P], C.c_int),
         "moe_last_error": ([], C.c_char_p),
         "moe_config_stats": ([C.POINTER(moe_config), C.POINTER(moe_stats)], C.c_int),
         "moe_stats": ([P, C.POINTER(moe_stats)], C.c_int),
@@ -223,6 +230,36 @@ class Layer:
         check(lib.moe_forward(self.h, C.c_void_p(X.data_ptr()), T, C.c_void_p(Y.data_ptr()),
                               rop, _stream_ptr(stream)))
         return Y
+
+    def backward(self, X, dY, stream=None) -> dict:
+        """moe_backward: returns dX (x dtype) and float32 gradients of every
+        weight, as torch tensors on the device."""
+        import torch
+        c = self.cfg
+        T, d, f, G, K, r = X.shape[0], c.d, c.f, c.G, c.K, c.r
+        P = 3 if c.act == ACT["swiglu"] else 2
+        dev = X.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        dims = [(d, f)] * (P - 1) + [(f, d)]
+        out = dict(dX=torch.empty_like(X), dW_grp=torch.empty((d, G), **f32),
+                   dW_exp=torch.empty((G, d, K), **f32), d_group_bias=torch.empty(G, **f32),
+                   d_expert_bias=torch.empty(self.E, **f32),
+                   dbase=[torch.empty((G, di, do), **f32) for di, do in dims],
+                   dA=[torch.empty((self.E, di, r), **f32) for di, do in dims] if r else None,
+                   dB=[torch.empty((self.E, do, r), **f32) for di, do in dims] if r else None)
+        g = moe_grads()
+        g.dW_grp = out["dW_grp"].data_ptr()
+        g.dW_exp = out["dW_exp"].data_ptr()
+        g.d_group_bias = out["d_group_bias"].data_ptr()
+        g.d_expert_bias = out["d_expert_bias"].data_ptr()
+        for p in range(P):
+            g.dbase[p] = out["dbase"][p].data_ptr()
+            if r:
+                g.dA[p] = out["dA"][p].data_ptr()
+                g.dB[p] = out["dB"][p].data_ptr()
+        check(lib.moe_backward(self.h, C.c_void_p(X.data_ptr()), T, C.c_void_p(dY.data_ptr()),
+                               C.c_void_p(out["dX"].data_ptr()), C.byref(g), _stream_ptr(stream)))
+        return out
 
     def stats(self) -> dict:
         st = moe_stats()

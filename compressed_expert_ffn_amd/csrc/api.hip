@@ -29,6 +29,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "pack.h"
+#include "train.h"
 
 using namespace cefn;
 
@@ -150,6 +151,7 @@ struct moe_handle {
   int prof_max = 0, prof_calls = 0, prof_mask = -1;
   std::vector<hipEvent_t> ev;          // [prof_max][kStages][2]
   std::vector<unsigned char> ev_used;  // [prof_max][kStages]
+  struct BwdState* bwd = nullptr;      // backward-pass layouts and workspace (built on first use)
 };
 
 namespace {
@@ -675,6 +677,35 @@ int weights_to_host(const moe_config& c, const moe_weights* w, moe_weights* hw,
   return MOE_OK;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------- backward ----
+// Plain k-major weight copies and the workspace of moe_backward, built on
+// its first call from the device layouts (no host copy of the weights is
+// kept).  U, E and the residual factors are kept as float32 for the
+// elementwise steps; GEMM operands are in the MFMA type.
+struct BwdState {
+  void *W1T = nullptr, *W1N = nullptr, *W2N = nullptr, *AtT = nullptr, *BdT = nullptr;
+  float *Atp = nullptr, *B1p = nullptr, *Adp = nullptr;
+  int NUb = 0, NEb = 0;
+  long Kg = 0, Ke = 0;
+  int *counts = nullptr, *offsets = nullptr, *perm = nullptr, *arow = nullptr, *grow = nullptr;
+  int *kpad_g = nullptr, *kpad_e = nullptr;
+  float *Zb = nullptr, *U = nullptr, *D = nullptr, *Eb = nullptr, *dZbar = nullptr, *hbar = nullptr;
+  float *q = nullptr, *wu2 = nullptr, *dw = nullptr, *ua = nullptr, *ea = nullptr, *dXb = nullptr, *ds = nullptr;
+  void *dz = nullptr, *wh = nullptr;
+  void *XTg = nullptr, *dZT = nullptr, *hbT = nullptr, *dYTg = nullptr, *dsdeT = nullptr;
+  void *XTe = nullptr, *dYTe = nullptr, *qT = nullptr, *uT = nullptr, *dzT = nullptr, *whT = nullptr;
+  void *eT = nullptr, *wu2T = nullptr;
+};
+
+namespace {
+
+void delete_bwd(moe_handle* h) {
+  delete h->bwd;
+  h->bwd = nullptr;
+}
+
 // router + scatter into the workspace (and the caller's buffers where given)
 // Where the routing pass left the lists the GEMMs read.
 struct RouteLive {
@@ -895,6 +926,7 @@ int moe_destroy(moe_handle* h) {
   (void)hipDeviceSynchronize();
   for (void* p : h->allocs) (void)hipFree(p);
   for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  delete_bwd(h);
   delete h;
   return MOE_OK;
 }
@@ -916,6 +948,59 @@ int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out,
 }  // extern "C"
 
 namespace {
+
+// Where one residual factor (projection p, A or B, expert i) lives in the
+// device layouts, in the terms of the decode kernel (kinds: 0 At, 1 B1,
+// 2 Ad, 3 Bd).
+struct FactorLoc {
+  int kind, n, aux0, aux1;
+  const void* src;
+  const uint16_t* sc;
+  long base, sbase;
+};
+
+FactorLoc locate_factor(const moe_handle* h, int proj, int which, int expert) {
+  const moe_config& c = h->cfg;
+  int di, dn;
+  dims(c, proj, di, dn);
+  FactorLoc L{};
+  L.n = which == 0 ? di : dn;
+  const int K = c.K, g = expert / K, j = expert % K, nfb = c.f / 32;
+  const bool int4 = c.resid == MOE_RESID_INT4_G32;
+  const bool down = proj == h->P - 1;
+  if (which == 0 && !down) {  // At
+    L.kind = 0;
+    L.src = h->At;
+    L.sc = h->At_s;
+    L.base = int4 ? g * h->at_gs : g * h->at_gs / 8;
+    L.sbase = g * h->at_sgs;
+    L.aux0 = (j * h->P_in + proj) * RPAD;
+    L.aux1 = c.d / 16;
+  } else if (which == 1 && !down) {  // B1
+    L.kind = 1;
+    L.src = h->B1;
+    L.sc = h->B1_s;
+    L.base = (long)(expert * h->P_in + proj) * nfb * 64;
+    L.sbase = (long)(expert * h->P_in + proj) * nfb * RPAD;
+    L.aux0 = 0;
+    L.aux1 = 1;
+  } else if (which == 0 && down) {  // Ad
+    L.kind = 2;
+    L.src = h->Ad;
+    L.sc = h->Ad_s;
+    L.base = (long)expert * nfb * 2 * 64;
+    L.sbase = (long)expert * nfb * RPAD;
+  } else {  // Bd
+    L.kind = 3;
+    L.src = h->Bd;
+    L.sc = h->Bd_s;
+    L.base = int4 ? g * h->bd_gs : g * h->bd_gs / 8;
+    L.sbase = (long)expert * (c.d / 32) * RPAD;
+    L.aux0 = j;
+    L.aux1 = h->NV / 16;
+  }
+  return L;
+}
 
 // The whole layer on workspace ws (T >= 1, arguments checked by the caller).
 // The last GEMM clears ws's counters again for the next pass.
@@ -1144,50 +1229,16 @@ int moe_debug_residual(moe_handle* h, int32_t proj, int32_t which, int32_t exper
   if (c.r == 0) return fail(MOE_ERR_INVALID_ARG, "layer has no residual");
   if (proj < 0 || proj >= h->P || (which != 0 && which != 1) || expert < 0 || expert >= h->E || !values)
     return fail(MOE_ERR_INVALID_ARG, "bad residual selector");
-  int di, dn;
-  dims(c, proj, di, dn);
-  const int n = which == 0 ? di : dn, r = c.r;
-  const int K = c.K, g = expert / K, j = expert % K, nfb = c.f / 32;
+  FactorLoc L = locate_factor(h, proj, which, expert);
+  const int n = L.n, r = c.r;
   const bool int4 = c.resid == MOE_RESID_INT4_G32;
-  const void* src = nullptr;
-  const uint16_t* sc = nullptr;
-  long base = 0, sbase = 0;
-  int kind = 0, aux0 = 0, aux1 = 0;
-  const bool down = proj == h->P - 1;
-  if (which == 0 && !down) {  // At
-    kind = 0;
-    src = h->At;
-    sc = h->At_s;
-    base = int4 ? g * h->at_gs : g * h->at_gs / 8;
-    sbase = g * h->at_sgs;
-    aux0 = (j * h->P_in + proj) * RPAD;
-    aux1 = c.d / 16;
-  } else if (which == 1 && !down) {  // B1
-    kind = 1;
-    src = h->B1;
-    sc = h->B1_s;
-    base = (long)(expert * h->P_in + proj) * nfb * 64;
-    sbase = (long)(expert * h->P_in + proj) * nfb * RPAD;
-    aux0 = 0;
-    aux1 = 1;
-  } else if (which == 0 && down) {  // Ad
-    kind = 2;
-    src = h->Ad;
-    sc = h->Ad_s;
-    base = (long)expert * nfb * 2 * 64;
-    sbase = (long)expert * nfb * RPAD;
-  } else {  // Bd
-    kind = 3;
-    src = h->Bd;
-    sc = h->Bd_s;
-    base = int4 ? g * h->bd_gs : g * h->bd_gs / 8;
-    sbase = (long)expert * (c.d / 32) * RPAD;
-    aux0 = j;
-    aux1 = h->NV / 16;
-  }
+  const int kind = L.kind, aux0 = L.aux0;
+  const long sbase = L.sbase;
+  const uint16_t* sc = L.sc;
   float* dout = nullptr;
   if (hipMalloc(&dout, sizeof(float) * (size_t)n * r) != hipSuccess) return fail(MOE_ERR_OOM, "debug buffer");
-  hipError_t e = launch_debug_decode(h->mma, c.resid, kind, src, sc, base, sbase, n, r, aux0, aux1, dout, nullptr);
+  hipError_t e = launch_debug_decode(h->mma, c.resid, kind, L.src, sc, L.base, sbase, n, r, aux0, L.aux1, dout, r,
+                                     nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(values, dout, sizeof(float) * (size_t)n * r, hipMemcpyDeviceToHost);
   (void)hipFree(dout);
@@ -1282,6 +1333,371 @@ int moe_profile_end(moe_handle* h, float* stage_ms, int32_t n_stages_cap, int32_
     std::snprintf(names, names_cap, "%s", all.c_str());
   }
   h->prof = false;
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---- backward pass -------------------------------------------------------
+namespace {
+
+// Build the backward layouts and workspace (first moe_backward call).
+int prepare_backward(moe_handle* h) {
+  if (h->bwd) return MOE_OK;
+  const moe_config& c = h->cfg;
+  std::unique_ptr<BwdState> B(new BwdState());
+  const int G = c.G, K = c.K, E = h->E, Pin = h->P_in, d = c.d, f = c.f, r = c.r, ty = h->mma;
+  const size_t es = elem_bytes(ty);
+  const long T = c.T_max, R = T * c.top_groups, Na = T * h->k;
+  hipStream_t st = nullptr;
+  hipError_t e;
+  char* tmp = nullptr;
+  auto alloc_bytes = [&](void** p, size_t bytes) -> int {
+    char* q = nullptr;
+    TRY(dalloc(h, &q, bytes + 256));
+    *p = q;
+    return MOE_OK;
+  };
+  auto alloc_f = [&](float** p, size_t n) { return dalloc(h, p, n + 64); };
+  auto alloc_i = [&](int** p, size_t n) { return dalloc(h, p, n + 64); };
+  // plain base weights
+  TRY(alloc_bytes(&B->W1T, (size_t)G * Pin * f * d * es));
+  TRY(alloc_bytes(&B->W1N, (size_t)G * Pin * f * d * es));
+  TRY(alloc_bytes(&B->W2N, (size_t)G * f * d * es));
+  const int swf = Pin > 1 ? f : 0;
+  e = launch_frag_to_plain(ty, h->W1, G, h->w1_gs, Pin * f, d, swf, false, B->W1T, (long)Pin * f * d, d, st);
+  if (e == hipSuccess)
+    e = launch_frag_to_plain(ty, h->W1, G, h->w1_gs, Pin * f, d, swf, true, B->W1N, (long)Pin * f * d, (long)Pin * f, st);
+  if (e == hipSuccess) e = launch_frag_to_plain(ty, h->W2, G, h->w2_gs, d, f, 0, true, B->W2N, (long)f * d, d, st);
+  if (e != hipSuccess) return hip_fail(h, e, "backward weight repack");
+  if (r > 0) {
+    B->NUb = K * Pin * 16;
+    B->NEb = K * 16;
+    TRY(alloc_f(&B->Atp, (size_t)E * Pin * d * 16));
+    TRY(alloc_f(&B->B1p, (size_t)E * Pin * f * 16));
+    TRY(alloc_f(&B->Adp, (size_t)E * f * 16));
+    float* Bdp = nullptr;
+    TRY(alloc_f(&Bdp, (size_t)E * d * 16));
+    e = launch_zero_f(B->Atp, (long)E * Pin * d * 16, st);
+    if (e == hipSuccess) e = launch_zero_f(B->B1p, (long)E * Pin * f * 16, st);
+    if (e == hipSuccess) e = launch_zero_f(B->Adp, (long)E * f * 16, st);
+    if (e == hipSuccess) e = launch_zero_f(Bdp, (long)E * d * 16, st);
+    for (int i = 0; i < E && e == hipSuccess; ++i)
+      for (int p = 0; p < h->P && e == hipSuccess; ++p)
+        for (int which = 0; which < 2 && e == hipSuccess; ++which) {
+          const FactorLoc L = locate_factor(h, p, which, i);
+          float* out;
+          if (p < Pin) out = which == 0 ? B->Atp + ((size_t)i * Pin + p) * d * 16 : B->B1p + ((size_t)i * Pin + p) * f * 16;
+          else out = which == 0 ? B->Adp + (size_t)i * f * 16 : Bdp + (size_t)i * d * 16;
+          e = launch_debug_decode(ty, c.resid, L.kind, L.src, L.sc, L.base, L.sbase, L.n, r, L.aux0, L.aux1, out, 16, st);
+        }
+    if (e != hipSuccess) return hip_fail(h, e, "backward factor decode");
+    TRY(alloc_bytes(&B->AtT, (size_t)G * B->NUb * d * es));
+    TRY(alloc_bytes(&B->BdT, (size_t)G * B->NEb * d * es));
+    e = launch_stack_factors(ty, B->Atp, G, K, Pin, d, B->NUb, B->AtT, st);
+    if (e == hipSuccess) e = launch_stack_factors(ty, Bdp, G, K, 1, d, B->NEb, B->BdT, st);
+    if (e != hipSuccess) return hip_fail(h, e, "backward factor stacking");
+  }
+  // workspace for T_max tokens
+  B->Kg = R + 64L * G;
+  B->Ke = Na + 64L * E;
+  TRY(alloc_i(&B->counts, E));
+  TRY(alloc_i(&B->offsets, E + 1));
+  TRY(alloc_i(&B->perm, Na));
+  TRY(alloc_i(&B->arow, Na));
+  TRY(alloc_i(&B->grow, R));
+  TRY(alloc_i(&B->kpad_g, G + 1));
+  TRY(alloc_i(&B->kpad_e, E + 1));
+  TRY(alloc_f(&B->Zb, (size_t)R * Pin * f));
+  TRY(alloc_f(&B->D, (size_t)R * f));
+  TRY(alloc_f(&B->dZbar, (size_t)R * Pin * f));
+  TRY(alloc_f(&B->hbar, (size_t)R * f));
+  TRY(alloc_f(&B->q, (size_t)Na * Pin * 16));
+  TRY(alloc_f(&B->wu2, (size_t)Na * 16));
+  TRY(alloc_f(&B->dw, (size_t)Na));
+  TRY(alloc_f(&B->ua, (size_t)Na * Pin * 16));
+  TRY(alloc_f(&B->ea, (size_t)Na * 16));
+  TRY(alloc_f(&B->dXb, (size_t)R * d));
+  TRY(alloc_f(&B->ds, (size_t)R * (1 + K)));
+  TRY(alloc_bytes(&B->dz, (size_t)Na * Pin * f * es));
+  TRY(alloc_bytes(&B->wh, (size_t)Na * f * es));
+  TRY(alloc_bytes(&B->XTg, (size_t)d * B->Kg * es));
+  TRY(alloc_bytes(&B->dZT, (size_t)Pin * f * B->Kg * es));
+  TRY(alloc_bytes(&B->hbT, (size_t)f * B->Kg * es));
+  TRY(alloc_bytes(&B->dYTg, (size_t)d * B->Kg * es));
+  TRY(alloc_bytes(&B->dsdeT, (size_t)(1 + K) * B->Kg * es));
+  if (r > 0) {
+    TRY(alloc_f(&B->U, (size_t)R * B->NUb));
+    TRY(alloc_f(&B->Eb, (size_t)R * B->NEb));
+    TRY(alloc_bytes(&B->XTe, (size_t)d * B->Ke * es));
+    TRY(alloc_bytes(&B->dYTe, (size_t)d * B->Ke * es));
+    TRY(alloc_bytes(&B->qT, (size_t)Pin * 16 * B->Ke * es));
+    TRY(alloc_bytes(&B->uT, (size_t)Pin * 16 * B->Ke * es));
+    TRY(alloc_bytes(&B->dzT, (size_t)Pin * f * B->Ke * es));
+    TRY(alloc_bytes(&B->whT, (size_t)f * B->Ke * es));
+    TRY(alloc_bytes(&B->eT, (size_t)16 * B->Ke * es));
+    TRY(alloc_bytes(&B->wu2T, (size_t)16 * B->Ke * es));
+  }
+  (void)tmp;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_ERR_HIP, "backward set-up failed");
+  h->bwd = B.release();
+  return MOE_OK;
+}
+
+BGemmArgs rgemm(const Workspace& ws, const int* gcounts, const int* goffsets, int G, long R, const void* a, long lda,
+                int a_dtype, const int* a_map, int a_div, const void* b, long b_sstride, int N, int K, float* c,
+                long ldc) {
+  (void)ws;
+  BGemmArgs g{};
+  g.mode = 0;
+  g.S = G;
+  g.seg_start = goffsets;
+  g.seg_count = gcounts;
+  g.a = a;
+  g.lda = lda;
+  g.a_dtype = a_dtype;
+  g.a_map = a_map;
+  g.a_div = a_div;
+  g.b = b;
+  g.ldb = K;
+  g.b_sstride = b_sstride;
+  g.c = c;
+  g.ldc = ldc;
+  g.N = N;
+  g.K = K;
+  g.n_store = N;
+  g.max_rows = (int)R;
+  return g;
+}
+
+BGemmArgs kgemm(int S, const int* kpad, int ty, const void* a, long lda, const void* b, long ldb, int M, int N,
+                float* c, long c_sstride, long ldc, int n_store) {
+  BGemmArgs g{};
+  g.mode = 1;
+  g.S = S;
+  g.kpad_off = kpad;
+  g.a = a;
+  g.lda = lda;
+  g.a_dtype = ty;
+  g.b = b;
+  g.ldb = ldb;
+  g.c = c;
+  g.c_sstride = c_sstride;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.n_store = n_store;
+  return g;
+}
+
+TransArgs tgather(int S, const int* start, const int* count, const int* kpad, const void* in, int in_dtype, long ld_in,
+                  int c0, int ncols, const int* map, int div, void* out, long ld_out, long max_k) {
+  TransArgs t{};
+  t.S = S;
+  t.start = start;
+  t.count = count;
+  t.kpad_off = kpad;
+  t.in = in;
+  t.in_dtype = in_dtype;
+  t.ld_in = ld_in;
+  t.c0 = c0;
+  t.ncols = ncols;
+  t.in_map = map;
+  t.in_div = div;
+  t.out = out;
+  t.ld_out = ld_out;
+  t.max_cols_k = (int)max_k;
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* dX, const moe_grads* gr,
+                 void* stream) {
+  if (!h || !gr) return fail(MOE_ERR_INVALID_ARG, "null handle or gradients");
+  const moe_config& c = h->cfg;
+  if (T < 0 || T > c.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, c.T_max);
+  if (T > 0 && (!X || !dY || !dX)) return fail(MOE_ERR_INVALID_ARG, "null X, dY or dX");
+  const int G = c.G, K = c.K, E = h->E, Pin = h->P_in, P = h->P, d = c.d, f = c.f, r = c.r, ty = h->mma;
+  const int kg = c.top_groups, k = h->k;
+  for (int p = 0; p < P; ++p)
+    if (!gr->dbase[p] || (r > 0 && (!gr->dA[p] || !gr->dB[p])))
+      return fail(MOE_ERR_INVALID_ARG, "gradient buffer of projection %d is null", p);
+  if (!gr->dW_grp) return fail(MOE_ERR_INVALID_ARG, "dW_grp is null");
+  TRY(prepare_backward(h));
+  BwdState* B = h->bwd;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+  if (T == 0) {
+    for (int p = 0; p < P; ++p) {
+      int di, dn;
+      dims(c, p, di, dn);
+      ok(launch_zero_f(gr->dbase[p], (long)G * di * dn, st));
+      if (r > 0) {
+        ok(launch_zero_f(gr->dA[p], (long)E * di * r, st));
+        ok(launch_zero_f(gr->dB[p], (long)E * dn * r, st));
+      }
+    }
+    ok(launch_zero_f(gr->dW_grp, (long)d * G, st));
+    if (gr->dW_exp) ok(launch_zero_f(gr->dW_exp, (long)G * d * K, st));
+    if (gr->d_group_bias) ok(launch_zero_f(gr->d_group_bias, G, st));
+    if (gr->d_expert_bias) ok(launch_zero_f(gr->d_expert_bias, E, st));
+    return e == hipSuccess ? MOE_OK : hip_fail(h, e, "backward (no tokens)");
+  }
+  // routing again (the forward pass's decisions), with the expert lists
+  Prof pf{h, st, -1};
+  RouteLive live{};
+  moe_route_out ro{};
+  ro.counts = B->counts;
+  ro.offsets = B->offsets;
+  ro.perm = B->perm;
+  TRY(run_route(h, h->ws, X, T, &ro, true, st, pf, live));
+  ok(launch_zero(h->ws.cc, h->ws.cc_n, st));
+  const long R = (long)T * kg, Na = (long)T * k;
+  const int* garow = h->ws.garow;
+  const size_t es = elem_bytes(ty);
+  // forward intermediates: Z = X W1_base per group row, U = X A1 stacked
+  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->W1T,
+                            (long)Pin * f * d, Pin * f, d, B->Zb, (long)Pin * f), st));
+  if (r > 0)
+    ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->AtT,
+                              (long)B->NUb * d, B->NUb, d, B->U, B->NUb), st));
+  // D = dY W2_base^T, E = dY B2 stacked
+  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->W2N,
+                            (long)f * d, f, d, B->D, f), st));
+  if (r > 0)
+    ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->BdT,
+                              (long)B->NEb * d, B->NEb, d, B->Eb, B->NEb), st));
+  {
+    ActBwdArgs aa{};
+    aa.R = (int)R;
+    aa.f = f;
+    aa.Pin = Pin;
+    aa.K = K;
+    aa.kg = kg;
+    aa.ke = c.top_experts;
+    aa.k = k;
+    aa.act = c.act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
+    aa.gcounts = live.gcounts;
+    aa.goffsets = live.goffsets;
+    aa.garow = garow;
+    aa.idx = live.idx;
+    aa.w = live.w;
+    aa.Zb = B->Zb;
+    aa.U = B->U;
+    aa.NU = B->NUb;
+    aa.B1p = B->B1p;
+    aa.Adp = B->Adp;
+    aa.D = B->D;
+    aa.Eb = B->Eb;
+    aa.NE = B->NEb;
+    aa.r = r;
+    aa.dZbar = B->dZbar;
+    aa.hbar = B->hbar;
+    aa.dz = B->dz;
+    aa.wh = B->wh;
+    aa.q = B->q;
+    aa.wu2 = B->wu2;
+    aa.dw = B->dw;
+    aa.ua = B->ua;
+    aa.ea = B->ea;
+    ok(launch_act_bwd(ty, aa, st));
+  }
+  // dX: base part per group row, then per token with the residual and router terms
+  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, MOE_F32, nullptr, 1,
+                            B->W1N, (long)Pin * f * d, d, Pin * f, B->dXb, d), st));
+  ok(launch_invert_rows(garow, (int)R, B->grow, st));
+  {
+    TokBwdArgs ta{};
+    ta.T = T;
+    ta.d = d;
+    ta.G = G;
+    ta.K = K;
+    ta.kg = kg;
+    ta.ke = c.top_experts;
+    ta.k = k;
+    ta.Pin = Pin;
+    ta.r = r;
+    ta.idx = live.idx;
+    ta.gidx = live.gidx;
+    ta.w = live.w;
+    ta.dw = B->dw;
+    ta.grow = B->grow;
+    ta.dXb = B->dXb;
+    ta.q = B->q;
+    ta.Atp = B->Atp;
+    ta.Wr = h->Wr;
+    ta.NCp = h->NCp;
+    ta.ds = B->ds;
+    ta.dX = dX;
+    ta.x_dtype = c.x_dtype;
+    ok(launch_tok_bwd(ta, st));
+  }
+  // weight gradients over each group's rows
+  ok(launch_pad_scan(live.gcounts, G, B->kpad_g, st));
+  const long Kg = B->Kg;
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, X, c.x_dtype, d, 0, d, garow, kg, B->XTg,
+                                 Kg, Kg), st));
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->dZbar, MOE_F32, (long)Pin * f, 0,
+                                 Pin * f, nullptr, 1, B->dZT, Kg, Kg), st));
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->hbar, MOE_F32, f, 0, f, nullptr, 1,
+                                 B->hbT, Kg, Kg), st));
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, dY, c.x_dtype, d, 0, d, garow, kg,
+                                 B->dYTg, Kg, Kg), st));
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->ds, MOE_F32, 1 + K, 0, 1 + K, garow, 1,
+                                 B->dsdeT, Kg, Kg), st));
+  for (int p = 0; p < Pin; ++p)
+    ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, static_cast<char*>(B->dZT) + (size_t)p * f * Kg * es, Kg,
+                              d, f, gr->dbase[p], (long)d * f, f, f), st));
+  ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->hbT, Kg, B->dYTg, Kg, f, d, gr->dbase[P - 1], (long)f * d, d, d),
+                  st));
+  // router weights and biases
+  ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, B->dsdeT, Kg, d, 1, gr->dW_grp, 1, G, 1), st));
+  if (K > 1 && gr->dW_exp)
+    ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, static_cast<char*>(B->dsdeT) + (size_t)Kg * es, Kg, d, K,
+                              gr->dW_exp, (long)d * K, K, K), st));
+  else if (gr->dW_exp)
+    ok(launch_zero_f(gr->dW_exp, (long)G * d * K, st));
+  if (gr->d_group_bias)
+    ok(launch_seg_colsum(B->ds, 1 + K, 1, live.goffsets, live.gcounts, garow, G, gr->d_group_bias, 1, st));
+  if (gr->d_expert_bias) {
+    if (K > 1)
+      ok(launch_seg_colsum(B->ds + 1, 1 + K, K, live.goffsets, live.gcounts, garow, G, gr->d_expert_bias, K, st));
+    else
+      ok(launch_zero_f(gr->d_expert_bias, E, st));
+  }
+  // residual factor gradients over each expert's assignments
+  if (r > 0) {
+    const long Ke = B->Ke;
+    ok(launch_assign_rows(B->perm, B->offsets, live.idx, E, k, (int)Na, B->arow, st));
+    ok(launch_pad_scan(B->counts, E, B->kpad_e, st));
+    auto eg = [&](const void* in, int dt, long ld, int ncols, int div, void* out) {
+      ok(launch_gather_t(ty, tgather(E, B->offsets, B->counts, B->kpad_e, in, dt, ld, 0, ncols, B->arow, div, out, Ke,
+                                     Ke), st));
+    };
+    eg(X, c.x_dtype, d, d, k, B->XTe);
+    eg(dY, c.x_dtype, d, d, k, B->dYTe);
+    eg(B->q, MOE_F32, (long)Pin * 16, Pin * 16, 1, B->qT);
+    eg(B->ua, MOE_F32, (long)Pin * 16, Pin * 16, 1, B->uT);
+    eg(B->dz, ty, (long)Pin * f, Pin * f, 1, B->dzT);
+    eg(B->wh, ty, f, f, 1, B->whT);
+    eg(B->ea, MOE_F32, 16, 16, 1, B->eT);
+    eg(B->wu2, MOE_F32, 16, 16, 1, B->wu2T);
+    for (int p = 0; p < Pin; ++p) {
+      ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, B->XTe, Ke, static_cast<char*>(B->qT) + (size_t)p * 16 * Ke * es,
+                                Ke, d, 16, gr->dA[p], (long)d * r, r, r), st));
+      ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, static_cast<char*>(B->dzT) + (size_t)p * f * Ke * es, Ke,
+                                static_cast<char*>(B->uT) + (size_t)p * 16 * Ke * es, Ke, f, 16, gr->dB[p],
+                                (long)f * r, r, r), st));
+    }
+    ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, B->whT, Ke, B->eT, Ke, f, 16, gr->dA[P - 1], (long)f * r, r, r), st));
+    ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, B->dYTe, Ke, B->wu2T, Ke, d, 16, gr->dB[P - 1], (long)d * r, r, r),
+                    st));
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward launch");
   return MOE_OK;
 }
 

@@ -1011,7 +1011,7 @@ __device__ __forceinline__ void perm_pos(int k, int& ks, int& h, int& e) {
 
 template <int TY>
 __global__ void debug_decode_kernel(int resid, int kind, const void* src, const uint16_t* scales, long base,
-                                    long sbase, int n, int r, int aux0, int aux1, float* out) {
+                                    long sbase, int n, int r, int aux0, int aux1, float* out, int ldo) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;  // entry index i = row * r + rho
   if (i >= n * r) return;
   const int row = i / r, rho = i % r;
@@ -1067,7 +1067,7 @@ __global__ void debug_decode_kernel(int resid, int kind, const void* src, const 
   } else {
     val = load_as_f32<TY>(static_cast<const TE<TY>*>(src), (base + fo) * 8 + e);
   }
-  out[i] = val;
+  out[(long)row * ldo + rho] = val;
 }
 
 // ---------------------------------------------------------------- launch --
@@ -1290,14 +1290,14 @@ hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_debug_decode(int mma_dtype, int resid, int kind, const void* src, const uint16_t* scales,
-                               long base, long sbase, int n, int r, int aux0, int aux1, float* out,
+                               long base, long sbase, int n, int r, int aux0, int aux1, float* out, int ldo,
                                hipStream_t st) {
   const int tot = n * r;
   dim3 grid((tot + 255) / 256), block(256);
   switch (mma_dtype) {
-    case DT_F32: hipLaunchKernelGGL(debug_decode_kernel<DT_F32>, grid, block, 0, st, resid, kind, src, scales, base, sbase, n, r, aux0, aux1, out); break;
-    case DT_F16: hipLaunchKernelGGL(debug_decode_kernel<DT_F16>, grid, block, 0, st, resid, kind, src, scales, base, sbase, n, r, aux0, aux1, out); break;
-    case DT_BF16: hipLaunchKernelGGL(debug_decode_kernel<DT_BF16>, grid, block, 0, st, resid, kind, src, scales, base, sbase, n, r, aux0, aux1, out); break;
+    case DT_F32: hipLaunchKernelGGL(debug_decode_kernel<DT_F32>, grid, block, 0, st, resid, kind, src, scales, base, sbase, n, r, aux0, aux1, out, ldo); break;
+    case DT_F16: hipLaunchKernelGGL(debug_decode_kernel<DT_F16>, grid, block, 0, st, resid, kind, src, scales, base, sbase, n, r, aux0, aux1, out, ldo); break;
+    case DT_BF16: hipLaunchKernelGGL(debug_decode_kernel<DT_BF16>, grid, block, 0, st, resid, kind, src, scales, base, sbase, n, r, aux0, aux1, out, ldo); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

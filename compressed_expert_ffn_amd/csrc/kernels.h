@@ -204,6 +204,6 @@ hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st);
 // Device-side decode of stored residual factors (test export).
 hipError_t launch_debug_decode(int mma_dtype, int resid, int kind, const void* src,
                                const uint16_t* scales, long base, long sbase, int n, int r,
-                               int aux0, int aux1, float* out, hipStream_t st);
+                               int aux0, int aux1, float* out, int ldo, hipStream_t st);
 
 }  // namespace cefn

@@ -1,0 +1,137 @@
+// Internal interface of the backward-pass kernels (train.hip) used by
+// api.hip.  All matrices the backward GEMMs read are row-major with the
+// contraction index k contiguous ("k-major"), in the MFMA type TY unless
+// noted; k ranges are padded to multiples of 64 with zeros.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cefn {
+
+// C[m][n] = sum_k A(m, k) B(n, k) over segments of rows (mode R) or of k
+// (mode K); fp32 C.
+//  mode R: segment s owns rows [seg_start[s], seg_start[s] + seg_count[s])
+//          of C (row-major, ldc); A row m of the segment is a_map ? source
+//          row a_map[seg_start[s] + m] / a_div : seg_start[s] + m of A
+//          (lda, type a_dtype, converted to TY on load); B = b + s * b_sstride
+//          ([N][K], ldb = K); K fixed (multiple of 64).
+//  mode K: every segment has M x N outputs at c + s * c_sstride (ldc); its
+//          k range is [kpad_off[s], kpad_off[s + 1]) of A ([M][*], lda) and
+//          B ([N][*], ldb), both TY.
+struct BGemmArgs {
+  int mode;  // 0 = R, 1 = K
+  int S;     // segments
+  const int* seg_start;
+  const int* seg_count;
+  const int* kpad_off;
+  const void* a;
+  long lda;
+  int a_dtype;
+  const int* a_map;
+  int a_div;
+  const void* b;
+  long ldb;
+  long b_sstride;
+  float* c;
+  long ldc;
+  long c_sstride;
+  int M, N, K;     // M: mode K only; N: columns computed; K: mode R only
+  int n_store;     // columns stored (<= N)
+  int max_rows;    // mode R: upper bound of the summed row count (grid size)
+};
+hipError_t launch_bgemm(int ty, const BGemmArgs& a, hipStream_t st);
+
+// out[c][kpad_off[s] + r] = TY(in(row(s, r), c0 + c)) for r < count[s], zero
+// for count[s] <= r < padded length; in rows are in_map ? in_map[start[s] + r]
+// / in_div : start[s] + r of a row-major [*][ld_in] matrix of in_dtype.
+struct TransArgs {
+  int S;
+  const int* start;
+  const int* count;
+  const int* kpad_off;
+  const void* in;
+  int in_dtype;
+  long ld_in;
+  int c0, ncols;
+  const int* in_map;
+  int in_div;
+  void* out;
+  long ld_out;
+  int max_cols_k;  // upper bound of kpad_off[S] (grid size)
+};
+hipError_t launch_gather_t(int ty, const TransArgs& a, hipStream_t st);
+
+// kpad_off[0] = 0, kpad_off[s + 1] = kpad_off[s] + roundup(count[s], 64)
+hipError_t launch_pad_scan(const int* count, int S, int* kpad_off, hipStream_t st);
+
+// Plain (row-major) copy of a fragment-major matrix frag(N, Kd), permuted
+// k order: out[ (transpose ? k : nmap(n)) * ld_out + (transpose ? nmap(n) : k) ]
+// with nmap the SwiGLU gate/up de-interleave when swiglu_f > 0 (fragment
+// column n holds projection (n / 32) & 1, column (n / 64) * 32 + n % 32).
+hipError_t launch_frag_to_plain(int ty, const void* frag, int G, long g_stride_in, int N, int Kd, int swiglu_f,
+                                bool transpose, void* out, long g_stride_out, long ld_out, hipStream_t st);
+
+// Per-row backward of the activation and the residual epilogue.
+struct ActBwdArgs {
+  int R, f, Pin, K, kg, ke, k, act;
+  const int* gcounts;
+  const int* goffsets;
+  const int* garow;     // row -> t*kg + group rank
+  const int* idx;       // [T][k]
+  const float* w;       // [T][k]
+  const float* Zb;      // [R][Pin f]
+  const float* U;       // [R][NU] (u of expert j, projection p at (j Pin + p) 16)
+  int NU;
+  const float* B1p;     // [E][Pin][f][16]
+  const float* Adp;     // [E][f][16]
+  const float* D;       // [R][f]
+  const float* Eb;      // [R][NE] (e of expert j at j 16)
+  int NE;
+  int r;                // residual rank (0: no residual)
+  float* dZbar;         // [R][Pin f]
+  float* hbar;          // [R][f]
+  void* dz;             // [T k][Pin f] TY
+  void* wh;             // [T k][f] TY
+  float* q;             // [T k][Pin 16]
+  float* wu2;           // [T k][16]
+  float* dw;            // [T k]
+  float* ua;            // [T k][Pin 16] u of the assignment's expert
+  float* ea;            // [T k][16]    e of the assignment's expert
+};
+hipError_t launch_act_bwd(int ty, const ActBwdArgs& a, hipStream_t st);
+
+// Per-token router backward and dX assembly.
+struct TokBwdArgs {
+  int T, d, G, K, kg, ke, k, Pin, r;
+  const int* idx;
+  const int* gidx;
+  const float* w;
+  const float* dw;
+  const int* grow;      // [T][kg]: group row of (t, group rank)
+  const float* dXb;     // [R][d]
+  const float* q;       // [T k][Pin 16]
+  const float* Atp;     // [E][Pin][d][16]
+  const float* Wr;      // router matrix [d/16][NCp][16]
+  int NCp;
+  float* ds;            // [T][kg] group-logit gradients
+  float* de;            // [T][kg][K] expert-logit gradients (zero for unchosen)
+  void* dX;             // [T][d] x dtype
+  int x_dtype;
+};
+hipError_t launch_tok_bwd(const TokBwdArgs& a, hipStream_t st);
+
+// row -> t*kg + rank map inverse: grow[t*kg + rank] = row
+hipError_t launch_invert_rows(const int* garow, int R, int* grow, hipStream_t st);
+// arow[p] = t*k + slot of expert-list position p (perm, offsets from moe_route)
+hipError_t launch_assign_rows(const int* perm, const int* offsets, const int* idx, int E, int k, int Na,
+                              int* arow, hipStream_t st);
+hipError_t launch_zero_f(float* p, long n, hipStream_t st);
+// out[s * ld_out + c] = sum over the rows of segment s of in[map(row)][c], c < ncols
+hipError_t launch_seg_colsum(const float* in, long ld_in, int ncols, const int* start, const int* count,
+                             const int* in_map, int S, float* out, long ld_out, hipStream_t st);
+// plain k-major copies of the residual factors for the backward GEMMs:
+// out[g][(j * P + p) * 16 + rho][k] = src[(g K + j)][p][k][rho] (TY), padded rows zero
+hipError_t launch_stack_factors(int ty, const float* src, int G, int K, int P, int n, int rows_out, void* out,
+                                hipStream_t st);
+
+}  // namespace cefn

@@ -190,6 +190,34 @@ int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y,
 int moe_forward_noalloc(moe_handle* h, const void* X, int32_t T, void* Y,
                         const moe_route_out* routing, void* stream);
 
+/* Gradients of the layer, caller-owned DEVICE buffers, float32, row-major,
+ * in the shapes of moe_weights (written, not accumulated). */
+typedef struct {
+  float* dW_grp;        /* [d][G] */
+  float* dW_exp;        /* [G][d][K]; may be NULL (zeros when K == 1) */
+  float* d_group_bias;  /* [G]; may be NULL */
+  float* d_expert_bias; /* [E]; may be NULL (zeros when K == 1) */
+  float* dbase[3];      /* [G][d_in][d_out] per projection */
+  float* dA[3];         /* [E][d_in][r] per projection (r > 0) */
+  float* dB[3];         /* [E][d_out][r] per projection (r > 0) */
+} moe_grads;
+
+/* Backward pass of moe_forward for one batch: the gradients of
+ * L = sum(dY * Y) with respect to X (dX, device [T][d] in x_dtype) and
+ * every stored weight, through the experts and through the gate (softmax
+ * over the chosen logits at each level; the top-k choice itself is held
+ * fixed).  The factored form is kept: the base terms run once per (token,
+ * group) -- D = dY W_down,base^T, dX gets dZbar W_in,base^T, dW_base^g =
+ * X_g^T dZbar_g and hbar_g^T dY_g -- and the residual factors get
+ * dA = dW~ B, dB = dW~^T A evaluated through rank-r products
+ * ("Breaking the MoE LLM Trilemma", papernotes.org note: key design 2 and
+ * the loss function / training strategy section).  INT4 residuals are
+ * differentiated at their dequantised values.  X and dY: device [T][d] in
+ * x_dtype.  The first call allocates the backward layouts and workspace for
+ * T_max tokens (synchronous); later calls only enqueue on stream. */
+int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* dX,
+                 const moe_grads* grads, void* stream);
+
 /* Free everything the handle owns (synchronises the device first).  NULL is
  * a no-op. */
 int moe_destroy(moe_handle* h);
