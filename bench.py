@@ -199,6 +199,72 @@ def cpu_baseline(w, inputs, budget_s: float) -> dict:
                 cpu_model=cpu_model(), nproc=os.cpu_count())
 
 
+def side_modes(args, w, inputs) -> None:
+    """The backward pass, or the forward pass with offloaded groups: one
+    JSON line with the time per call (HIP events around the timed calls on
+    the launch stream) and the work rate."""
+    import numpy as np
+    import torch
+    from compressed_expert_ffn_amd import _lib as L
+    from compressed_expert_ffn_amd import synth
+    lay = L.Layer(L.config_from_workload(w), inputs)
+    Xh = inputs["X"]
+    if w.x_dtype == "bf16":
+        X = torch.from_numpy(Xh.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        X = torch.from_numpy(Xh).cuda()
+    out = dict(metric=args.mode, workload=w.name, T=w.T, steps=args.steps, warmup=args.warmup)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.mode == "backward":
+        dY32 = np.random.default_rng(17).standard_normal((w.T, w.d)).astype(np.float32)
+        dYs = synth.to_storage(dY32, w.x_dtype)
+        dY = (torch.from_numpy(dYs.view(np.int16)).cuda().view(torch.bfloat16) if w.x_dtype == "bf16"
+              else torch.from_numpy(dYs).cuda())
+        for _ in range(max(1, args.warmup)):
+            lay.backward(X, dY)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(args.steps):
+            lay.backward(X, dY)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        flops = 2 * w.algorithmic_flops()["total"]
+        out.update(ms_per_call=round(ms, 4), tokens_per_s=round(w.T / (ms * 1e-3), 1),
+                   algorithmic_tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+                   note="algorithmic work counted as twice the forward pass's; the recomputed forward "
+                        "intermediates are overhead")
+    else:
+        slots = args.slots or max(1, w.G // 2)
+        lay.offload_enable(slots)
+        Y = torch.empty_like(X)
+        rng_batches = [X] + [(torch.from_numpy(synth.draw_x(w, seed=500 + i).view(np.int16)).cuda()
+                              .view(torch.bfloat16) if w.x_dtype == "bf16"
+                              else torch.from_numpy(synth.draw_x(w, seed=500 + i)).cuda()) for i in range(3)]
+        for i in range(max(1, args.warmup)):
+            lay.forward_offload(rng_batches[i % 4], Y)
+        torch.cuda.synchronize()
+        s0 = lay.offload_stats()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            lay.forward_offload(rng_batches[i % 4], Y)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        s1 = lay.offload_stats()
+        d = {k: s1[k] - s0[k] for k in s1}
+        out.update(slots=slots, groups=w.G, ms_per_call=round(ms, 4), tokens_per_s=round(w.T / (ms * 1e-3), 1),
+                   h2d_gb_per_s=round(d["bytes_h2d"] / (ms * 1e-3 * args.steps) / 1e9, 2),
+                   loads_per_call=round(d["group_loads"] / args.steps, 2),
+                   hits_per_call=round(d["group_hits"] / args.steps, 2),
+                   prefetched_per_call=round(d["prefetched"] / args.steps, 2),
+                   passes_per_call=round(d["passes"] / args.steps, 2),
+                   note="batches rotate over 4 seeded token sets; host wall clock per call (the call "
+                        "synchronises once to read the touched groups)")
+    lay.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +274,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0,
                     help="weight copies rotated between steps (0: 2 for the decode layer, else 1)")
     ap.add_argument("--no-graph", action="store_true", help="plain stream launches only")
+    ap.add_argument("--mode", choices=("forward", "backward", "offload"), default="forward",
+                    help="backward: time moe_backward; offload: moe_forward_offload with --slots device slots")
+    ap.add_argument("--slots", type=int, default=0, help="offload mode: device group slots (0: G/2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -236,6 +305,9 @@ def main():
 
     w = WORKLOADS[args.workload]
     inputs = synth.make_layer(w)
+    if args.mode != "forward":
+        side_modes(args, w, inputs)
+        return
     copies = args.copies or (2 if w.index == 4 else 1)
     lays = [L.Layer(L.config_from_workload(w), inputs) for _ in range(copies)]
     lay = lays[0]

@@ -49,6 +49,11 @@ class moe_grads(C.Structure):
                 ("dB", C.c_void_p * 3)]
 
 
+class moe_offload_stats_t(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("calls", "group_loads", "group_hits", "prefetched", "bytes_h2d",
+                                          "passes")]
+
+
 class moe_cluster_config(C.Structure):
     _fields_ = [("E", C.c_int32), ("G", C.c_int32), ("d", C.c_int32), ("n_param", C.c_int64),
                 ("alpha", C.c_double), ("beta", C.c_double), ("tau", C.c_double), ("eps", C.c_double),
@@ -79,6 +84,9 @@ def _load():
         "moe_forward_noalloc": ([P, P, C.c_int32, P, C.POINTER(moe_route_out), P], C.c_int),
         "moe_destroy": ([P], C.c_int),
         "moe_backward": ([P, P, C.c_int32, P, P, C.POINTER(moe_grads), P], C.c_int),
+        "moe_offload_enable": ([P, C.c_int32], C.c_int),
+        "moe_forward_offload": ([P, P, C.c_int32, P, C.POINTER(moe_route_out), P], C.c_int),
+        "moe_offload_stats": ([P, C.POINTER(moe_offload_stats_t)], C.c_int),
         "moe_last_error": ([], C.c_char_p),
         "moe_config_stats": ([C.POINTER(moe_config), C.POINTER(moe_stats)], C.c_int),
         "moe_stats": ([P, C.POINTER(moe_stats)], C.c_int),
@@ -230,6 +238,25 @@ class Layer:
         check(lib.moe_forward(self.h, C.c_void_p(X.data_ptr()), T, C.c_void_p(Y.data_ptr()),
                               rop, _stream_ptr(stream)))
         return Y
+
+    def offload_enable(self, slots: int):
+        check(lib.moe_offload_enable(self.h, slots))
+
+    def forward_offload(self, X, Y=None, route_bufs=None, stream=None):
+        import torch
+        T = X.shape[0]
+        if Y is None:
+            Y = torch.empty((T, self.cfg.d), dtype=self._torch_x_dtype(), device=X.device)
+        ro = self._route_struct(route_bufs)
+        rop = C.byref(ro) if route_bufs is not None else None
+        check(lib.moe_forward_offload(self.h, C.c_void_p(X.data_ptr()), T, C.c_void_p(Y.data_ptr()), rop,
+                                      _stream_ptr(stream)))
+        return Y
+
+    def offload_stats(self) -> dict:
+        st = moe_offload_stats_t()
+        check(lib.moe_offload_stats(self.h, C.byref(st)))
+        return {n: getattr(st, n) for n, _ in moe_offload_stats_t._fields_}
 
     def backward(self, X, dY, stream=None) -> dict:
         """moe_backward: returns dX (x dtype) and float32 gradients of every

@@ -134,6 +134,7 @@ __global__ __launch_bounds__(64 * NWU) void ugemm_kernel(GemmArgs a) {
   TileCoord tc;
   if (!map_tile(blockIdx.x, a.gcounts, a.G, 32, (a.NU + BW - 1) / BW, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
+  const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = a.goffsets[g] + m0;
   const int KT = a.d / KB;
@@ -159,11 +160,11 @@ __global__ __launch_bounds__(64 * NWU) void ugemm_kernel(GemmArgs a) {
   };
   const int KS = a.d / 16;
   if constexpr (INT4) {
-    WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride, KS};
+    WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + wg * a.bw_gstride, a.bw_scale + wg * a.bws_gstride, KS};
     ws.ks0 = k0 * 4;
     run(ws);
   } else {
-    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, KS};
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + wg * a.bw_gstride / 8, KS};
     ws.ks0 = k0 * 4;
     run(ws);
   }
@@ -210,6 +211,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT <= 4) ? 2 : 1) void ugemm_
   TileCoord tc;
   if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.NU + BNT - 1) / BNT, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
+  const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nbw = (tc.nt * BNT + wave * 32 * CBT) / 32;
   const bool active = nbw * 32 < a.NU;
@@ -225,10 +227,10 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT <= 4) ? 2 : 1) void ugemm_
   zero_acc<RT, CBT>(acc);
   const int KS = a.d / 16;
   if constexpr (INT4) {
-    WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + g * a.bw_gstride, a.bw_scale + g * a.bws_gstride, KS};
+    WInt4ColK<TY> ws{static_cast<const uint32_t*>(a.Bw) + wg * a.bw_gstride, a.bw_scale + wg * a.bws_gstride, KS};
     run_tile<TY, RT, CBT>(a.d / KB, to, ws, nb0, tl, lane, acc);
   } else {
-    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, KS};
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + wg * a.bw_gstride / 8, KS};
     run_tile<TY, RT, CBT>(a.d / KB, to, ws, nb0, tl, lane, acc);
   }
   if (!active) return;
@@ -292,6 +294,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   TileCoord tc;
   if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (N + BNFT - 1) / BNFT, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
+  const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nbw = KS ? tc.nt * CB : (tc.nt * BNF + wave * 64) / 32;
   const bool active = nbw * 32 < N;
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     });
     using WO = WDirect<WPlain<TY>, CB>;
     WO wo;
-    wo.src = WPlain<TY>{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
+    wo.src = WPlain<TY>{static_cast<const F*>(a.Bw) + wg * a.bw_gstride / 8, a.d / 16};
     wo.src.ks0 = k0 * 4;
     wo.nb0 = nb0;
     Mainloop<TY, 1, CB, TD, WO, 2> ml{td, wo, lane};
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
       const int m = blk * 32 + r;
       return m0 + m < M ? (long)(a.garow[row0 + s_perm[m]] / a.kg) : -1L;
     });
-    WPlain<TY> ws{static_cast<const F*>(a.Bw) + g * a.bw_gstride / 8, a.d / 16};
+    WPlain<TY> ws{static_cast<const F*>(a.Bw) + wg * a.bw_gstride / 8, a.d / 16};
     run_tile<TY, RT>(a.d / KB, to, ws, nb0, tl, lane, acc);  // ends with a barrier
   }
 
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   // issue the loads of step (t, j)
   auto load_ops = [&](int t, int j, EOps<TY, PIN, NFB>& o) __attribute__((always_inline)) {
     const int m = t * 32 + (lane & 31);
-    const int ex = g * K + j;
+    const int ex = wg * K + j;
     o.wgt = s_w[m * K + j];
     o.slot = s_slot[m * K + j];
     if constexpr (RES != ER_NONE) {
@@ -715,6 +718,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
   TileCoord tc;
   if (!map_tile(blockIdx.x / S, a.gcounts, a.G, BMT, (a.d + BNF - 1) / BNF, tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
+  const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nbw = (tc.nt * BNF + wave * 64) / 32;
   const bool active = nbw * 32 < a.d;
@@ -734,7 +738,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
     // hbar . W2_base^g over this split's stages
     TShared<TY, TY, RT> to;
     to.init(static_cast<const TE<TY>*>(a.H) + (long)k0 * KB, a.f, rows);
-    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8 + (long)k0 * 4 * 64, a.f / 16};
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + wg * a.bw_gstride / 8 + (long)k0 * 4 * 64, a.f / 16};
     run_tile<TY, RT>(k1 - k0, to, ws, nb0, tl, lane, acc);
   }
   if (a.NV > 0 && split == 0) {
@@ -743,11 +747,11 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
     to.init(static_cast<const TE<TY>*>(a.V), a.NV, rows);
     const int KS = a.NV / 16;
     if constexpr (INT4) {
-      WInt4Tail<TY> ws{static_cast<const uint32_t*>(a.Bd) + g * a.bd_gstride,
-                       a.bd_scale + (long)g * a.K * (a.d / 32) * RPAD, KS, a.K, a.d / 32};
+      WInt4Tail<TY> ws{static_cast<const uint32_t*>(a.Bd) + wg * a.bd_gstride,
+                       a.bd_scale + (long)wg * a.K * (a.d / 32) * RPAD, KS, a.K, a.d / 32};
       run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, lane, acc);
     } else {
-      WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bd) + g * a.bd_gstride / 8, KS};
+      WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bd) + wg * a.bd_gstride / 8, KS};
       run_tile<TY, RT>(a.NV / KB, to, ws, nb0, tl, lane, acc);
     }
   }
@@ -791,6 +795,7 @@ __global__ __launch_bounds__(256) void gemm2k_kernel(GemmArgs a) {
   TileCoord tc;
   if (!map_tile(blockIdx.x, a.gcounts, a.G, 32 * RT, (a.d + CB_ * 32 - 1) / (CB_ * 32), tc)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
+  const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = a.goffsets[g] + m0;
   const int nb0 = tc.nt * CB_;
@@ -817,18 +822,18 @@ __global__ __launch_bounds__(256) void gemm2k_kernel(GemmArgs a) {
   {
     const int KT = a.f / KB;
     const int k0 = wave * KT / 4, k1 = (wave + 1) * KT / 4;
-    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + g * a.bw_gstride / 8, a.f / 16};
+    WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bw) + wg * a.bw_gstride / 8, a.f / 16};
     ws.ks0 = k0 * 4;
     run(static_cast<const TE<TY>*>(a.H) + (long)k0 * KB, a.f, ws, k1 - k0);
   }
   if (a.NV > 0 && wave == 3) {
     const int KS = a.NV / 16;
     if constexpr (INT4) {
-      WInt4Tail<TY> ws{static_cast<const uint32_t*>(a.Bd) + g * a.bd_gstride,
-                       a.bd_scale + (long)g * a.K * (a.d / 32) * RPAD, KS, a.K, a.d / 32};
+      WInt4Tail<TY> ws{static_cast<const uint32_t*>(a.Bd) + wg * a.bd_gstride,
+                       a.bd_scale + (long)wg * a.K * (a.d / 32) * RPAD, KS, a.K, a.d / 32};
       run(static_cast<const TE<TY>*>(a.V), a.NV, ws, a.NV / KB);
     } else {
-      WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bd) + g * a.bd_gstride / 8, KS};
+      WPlain<TY> ws{static_cast<const FragT<TY>*>(a.Bd) + wg * a.bd_gstride / 8, KS};
       run(static_cast<const TE<TY>*>(a.V), a.NV, ws, a.NV / KB);
     }
   }

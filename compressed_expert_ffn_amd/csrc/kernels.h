@@ -121,6 +121,7 @@ struct GemmArgs {
   int* zero_ptr;        // cleared by the output GEMM's first block
   int zero_n;
   int rows_sorted;      // G1: group lists already ordered by expert set (tiles keep that order)
+  const int* gslot;     // weights of group g sit at slot gslot[g] of the weight arrays (null: g)
 };
 
 struct VReduceArgs {

@@ -218,6 +218,43 @@ typedef struct {
 int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* dX,
                  const moe_grads* grads, void* stream);
 
+/* ---- idle-group offload ---------------------------------------------------
+ * Whole groups of experts (a group's base and its experts' residual factors:
+ * the unit the grouping makes, "Breaking the MoE LLM Trilemma" key design 4)
+ * move to pinned host memory, and `slots` device slots hold the groups in
+ * use; a group is swapped in when a batch routes tokens to it, the least
+ * recently used resident group making room ("混合专家模型的路由机制与工程落地",
+ * jiusizaji.com, section 6.2: swap inactive experts out, swap them in on
+ * use, prefetch from the current batch's routing what the next batch will
+ * need).  moe_offload_enable converts a created handle (synchronous;
+ * 1 <= slots <= G); afterwards only moe_forward_offload and moe_route run on
+ * it (moe_forward, moe_forward_noalloc and moe_backward return
+ * MOE_ERR_UNSUPPORTED). */
+typedef struct {
+  int64_t calls;        /* moe_forward_offload calls */
+  int64_t group_loads;  /* groups copied in because a batch needed them */
+  int64_t group_hits;   /* needed groups that were already resident */
+  int64_t prefetched;   /* groups copied in ahead of use (by recent use) */
+  int64_t bytes_h2d;    /* host-to-device bytes of group weights */
+  int64_t passes;       /* GEMM passes (more than one when a batch needs more groups than slots) */
+} moe_offload_stats_t;
+
+int moe_offload_enable(moe_handle* h, int32_t slots);
+
+/* The layer with offloaded groups: routing on the device, then the host reads
+ * which groups the batch touches (one device-to-host copy of the group counts
+ * and a synchronisation of stream), copies the missing groups into slots on a
+ * copy stream, and runs the grouped GEMMs once the copies of their groups
+ * are done.  A batch that needs more groups than slots runs in passes of
+ * slots/2 groups, the next pass's copies overlapping the current pass's
+ * GEMMs.  After the batch, groups used often recently are copied into slots
+ * of groups used less (prefetch).  Results equal moe_forward's.  Arguments as
+ * moe_forward; calls on one handle must use one stream. */
+int moe_forward_offload(moe_handle* h, const void* X, int32_t T, void* Y,
+                        const moe_route_out* routing, void* stream);
+
+int moe_offload_stats(const moe_handle* h, moe_offload_stats_t* out);
+
 /* Free everything the handle owns (synchronises the device first).  NULL is
  * a no-op. */
 int moe_destroy(moe_handle* h);
