@@ -49,7 +49,12 @@ struct TileCoord {
 
 // The group counts (G <= 256) are loaded by all lanes at once and walked
 // with lane reads, so a workgroup pays one load latency here, not G.
-__device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileCoord& tc) {
+// S > 1 (a k split of the down projection): the logical tiles are the S
+// splits of every tile with the split outermost, so an XCD's contiguous run
+// stays inside one split, where neighbouring tiles share rows or weight
+// columns (the splits of one tile share nothing); *split receives it.
+__device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileCoord& tc, int S = 1,
+                         int* split = nullptr) {
   const int lane = threadIdx.x & 63;
   int cnt[4];
 #pragma unroll
@@ -65,10 +70,13 @@ __device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileC
   };
   int total = 0;
   for (int gg = 0; gg < G; ++gg) total += (count_of(gg) + BM - 1) / BM * NT;
-  if (i >= total) return false;
+  const int all = total * S;
+  if (i >= all) return false;
   const int x = i & 7, j = i >> 3;
-  const int q = total >> 3, rem = total & 7;
+  const int q = all >> 3, rem = all & 7;
   int L = x * q + min(x, rem) + j;
+  if (split) *split = L / total;
+  L %= total;
   for (int gg = 0; gg < G; ++gg) {
     const int Mg = count_of(gg);
     const int mt = (Mg + BM - 1) / BM;
@@ -714,9 +722,9 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
     for (int i = threadIdx.x; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
   }
   const int S = a.ksplit;
-  const int split = blockIdx.x % S;
+  int split = 0;
   TileCoord tc;
-  if (!map_tile(blockIdx.x / S, a.gcounts, a.G, BMT, (a.d + BNF - 1) / BNF, tc)) return;
+  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.d + BNF - 1) / BNF, tc, S, &split)) return;
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
