@@ -686,15 +686,16 @@ int weights_to_host(const moe_config& c, const moe_weights* w, moe_weights* hw,
 // kept).  U, E and the residual factors are kept as float32 for the
 // elementwise steps; GEMM operands are in the MFMA type.
 struct BwdState {
-  void *W1T = nullptr, *W1N = nullptr, *W2N = nullptr, *AtT = nullptr, *BdT = nullptr;
+  void *W1T = nullptr, *W1N = nullptr, *W2N = nullptr, *AtT = nullptr, *BdT = nullptr, *A1T = nullptr;
   float *Atp = nullptr, *B1p = nullptr, *Adp = nullptr;
   int NUb = 0, NEb = 0;
-  long Kg = 0, Ke = 0;
-  int *counts = nullptr, *offsets = nullptr, *perm = nullptr, *arow = nullptr, *grow = nullptr;
-  int *kpad_g = nullptr, *kpad_e = nullptr;
-  float *Zb = nullptr, *U = nullptr, *D = nullptr, *Eb = nullptr, *dZbar = nullptr, *hbar = nullptr;
-  float *q = nullptr, *wu2 = nullptr, *dw = nullptr, *ua = nullptr, *ea = nullptr, *dXb = nullptr, *ds = nullptr;
-  void *dz = nullptr, *wh = nullptr;
+  long Kg = 0, Ke = 0, part_cap = 0;
+  int *counts = nullptr, *offsets = nullptr, *perm = nullptr, *arow = nullptr, *apos = nullptr, *prow = nullptr;
+  int *grow = nullptr, *kpad_g = nullptr, *kpad_e = nullptr;
+  float *Zb = nullptr, *U = nullptr, *D = nullptr, *Eb = nullptr, *pw = nullptr, *part = nullptr;
+  float *q = nullptr, *wu2 = nullptr, *dw = nullptr, *ua = nullptr, *ea = nullptr, *dXb = nullptr, *dXr = nullptr;
+  float *ds = nullptr;
+  void *dz = nullptr, *wh = nullptr, *dZbar = nullptr, *hbar = nullptr;
   void *XTg = nullptr, *dZT = nullptr, *hbT = nullptr, *dYTg = nullptr, *dsdeT = nullptr;
   void *XTe = nullptr, *dYTe = nullptr, *qT = nullptr, *uT = nullptr, *dzT = nullptr, *whT = nullptr;
   void *eT = nullptr, *wu2T = nullptr;
@@ -1490,29 +1491,33 @@ int prepare_backward(moe_handle* h) {
     if (e != hipSuccess) return hip_fail(h, e, "backward factor decode");
     TRY(alloc_bytes(&B->AtT, (size_t)G * B->NUb * d * es));
     TRY(alloc_bytes(&B->BdT, (size_t)G * B->NEb * d * es));
+    TRY(alloc_bytes(&B->A1T, (size_t)E * d * 64 * es));
     e = launch_stack_factors(ty, B->Atp, G, K, Pin, d, B->NUb, B->AtT, st);
     if (e == hipSuccess) e = launch_stack_factors(ty, Bdp, G, K, 1, d, B->NEb, B->BdT, st);
+    if (e == hipSuccess) e = launch_a1t(ty, B->Atp, E, Pin, d, B->A1T, st);
     if (e != hipSuccess) return hip_fail(h, e, "backward factor stacking");
   }
   // workspace for T_max tokens
   B->Kg = R + 64L * G;
   B->Ke = Na + 64L * E;
+  // act_splits(Na) * Na <= 1024 * 64 + Na for every Na
+  B->part_cap = 1024L * 64 + Na;
   TRY(alloc_i(&B->counts, E));
   TRY(alloc_i(&B->offsets, E + 1));
   TRY(alloc_i(&B->perm, Na));
   TRY(alloc_i(&B->arow, Na));
+  TRY(alloc_i(&B->apos, Na));
+  TRY(alloc_i(&B->prow, Na));
   TRY(alloc_i(&B->grow, R));
   TRY(alloc_i(&B->kpad_g, G + 1));
   TRY(alloc_i(&B->kpad_e, E + 1));
+  TRY(alloc_f(&B->pw, (size_t)Na));
+  TRY(alloc_f(&B->part, (size_t)B->part_cap * ACT_PART));
   TRY(alloc_f(&B->Zb, (size_t)R * Pin * f));
   TRY(alloc_f(&B->D, (size_t)R * f));
-  TRY(alloc_f(&B->dZbar, (size_t)R * Pin * f));
-  TRY(alloc_f(&B->hbar, (size_t)R * f));
-  TRY(alloc_f(&B->q, (size_t)Na * Pin * 16));
-  TRY(alloc_f(&B->wu2, (size_t)Na * 16));
+  TRY(alloc_bytes(&B->dZbar, (size_t)R * Pin * f * es));
+  TRY(alloc_bytes(&B->hbar, (size_t)R * f * es));
   TRY(alloc_f(&B->dw, (size_t)Na));
-  TRY(alloc_f(&B->ua, (size_t)Na * Pin * 16));
-  TRY(alloc_f(&B->ea, (size_t)Na * 16));
   TRY(alloc_f(&B->dXb, (size_t)R * d));
   TRY(alloc_f(&B->ds, (size_t)R * (1 + K)));
   TRY(alloc_bytes(&B->dz, (size_t)Na * Pin * f * es));
@@ -1525,6 +1530,11 @@ int prepare_backward(moe_handle* h) {
   if (r > 0) {
     TRY(alloc_f(&B->U, (size_t)R * B->NUb));
     TRY(alloc_f(&B->Eb, (size_t)R * B->NEb));
+    TRY(alloc_f(&B->q, (size_t)Na * 64));
+    TRY(alloc_f(&B->wu2, (size_t)Na * 16));
+    TRY(alloc_f(&B->ua, (size_t)Na * 64));
+    TRY(alloc_f(&B->ea, (size_t)Na * 16));
+    TRY(alloc_f(&B->dXr, (size_t)Na * d));
     TRY(alloc_bytes(&B->XTe, (size_t)d * B->Ke * es));
     TRY(alloc_bytes(&B->dYTe, (size_t)d * B->Ke * es));
     TRY(alloc_bytes(&B->qT, (size_t)Pin * 16 * B->Ke * es));
@@ -1538,6 +1548,15 @@ int prepare_backward(moe_handle* h) {
   if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_ERR_HIP, "backward set-up failed");
   h->bwd = B.release();
   return MOE_OK;
+}
+
+// Column splits of the activation backward: enough workgroups for the chip
+// (about 1024) when there are few 64-position tiles.
+int act_splits(long Na, int f) {
+  const long tiles = std::max(1L, (Na + 63) / 64);
+  long ns = (1024 + tiles - 1) / tiles;
+  ns = std::min<long>(ns, f / 64);
+  return (int)std::max(1L, ns);
 }
 
 BGemmArgs rgemm(const Workspace& ws, const int* gcounts, const int* goffsets, int G, long R, const void* a, long lda,
@@ -1668,79 +1687,105 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   if (r > 0)
     ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->BdT,
                               (long)B->NEb * d, B->NEb, d, B->Eb, B->NEb), st));
+  // per expert-list position: assignment, row, weight, u and e
+  const int ke = c.top_experts;
+  ok(launch_invert_rows(garow, (int)R, B->grow, st));
+  ok(launch_pad_scan(B->counts, E, B->kpad_e, st));
   {
-    ActBwdArgs aa{};
-    aa.R = (int)R;
+    AssignArgs as{};
+    as.Na = (int)Na;
+    as.E = E;
+    as.K = K;
+    as.k = k;
+    as.ke = ke;
+    as.Pin = Pin;
+    as.r = r;
+    as.perm = B->perm;
+    as.offsets = B->offsets;
+    as.idx = live.idx;
+    as.w = live.w;
+    as.grow = B->grow;
+    as.U = B->U;
+    as.NU = B->NUb;
+    as.Eb = B->Eb;
+    as.NE = B->NEb;
+    as.arow = B->arow;
+    as.apos = B->apos;
+    as.prow = B->prow;
+    as.pw = B->pw;
+    as.ua = B->ua;
+    as.ea = B->ea;
+    ok(launch_gather_assign(as, st));
+  }
+  // activation backward over expert tiles, then the per-position sums
+  const int NS = act_splits(Na, f);
+  if ((long)NS * Na > B->part_cap) return fail(MOE_ERR_UNSUPPORTED, "activation partials exceed their buffer");
+  {
+    ActArgs aa{};
+    aa.Na = (int)Na;
+    aa.E = E;
     aa.f = f;
     aa.Pin = Pin;
-    aa.K = K;
-    aa.kg = kg;
-    aa.ke = c.top_experts;
-    aa.k = k;
     aa.act = c.act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
-    aa.gcounts = live.gcounts;
-    aa.goffsets = live.goffsets;
-    aa.garow = garow;
-    aa.idx = live.idx;
-    aa.w = live.w;
-    aa.Zb = B->Zb;
-    aa.U = B->U;
-    aa.NU = B->NUb;
-    aa.B1p = B->B1p;
-    aa.Adp = B->Adp;
-    aa.D = B->D;
-    aa.Eb = B->Eb;
-    aa.NE = B->NEb;
     aa.r = r;
-    aa.dZbar = B->dZbar;
-    aa.hbar = B->hbar;
-    aa.dz = B->dz;
-    aa.wh = B->wh;
-    aa.q = B->q;
-    aa.wu2 = B->wu2;
-    aa.dw = B->dw;
+    aa.NS = NS;
+    aa.offsets = B->offsets;
+    aa.counts = B->counts;
+    aa.kpad = B->kpad_e;
+    aa.prow = B->prow;
+    aa.pw = B->pw;
     aa.ua = B->ua;
     aa.ea = B->ea;
-    ok(launch_act_bwd(ty, aa, st));
+    aa.Zb = B->Zb;
+    aa.D = B->D;
+    aa.B1p = B->B1p;
+    aa.Adp = B->Adp;
+    aa.dz = B->dz;
+    aa.wh = B->wh;
+    aa.part = B->part;
+    ok(launch_act(ty, aa, st));
   }
-  // dX: base part per group row, then per token with the residual and router terms
-  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, MOE_F32, nullptr, 1,
+  ok(launch_act_finish(B->part, NS, (int)Na, Pin, r, B->pw, B->ea, B->arow, B->q, B->wu2, B->dw, st));
+  ok(launch_row_sums(ty, B->dz, B->wh, garow, B->apos, (int)R, kg, ke, k, f, Pin, B->dZbar, B->hbar, st));
+  // dX: base part per group row, residual part per position, then per token
+  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, ty, nullptr, 1,
                             B->W1N, (long)Pin * f * d, d, Pin * f, B->dXb, d), st));
-  ok(launch_invert_rows(garow, (int)R, B->grow, st));
+  if (r > 0)
+    ok(launch_bgemm(ty, rgemm(h->ws, B->counts, B->offsets, E, Na, B->q, 64, MOE_F32, nullptr, 1, B->A1T,
+                              (long)d * 64, d, 64, B->dXr, d), st));
   {
-    TokBwdArgs ta{};
+    TokArgs ta{};
     ta.T = T;
     ta.d = d;
     ta.G = G;
     ta.K = K;
     ta.kg = kg;
-    ta.ke = c.top_experts;
+    ta.ke = ke;
     ta.k = k;
-    ta.Pin = Pin;
     ta.r = r;
     ta.idx = live.idx;
     ta.gidx = live.gidx;
     ta.w = live.w;
     ta.dw = B->dw;
     ta.grow = B->grow;
+    ta.apos = B->apos;
     ta.dXb = B->dXb;
-    ta.q = B->q;
-    ta.Atp = B->Atp;
+    ta.dXr = B->dXr;
     ta.Wr = h->Wr;
     ta.NCp = h->NCp;
     ta.ds = B->ds;
     ta.dX = dX;
     ta.x_dtype = c.x_dtype;
-    ok(launch_tok_bwd(ta, st));
+    ok(launch_tok(ta, st));
   }
   // weight gradients over each group's rows
   ok(launch_pad_scan(live.gcounts, G, B->kpad_g, st));
   const long Kg = B->Kg;
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, X, c.x_dtype, d, 0, d, garow, kg, B->XTg,
                                  Kg, Kg), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->dZbar, MOE_F32, (long)Pin * f, 0,
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->dZbar, ty, (long)Pin * f, 0,
                                  Pin * f, nullptr, 1, B->dZT, Kg, Kg), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->hbar, MOE_F32, f, 0, f, nullptr, 1,
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->hbar, ty, f, 0, f, nullptr, 1,
                                  B->hbT, Kg, Kg), st));
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, dY, c.x_dtype, d, 0, d, garow, kg,
                                  B->dYTg, Kg, Kg), st));
@@ -1769,20 +1814,19 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   // residual factor gradients over each expert's assignments
   if (r > 0) {
     const long Ke = B->Ke;
-    ok(launch_assign_rows(B->perm, B->offsets, live.idx, E, k, (int)Na, B->arow, st));
-    ok(launch_pad_scan(B->counts, E, B->kpad_e, st));
-    auto eg = [&](const void* in, int dt, long ld, int ncols, int div, void* out) {
-      ok(launch_gather_t(ty, tgather(E, B->offsets, B->counts, B->kpad_e, in, dt, ld, 0, ncols, B->arow, div, out, Ke,
+    // X and dY rows by token; the rest is stored by position already
+    auto eg = [&](const void* in, int dt, long ld, int ncols, const int* map, int div, void* out) {
+      ok(launch_gather_t(ty, tgather(E, B->offsets, B->counts, B->kpad_e, in, dt, ld, 0, ncols, map, div, out, Ke,
                                      Ke), st));
     };
-    eg(X, c.x_dtype, d, d, k, B->XTe);
-    eg(dY, c.x_dtype, d, d, k, B->dYTe);
-    eg(B->q, MOE_F32, (long)Pin * 16, Pin * 16, 1, B->qT);
-    eg(B->ua, MOE_F32, (long)Pin * 16, Pin * 16, 1, B->uT);
-    eg(B->dz, ty, (long)Pin * f, Pin * f, 1, B->dzT);
-    eg(B->wh, ty, f, f, 1, B->whT);
-    eg(B->ea, MOE_F32, 16, 16, 1, B->eT);
-    eg(B->wu2, MOE_F32, 16, 16, 1, B->wu2T);
+    eg(X, c.x_dtype, d, d, B->arow, k, B->XTe);
+    eg(dY, c.x_dtype, d, d, B->arow, k, B->dYTe);
+    eg(B->q, MOE_F32, 64, Pin * 16, nullptr, 1, B->qT);
+    eg(B->ua, MOE_F32, 64, Pin * 16, nullptr, 1, B->uT);
+    eg(B->dz, ty, (long)Pin * f, Pin * f, nullptr, 1, B->dzT);
+    eg(B->wh, ty, f, f, nullptr, 1, B->whT);
+    eg(B->ea, MOE_F32, 16, 16, nullptr, 1, B->eT);
+    eg(B->wu2, MOE_F32, 16, 16, nullptr, 1, B->wu2T);
     for (int p = 0; p < Pin; ++p) {
       ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, B->XTe, Ke, static_cast<char*>(B->qT) + (size_t)p * 16 * Ke * es,
                                 Ke, d, 16, gr->dA[p], (long)d * r, r, r), st));

@@ -71,60 +71,91 @@ hipError_t launch_pad_scan(const int* count, int S, int* kpad_off, hipStream_t s
 hipError_t launch_frag_to_plain(int ty, const void* frag, int G, long g_stride_in, int N, int Kd, int swiglu_f,
                                 bool transpose, void* out, long g_stride_out, long ld_out, hipStream_t st);
 
-// Per-row backward of the activation and the residual epilogue.
-struct ActBwdArgs {
-  int R, f, Pin, K, kg, ke, k, act;
-  const int* gcounts;
-  const int* goffsets;
-  const int* garow;     // row -> t*kg + group rank
-  const int* idx;       // [T][k]
-  const float* w;       // [T][k]
-  const float* Zb;      // [R][Pin f]
-  const float* U;       // [R][NU] (u of expert j, projection p at (j Pin + p) 16)
+// Per expert-list position p (expert-major, tokens ascending inside an
+// expert): the assignment t*k + slot, its group row, gate weight and the
+// row's u and e vectors of that expert, gathered once; apos inverts arow.
+struct AssignArgs {
+  int Na, E, K, k, ke, Pin, r;
+  const int* perm;     // [Na] token of position p
+  const int* offsets;  // [E+1]
+  const int* idx;      // [T][k]
+  const float* w;      // [T][k]
+  const int* grow;     // [T kg] (t, group rank) -> group row
+  const float* U;      // [R][NU]: u of expert j, projection p at (j Pin + p) 16
   int NU;
-  const float* B1p;     // [E][Pin][f][16]
-  const float* Adp;     // [E][f][16]
-  const float* D;       // [R][f]
-  const float* Eb;      // [R][NE] (e of expert j at j 16)
+  const float* Eb;     // [R][NE]: e of expert j at j 16
   int NE;
-  int r;                // residual rank (0: no residual)
-  float* dZbar;         // [R][Pin f]
-  float* hbar;          // [R][f]
-  void* dz;             // [T k][Pin f] TY
-  void* wh;             // [T k][f] TY
-  float* q;             // [T k][Pin 16]
-  float* wu2;           // [T k][16]
-  float* dw;            // [T k]
-  float* ua;            // [T k][Pin 16] u of the assignment's expert
-  float* ea;            // [T k][16]    e of the assignment's expert
+  int* arow;           // [Na]  t*k + slot
+  int* apos;           // [T k] position of (t, slot)
+  int* prow;           // [Na]  group row
+  float* pw;           // [Na]  gate weight
+  float* ua;           // [Na][64]  u_gate | u_up | zeros (r > 0)
+  float* ea;           // [Na][16]  (r > 0)
 };
-hipError_t launch_act_bwd(int ty, const ActBwdArgs& a, hipStream_t st);
+hipError_t launch_gather_assign(const AssignArgs& a, hipStream_t st);
 
-// Per-token router backward and dX assembly.
-struct TokBwdArgs {
-  int T, d, G, K, kg, ke, k, Pin, r;
+// Activation backward over tiles of 64 positions of one expert, column
+// split blockIdx.y of NS: z = Z + u B1^T, dh = w (D + e A2^T), h = act(z),
+// dz = act'(z) dh.  Writes dz [Na][Pin f] and w h [Na][f] (type TY) and,
+// per position and split, the column sums (dz_gate B1_gate, dz_up B1_up,
+// h A2, <D, h>) to part[s][p][0..49).
+struct ActArgs {
+  int Na, E, f, Pin, act, r, NS;
+  const int* offsets;
+  const int* counts;
+  const int* kpad;     // [E+1] 64-padded prefix of counts (tile walk)
+  const int* prow;
+  const float* pw;
+  const float* ua;
+  const float* ea;
+  const float* Zb;     // [R][Pin f]
+  const float* D;      // [R][f]
+  const float* B1p;    // [E][Pin][f][16]
+  const float* Adp;    // [E][f][16]
+  void* dz;
+  void* wh;
+  float* part;         // [NS][Na][64]
+};
+constexpr int ACT_PART = 64;
+hipError_t launch_act(int ty, const ActArgs& a, hipStream_t st);
+
+// Sums the NS partials of each position in split order: q[p][0..Pin 16)
+// (q[p][Pin 16..64) = 0), wu2[p] = w_p (h A2), dw[arow[p]] = <D, h> + <e, h A2>.
+hipError_t launch_act_finish(const float* part, int NS, int Na, int Pin, int r, const float* pw, const float* ea,
+                             const int* arow, float* q, float* wu2, float* dw, hipStream_t st);
+
+// dZbar[row] = sum over the row's ke assignments (slot order) of dz and
+// hbar[row] likewise of w h; fp32 sums stored in type TY.
+hipError_t launch_row_sums(int ty, const void* dz, const void* wh, const int* garow, const int* apos, int R, int kg,
+                           int ke, int k, int f, int Pin, void* dZbar, void* hbar, hipStream_t st);
+
+// Per-token router backward and dX assembly: dX = sum over the token's
+// group rows of dXb + sum over its assignments of dXr + router terms.
+struct TokArgs {
+  int T, d, G, K, kg, ke, k, r;
   const int* idx;
   const int* gidx;
   const float* w;
-  const float* dw;
-  const int* grow;      // [T][kg]: group row of (t, group rank)
+  const float* dw;      // [T k]
+  const int* grow;      // [T kg]
+  const int* apos;      // [T k]
   const float* dXb;     // [R][d]
-  const float* q;       // [T k][Pin 16]
-  const float* Atp;     // [E][Pin][d][16]
+  const float* dXr;     // [Na][d] (r > 0)
   const float* Wr;      // router matrix [d/16][NCp][16]
   int NCp;
-  float* ds;            // [T][kg] group-logit gradients
-  float* de;            // [T][kg][K] expert-logit gradients (zero for unchosen)
-  void* dX;             // [T][d] x dtype
+  float* ds;            // [T kg][1 + K] group / expert logit gradients
+  void* dX;
   int x_dtype;
 };
-hipError_t launch_tok_bwd(const TokBwdArgs& a, hipStream_t st);
+hipError_t launch_tok(const TokArgs& a, hipStream_t st);
 
 // row -> t*kg + rank map inverse: grow[t*kg + rank] = row
 hipError_t launch_invert_rows(const int* garow, int R, int* grow, hipStream_t st);
-// arow[p] = t*k + slot of expert-list position p (perm, offsets from moe_route)
-hipError_t launch_assign_rows(const int* perm, const int* offsets, const int* idx, int E, int k, int Na,
-                              int* arow, hipStream_t st);
+
+// A1T[e][n][p*16 + rho] = Atp[e][p][n][rho] in type TY, zero for k >= Pin*16
+// (the k-major operand of dXr = q A1^T, K = 64).
+hipError_t launch_a1t(int ty, const float* Atp, int E, int Pin, int d, void* A1T, hipStream_t st);
+
 hipError_t launch_zero_f(float* p, long n, hipStream_t st);
 // out[s * ld_out + c] = sum over the rows of segment s of in[map(row)][c], c < ncols
 hipError_t launch_seg_colsum(const float* in, long ld_in, int ncols, const int* start, const int* count,

@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(256) bgemm_kernel(BGemmArgs a) {
   int s = 0, m0 = 0, M = 0, K = 0, n0 = 0;
   long crow0 = 0, kofs = 0;
   if (a.mode == 0) {
-    // walk the segments' row tiles (S <= 256)
+    // walk the segments' row tiles (S <= 1024)
     int i = blockIdx.x;
     n0 = (i % NT) * BT;
     i /= NT;
@@ -193,127 +193,279 @@ __device__ __forceinline__ float gelu_t(float z, float& dgelu) {
   return 0.5f * z * (1.0f + t);
 }
 
-// block-wide sum of NV values per thread (256 threads), result in red[0..NV)
-template <int NV>
-__device__ void block_sum(float (&v)[NV], float* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    float x = v[i];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    v[i] = x;
+// Four consecutive values of type TY, as one 8- or 16-byte access.
+template <int TY>
+__device__ __forceinline__ void store4(TE<TY>* p, const float (&v)[4]) {
+  if constexpr (TY == DT_F32) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint2 u;
+    u.x = (uint32_t)from_f32<TY>(v[0]) | ((uint32_t)from_f32<TY>(v[1]) << 16);
+    u.y = (uint32_t)from_f32<TY>(v[2]) | ((uint32_t)from_f32<TY>(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
   }
-  __syncthreads();
-  if (lane == 0)
+}
+template <int TY>
+__device__ __forceinline__ void load4_add(const TE<TY>* p, float (&v)[4]) {
+  if constexpr (TY == DT_F32) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const uint16_t h[4] = {(uint16_t)(u.x & 0xFFFFu), (uint16_t)(u.x >> 16), (uint16_t)(u.y & 0xFFFFu),
+                           (uint16_t)(u.y >> 16)};
 #pragma unroll
-    for (int i = 0; i < NV; ++i) red[wv * NV + i] = v[i];
-  __syncthreads();
-  if (tid < NV) red[4 * NV + tid] = red[tid] + red[NV + tid] + red[2 * NV + tid] + red[3 * NV + tid];
-  __syncthreads();
+    for (int i = 0; i < 4; ++i) v[i] += load_as_f32<TY>(h, i);
+  }
 }
 
-// One workgroup per group row; the row's chosen experts one after another.
-template <int TY>
-__global__ void __launch_bounds__(256) act_bwd_kernel(ActBwdArgs a) {
-  const int row = blockIdx.x;
-  if (row >= a.R) return;
-  __shared__ float red[5 * 49];
-  const int ar = a.garow[row];
-  const int t = ar / a.kg, rank = ar % a.kg;
-  const int f = a.f, Pin = a.Pin, tid = threadIdx.x;
-  const float* zb = a.Zb + (long)row * Pin * f;
-  const float* dr = a.D + (long)row * f;
-  float* dzb = a.dZbar + (long)row * Pin * f;
-  float* hb = a.hbar + (long)row * f;
-  for (int c = tid; c < f; c += 256) {
-    hb[c] = 0.f;
-    for (int p = 0; p < Pin; ++p) dzb[p * f + c] = 0.f;
+// Per expert-list position: assignment, row, weight and the u / e vectors.
+__global__ void gather_assign_kernel(AssignArgs a) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= a.Na) return;
+  // expert of position p: the last e with offsets[e] <= p
+  int lo = 0, hi = a.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.offsets[mid] <= p) lo = mid;
+    else hi = mid - 1;
   }
-  for (int sl = 0; sl < a.ke; ++sl) {
-    const int slot = rank * a.ke + sl;
-    const long asg = (long)t * a.k + slot;
-    const int i = a.idx[asg];
-    const int j = i % a.K;
-    const float wt = a.w[asg];
-    float ug[16], uu[16], ev[16];
+  const int t = a.perm[p];
+  int slot = 0;
+  for (int s = 0; s < a.k; ++s)
+    if (a.idx[(long)t * a.k + s] == lo) slot = s;
+  const long asg = (long)t * a.k + slot;
+  a.arow[p] = (int)asg;
+  a.apos[asg] = p;
+  const int row = a.grow[(long)t * (a.k / a.ke) + slot / a.ke];
+  a.prow[p] = row;
+  a.pw[p] = a.w[asg];
+  if (a.r > 0) {
+    const int j = lo % a.K;
+    const float* u = a.U + (long)row * a.NU + (long)j * a.Pin * 16;
+    float* uo = a.ua + (long)p * 64;
+    for (int x = 0; x < 64; ++x) uo[x] = x < a.Pin * 16 ? u[x] : 0.f;
+    const float* ev = a.Eb + (long)row * a.NE + j * 16;
+    for (int x = 0; x < 16; ++x) a.ea[(long)p * 16 + x] = ev[x];
+  }
+}
+
+// A workgroup takes 64 positions of one expert (4 lanes per position, each
+// lane 4 consecutive columns of every 16) over its split's 64-column chunks;
+// the chunk's factor rows B1_gate, B1_up, A2 [64][16] sit in LDS, so each is
+// read from memory once per tile instead of once per assignment.  The
+// column sums stay in registers and are reduced over the 4 lanes at the end.
+template <int TY, int PIN, bool RES>
+__global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
+  __shared__ float4 fs[3][64][4];
+  const int tile = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  if (tile * 64 >= a.kpad[a.E]) return;
+  // expert of the tile: the last e with kpad[e] <= tile * 64 (never empty)
+  int lo = 0, hi = a.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.kpad[mid] <= tile * 64) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int p0 = a.offsets[e] + (tile * 64 - a.kpad[e]);
+  const int n = min(64, a.offsets[e] + a.counts[e] - p0);
+  const int pl = tid >> 2, cg = tid & 3;
+  const bool valid = pl < n;
+  const int p = valid ? p0 + pl : p0;
+  const int f = a.f;
+  const int row = a.prow[p];
+  const float wt = valid ? a.pw[p] : 0.f;
+  float ug[16], uu[16], ev[16];
+  float qg[16], qu[16], u2[16], dd = 0.f;
 #pragma unroll
-    for (int rho = 0; rho < 16; ++rho) {
-      ug[rho] = a.r ? a.U[(long)row * a.NU + (j * Pin + 0) * 16 + rho] : 0.f;
-      uu[rho] = (a.r && Pin > 1) ? a.U[(long)row * a.NU + (j * Pin + 1) * 16 + rho] : 0.f;
-      ev[rho] = a.r ? a.Eb[(long)row * a.NE + j * 16 + rho] : 0.f;
+  for (int x = 0; x < 16; ++x) {
+    ug[x] = RES ? a.ua[(long)p * 64 + x] : 0.f;
+    uu[x] = (RES && PIN > 1) ? a.ua[(long)p * 64 + 16 + x] : 0.f;
+    ev[x] = RES ? a.ea[(long)p * 16 + x] : 0.f;
+    qg[x] = qu[x] = u2[x] = 0.f;
+  }
+  const int nch = f / 64;
+  const int ch0 = (int)((long)split * nch / a.NS), ch1 = (int)((long)(split + 1) * nch / a.NS);
+  const float* zrow = a.Zb + (long)row * PIN * f;
+  const float* drow = a.D + (long)row * f;
+  TE<TY>* dzo = static_cast<TE<TY>*>(a.dz) + (long)p * PIN * f;
+  TE<TY>* who = static_cast<TE<TY>*>(a.wh) + (long)p * f;
+  const float4* b1g = reinterpret_cast<const float4*>(a.B1p + (long)e * PIN * f * 16);
+  const float4* b1u = reinterpret_cast<const float4*>(a.B1p + ((long)e * PIN + (PIN - 1)) * f * 16);
+  const float4* adp = reinterpret_cast<const float4*>(a.Adp + (long)e * f * 16);
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int c0 = ch * 64;
+    if (RES) {
+      __syncthreads();
+      fs[0][tid >> 2][tid & 3] = b1g[(long)c0 * 4 + tid];
+      if (PIN > 1) fs[1][tid >> 2][tid & 3] = b1u[(long)c0 * 4 + tid];
+      fs[2][tid >> 2][tid & 3] = adp[(long)c0 * 4 + tid];
+      __syncthreads();
     }
-    // per-thread partial sums: q (dz B1, Pin x 16), u2 (h A2, 16), <D, h>
-    float part[49];
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+      const int cl = cg * 4 + 16 * i, c = c0 + cl;
+      const float4 zg4 = *reinterpret_cast<const float4*>(zrow + c);
+      float4 zu4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (PIN > 1) zu4 = *reinterpret_cast<const float4*>(zrow + f + c);
+      const float4 d4 = *reinterpret_cast<const float4*>(drow + c);
+      const float zgv[4] = {zg4.x, zg4.y, zg4.z, zg4.w}, zuv[4] = {zu4.x, zu4.y, zu4.z, zu4.w};
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+      float og[4], ou[4], oh[4];
+      // one column at a time (keeps the factor values of a single column live)
+#pragma unroll 1
+      for (int jj = 0; jj < 4; ++jj) {
+        float bg[16], bu[16], ba[16];
+        float zg = 0.f, zu = 0.f, dh = 0.f, dj = 0.f;
 #pragma unroll
-    for (int x = 0; x < 49; ++x) part[x] = 0.f;
-    const float* b1g = a.B1p + ((long)i * Pin + 0) * f * 16;
-    const float* b1u = a.B1p + ((long)i * Pin + (Pin > 1 ? 1 : 0)) * f * 16;
-    const float* ad = a.Adp + (long)i * f * 16;
-    TE<TY>* dzo = static_cast<TE<TY>*>(a.dz) + asg * Pin * f;
-    TE<TY>* who = static_cast<TE<TY>*>(a.wh) + asg * f;
-    for (int c = tid; c < f; c += 256) {
-      float zg = zb[c], zu = Pin > 1 ? zb[f + c] : 0.f;
-      float dh = dr[c];
-      if (a.r) {
+        for (int x = 0; x < 4; ++x)
+          if (x == jj) {
+            zg = zgv[x];
+            zu = zuv[x];
+            dj = dv[x];
+          }
+        dh = dj;
+        if (RES) {
 #pragma unroll
-        for (int rho = 0; rho < 16; ++rho) {
-          zg += ug[rho] * b1g[c * 16 + rho];
-          if (Pin > 1) zu += uu[rho] * b1u[c * 16 + rho];
-          dh += ev[rho] * ad[c * 16 + rho];
+          for (int q = 0; q < 4; ++q) {
+            const float4 x = fs[0][cl + jj][q];
+            bg[4 * q] = x.x; bg[4 * q + 1] = x.y; bg[4 * q + 2] = x.z; bg[4 * q + 3] = x.w;
+            const float4 y = fs[2][cl + jj][q];
+            ba[4 * q] = y.x; ba[4 * q + 1] = y.y; ba[4 * q + 2] = y.z; ba[4 * q + 3] = y.w;
+            if (PIN > 1) {
+              const float4 z = fs[1][cl + jj][q];
+              bu[4 * q] = z.x; bu[4 * q + 1] = z.y; bu[4 * q + 2] = z.z; bu[4 * q + 3] = z.w;
+            }
+          }
+#pragma unroll
+          for (int rho = 0; rho < 16; ++rho) {
+            zg += ug[rho] * bg[rho];
+            if (PIN > 1) zu += uu[rho] * bu[rho];
+            dh += ev[rho] * ba[rho];
+          }
+        }
+        dh *= wt;
+        float h, dzg, dzu = 0.f;
+        if (a.act == ACT_SWIGLU) {
+          const float sg = sigm(zg), sl = zg * sg;
+          h = sl * zu;
+          dzu = dh * sl;
+          dzg = dh * zu * sg * (1.0f + zg * (1.0f - sg));
+        } else {
+          float dg;
+          h = gelu_t(zg, dg);
+          dzg = dh * dg;
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (x == jj) {
+            og[x] = dzg;
+            ou[x] = dzu;
+            oh[x] = wt * h;
+          }
+        dd += dj * h;
+        if (RES) {
+#pragma unroll
+          for (int rho = 0; rho < 16; ++rho) {
+            qg[rho] += dzg * bg[rho];
+            if (PIN > 1) qu[rho] += dzu * bu[rho];
+            u2[rho] += h * ba[rho];
+          }
         }
       }
-      dh *= wt;
-      float h, dzg, dzu = 0.f;
-      if (a.act == ACT_SWIGLU) {
-        const float sg = sigm(zg), sl_ = zg * sg;
-        h = sl_ * zu;
-        dzu = dh * sl_;
-        dzg = dh * zu * sg * (1.0f + zg * (1.0f - sg));
-      } else {
-        float dg;
-        h = gelu_t(zg, dg);
-        dzg = dh * dg;
+      if (valid) {
+        store4<TY>(dzo + c, og);
+        if (PIN > 1) store4<TY>(dzo + f + c, ou);
+        store4<TY>(who + c, oh);
       }
-      dzb[c] += dzg;
-      if (Pin > 1) dzb[f + c] += dzu;
-      hb[c] += wt * h;
-      dzo[c] = from_f32<TY>(dzg);
-      if (Pin > 1) dzo[f + c] = from_f32<TY>(dzu);
-      who[c] = from_f32<TY>(wt * h);
-      part[48] += dr[c] * h;
-      if (a.r) {
+    }
+  }
+  // reduce over the 4 lanes of the position (adjacent lanes)
+  dd += __shfl_xor(dd, 1);
+  dd += __shfl_xor(dd, 2);
+  if (RES) {
 #pragma unroll
-        for (int rho = 0; rho < 16; ++rho) {
-          part[rho] += dzg * b1g[c * 16 + rho];
-          if (Pin > 1) part[16 + rho] += dzu * b1u[c * 16 + rho];
-          part[32 + rho] += h * ad[c * 16 + rho];
-        }
+    for (int x = 0; x < 16; ++x) {
+      qg[x] += __shfl_xor(qg[x], 1);
+      qg[x] += __shfl_xor(qg[x], 2);
+      if (PIN > 1) {
+        qu[x] += __shfl_xor(qu[x], 1);
+        qu[x] += __shfl_xor(qu[x], 2);
       }
+      u2[x] += __shfl_xor(u2[x], 1);
+      u2[x] += __shfl_xor(u2[x], 2);
     }
-    block_sum<49>(part, red);
-    if (tid < 16) {
-      a.q[asg * Pin * 16 + tid] = red[4 * 49 + tid];
-      if (Pin > 1) a.q[asg * Pin * 16 + 16 + tid] = red[4 * 49 + 16 + tid];
-      a.wu2[asg * 16 + tid] = wt * red[4 * 49 + 32 + tid];
-      a.ea[asg * 16 + tid] = ev[tid];
-      a.ua[asg * Pin * 16 + tid] = ug[tid];
-      if (Pin > 1) a.ua[asg * Pin * 16 + 16 + tid] = uu[tid];
+  }
+  if (valid && cg == 0) {
+    float* po = a.part + ((long)split * a.Na + p) * ACT_PART;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      po[x] = qg[x];
+      po[16 + x] = qu[x];
+      po[32 + x] = u2[x];
     }
-    if (tid == 0) {
-      float dw = red[4 * 49 + 48];
-      for (int rho = 0; rho < 16; ++rho) dw += ev[rho] * red[4 * 49 + 32 + rho];
-      a.dw[asg] = dw;
+    po[48] = dd;
+  }
+}
+
+__global__ void act_finish_kernel(const float* part, int NS, int Na, int Pin, int r, const float* pw,
+                                  const float* ea, const int* arow, float* q, float* wu2, float* dw) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= Na) return;
+  float acc[49];
+#pragma unroll
+  for (int x = 0; x < 49; ++x) acc[x] = 0.f;
+  for (int s = 0; s < NS; ++s) {
+    const float* pp = part + ((long)s * Na + p) * ACT_PART;
+#pragma unroll
+    for (int x = 0; x < 49; ++x) acc[x] += pp[x];
+  }
+  float dwv = acc[48];
+  if (r > 0) {
+    float* qo = q + (long)p * 64;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      qo[x] = acc[x];
+      qo[16 + x] = Pin > 1 ? acc[16 + x] : 0.f;
+      qo[32 + x] = 0.f;
+      qo[48 + x] = 0.f;
+      wu2[(long)p * 16 + x] = pw[p] * acc[32 + x];
+      dwv += ea[(long)p * 16 + x] * acc[32 + x];
     }
-    __syncthreads();
+  }
+  dw[arow[p]] = dwv;
+}
+
+// One workgroup per group row: dZbar and hbar as sums over its assignments.
+template <int TY>
+__global__ void __launch_bounds__(256) row_sums_kernel(const TE<TY>* dz, const TE<TY>* wh, const int* garow,
+                                                       const int* apos, int kg, int ke, int k, int f, int Pin,
+                                                       TE<TY>* dZbar, TE<TY>* hbar) {
+  const int row = blockIdx.x;
+  const int ar = garow[row];
+  const int t = ar / kg, rank = ar % kg;
+  int pos[MAX_SLOTS];
+  for (int sl = 0; sl < ke; ++sl) pos[sl] = apos[(long)t * k + rank * ke + sl];
+  const long W = (long)Pin * f;
+  for (int c = threadIdx.x * 4; c < W; c += 1024) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < ke; ++sl) load4_add<TY>(dz + pos[sl] * W + c, v);
+    store4<TY>(dZbar + row * W + c, v);
+  }
+  for (int c = threadIdx.x * 4; c < f; c += 1024) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < ke; ++sl) load4_add<TY>(wh + (long)pos[sl] * f + c, v);
+    store4<TY>(hbar + (long)row * f + c, v);
   }
 }
 
 // --------------------------------------------------- token: router + dX ----
 // One workgroup per token: softmax backward of the gate (w = p_g q_j), then
-// dX = sum over the token's group rows of dXb + residual and router terms.
+// dX = sum over the token's group rows of dXb, over its assignments of dXr,
+// plus the router terms.
 template <int XT>
-__global__ void __launch_bounds__(256) tok_bwd_kernel(TokBwdArgs a) {
+__global__ void __launch_bounds__(256) tok_kernel(TokArgs a) {
   const int t = blockIdx.x;
   if (t >= a.T) return;
   __shared__ float dsv[MAX_KG];
@@ -344,7 +496,7 @@ __global__ void __launch_bounds__(256) tok_bwd_kernel(TokBwdArgs a) {
     for (int g = 0; g < a.kg; ++g) dsv[g] = pg[g] * (dp[g] - sp);
   }
   __syncthreads();
-  // logit gradients out: ds [T][kg], de [T][kg][K] (zeros for the unchosen)
+  // logit gradients out: ds [T][kg][1 + K] (zeros for the unchosen experts)
   for (int x = tid; x < a.kg * (1 + a.K); x += 256) {
     const int g = x / (1 + a.K), c = x % (1 + a.K);
     float v;
@@ -359,7 +511,6 @@ __global__ void __launch_bounds__(256) tok_bwd_kernel(TokBwdArgs a) {
     }
     a.ds[((long)t * a.kg + g) * (1 + a.K) + c] = v;
   }
-  // dX
   for (int cc = tid; cc < a.d; cc += 256) {
     float v = 0.f;
     const float* wcol = a.Wr + ((long)(cc >> 4) * a.NCp) * 16 + (cc & 15);
@@ -370,16 +521,8 @@ __global__ void __launch_bounds__(256) tok_bwd_kernel(TokBwdArgs a) {
       v += dsv[g] * wcol[gg * 16];
       for (int b = 0; b < a.ke; ++b) {
         const long s = (long)t * a.k + g * a.ke + b;
-        const int ii = a.idx[s];
-        if (a.K > 1) v += dev[g * a.ke + b] * wcol[(a.G + ii) * 16];
-        if (a.r) {
-          for (int p = 0; p < a.Pin; ++p) {
-            const float* qv = a.q + (s * a.Pin + p) * 16;
-            const float* at = a.Atp + (((long)ii * a.Pin + p) * a.d + cc) * 16;
-#pragma unroll
-            for (int rho = 0; rho < 16; ++rho) v += qv[rho] * at[rho];
-          }
-        }
+        if (a.K > 1) v += dev[g * a.ke + b] * wcol[(a.G + a.idx[s]) * 16];
+        if (a.r) v += a.dXr[(long)a.apos[s] * a.d + cc];
       }
     }
     static_cast<TE<XT>*>(a.dX)[(long)t * a.d + cc] = from_f32<XT>(v);
@@ -391,22 +534,17 @@ __global__ void invert_rows_kernel(const int* garow, int R, int* grow) {
   if (r < R) grow[garow[r]] = r;
 }
 
-__global__ void assign_rows_kernel(const int* perm, const int* offsets, const int* idx, int E, int k, int Na,
-                                   int* arow) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= Na) return;
-  // expert of position p: the last e with offsets[e] <= p
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (offsets[mid] <= p) lo = mid;
-    else hi = mid - 1;
+template <int TY>
+__global__ void a1t_kernel(const float* Atp, int E, int Pin, int d, TE<TY>* out) {
+  const long total = (long)E * d * 64;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+    const int kk = (int)(i & 63);
+    const long en = i >> 6;
+    const int e = (int)(en / d), nn = (int)(en % d);
+    float v = 0.f;
+    if (kk < Pin * 16) v = Atp[(((long)e * Pin + kk / 16) * d + nn) * 16 + (kk & 15)];
+    out[i] = from_f32<TY>(v);
   }
-  const int t = perm[p];
-  int slot = 0;
-  for (int s = 0; s < k; ++s)
-    if (idx[(long)t * k + s] == lo) slot = s;
-  arow[p] = t * k + slot;
 }
 
 __global__ void seg_colsum_kernel(const float* in, long ld_in, int ncols, const int* start, const int* count,
@@ -508,24 +646,70 @@ hipError_t launch_frag_to_plain(int ty, const void* frag, int G, long gsi, int N
   return hipGetLastError();
 }
 
-hipError_t launch_act_bwd(int ty, const ActBwdArgs& a, hipStream_t st) {
-  if (a.R <= 0) return hipSuccess;
-  dim3 grid(a.R), block(256);
-  switch (ty) {
-    case DT_F32: hipLaunchKernelGGL(act_bwd_kernel<DT_F32>, grid, block, 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL(act_bwd_kernel<DT_F16>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(act_bwd_kernel<DT_BF16>, grid, block, 0, st, a); break;
-  }
+hipError_t launch_gather_assign(const AssignArgs& a, hipStream_t st) {
+  if (a.Na <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_assign_kernel, dim3((a.Na + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_tok_bwd(const TokBwdArgs& a, hipStream_t st) {
+hipError_t launch_act(int ty, const ActArgs& a, hipStream_t st) {
+  if (a.Na <= 0) return hipSuccess;
+  if (a.f % 64 || a.NS < 1 || a.NS > a.f / 64 || a.Pin < 1 || a.Pin > 2) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.Na + 63) / 64 + a.E), (unsigned)a.NS), block(256);
+#define AK(TY)                                                                     \
+  do {                                                                             \
+    if (a.Pin == 2) {                                                              \
+      if (a.r) hipLaunchKernelGGL((act_kernel<TY, 2, true>), grid, block, 0, st, a);  \
+      else hipLaunchKernelGGL((act_kernel<TY, 2, false>), grid, block, 0, st, a);     \
+    } else {                                                                       \
+      if (a.r) hipLaunchKernelGGL((act_kernel<TY, 1, true>), grid, block, 0, st, a);  \
+      else hipLaunchKernelGGL((act_kernel<TY, 1, false>), grid, block, 0, st, a);     \
+    }                                                                              \
+  } while (0)
+  switch (ty) {
+    case DT_F32: AK(DT_F32); break;
+    case DT_F16: AK(DT_F16); break;
+    default: AK(DT_BF16); break;
+  }
+#undef AK
+  return hipGetLastError();
+}
+
+hipError_t launch_act_finish(const float* part, int NS, int Na, int Pin, int r, const float* pw, const float* ea,
+                             const int* arow, float* q, float* wu2, float* dw, hipStream_t st) {
+  if (Na <= 0) return hipSuccess;
+  hipLaunchKernelGGL(act_finish_kernel, dim3((Na + 255) / 256), dim3(256), 0, st, part, NS, Na, Pin, r, pw, ea, arow,
+                     q, wu2, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sums(int ty, const void* dz, const void* wh, const int* garow, const int* apos, int R, int kg,
+                           int ke, int k, int f, int Pin, void* dZbar, void* hbar, hipStream_t st) {
+  if (R <= 0) return hipSuccess;
+  if (ke > MAX_SLOTS || f % 4) return hipErrorInvalidValue;
+  dim3 grid(R), block(256);
+  if (ty == DT_F32)
+    hipLaunchKernelGGL(row_sums_kernel<DT_F32>, grid, block, 0, st, static_cast<const float*>(dz),
+                       static_cast<const float*>(wh), garow, apos, kg, ke, k, f, Pin, static_cast<float*>(dZbar),
+                       static_cast<float*>(hbar));
+  else if (ty == DT_F16)
+    hipLaunchKernelGGL(row_sums_kernel<DT_F16>, grid, block, 0, st, static_cast<const uint16_t*>(dz),
+                       static_cast<const uint16_t*>(wh), garow, apos, kg, ke, k, f, Pin,
+                       static_cast<uint16_t*>(dZbar), static_cast<uint16_t*>(hbar));
+  else
+    hipLaunchKernelGGL(row_sums_kernel<DT_BF16>, grid, block, 0, st, static_cast<const uint16_t*>(dz),
+                       static_cast<const uint16_t*>(wh), garow, apos, kg, ke, k, f, Pin,
+                       static_cast<uint16_t*>(dZbar), static_cast<uint16_t*>(hbar));
+  return hipGetLastError();
+}
+
+hipError_t launch_tok(const TokArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
   dim3 grid(a.T), block(256);
   switch (a.x_dtype) {
-    case DT_F32: hipLaunchKernelGGL(tok_bwd_kernel<DT_F32>, grid, block, 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL(tok_bwd_kernel<DT_F16>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(tok_bwd_kernel<DT_BF16>, grid, block, 0, st, a); break;
+    case DT_F32: hipLaunchKernelGGL(tok_kernel<DT_F32>, grid, block, 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL(tok_kernel<DT_F16>, grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL(tok_kernel<DT_BF16>, grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -536,10 +720,14 @@ hipError_t launch_invert_rows(const int* garow, int R, int* grow, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_assign_rows(const int* perm, const int* offsets, const int* idx, int E, int k, int Na, int* arow,
-                              hipStream_t st) {
-  if (Na <= 0) return hipSuccess;
-  hipLaunchKernelGGL(assign_rows_kernel, dim3((Na + 255) / 256), dim3(256), 0, st, perm, offsets, idx, E, k, Na, arow);
+hipError_t launch_a1t(int ty, const float* Atp, int E, int Pin, int d, void* A1T, hipStream_t st) {
+  dim3 grid(1024), block(256);
+  if (ty == DT_F32)
+    hipLaunchKernelGGL(a1t_kernel<DT_F32>, grid, block, 0, st, Atp, E, Pin, d, static_cast<float*>(A1T));
+  else if (ty == DT_F16)
+    hipLaunchKernelGGL(a1t_kernel<DT_F16>, grid, block, 0, st, Atp, E, Pin, d, static_cast<uint16_t*>(A1T));
+  else
+    hipLaunchKernelGGL(a1t_kernel<DT_BF16>, grid, block, 0, st, Atp, E, Pin, d, static_cast<uint16_t*>(A1T));
   return hipGetLastError();
 }
 
