@@ -82,39 +82,41 @@ __global__ void __launch_bounds__(256) bgemm_kernel(BGemmArgs a) {
     kofs = a.kpad_off[s];
     K = a.kpad_off[s + 1] - a.kpad_off[s];
   }
+  // B rows ride the lane index of the MFMA result and A rows its register
+  // index, so a store writes 32 consecutive columns of one row of C.
   f16v acc[2][2];
   zero_acc<2, 2>(acc);
   const int KT = K / KB;
   if (KT > 0) {
-    TDirect<SA, TY, 2> to;
+    TDirect<TY, TY, 2> bt;
+    const TE<TY>* bbase = static_cast<const TE<TY>*>(a.b) + (a.mode == 0 ? (long)s * a.b_sstride : kofs);
+    bt.init(bbase, a.ldb, lane, [&](int t) -> long {
+      const int n = n0 + wn * 64 + t * 32 + (lane & 31);
+      return n < a.N ? n : -1;
+    });
+    BOperand<SA, TY> ao;
     const TE<SA>* abase = static_cast<const TE<SA>*>(a.a) + kofs;
-    to.init(abase, a.lda, lane, [&](int t) -> long {
-      const int m = m0 + wm * 64 + t * 32 + (lane & 31);
+    ao.td.init(abase, a.lda, lane, [&](int c) -> long {
+      const int m = m0 + wm * 64 + c * 32 + (lane & 31);
       if (m >= M) return -1;
       if (a.mode == 1) return m;
       const long pos = crow0 + m;
       return a.a_map ? (long)(a.a_map[pos] / a.a_div) : pos;
     });
-    BOperand<TY, TY> bo;
-    const TE<TY>* bbase = static_cast<const TE<TY>*>(a.b) + (a.mode == 0 ? (long)s * a.b_sstride : kofs);
-    bo.td.init(bbase, a.ldb, lane, [&](int c) -> long {
-      const int n = n0 + wn * 64 + c * 32 + (lane & 31);
-      return n < a.N ? n : -1;
-    });
-    Mainloop<TY, 2, 2, TDirect<SA, TY, 2>, BOperand<TY, TY>, 1> ml{to, bo, lane};
-    ml.template run<typename TDirect<SA, TY, 2>::Raw[2][4], typename BOperand<TY, TY>::Raw[2][4]>(KT, acc);
+    Mainloop<TY, 2, 2, TDirect<TY, TY, 2>, BOperand<SA, TY>, 1> ml{bt, ao, lane};
+    ml.template run<typename TDirect<TY, TY, 2>::Raw[2][4], typename BOperand<SA, TY>::Raw[2][4]>(KT, acc);
   }
   float* cbase = a.c + (a.mode == 0 ? crow0 * a.ldc : (long)s * a.c_sstride);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int m = m0 + wm * 64 + t * 32 + (lane & 31);
-    if (m >= M) continue;
+    const int n = n0 + wn * 64 + t * 32 + (lane & 31);
+    if (n >= a.n_store) continue;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int n = n0 + wn * 64 + c * 32 + acc32_row(v, lane);
-        if (n < a.n_store) cbase[(long)m * a.ldc + n] = acc[t][c][v];
+        const int m = m0 + wm * 64 + c * 32 + acc32_row(v, lane);
+        if (m < M) cbase[(long)m * a.ldc + n] = acc[t][c][v];
       }
   }
 }
