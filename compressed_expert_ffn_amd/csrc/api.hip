@@ -686,10 +686,12 @@ int weights_to_host(const moe_config& c, const moe_weights* w, moe_weights* hw,
 // kept).  U, E and the residual factors are kept as float32 for the
 // elementwise steps; GEMM operands are in the MFMA type.
 struct BwdState {
-  void *W1T = nullptr, *W1N = nullptr, *W2N = nullptr, *AtT = nullptr, *BdT = nullptr, *A1T = nullptr;
+  // fragment-major (tile engine layout) B operands: W1^T [d][Pin f], W2^T
+  // [f][d], stacked A1 [NUp][d] and B2 [NEp][d] per group, A1 [d][64] per expert
+  void *W1F = nullptr, *W2F = nullptr, *AtF = nullptr, *BdF = nullptr, *A1F = nullptr;
   float *Atp = nullptr, *B1p = nullptr, *Adp = nullptr;
-  int NUb = 0, NEb = 0;
-  long Kg = 0, Ke = 0, part_cap = 0;
+  int NUb = 0, NEb = 0, NUp = 0, NEp = 0;  // stacked factor rows, and rounded up to 64
+  long Kg = 0, KgF = 0, Ke = 0, part_cap = 0;
   int *counts = nullptr, *offsets = nullptr, *perm = nullptr, *arow = nullptr, *apos = nullptr, *prow = nullptr;
   int *grow = nullptr, *kpad_g = nullptr, *kpad_e = nullptr;
   float *Zb = nullptr, *U = nullptr, *D = nullptr, *Eb = nullptr, *pw = nullptr, *part = nullptr;
@@ -1457,19 +1459,30 @@ int prepare_backward(moe_handle* h) {
   };
   auto alloc_f = [&](float** p, size_t n) { return dalloc(h, p, n + 64); };
   auto alloc_i = [&](int** p, size_t n) { return dalloc(h, p, n + 64); };
-  // plain base weights
-  TRY(alloc_bytes(&B->W1T, (size_t)G * Pin * f * d * es));
-  TRY(alloc_bytes(&B->W1N, (size_t)G * Pin * f * d * es));
-  TRY(alloc_bytes(&B->W2N, (size_t)G * f * d * es));
+  // plain copies go through one scratch buffer into the fragment-major images
+  size_t tmp_bytes = (size_t)G * Pin * f * d * es;
+  if (r > 0) tmp_bytes = std::max({tmp_bytes, (size_t)E * d * 64 * es, (size_t)G * K * Pin * 16 * d * es});
+  struct Tmp {
+    char* p = nullptr;
+    ~Tmp() {
+      if (p) (void)hipFree(p);
+    }
+  } scratch;
+  if (hipMalloc(&scratch.p, tmp_bytes) != hipSuccess) return fail(MOE_ERR_OOM, "backward set-up scratch");
+  tmp = scratch.p;
+  TRY(alloc_bytes(&B->W1F, (size_t)G * Pin * f * d * es));
+  TRY(alloc_bytes(&B->W2F, (size_t)G * f * d * es));
   const int swf = Pin > 1 ? f : 0;
-  e = launch_frag_to_plain(ty, h->W1, G, h->w1_gs, Pin * f, d, swf, false, B->W1T, (long)Pin * f * d, d, st);
-  if (e == hipSuccess)
-    e = launch_frag_to_plain(ty, h->W1, G, h->w1_gs, Pin * f, d, swf, true, B->W1N, (long)Pin * f * d, (long)Pin * f, st);
-  if (e == hipSuccess) e = launch_frag_to_plain(ty, h->W2, G, h->w2_gs, d, f, 0, true, B->W2N, (long)f * d, d, st);
+  e = launch_frag_to_plain(ty, h->W1, G, h->w1_gs, Pin * f, d, swf, true, tmp, (long)Pin * f * d, (long)Pin * f, st);
+  if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)Pin * f * d, d, Pin * f, B->W1F, (long)Pin * f * d, st);
+  if (e == hipSuccess) e = launch_frag_to_plain(ty, h->W2, G, h->w2_gs, d, f, 0, true, tmp, (long)f * d, d, st);
+  if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)f * d, f, d, B->W2F, (long)f * d, st);
   if (e != hipSuccess) return hip_fail(h, e, "backward weight repack");
   if (r > 0) {
     B->NUb = K * Pin * 16;
     B->NEb = K * 16;
+    B->NUp = (B->NUb + 63) / 64 * 64;
+    B->NEp = (B->NEb + 63) / 64 * 64;
     TRY(alloc_f(&B->Atp, (size_t)E * Pin * d * 16));
     TRY(alloc_f(&B->B1p, (size_t)E * Pin * f * 16));
     TRY(alloc_f(&B->Adp, (size_t)E * f * 16));
@@ -1489,17 +1502,23 @@ int prepare_backward(moe_handle* h) {
           e = launch_debug_decode(ty, c.resid, L.kind, L.src, L.sc, L.base, L.sbase, L.n, r, L.aux0, L.aux1, out, 16, st);
         }
     if (e != hipSuccess) return hip_fail(h, e, "backward factor decode");
-    TRY(alloc_bytes(&B->AtT, (size_t)G * B->NUb * d * es));
-    TRY(alloc_bytes(&B->BdT, (size_t)G * B->NEb * d * es));
-    TRY(alloc_bytes(&B->A1T, (size_t)E * d * 64 * es));
-    e = launch_stack_factors(ty, B->Atp, G, K, Pin, d, B->NUb, B->AtT, st);
-    if (e == hipSuccess) e = launch_stack_factors(ty, Bdp, G, K, 1, d, B->NEb, B->BdT, st);
-    if (e == hipSuccess) e = launch_a1t(ty, B->Atp, E, Pin, d, B->A1T, st);
+    TRY(alloc_bytes(&B->AtF, (size_t)G * B->NUp * d * es));
+    TRY(alloc_bytes(&B->BdF, (size_t)G * B->NEp * d * es));
+    TRY(alloc_bytes(&B->A1F, (size_t)E * d * 64 * es));
+    e = launch_stack_factors(ty, B->Atp, G, K, Pin, d, B->NUb, tmp, st);
+    if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)B->NUb * d, B->NUb, d, B->AtF, (long)B->NUp * d, st);
+    if (e == hipSuccess) e = launch_stack_factors(ty, Bdp, G, K, 1, d, B->NEb, tmp, st);
+    if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)B->NEb * d, B->NEb, d, B->BdF, (long)B->NEp * d, st);
+    if (e == hipSuccess) e = launch_a1t(ty, B->Atp, E, Pin, d, tmp, st);
+    if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, E, (long)d * 64, d, 64, B->A1F, (long)d * 64, st);
     if (e != hipSuccess) return hip_fail(h, e, "backward factor stacking");
   }
+  if (hipStreamSynchronize(st) != hipSuccess) return fail(MOE_ERR_HIP, "backward weight repack failed");
   // workspace for T_max tokens
-  B->Kg = R + 64L * G;
-  B->Ke = Na + 64L * E;
+  // (multiples of 64, so every transposed row starts 128-byte aligned)
+  B->Kg = (R + 64L * G + 63) / 64 * 64;
+  B->KgF = B->Kg;
+  B->Ke = (Na + 64L * E + 63) / 64 * 64;
   // act_splits(Na) * Na <= 1024 * 64 + Na for every Na
   B->part_cap = 1024L * 64 + Na;
   TRY(alloc_i(&B->counts, E));
@@ -1523,9 +1542,9 @@ int prepare_backward(moe_handle* h) {
   TRY(alloc_bytes(&B->dz, (size_t)Na * Pin * f * es));
   TRY(alloc_bytes(&B->wh, (size_t)Na * f * es));
   TRY(alloc_bytes(&B->XTg, (size_t)d * B->Kg * es));
-  TRY(alloc_bytes(&B->dZT, (size_t)Pin * f * B->Kg * es));
+  TRY(alloc_bytes(&B->dZT, (size_t)Pin * f * B->KgF * es));
   TRY(alloc_bytes(&B->hbT, (size_t)f * B->Kg * es));
-  TRY(alloc_bytes(&B->dYTg, (size_t)d * B->Kg * es));
+  TRY(alloc_bytes(&B->dYTg, (size_t)d * B->KgF * es));
   TRY(alloc_bytes(&B->dsdeT, (size_t)(1 + K) * B->Kg * es));
   if (r > 0) {
     TRY(alloc_f(&B->U, (size_t)R * B->NUb));
@@ -1585,6 +1604,12 @@ BGemmArgs rgemm(const Workspace& ws, const int* gcounts, const int* goffsets, in
   return g;
 }
 
+// the wide kernel's N (a multiple of 64) over a B padded to that many rows
+BGemmArgs widen(BGemmArgs g, int n_padded) {
+  g.N = n_padded;
+  return g;
+}
+
 BGemmArgs kgemm(int S, const int* kpad, int ty, const void* a, long lda, const void* b, long ldb, int M, int N,
                 float* c, long c_sstride, long ldc, int n_store) {
   BGemmArgs g{};
@@ -1606,8 +1631,9 @@ BGemmArgs kgemm(int S, const int* kpad, int ty, const void* a, long lda, const v
 }
 
 TransArgs tgather(int S, const int* start, const int* count, const int* kpad, const void* in, int in_dtype, long ld_in,
-                  int c0, int ncols, const int* map, int div, void* out, long ld_out, long max_k) {
+                  int c0, int ncols, const int* map, int div, void* out, long ld_out, long max_k, int frag = 0) {
   TransArgs t{};
+  t.frag = frag;
   t.S = S;
   t.start = start;
   t.count = count;
@@ -1676,17 +1702,22 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   const int* garow = h->ws.garow;
   const size_t es = elem_bytes(ty);
   // forward intermediates: Z = X W1_base per group row, U = X A1 stacked
-  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->W1T,
-                            (long)Pin * f * d, Pin * f, d, B->Zb, (long)Pin * f), st));
+  // (the forward pass's own fragment-major W1, SwiGLU-interleaved columns)
+  {
+    BGemmArgs g = rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, h->W1, h->w1_gs,
+                        Pin * f, d, B->Zb, (long)Pin * f);
+    g.swf = Pin > 1 ? f : 0;
+    ok(launch_fgemm(ty, g, st));
+  }
   if (r > 0)
-    ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->AtT,
-                              (long)B->NUb * d, B->NUb, d, B->U, B->NUb), st));
+    ok(launch_fgemm(ty, widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->AtF,
+                                    (long)B->NUp * d, B->NUb, d, B->U, B->NUb), B->NUp), st));
   // D = dY W2_base^T, E = dY B2 stacked
-  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->W2N,
+  ok(launch_fgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->W2F,
                             (long)f * d, f, d, B->D, f), st));
   if (r > 0)
-    ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->BdT,
-                              (long)B->NEb * d, B->NEb, d, B->Eb, B->NEb), st));
+    ok(launch_fgemm(ty, widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->BdF,
+                                    (long)B->NEp * d, B->NEb, d, B->Eb, B->NEb), B->NEp), st));
   // per expert-list position: assignment, row, weight, u and e
   const int ke = c.top_experts;
   ok(launch_invert_rows(garow, (int)R, B->grow, st));
@@ -1748,10 +1779,10 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   ok(launch_act_finish(B->part, NS, (int)Na, Pin, r, B->pw, B->ea, B->arow, B->q, B->wu2, B->dw, st));
   ok(launch_row_sums(ty, B->dz, B->wh, garow, B->apos, (int)R, kg, ke, k, f, Pin, B->dZbar, B->hbar, st));
   // dX: base part per group row, residual part per position, then per token
-  ok(launch_bgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, ty, nullptr, 1,
-                            B->W1N, (long)Pin * f * d, d, Pin * f, B->dXb, d), st));
+  ok(launch_fgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, ty, nullptr, 1,
+                            B->W1F, (long)Pin * f * d, d, Pin * f, B->dXb, d), st));
   if (r > 0)
-    ok(launch_bgemm(ty, rgemm(h->ws, B->counts, B->offsets, E, Na, B->q, 64, MOE_F32, nullptr, 1, B->A1T,
+    ok(launch_fgemm(ty, rgemm(h->ws, B->counts, B->offsets, E, Na, B->q, 64, MOE_F32, nullptr, 1, B->A1F,
                               (long)d * 64, d, 64, B->dXr, d), st));
   {
     TokArgs ta{};
@@ -1780,21 +1811,21 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   }
   // weight gradients over each group's rows
   ok(launch_pad_scan(live.gcounts, G, B->kpad_g, st));
-  const long Kg = B->Kg;
+  const long Kg = B->Kg, KgF = B->KgF;
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, X, c.x_dtype, d, 0, d, garow, kg, B->XTg,
                                  Kg, Kg), st));
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->dZbar, ty, (long)Pin * f, 0,
-                                 Pin * f, nullptr, 1, B->dZT, Kg, Kg), st));
+                                 Pin * f, nullptr, 1, B->dZT, KgF, Kg, 1), st));
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->hbar, ty, f, 0, f, nullptr, 1,
                                  B->hbT, Kg, Kg), st));
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, dY, c.x_dtype, d, 0, d, garow, kg,
-                                 B->dYTg, Kg, Kg), st));
+                                 B->dYTg, KgF, Kg, 1), st));
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->ds, MOE_F32, 1 + K, 0, 1 + K, garow, 1,
                                  B->dsdeT, Kg, Kg), st));
   for (int p = 0; p < Pin; ++p)
-    ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, static_cast<char*>(B->dZT) + (size_t)p * f * Kg * es, Kg,
-                              d, f, gr->dbase[p], (long)d * f, f, f), st));
-  ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->hbT, Kg, B->dYTg, Kg, f, d, gr->dbase[P - 1], (long)f * d, d, d),
+    ok(launch_fgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, static_cast<char*>(B->dZT) + (size_t)p * f * KgF * es,
+                              KgF, d, f, gr->dbase[p], (long)d * f, f, f), st));
+  ok(launch_fgemm(ty, kgemm(G, B->kpad_g, ty, B->hbT, Kg, B->dYTg, KgF, f, d, gr->dbase[P - 1], (long)f * d, d, d),
                   st));
   // router weights and biases
   ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, B->dsdeT, Kg, d, 1, gr->dW_grp, 1, G, 1), st));

@@ -38,8 +38,22 @@ struct BGemmArgs {
   int M, N, K;     // M: mode K only; N: columns computed; K: mode R only
   int n_store;     // columns stored (<= N)
   int max_rows;    // mode R: upper bound of the summed row count (grid size)
+  int swf;         // launch_fgemm only (see there)
 };
 hipError_t launch_bgemm(int ty, const BGemmArgs& a, hipStream_t st);
+
+// Wide variant (N a multiple of 64): B is fragment-major, [N/32][Kd/16][64
+// lanes] fragments in the tile engine's permuted k order (Kd = K in mode R,
+// ldb = the padded total in mode K, k-step offset kpad_off[s] / 16), and A
+// rows are staged through LDS; 128 x 256 tiles of C (64 x 256 in fp32).
+// swf > 0: B is the SwiGLU-interleaved first projection, whose fragment
+// column n is C column ((n / 32) & 1) swf + (n / 64) 32 + n % 32.
+hipError_t launch_fgemm(int ty, const BGemmArgs& a, hipStream_t st);
+
+// Fragment-major copy of row-major [G][N][Kd] (type TY, group strides in
+// elements), rows padded with zeros to a multiple of 64.
+hipError_t launch_plain_to_frag(int ty, const void* in, int G, long g_stride_in, int N, int Kd, void* out,
+                                long g_stride_out, hipStream_t st);
 
 // out[c][kpad_off[s] + r] = TY(in(row(s, r), c0 + c)) for r < count[s], zero
 // for count[s] <= r < padded length; in rows are in_map ? in_map[start[s] + r]
@@ -58,6 +72,8 @@ struct TransArgs {
   void* out;
   long ld_out;
   int max_cols_k;  // upper bound of kpad_off[S] (grid size)
+  int frag;        // 1: write the fragment-major image of out ([rows/32][ld_out/16][64]
+                   // fragments, rows padded with zeros to a multiple of 32)
 };
 hipError_t launch_gather_t(int ty, const TransArgs& a, hipStream_t st);
 

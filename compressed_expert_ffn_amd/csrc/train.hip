@@ -121,6 +121,123 @@ __global__ void __launch_bounds__(256) bgemm_kernel(BGemmArgs a) {
   }
 }
 
+// Index of element (n, k) in a fragment-major matrix of KS k-steps.
+__device__ __forceinline__ long frag_index(long n, long k, long KS) {
+  const long ks = (k >> 6) * 4 + ((k & 31) >> 3);
+  return ((n >> 5) * KS + ks) * 512 + ((n & 31) + 32 * ((k & 63) >> 5)) * 8 + (k & 7);
+}
+
+// ------------------------------------------------------ wide segment GEMM --
+// 32 RT rows of A (LDS, double-buffered) x 256 columns of B (four wavefronts
+// of 64 columns, fragment-major, straight from memory): the forward pass's
+// main loop with plain gathered rows on the token side.  KT = 0 (an empty
+// k segment) stores zeros.
+template <int TY, int SA, int RT>
+__global__ void __launch_bounds__(256) fgemm_kernel(BGemmArgs a) {
+  using F = FragT<TY>;
+  constexpr int FM = 32 * RT, FN = 256;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  F* tl = reinterpret_cast<F*>(smem);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int NT = (a.N + FN - 1) / FN;
+  int s = 0, m0 = 0, M = 0, K = 0, n0 = 0;
+  long crow0 = 0, kofs = 0;
+  if (a.mode == 0) {
+    int i = blockIdx.x;
+    n0 = (i % NT) * FN;
+    i /= NT;
+    bool found = false;
+    for (int q = 0; q < a.S; ++q) {
+      const int cnt = a.seg_count[q];
+      const int mt = (cnt + FM - 1) / FM;
+      if (i < mt) {
+        s = q;
+        m0 = i * FM;
+        M = cnt;
+        found = true;
+        break;
+      }
+      i -= mt;
+    }
+    if (!found) return;
+    K = a.K;
+    crow0 = a.seg_start[s];
+  } else {
+    const int MT = (a.M + FM - 1) / FM;
+    int i = blockIdx.x;
+    n0 = (i % NT) * FN;
+    i /= NT;
+    m0 = (i % MT) * FM;
+    s = i / MT;
+    if (s >= a.S) return;
+    M = a.M;
+    kofs = a.kpad_off[s];
+    K = a.kpad_off[s + 1] - a.kpad_off[s];
+  }
+  const int NB = (a.N + 63) / 64 * 2;  // 32-column blocks of B
+  const int nbw = n0 / 32 + wave * 2;
+  const bool active = nbw * 32 < a.N;
+  const int nb0 = active ? nbw : NB - 2;
+  f16v acc[RT][2];
+  zero_acc<RT, 2>(acc);
+  const int KT = K / KB;
+  if (KT > 0) {
+    TShared<SA, TY, RT> to;
+    to.init(static_cast<const TE<SA>*>(a.a) + kofs, a.lda, [&](int blk, int r) -> long {
+      const int m = m0 + blk * 32 + r;
+      if (m >= M) return -1;
+      if (a.mode == 1) return m;
+      const long pos = crow0 + m;
+      return a.a_map ? (long)(a.a_map[pos] / a.a_div) : pos;
+    });
+    const F* bb = static_cast<const F*>(a.b) + (a.mode == 0 ? (long)s * a.b_sstride / 8 : 0);
+    WPlain<TY> ws{bb, (int)(a.mode == 0 ? K / 16 : a.ldb / 16)};
+    ws.ks0 = (int)(kofs / 16);
+    MainloopTW<TY, RT, 2, TShared<SA, TY, RT>, WPlain<TY>, 1> ml{to, ws, nb0, tl, lane};
+    ml.run(KT, acc);
+  }
+  if (!active) return;
+  float* cbase = a.c + (a.mode == 0 ? crow0 * a.ldc : (long)s * a.c_sstride);
+  const bool vec = ((reinterpret_cast<uintptr_t>(a.c) | (uintptr_t)(a.ldc * 4) | (uintptr_t)(a.c_sstride * 4)) & 15) == 0;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int m = m0 + t * 32 + (lane & 31);
+    if (m >= M) continue;
+    float* crow = cbase + (long)m * a.ldc;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int nb = nb0 + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = acc32_row(4 * q, lane);  // 4 consecutive columns nl .. nl + 3
+        const int n = nb * 32 + nl;
+        const int col = a.swf > 0 ? ((nb & 1) * a.swf + (nb >> 1) * 32 + nl) : n;
+        if (vec && n + 3 < a.n_store) {
+          *reinterpret_cast<f4v*>(crow + col) = f4v{acc[t][c][4 * q], acc[t][c][4 * q + 1], acc[t][c][4 * q + 2],
+                                                     acc[t][c][4 * q + 3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (n + i < a.n_store) crow[col + i] = acc[t][c][4 * q + i];
+        }
+      }
+    }
+  }
+}
+
+template <int TY>
+__global__ void plain_to_frag_kernel(const TE<TY>* in, int G, long gsi, int N, int Kd, TE<TY>* out, long gso) {
+  const int Np = (N + 63) / 64 * 64;
+  const long total = (long)G * Np * Kd;
+  const long KS = Kd / 16;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+    const int g = (int)(i / ((long)Np * Kd));
+    const long rem = i - (long)g * Np * Kd;
+    const int n = (int)(rem / Kd), k = (int)(rem % Kd);
+    out[g * gso + frag_index(n, k, KS)] = n < N ? in[g * gsi + (long)n * Kd + k] : from_f32<TY>(0.f);
+  }
+}
+
 // ------------------------------------------------- gather + transpose ------
 // One block per 64 k-columns (a padded slice of one segment) x 64 output
 // rows; reads 64 source rows, writes 64 k-contiguous runs.
@@ -149,6 +266,14 @@ __global__ void __launch_bounds__(256) gather_t_kernel(TransArgs a) {
   }
   __syncthreads();
   TE<TY>* out = static_cast<TE<TY>*>(a.out);
+  if (a.frag) {
+    const int rows = (a.ncols + 31) / 32 * 32;
+    for (int i = tid; i < 64 * 64; i += 256) {
+      const int cc = i / 64, rr = i % 64;
+      if (c0 + cc < rows) out[frag_index(c0 + cc, kc + rr, a.ld_out / 16)] = from_f32<TY>(tileS[rr][cc]);
+    }
+    return;
+  }
   for (int i = tid; i < 64 * 64; i += 256) {
     const int cc = i / 64, rr = i % 64;
     if (c0 + cc < a.ncols) out[(long)(c0 + cc) * a.ld_out + kc + rr] = from_f32<TY>(tileS[rr][cc]);
@@ -610,6 +735,44 @@ hipError_t launch_bgemm(int ty, const BGemmArgs& a, hipStream_t st) {
     else BG(DT_BF16, DT_BF16);
   }
 #undef BG
+  return hipGetLastError();
+}
+
+hipError_t launch_fgemm(int ty, const BGemmArgs& a, hipStream_t st) {
+  if (a.N % 64) return hipErrorInvalidValue;
+  const int RT = ty == DT_F32 ? 2 : 4, FM = 32 * RT;
+  const int NT = (a.N + 255) / 256;
+  long blocks;
+  if (a.mode == 0) blocks = ((long)a.max_rows / FM + a.S) * NT;
+  else blocks = (long)a.S * ((a.M + FM - 1) / FM) * NT;
+  if (blocks <= 0) return hipSuccess;
+  dim3 grid((unsigned)blocks), block(256);
+  const size_t lds = (size_t)2 * RT * 4 * 64 * (ty == DT_F32 ? 32 : 16);
+#define FG(TY, SA, R) hipLaunchKernelGGL((fgemm_kernel<TY, SA, R>), grid, block, lds, st, a)
+  if (ty == DT_F32) {
+    FG(DT_F32, DT_F32, 2);
+  } else if (ty == DT_F16) {
+    if (a.a_dtype == DT_F32) FG(DT_F16, DT_F32, 4);
+    else if (a.a_dtype == DT_BF16) FG(DT_F16, DT_BF16, 4);
+    else FG(DT_F16, DT_F16, 4);
+  } else {
+    if (a.a_dtype == DT_F32) FG(DT_BF16, DT_F32, 4);
+    else FG(DT_BF16, DT_BF16, 4);
+  }
+#undef FG
+  return hipGetLastError();
+}
+
+hipError_t launch_plain_to_frag(int ty, const void* in, int G, long gsi, int N, int Kd, void* out, long gso,
+                                hipStream_t st) {
+  if (Kd % 64) return hipErrorInvalidValue;
+  dim3 grid(2048), block(256);
+  if (ty == DT_F32)
+    hipLaunchKernelGGL(plain_to_frag_kernel<DT_F32>, grid, block, 0, st, static_cast<const float*>(in), G, gsi, N, Kd,
+                       static_cast<float*>(out), gso);
+  else
+    hipLaunchKernelGGL(plain_to_frag_kernel<DT_F16>, grid, block, 0, st, static_cast<const uint16_t*>(in), G, gsi, N,
+                       Kd, static_cast<uint16_t*>(out), gso);
   return hipGetLastError();
 }
 
