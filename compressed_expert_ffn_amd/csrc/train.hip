@@ -254,29 +254,64 @@ __global__ void __launch_bounds__(256) gather_t_kernel(TransArgs a) {
   const int r0 = kc - a.kpad_off[s];
   const int cnt = a.count[s];
   const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * 64; i += 256) {
-    const int rr = i / 64, cc = i % 64;  // source row r0 + rr, column c0 + cc
-    float v = 0.f;
-    if (r0 + rr < cnt && c0 + cc < a.ncols) {
-      const long pos = (long)a.start[s] + r0 + rr;
-      const long row = a.in_map ? (long)(a.in_map[pos] / a.in_div) : pos;
-      v = load_as_f32<SI>(static_cast<const TE<SI>*>(a.in), row * a.ld_in + a.c0 + c0 + cc);
+  const TE<SI>* in = static_cast<const TE<SI>*>(a.in);
+  // rows of 8 consecutive columns per thread when the source allows it
+  const bool vin = (a.ld_in % 8 == 0) && (a.c0 % 8 == 0) && (a.ncols % 8 == 0);
+  if (vin) {
+    for (int i = tid; i < 64 * 8; i += 256) {
+      const int rr = i >> 3, cq = (i & 7) * 8;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (r0 + rr < cnt && c0 + cq < a.ncols) {
+        const long pos = (long)a.start[s] + r0 + rr;
+        const long row = a.in_map ? (long)(a.in_map[pos] / a.in_div) : pos;
+        const RawT<SI> raw = ld_raw<SI>(in + row * a.ld_in + a.c0 + c0 + cq);
+        if constexpr (SI == DT_F32) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = raw[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t h = static_cast<uint16_t>((raw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            v[e] = SI == DT_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tileS[rr][cq + e] = v[e];
     }
-    tileS[rr][cc] = v;
+  } else {
+    for (int i = tid; i < 64 * 64; i += 256) {
+      const int rr = i / 64, cc = i % 64;  // source row r0 + rr, column c0 + cc
+      float v = 0.f;
+      if (r0 + rr < cnt && c0 + cc < a.ncols) {
+        const long pos = (long)a.start[s] + r0 + rr;
+        const long row = a.in_map ? (long)(a.in_map[pos] / a.in_div) : pos;
+        v = load_as_f32<SI>(in, row * a.ld_in + a.c0 + c0 + cc);
+      }
+      tileS[rr][cc] = v;
+    }
   }
   __syncthreads();
+  // 8 consecutive k of one output row per thread (one 16- or 32-byte store)
   TE<TY>* out = static_cast<TE<TY>*>(a.out);
-  if (a.frag) {
-    const int rows = (a.ncols + 31) / 32 * 32;
-    for (int i = tid; i < 64 * 64; i += 256) {
-      const int cc = i / 64, rr = i % 64;
-      if (c0 + cc < rows) out[frag_index(c0 + cc, kc + rr, a.ld_out / 16)] = from_f32<TY>(tileS[rr][cc]);
+  const int rows = a.frag ? (a.ncols + 31) / 32 * 32 : a.ncols;
+  for (int i = tid; i < 64 * 8; i += 256) {
+    const int cc = i >> 3, rq = (i & 7) * 8;
+    if (c0 + cc >= rows) continue;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tileS[rq + e][cc];
+    TE<TY>* dst = out + (a.frag ? frag_index(c0 + cc, kc + rq, a.ld_out / 16) : (long)(c0 + cc) * a.ld_out + kc + rq);
+    if constexpr (TY == DT_F32) {
+      reinterpret_cast<f4v*>(dst)[0] = f4v{v[0], v[1], v[2], v[3]};
+      reinterpret_cast<f4v*>(dst)[1] = f4v{v[4], v[5], v[6], v[7]};
+    } else {
+      u4v w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = static_cast<uint32_t>(from_f32<TY>(v[2 * q])) | (static_cast<uint32_t>(from_f32<TY>(v[2 * q + 1])) << 16);
+      *reinterpret_cast<u4v*>(dst) = w;
     }
-    return;
-  }
-  for (int i = tid; i < 64 * 64; i += 256) {
-    const int cc = i / 64, rr = i % 64;
-    if (c0 + cc < a.ncols) out[(long)(c0 + cc) * a.ld_out + kc + rr] = from_f32<TY>(tileS[rr][cc]);
   }
 }
 
