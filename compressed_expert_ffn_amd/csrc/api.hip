@@ -693,7 +693,7 @@ struct BwdState {
   int NUb = 0, NEb = 0, NUp = 0, NEp = 0;  // stacked factor rows, and rounded up to 64
   long Kg = 0, KgF = 0, Ke = 0, part_cap = 0;
   int *counts = nullptr, *offsets = nullptr, *perm = nullptr, *arow = nullptr, *apos = nullptr, *prow = nullptr;
-  int *grow = nullptr, *kpad_g = nullptr, *kpad_e = nullptr;
+  int *grow = nullptr, *kpad_g = nullptr, *kpad_e = nullptr, *toff_g = nullptr, *toff_e = nullptr;
   float *Zb = nullptr, *U = nullptr, *D = nullptr, *Eb = nullptr, *pw = nullptr, *part = nullptr;
   float *q = nullptr, *wu2 = nullptr, *dw = nullptr, *ua = nullptr, *ea = nullptr, *dXb = nullptr, *dXr = nullptr;
   float *ds = nullptr;
@@ -1519,7 +1519,7 @@ int prepare_backward(moe_handle* h) {
   B->Kg = (R + 64L * G + 63) / 64 * 64;
   B->KgF = B->Kg;
   B->Ke = (Na + 64L * E + 63) / 64 * 64;
-  // act_splits(Na) * Na <= 1024 * 64 + Na for every Na
+  // act_splits(Na, E, f) * Na <= 1024 * 64 + Na for every Na
   B->part_cap = 1024L * 64 + Na;
   TRY(alloc_i(&B->counts, E));
   TRY(alloc_i(&B->offsets, E + 1));
@@ -1530,6 +1530,8 @@ int prepare_backward(moe_handle* h) {
   TRY(alloc_i(&B->grow, R));
   TRY(alloc_i(&B->kpad_g, G + 1));
   TRY(alloc_i(&B->kpad_e, E + 1));
+  TRY(alloc_i(&B->toff_g, G + 1));
+  TRY(alloc_i(&B->toff_e, E + 1));
   TRY(alloc_f(&B->pw, (size_t)Na));
   TRY(alloc_f(&B->part, (size_t)B->part_cap * ACT_PART));
   TRY(alloc_f(&B->Zb, (size_t)R * Pin * f));
@@ -1571,8 +1573,9 @@ int prepare_backward(moe_handle* h) {
 
 // Column splits of the activation backward: enough workgroups for the chip
 // (about 1024) when there are few 64-position tiles.
-int act_splits(long Na, int f) {
-  const long tiles = std::max(1L, (Na + 63) / 64);
+int act_splits(long Na, int E, int f) {
+  // tiles: full ones plus about half of the experts' partial ones
+  const long tiles = std::max(1L, (Na + 63) / 64 + std::min<long>(E, Na) / 2);
   long ns = (1024 + tiles - 1) / tiles;
   ns = std::min<long>(ns, f / 64);
   return (int)std::max(1L, ns);
@@ -1702,22 +1705,30 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   const int* garow = h->ws.garow;
   const size_t es = elem_bytes(ty);
   // forward intermediates: Z = X W1_base per group row, U = X A1 stacked
+  // row tiles of the wide GEMMs per group and per expert
+  const int fm = fgemm_rows(ty);
+  ok(launch_tile_scan(live.gcounts, G, fm, B->toff_g, st));
+  ok(launch_tile_scan(B->counts, E, fm, B->toff_e, st));
+  auto tg = [&](BGemmArgs g) {
+    g.tile_off = g.S == E && g.seg_count == B->counts ? B->toff_e : B->toff_g;
+    return g;
+  };
   // (the forward pass's own fragment-major W1, SwiGLU-interleaved columns)
   {
     BGemmArgs g = rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, h->W1, h->w1_gs,
                         Pin * f, d, B->Zb, (long)Pin * f);
     g.swf = Pin > 1 ? f : 0;
-    ok(launch_fgemm(ty, g, st));
+    ok(launch_fgemm(ty, tg(g), st));
   }
   if (r > 0)
-    ok(launch_fgemm(ty, widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->AtF,
-                                    (long)B->NUp * d, B->NUb, d, B->U, B->NUb), B->NUp), st));
+    ok(launch_fgemm(ty, tg(widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->AtF,
+                                       (long)B->NUp * d, B->NUb, d, B->U, B->NUb), B->NUp)), st));
   // D = dY W2_base^T, E = dY B2 stacked
-  ok(launch_fgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->W2F,
-                            (long)f * d, f, d, B->D, f), st));
+  ok(launch_fgemm(ty, tg(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->W2F,
+                               (long)f * d, f, d, B->D, f)), st));
   if (r > 0)
-    ok(launch_fgemm(ty, widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->BdF,
-                                    (long)B->NEp * d, B->NEb, d, B->Eb, B->NEb), B->NEp), st));
+    ok(launch_fgemm(ty, tg(widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->BdF,
+                                       (long)B->NEp * d, B->NEb, d, B->Eb, B->NEb), B->NEp)), st));
   // per expert-list position: assignment, row, weight, u and e
   const int ke = c.top_experts;
   ok(launch_invert_rows(garow, (int)R, B->grow, st));
@@ -1749,7 +1760,7 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
     ok(launch_gather_assign(as, st));
   }
   // activation backward over expert tiles, then the per-position sums
-  const int NS = act_splits(Na, f);
+  const int NS = act_splits(Na, E, f);
   if ((long)NS * Na > B->part_cap) return fail(MOE_ERR_UNSUPPORTED, "activation partials exceed their buffer");
   {
     ActArgs aa{};
@@ -1779,11 +1790,11 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   ok(launch_act_finish(B->part, NS, (int)Na, Pin, r, B->pw, B->ea, B->arow, B->q, B->wu2, B->dw, st));
   ok(launch_row_sums(ty, B->dz, B->wh, garow, B->apos, (int)R, kg, ke, k, f, Pin, B->dZbar, B->hbar, st));
   // dX: base part per group row, residual part per position, then per token
-  ok(launch_fgemm(ty, rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, ty, nullptr, 1,
-                            B->W1F, (long)Pin * f * d, d, Pin * f, B->dXb, d), st));
+  ok(launch_fgemm(ty, tg(rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, ty, nullptr, 1,
+                               B->W1F, (long)Pin * f * d, d, Pin * f, B->dXb, d)), st));
   if (r > 0)
-    ok(launch_fgemm(ty, rgemm(h->ws, B->counts, B->offsets, E, Na, B->q, 64, MOE_F32, nullptr, 1, B->A1F,
-                              (long)d * 64, d, 64, B->dXr, d), st));
+    ok(launch_fgemm(ty, tg(rgemm(h->ws, B->counts, B->offsets, E, Na, B->q, 64, MOE_F32, nullptr, 1, B->A1F,
+                                 (long)d * 64, d, 64, B->dXr, d)), st));
   {
     TokArgs ta{};
     ta.T = T;

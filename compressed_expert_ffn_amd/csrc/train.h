@@ -39,6 +39,8 @@ struct BGemmArgs {
   int n_store;     // columns stored (<= N)
   int max_rows;    // mode R: upper bound of the summed row count (grid size)
   int swf;         // launch_fgemm only (see there)
+  const int* tile_off;  // mode R, optional: [S+1] prefix of the segments' row
+                        // tile counts at the kernel's tile height
 };
 hipError_t launch_bgemm(int ty, const BGemmArgs& a, hipStream_t st);
 
@@ -76,6 +78,11 @@ struct TransArgs {
                    // fragments, rows padded with zeros to a multiple of 32)
 };
 hipError_t launch_gather_t(int ty, const TransArgs& a, hipStream_t st);
+
+// tile_off[0] = 0, tile_off[s + 1] = tile_off[s] + ceil(count[s] / rows)
+hipError_t launch_tile_scan(const int* count, int S, int rows, int* tile_off, hipStream_t st);
+// row tile height of launch_fgemm for MFMA type ty (launch_bgemm: 128)
+int fgemm_rows(int ty);
 
 // kpad_off[0] = 0, kpad_off[s + 1] = kpad_off[s] + roundup(count[s], 64)
 hipError_t launch_pad_scan(const int* count, int S, int* kpad_off, hipStream_t st);

@@ -42,6 +42,38 @@ struct BOperand {
   __device__ void fetch(int kt, int, Raw (&r)[2][4]) const { td.fetch(kt, r); }
 };
 
+// Mode R: row tile i (of TR rows) of the segments, through the tile prefix
+// (binary search) when there is one, else by walking the segments.
+template <int TR>
+__device__ __forceinline__ bool seg_tile(const BGemmArgs& a, int i, int& s, int& m0, int& M) {
+  if (a.tile_off) {
+    if (i >= a.tile_off[a.S]) return false;
+    // the last segment whose first tile is <= i (never an empty one)
+    int lo = 0, hi = a.S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tile_off[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    s = lo;
+    m0 = (i - a.tile_off[lo]) * TR;
+    M = a.seg_count[lo];
+    return true;
+  }
+  for (int q = 0; q < a.S; ++q) {
+    const int cnt = a.seg_count[q];
+    const int mt = (cnt + TR - 1) / TR;
+    if (i < mt) {
+      s = q;
+      m0 = i * TR;
+      M = cnt;
+      return true;
+    }
+    i -= mt;
+  }
+  return false;
+}
+
 template <int TY, int SA>
 __global__ void __launch_bounds__(256) bgemm_kernel(BGemmArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -50,24 +82,9 @@ __global__ void __launch_bounds__(256) bgemm_kernel(BGemmArgs a) {
   int s = 0, m0 = 0, M = 0, K = 0, n0 = 0;
   long crow0 = 0, kofs = 0;
   if (a.mode == 0) {
-    // walk the segments' row tiles (S <= 1024)
-    int i = blockIdx.x;
+    const int i = blockIdx.x;
     n0 = (i % NT) * BT;
-    i /= NT;
-    bool found = false;
-    for (int q = 0; q < a.S; ++q) {
-      const int cnt = a.seg_count[q];
-      const int mt = (cnt + BT - 1) / BT;
-      if (i < mt) {
-        s = q;
-        m0 = i * BT;
-        M = cnt;
-        found = true;
-        break;
-      }
-      i -= mt;
-    }
-    if (!found) return;
+    if (!seg_tile<BT>(a, i / NT, s, m0, M)) return;
     K = a.K;
     crow0 = a.seg_start[s];
   } else {
@@ -143,23 +160,9 @@ __global__ void __launch_bounds__(256) fgemm_kernel(BGemmArgs a) {
   int s = 0, m0 = 0, M = 0, K = 0, n0 = 0;
   long crow0 = 0, kofs = 0;
   if (a.mode == 0) {
-    int i = blockIdx.x;
+    const int i = blockIdx.x;
     n0 = (i % NT) * FN;
-    i /= NT;
-    bool found = false;
-    for (int q = 0; q < a.S; ++q) {
-      const int cnt = a.seg_count[q];
-      const int mt = (cnt + FM - 1) / FM;
-      if (i < mt) {
-        s = q;
-        m0 = i * FM;
-        M = cnt;
-        found = true;
-        break;
-      }
-      i -= mt;
-    }
-    if (!found) return;
+    if (!seg_tile<FM>(a, i / NT, s, m0, M)) return;
     K = a.K;
     crow0 = a.seg_start[s];
   } else {
@@ -312,6 +315,17 @@ __global__ void __launch_bounds__(256) gather_t_kernel(TransArgs a) {
         w[q] = static_cast<uint32_t>(from_f32<TY>(v[2 * q])) | (static_cast<uint32_t>(from_f32<TY>(v[2 * q + 1])) << 16);
       *reinterpret_cast<u4v*>(dst) = w;
     }
+  }
+}
+
+__global__ void tile_scan_kernel(const int* count, int S, int rows, int* off) {
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int s = 0; s < S; ++s) {
+      off[s] = acc;
+      acc += (count[s] + rows - 1) / rows;
+    }
+    off[S] = acc;
   }
 }
 
@@ -623,9 +637,10 @@ __global__ void __launch_bounds__(256) row_sums_kernel(const TE<TY>* dz, const T
 }
 
 // --------------------------------------------------- token: router + dX ----
-// One workgroup per token: softmax backward of the gate (w = p_g q_j), then
-// dX = sum over the token's group rows of dXb, over its assignments of dXr,
-// plus the router terms.
+// One workgroup per (token, 512 columns): softmax backward of the gate
+// (w = p_g q_j; every column block of the token repeats it, the first one
+// stores the logit gradients), then dX = sum over the token's group rows of
+// dXb, over its assignments of dXr, plus the router terms.
 template <int XT>
 __global__ void __launch_bounds__(256) tok_kernel(TokArgs a) {
   const int t = blockIdx.x;
@@ -659,7 +674,7 @@ __global__ void __launch_bounds__(256) tok_kernel(TokArgs a) {
   }
   __syncthreads();
   // logit gradients out: ds [T][kg][1 + K] (zeros for the unchosen experts)
-  for (int x = tid; x < a.kg * (1 + a.K); x += 256) {
+  for (int x = tid; blockIdx.y == 0 && x < a.kg * (1 + a.K); x += 256) {
     const int g = x / (1 + a.K), c = x % (1 + a.K);
     float v;
     if (c == 0) {
@@ -673,7 +688,9 @@ __global__ void __launch_bounds__(256) tok_kernel(TokArgs a) {
     }
     a.ds[((long)t * a.kg + g) * (1 + a.K) + c] = v;
   }
-  for (int cc = tid; cc < a.d; cc += 256) {
+  // this workgroup's 512 columns of dX
+  const int cend = min(a.d, (int)(blockIdx.y + 1) * 512);
+  for (int cc = blockIdx.y * 512 + tid; cc < cend; cc += 256) {
     float v = 0.f;
     const float* wcol = a.Wr + ((long)(cc >> 4) * a.NCp) * 16 + (cc & 15);
     for (int g = 0; g < a.kg; ++g) {
@@ -829,6 +846,13 @@ hipError_t launch_gather_t(int ty, const TransArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_tile_scan(const int* count, int S, int rows, int* tile_off, hipStream_t st) {
+  hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(64), 0, st, count, S, rows, tile_off);
+  return hipGetLastError();
+}
+
+int fgemm_rows(int ty) { return ty == DT_F32 ? 64 : 128; }
+
 hipError_t launch_pad_scan(const int* count, int S, int* kpad_off, hipStream_t st) {
   hipLaunchKernelGGL(pad_scan_kernel, dim3(1), dim3(64), 0, st, count, S, kpad_off);
   return hipGetLastError();
@@ -905,7 +929,7 @@ hipError_t launch_row_sums(int ty, const void* dz, const void* wh, const int* ga
 
 hipError_t launch_tok(const TokArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
-  dim3 grid(a.T), block(256);
+  dim3 grid(a.T, (a.d + 511) / 512), block(256);
   switch (a.x_dtype) {
     case DT_F32: hipLaunchKernelGGL(tok_kernel<DT_F32>, grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL(tok_kernel<DT_F16>, grid, block, 0, st, a); break;
