@@ -318,26 +318,24 @@ __global__ void __launch_bounds__(256) gather_t_kernel(TransArgs a) {
   }
 }
 
-__global__ void tile_scan_kernel(const int* count, int S, int rows, int* off) {
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int s = 0; s < S; ++s) {
-      off[s] = acc;
-      acc += (count[s] + rows - 1) / rows;
-    }
-    off[S] = acc;
+// Exclusive prefix of ceil(count[s] / rows) * mult over S <= 1024 segments,
+// by one workgroup of 1024 threads (off[S] = the total).
+__global__ void __launch_bounds__(1024) seg_scan_kernel(const int* count, int S, int rows, int mult, int* off) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int v = tid < S ? (count[tid] + rows - 1) / rows * mult : 0;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
   }
-}
-
-__global__ void pad_scan_kernel(const int* count, int S, int* off) {
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int s = 0; s < S; ++s) {
-      off[s] = acc;
-      acc += (count[s] + 63) / 64 * 64;
-    }
-    off[S] = acc;
-  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wv; ++w) base += wsum[w];
+  if (tid < S) off[tid] = base + inc - v;
+  if (tid == S - 1) off[S] = base + inc;
 }
 
 // ------------------------------------------------------ fragment -> plain --
@@ -395,9 +393,10 @@ __device__ __forceinline__ void load4_add(const TE<TY>* p, float (&v)[4]) {
   }
 }
 
-// Per expert-list position: assignment, row, weight and the u / e vectors.
-__global__ void gather_assign_kernel(AssignArgs a) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+// Per expert-list position (one wavefront each): assignment, row, weight
+// and the u / e vectors.
+__global__ void __launch_bounds__(256) gather_assign_kernel(AssignArgs a) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6), x = threadIdx.x & 63;
   if (p >= a.Na) return;
   // expert of position p: the last e with offsets[e] <= p
   int lo = 0, hi = a.E - 1;
@@ -407,22 +406,22 @@ __global__ void gather_assign_kernel(AssignArgs a) {
     else hi = mid - 1;
   }
   const int t = a.perm[p];
-  int slot = 0;
-  for (int s = 0; s < a.k; ++s)
-    if (a.idx[(long)t * a.k + s] == lo) slot = s;
+  // slot of expert lo among the token's k choices (lanes compare in parallel)
+  const bool hit = x < a.k && a.idx[(long)t * a.k + x] == lo;
+  const unsigned long long m = __ballot(hit);
+  const int slot = m ? __ffsll((long long)m) - 1 : 0;
   const long asg = (long)t * a.k + slot;
-  a.arow[p] = (int)asg;
-  a.apos[asg] = p;
   const int row = a.grow[(long)t * (a.k / a.ke) + slot / a.ke];
-  a.prow[p] = row;
-  a.pw[p] = a.w[asg];
+  if (x == 0) {
+    a.arow[p] = (int)asg;
+    a.apos[asg] = p;
+    a.prow[p] = row;
+    a.pw[p] = a.w[asg];
+  }
   if (a.r > 0) {
     const int j = lo % a.K;
-    const float* u = a.U + (long)row * a.NU + (long)j * a.Pin * 16;
-    float* uo = a.ua + (long)p * 64;
-    for (int x = 0; x < 64; ++x) uo[x] = x < a.Pin * 16 ? u[x] : 0.f;
-    const float* ev = a.Eb + (long)row * a.NE + j * 16;
-    for (int x = 0; x < 16; ++x) a.ea[(long)p * 16 + x] = ev[x];
+    a.ua[(long)p * 64 + x] = x < a.Pin * 16 ? a.U[(long)row * a.NU + (long)j * a.Pin * 16 + x] : 0.f;
+    if (x < 16) a.ea[(long)p * 16 + x] = a.Eb[(long)row * a.NE + j * 16 + x];
   }
 }
 
@@ -585,32 +584,26 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
   }
 }
 
-__global__ void act_finish_kernel(const float* part, int NS, int Na, int Pin, int r, const float* pw,
-                                  const float* ea, const int* arow, float* q, float* wu2, float* dw) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+// One wavefront per position: lane x < 49 sums value x over the splits.
+__global__ void __launch_bounds__(256) act_finish_kernel(const float* part, int NS, int Na, int Pin, int r,
+                                                         const float* pw, const float* ea, const int* arow, float* q,
+                                                         float* wu2, float* dw) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6), x = threadIdx.x & 63;
   if (p >= Na) return;
-  float acc[49];
+  float acc = 0.f;
+  if (x < 49)
+    for (int s = 0; s < NS; ++s) acc += part[((long)s * Na + p) * ACT_PART + x];
+  // <e, h A2> over lanes 32..47, added to <D, h> of lane 48 in a fixed order
+  float t = (r > 0 && x >= 32 && x < 48) ? ea[(long)p * 16 + (x - 32)] * acc : 0.f;
 #pragma unroll
-  for (int x = 0; x < 49; ++x) acc[x] = 0.f;
-  for (int s = 0; s < NS; ++s) {
-    const float* pp = part + ((long)s * Na + p) * ACT_PART;
-#pragma unroll
-    for (int x = 0; x < 49; ++x) acc[x] += pp[x];
-  }
-  float dwv = acc[48];
+  for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+  const float dd = __shfl(acc, 48);
   if (r > 0) {
-    float* qo = q + (long)p * 64;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      qo[x] = acc[x];
-      qo[16 + x] = Pin > 1 ? acc[16 + x] : 0.f;
-      qo[32 + x] = 0.f;
-      qo[48 + x] = 0.f;
-      wu2[(long)p * 16 + x] = pw[p] * acc[32 + x];
-      dwv += ea[(long)p * 16 + x] * acc[32 + x];
-    }
+    if (x < 32) q[(long)p * 64 + x] = (x < 16 || Pin > 1) ? acc : 0.f;
+    else q[(long)p * 64 + x] = 0.f;
+    if (x >= 32 && x < 48) wu2[(long)p * 16 + (x - 32)] = pw[p] * acc;
   }
-  dw[arow[p]] = dwv;
+  if (x == 0) dw[arow[p]] = dd + t;
 }
 
 // One workgroup per group row: dZbar and hbar as sums over its assignments.
@@ -847,14 +840,16 @@ hipError_t launch_gather_t(int ty, const TransArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tile_scan(const int* count, int S, int rows, int* tile_off, hipStream_t st) {
-  hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(64), 0, st, count, S, rows, tile_off);
+  if (S < 1 || S > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(1024), 0, st, count, S, rows, 1, tile_off);
   return hipGetLastError();
 }
 
 int fgemm_rows(int ty) { return ty == DT_F32 ? 64 : 128; }
 
 hipError_t launch_pad_scan(const int* count, int S, int* kpad_off, hipStream_t st) {
-  hipLaunchKernelGGL(pad_scan_kernel, dim3(1), dim3(64), 0, st, count, S, kpad_off);
+  if (S < 1 || S > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(1024), 0, st, count, S, 64, 64, kpad_off);
   return hipGetLastError();
 }
 
@@ -872,7 +867,8 @@ hipError_t launch_frag_to_plain(int ty, const void* frag, int G, long gsi, int N
 
 hipError_t launch_gather_assign(const AssignArgs& a, hipStream_t st) {
   if (a.Na <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_assign_kernel, dim3((a.Na + 255) / 256), dim3(256), 0, st, a);
+  if (a.k > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_assign_kernel, dim3((a.Na + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -902,8 +898,8 @@ hipError_t launch_act(int ty, const ActArgs& a, hipStream_t st) {
 hipError_t launch_act_finish(const float* part, int NS, int Na, int Pin, int r, const float* pw, const float* ea,
                              const int* arow, float* q, float* wu2, float* dw, hipStream_t st) {
   if (Na <= 0) return hipSuccess;
-  hipLaunchKernelGGL(act_finish_kernel, dim3((Na + 255) / 256), dim3(256), 0, st, part, NS, Na, Pin, r, pw, ea, arow,
-                     q, wu2, dw);
+  hipLaunchKernelGGL(act_finish_kernel, dim3((Na + 3) / 4), dim3(256), 0, st, part, NS, Na, Pin, r, pw, ea, arow, q,
+                     wu2, dw);
   return hipGetLastError();
 }
 
