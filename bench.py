@@ -154,6 +154,36 @@ def copy_calibration(mib: int) -> None:
     print(f"copied {mib} MiB x5", flush=True)
 
 
+def blas_reference(w) -> None:
+    """The layer's two base GEMMs as plain batched library GEMMs (torch.matmul,
+    hipBLASLt on ROCm), rows split evenly over the groups: a reference point
+    for the main loop, not part of the layer."""
+    import torch
+    torch.manual_seed(0)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.base_dtype]
+    G, rows = w.G, w.T * w.top_groups
+    m = rows // G
+    x = torch.randn(G, m, w.d, device="cuda", dtype=dt)
+    w1 = torch.randn(G, w.d, w.P_in * w.f, device="cuda", dtype=dt) / w.d ** 0.5
+    hh = torch.randn(G, m, w.f, device="cuda", dtype=dt)
+    w2 = torch.randn(G, w.f, w.d, device="cuda", dtype=dt) / w.f ** 0.5
+    out = {}
+    for name, a, b in (("gemm1", x, w1), ("gemm2", hh, w2)):
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(10):
+            torch.matmul(a, b)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / 10
+        fl = 2.0 * G * m * a.shape[2] * b.shape[2]
+        out[name] = {"shape": [G, m, a.shape[2], b.shape[2]], "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+    print(json.dumps({"blas_reference": w.name, **out}), flush=True)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -282,6 +312,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of --copy-mib MiB (counter scaling)")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="only time the workload's base GEMM shapes as plain library GEMMs")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/pmc_traffic.json from rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
@@ -291,6 +323,10 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration(args.copy_mib)
+        return
+    if args.blas_reference:
+        from compressed_expert_ffn_amd.workloads import WORKLOADS
+        blas_reference(WORKLOADS[args.workload])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this layer is built and measured on one GPU only; "

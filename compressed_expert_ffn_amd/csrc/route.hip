@@ -347,12 +347,40 @@ __device__ __forceinline__ float score_bias(const RouteArgs& a, int c) {
   return a.ebias ? a.ebias[c - a.G] : 0.f;
 }
 
-// Wavefront top-k: the n candidates sv[0..n) are spread over the lanes
-// (candidate c on lane c % 64); each round takes the best remaining one by a
-// butterfly over the lanes -- higher score first, ties to the lower index,
-// NaN as -inf (the order keep_best gives).  Selection r ends up in lane r's
-// (myv, myi).  k <= n, k <= 64.
+// Wavefront top-k in the order keep_best gives (higher score first, ties to
+// the lower index, NaN as -inf).  Up to 64 candidates: lane c ranks
+// candidate c by counting the candidates ahead of it.  More: candidate c
+// sits on lane c % 64 and each round takes the best remaining one by a
+// butterfly over the lanes.  Selection r ends up in lane r's (myv, myi).
+// k <= n, k <= 64.
 __device__ void wave_topk(const float* sv, int n, int k, int lane, float& myv, int& myi) {
+  if (n <= 64) {
+    // one candidate per lane, ranked against all n in that same order (a
+    // total order, so the ranks are 0 .. n-1): no cross-lane rounds
+    float v = -INFINITY;
+    if (lane < n) {
+      v = sv[lane];
+      v = (v == v) ? v : -INFINITY;
+    }
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      float u = sv[j];
+      u = (u == u) ? u : -INFINITY;
+      rank += (u > v || (u == v && j < lane)) ? 1 : 0;
+    }
+    myv = -INFINITY;
+    myi = -1;
+    for (int r = 0; r < k; ++r) {
+      const unsigned long long m = __ballot(lane < n && rank == r);
+      const int c = __ffsll((long long)m) - 1;
+      if (lane == r) {
+        float u = sv[c];
+        myv = (u == u) ? u : -INFINITY;
+        myi = c;
+      }
+    }
+    return;
+  }
   uint32_t used = 0;  // bit q: candidate lane + 64 q taken
   myv = -INFINITY;
   myi = -1;

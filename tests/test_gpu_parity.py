@@ -234,6 +234,49 @@ def test_routing_ties_go_to_the_lower_index(wi):
         lay.close()
 
 
+# Candidate sets past one wavefront (over 64 groups or experts: the round-
+# by-round butterfly selection) and up to it (rank counting), on the
+# separate logits + selection path (more than 128 score columns).
+WIDE_ROUTERS = [
+    dict(G=130, K=1, top_groups=3, top_experts=1, x_dtype="f32", base_dtype="f32"),
+    dict(G=4, K=100, top_groups=2, top_experts=5, x_dtype="bf16", base_dtype="bf16"),
+    dict(G=16, K=64, top_groups=2, top_experts=4, x_dtype="f16", base_dtype="f16"),
+]
+
+
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("ci", range(len(WIDE_ROUTERS)))
+def test_routing_wide_candidate_sets(ci, ties):
+    """Routing with 64 to 400 candidates per selection matches the oracle bit
+    for bit, with random scores and with every score tied to others."""
+    from compressed_expert_ffn_amd import synth
+    from tests.layers import oracle_layer
+    L = _lib()
+    w = dataclasses.replace(WORKLOADS[0], name="wide_router", T=160, d=256, f=64, r=0, resid="none",
+                            act="swiglu", **WIDE_ROUTERS[ci])
+    say(f"[wide router] {WIDE_ROUTERS[ci]} ties={ties}")
+    if ties:
+        inputs = synth.make_layer(w)
+        wT = dataclasses.replace(w, T=inputs["X"].shape[0])
+        rng = np.random.default_rng(11)
+        inputs["W_grp"] = np.zeros_like(inputs["W_grp"])
+        if inputs["W_exp"] is not None:
+            inputs["W_exp"] = np.zeros_like(inputs["W_exp"])
+        inputs["group_bias"] = (rng.integers(0, 3, size=w.G) * 0.5).astype(np.float32)
+        if w.K > 1:
+            inputs["expert_bias"] = (rng.integers(0, 3, size=w.E) * 0.5).astype(np.float32)
+        layer = oracle_layer(wT, inputs)
+    else:
+        wT, inputs, layer = make_parity_layer(w)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        rt = O.route(layer)
+        got = route_to_host(lay.route(x_to_device(inputs["X"], w.x_dtype)))
+        check_routing(got, rt, wT, wT.T)
+    finally:
+        lay.close()
+
+
 # Column counts that leave the last 256-column tile partly empty (idle
 # wavefronts in the input projection: P_in * f not a multiple of 256; in the
 # down projection: d not a multiple of 256).
