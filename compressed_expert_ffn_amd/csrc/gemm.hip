@@ -1193,11 +1193,11 @@ hipError_t go_nw(KF kfn, dim3 grid, int nw, size_t lds, const GemmArgs& a, hipSt
 template <int XT, int TY, int CB_, bool INT4>
 hipError_t launch_ugemm_cb(const GemmArgs& a, dim3 grid, hipStream_t st) {
   // 8 wavefronts (a dependent chain half as long) when there are fewer
-  // workgroups than compute units and every wavefront keeps at least 2
-  // stages of d; 64-column 16-bit tiles only (the others would spill at two
-  // wavefronts per SIMD)
-  if constexpr (CB_ == 2 && TY != DT_F32) {
-    if (grid.x < 256 && a.d / KB >= 16)
+  // workgroups than two per compute unit and every wavefront keeps at least
+  // 2 stages of d; 32- and 64-column 16-bit tiles only (the others would
+  // spill at two wavefronts per SIMD)
+  if constexpr (CB_ <= 2 && TY != DT_F32) {
+    if (grid.x < 512 && a.d / KB >= 16)
       return go_nw(ugemm_kernel<XT, TY, CB_, INT4, 8>, grid, 8, (size_t)8 * CB_ * 16 * 64 * sizeof(float), a, st);
   }
   return go_nw(ugemm_kernel<XT, TY, CB_, INT4, 4>, grid, 4, (size_t)4 * CB_ * 16 * 64 * sizeof(float), a, st);
@@ -1209,6 +1209,12 @@ hipError_t launch_ugemm_t(const GemmArgs& a, int max_mtiles, hipStream_t st) {
   // INT4 factors are decoded per use: narrower tiles keep two workgroups per
   // compute unit to overlap the decode with the other's loads; narrower
   // tiles also when the wider ones would leave most compute units idle
+  // few INT4 tiles (decode-shaped batches): 32-column tiles, twice the
+  // workgroups streaming the factors (decode layer 20 -> 17.5 us)
+  if (int4 && (long)max_mtiles * ((a.NU + 63) / 64) < 256) {
+    const dim3 grid((unsigned)max_mtiles * ((a.NU + 31) / 32));
+    return launch_ugemm_cb<XT, TY, 1, true>(a, grid, st);
+  }
   if (a.NU <= 64 || int4 || (long)max_mtiles * ((a.NU + 63) / 64) < 256) {
     const dim3 grid((unsigned)max_mtiles * ((a.NU + 63) / 64));
     if (int4) return launch_ugemm_cb<XT, TY, 2, true>(a, grid, st);
