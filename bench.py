@@ -420,6 +420,22 @@ def main():
 
     ms = ms_stream if ms_graph is None else min(ms_stream, ms_graph)
     launch = "stream" if ms_graph is None or ms_stream <= ms_graph else "hipgraph"
+
+    # per-step latency distribution: the same launch form, each step
+    # bracketed by HIP events on the launch stream
+    nlat = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nlat)]
+    for i in range(nlat):
+        evs[i][0].record()
+        if launch == "hipgraph":
+            graphs[i % copies].replay()
+        else:
+            step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    lat = np.sort(np.array([a.elapsed_time(b) for a, b in evs]))
+    step_lat = dict(n=nlat, p10=round(float(np.percentile(lat, 10)), 5), p50=round(float(np.percentile(lat, 50)), 5),
+                    p90=round(float(np.percentile(lat, 90)), 5))
     value = w.T / (ms * 1e-3)
 
     hbm_bound = w.index == 4
@@ -451,6 +467,7 @@ def main():
         assignments_per_s=round(w.T * w.k / (ms * 1e-3), 1),
         layer_tflops=round(total_flops / (ms * 1e-3) / 1e12, 2),
         ms_stream=round(ms_stream, 5), ms_graph=None if ms_graph is None else round(ms_graph, 5),
+        step_ms_events=step_lat,
         stage_ms={k: round(v, 5) for k, v in stage_ms.items() if v > 0},
         touched_groups=tg, touched_experts=te,
         expert_load_max_over_avg=round(float(counts.max() / max(counts.mean(), 1e-9)), 3),
