@@ -1805,6 +1805,8 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
     ta.ke = ke;
     ta.k = k;
     ta.r = r;
+    // few tokens: several workgroups per token
+    ta.cols = T >= 1024 ? (d + 3) / 4 * 4 : 512;
     ta.idx = live.idx;
     ta.gidx = live.gidx;
     ta.w = live.w;

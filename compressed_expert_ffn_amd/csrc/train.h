@@ -156,6 +156,7 @@ hipError_t launch_row_sums(int ty, const void* dz, const void* wh, const int* ga
 // group rows of dXb + sum over its assignments of dXr + router terms.
 struct TokArgs {
   int T, d, G, K, kg, ke, k, r;
+  int cols;             // dX columns per workgroup (a multiple of 4)
   const int* idx;
   const int* gidx;
   const float* w;

@@ -630,10 +630,10 @@ __global__ void __launch_bounds__(256) row_sums_kernel(const TE<TY>* dz, const T
 }
 
 // --------------------------------------------------- token: router + dX ----
-// One workgroup per (token, 512 columns): softmax backward of the gate
-// (w = p_g q_j; every column block of the token repeats it, the first one
-// stores the logit gradients), then dX = sum over the token's group rows of
-// dXb, over its assignments of dXr, plus the router terms.
+// One workgroup per (token, block of a.cols columns): softmax backward of
+// the gate (w = p_g q_j; every column block of the token repeats it, the
+// first one stores the logit gradients), then dX = sum over the token's
+// group rows of dXb, over its assignments of dXr, plus the router terms.
 template <int XT>
 __global__ void __launch_bounds__(256) tok_kernel(TokArgs a) {
   const int t = blockIdx.x;
@@ -681,23 +681,39 @@ __global__ void __launch_bounds__(256) tok_kernel(TokArgs a) {
     }
     a.ds[((long)t * a.kg + g) * (1 + a.K) + c] = v;
   }
-  // this workgroup's 512 columns of dX
-  const int cend = min(a.d, (int)(blockIdx.y + 1) * 512);
-  for (int cc = blockIdx.y * 512 + tid; cc < cend; cc += 256) {
-    float v = 0.f;
+  // this workgroup's columns of dX, 4 consecutive per thread
+  __shared__ int srow[MAX_KG], sgg[MAX_KG], sex[MAX_SLOTS], spos[MAX_SLOTS];
+  if (tid < a.kg) {
+    srow[tid] = a.grow[(long)t * a.kg + tid];
+    sgg[tid] = a.gidx[(long)t * a.kg + tid];
+  }
+  if (tid < a.k) {
+    sex[tid] = a.idx[(long)t * a.k + tid];
+    spos[tid] = a.r ? a.apos[(long)t * a.k + tid] : 0;
+  }
+  __syncthreads();
+  const int cbeg = blockIdx.y * a.cols, cend = min(a.d, cbeg + a.cols);
+  auto ld4 = [](const float* p) { return *reinterpret_cast<const float4*>(p); };
+  for (int cc = cbeg + tid * 4; cc < cend; cc += 1024) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](float s, const float4& x) {
+      v.x += s * x.x;
+      v.y += s * x.y;
+      v.z += s * x.z;
+      v.w += s * x.w;
+    };
     const float* wcol = a.Wr + ((long)(cc >> 4) * a.NCp) * 16 + (cc & 15);
     for (int g = 0; g < a.kg; ++g) {
-      const int row = a.grow[(long)t * a.kg + g];
-      v += a.dXb[(long)row * a.d + cc];
-      const int gg = a.gidx[(long)t * a.kg + g];
-      v += dsv[g] * wcol[gg * 16];
+      add(1.f, ld4(a.dXb + (long)srow[g] * a.d + cc));
+      add(dsv[g], ld4(wcol + sgg[g] * 16));
       for (int b = 0; b < a.ke; ++b) {
-        const long s = (long)t * a.k + g * a.ke + b;
-        if (a.K > 1) v += dev[g * a.ke + b] * wcol[(a.G + a.idx[s]) * 16];
-        if (a.r) v += a.dXr[(long)a.apos[s] * a.d + cc];
+        const int sl = g * a.ke + b;
+        if (a.K > 1) add(dev[sl], ld4(wcol + (a.G + sex[sl]) * 16));
+        if (a.r) add(1.f, ld4(a.dXr + (long)spos[sl] * a.d + cc));
       }
     }
-    static_cast<TE<XT>*>(a.dX)[(long)t * a.d + cc] = from_f32<XT>(v);
+    const float o[4] = {v.x, v.y, v.z, v.w};
+    store4<XT>(static_cast<TE<XT>*>(a.dX) + (long)t * a.d + cc, o);
   }
 }
 
@@ -925,7 +941,8 @@ hipError_t launch_row_sums(int ty, const void* dz, const void* wh, const int* ga
 
 hipError_t launch_tok(const TokArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
-  dim3 grid(a.T, (a.d + 511) / 512), block(256);
+  if (a.cols <= 0 || a.cols % 4 || a.d % 16) return hipErrorInvalidValue;
+  dim3 grid(a.T, (a.d + a.cols - 1) / a.cols), block(256);
   switch (a.x_dtype) {
     case DT_F32: hipLaunchKernelGGL(tok_kernel<DT_F32>, grid, block, 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL(tok_kernel<DT_F16>, grid, block, 0, st, a); break;

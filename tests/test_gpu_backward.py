@@ -28,6 +28,8 @@ CASES = [
     (2, dict(T=256, d=512, f=1024)),
     (3, dict(T=150, act="gelu_tanh", x_dtype="bf16", base_dtype="bf16")),
     (1, dict(T=130, top_groups=2, G=4, K=4, resid="int4_g32", r=12)),
+    (1, dict(T=1)),
+    (4, dict(T=3)),
 ]
 
 
@@ -83,5 +85,25 @@ def test_backward_matches_oracle(wi, chg):
 
         for (k1, t1), (k2, t2) in zip(flat(out), flat(out2)):
             assert k1 == k2 and torch.equal(t1, t2), k1
+    finally:
+        lay.close()
+
+
+def test_backward_without_tokens_writes_zero_gradients():
+    """T = 0: every gradient buffer is written with zeros (the caller's
+    buffers start as garbage)."""
+    import torch
+    from compressed_expert_ffn_amd import _lib as L
+    w = dataclasses.replace(WORKLOADS[1], T=64)
+    wT, inputs, layer = make_parity_layer(w)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        X = x_to_device(inputs["X"], w.x_dtype)[:0]
+        out = lay.backward(X, X)
+        torch.cuda.synchronize()
+        for k, v in out.items():
+            for t in (v if isinstance(v, (list, tuple)) else [v]):
+                if t is not None and t.numel():
+                    assert float(t.float().abs().max()) == 0.0, k
     finally:
         lay.close()
