@@ -691,7 +691,7 @@ struct BwdState {
   void *W1F = nullptr, *W2F = nullptr, *AtF = nullptr, *BdF = nullptr, *A1F = nullptr;
   float *Atp = nullptr, *B1p = nullptr, *Adp = nullptr;
   int NUb = 0, NEb = 0, NUp = 0, NEp = 0;  // stacked factor rows, and rounded up to 64
-  long Kg = 0, KgF = 0, Ke = 0, part_cap = 0;
+  long Kg = 0, KgF = 0, part_cap = 0;
   int *counts = nullptr, *offsets = nullptr, *perm = nullptr, *arow = nullptr, *apos = nullptr, *prow = nullptr;
   int *grow = nullptr, *kpad_g = nullptr, *kpad_e = nullptr, *toff_g = nullptr, *toff_e = nullptr;
   float *Zb = nullptr, *U = nullptr, *D = nullptr, *Eb = nullptr, *pw = nullptr, *part = nullptr;
@@ -699,8 +699,6 @@ struct BwdState {
   float *ds = nullptr;
   void *dz = nullptr, *wh = nullptr, *dZbar = nullptr, *hbar = nullptr;
   void *XTg = nullptr, *dZT = nullptr, *hbT = nullptr, *dYTg = nullptr, *dsdeT = nullptr;
-  void *XTe = nullptr, *dYTe = nullptr, *qT = nullptr, *uT = nullptr, *dzT = nullptr, *whT = nullptr;
-  void *eT = nullptr, *wu2T = nullptr;
 };
 
 // ------------------------------------------------------ group offload ----
@@ -1518,7 +1516,6 @@ int prepare_backward(moe_handle* h) {
   // (multiples of 64, so every transposed row starts 128-byte aligned)
   B->Kg = (R + 64L * G + 63) / 64 * 64;
   B->KgF = B->Kg;
-  B->Ke = (Na + 64L * E + 63) / 64 * 64;
   // act_splits(Na, E, f) * Na <= 1024 * 64 + Na for every Na
   B->part_cap = 1024L * 64 + Na;
   TRY(alloc_i(&B->counts, E));
@@ -1556,14 +1553,6 @@ int prepare_backward(moe_handle* h) {
     TRY(alloc_f(&B->ua, (size_t)Na * 64));
     TRY(alloc_f(&B->ea, (size_t)Na * 16));
     TRY(alloc_f(&B->dXr, (size_t)Na * d));
-    TRY(alloc_bytes(&B->XTe, (size_t)d * B->Ke * es));
-    TRY(alloc_bytes(&B->dYTe, (size_t)d * B->Ke * es));
-    TRY(alloc_bytes(&B->qT, (size_t)Pin * 16 * B->Ke * es));
-    TRY(alloc_bytes(&B->uT, (size_t)Pin * 16 * B->Ke * es));
-    TRY(alloc_bytes(&B->dzT, (size_t)Pin * f * B->Ke * es));
-    TRY(alloc_bytes(&B->whT, (size_t)f * B->Ke * es));
-    TRY(alloc_bytes(&B->eT, (size_t)16 * B->Ke * es));
-    TRY(alloc_bytes(&B->wu2T, (size_t)16 * B->Ke * es));
   }
   (void)tmp;
   if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_ERR_HIP, "backward set-up failed");
@@ -1855,32 +1844,41 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
     else
       ok(launch_zero_f(gr->d_expert_bias, E, st));
   }
-  // residual factor gradients over each expert's assignments
+  // residual factor gradients over each expert's assignments (position
+  // order), the row operands transposed on the fly
   if (r > 0) {
-    const long Ke = B->Ke;
-    // X and dY rows by token; the rest is stored by position already
-    auto eg = [&](const void* in, int dt, long ld, int ncols, const int* map, int div, void* out) {
-      ok(launch_gather_t(ty, tgather(E, B->offsets, B->counts, B->kpad_e, in, dt, ld, 0, ncols, map, div, out, Ke,
-                                     Ke), st));
+    auto tg = [&](const void* A, int adt, long lda, int ac0, const int* amap, int adiv, const float* Bm, long ldb,
+                  int bc0, int N, int M, float* clo, float* chi) {
+      TGemmArgs t{};
+      t.S = E;
+      t.seg_start = B->offsets;
+      t.seg_count = B->counts;
+      t.a = A;
+      t.a_dtype = adt;
+      t.lda = lda;
+      t.a_c0 = ac0;
+      t.a_map = amap;
+      t.a_div = adiv;
+      t.b = Bm;
+      t.ldb = ldb;
+      t.b_c0 = bc0;
+      t.N = N;
+      t.M = M;
+      t.c_lo = clo;
+      t.c_hi = chi;
+      t.c_sstride = (long)M * r;
+      t.ldc = r;
+      t.n_store = r;
+      ok(launch_tgemm(ty, t, st));
     };
-    eg(X, c.x_dtype, d, d, B->arow, k, B->XTe);
-    eg(dY, c.x_dtype, d, d, B->arow, k, B->dYTe);
-    eg(B->q, MOE_F32, 64, Pin * 16, nullptr, 1, B->qT);
-    eg(B->ua, MOE_F32, 64, Pin * 16, nullptr, 1, B->uT);
-    eg(B->dz, ty, (long)Pin * f, Pin * f, nullptr, 1, B->dzT);
-    eg(B->wh, ty, f, f, nullptr, 1, B->whT);
-    eg(B->ea, MOE_F32, 16, 16, nullptr, 1, B->eT);
-    eg(B->wu2, MOE_F32, 16, 16, nullptr, 1, B->wu2T);
-    for (int p = 0; p < Pin; ++p) {
-      ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, B->XTe, Ke, static_cast<char*>(B->qT) + (size_t)p * 16 * Ke * es,
-                                Ke, d, 16, gr->dA[p], (long)d * r, r, r), st));
-      ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, static_cast<char*>(B->dzT) + (size_t)p * f * Ke * es, Ke,
-                                static_cast<char*>(B->uT) + (size_t)p * 16 * Ke * es, Ke, f, 16, gr->dB[p],
-                                (long)f * r, r, r), st));
-    }
-    ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, B->whT, Ke, B->eT, Ke, f, 16, gr->dA[P - 1], (long)f * r, r, r), st));
-    ok(launch_bgemm(ty, kgemm(E, B->kpad_e, ty, B->dYTe, Ke, B->wu2T, Ke, d, 16, gr->dB[P - 1], (long)d * r, r, r),
-                    st));
+    // dA1_p = X^T q_p (both input projections in one pass over X)
+    tg(X, c.x_dtype, d, 0, B->arow, k, B->q, 64, 0, Pin * 16, d, gr->dA[0], Pin > 1 ? gr->dA[1] : nullptr);
+    // dB1_p = dz_p^T u_p
+    for (int p = 0; p < Pin; ++p)
+      tg(B->dz, ty, (long)Pin * f, p * f, nullptr, 1, B->ua, 64, p * 16, 16, f, gr->dB[p], nullptr);
+    // dA2 = (w h)^T e, dB2 = dY^T (w h A2)
+    tg(B->wh, ty, f, 0, nullptr, 1, B->ea, 16, 0, 16, f, gr->dA[P - 1], nullptr);
+    tg(dY, c.x_dtype, d, 0, B->arow, k, B->wu2, 16, 0, 16, d, gr->dB[P - 1], nullptr);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backward launch");
   return MOE_OK;

@@ -52,6 +52,34 @@ hipError_t launch_bgemm(int ty, const BGemmArgs& a, hipStream_t st);
 // column n is C column ((n / 32) & 1) swf + (n / 64) 32 + n % 32.
 hipError_t launch_fgemm(int ty, const BGemmArgs& a, hipStream_t st);
 
+// Thin products over segments of rows, transposed on the fly:
+//   C[s][m][n] = sum over rows p of segment s of A(p, m) B(p, n), n < N <= 32,
+// A rows a_map ? a_map[p] / a_div : p of a row-major matrix (type a_dtype,
+// ld lda, columns from a_c0), B rows p of a row-major fp32 matrix (ldb,
+// columns from b_c0).  Column n of C goes to c_lo (n < 16) or c_hi (n - 16)
+// at [s * c_sstride + m * ldc + n % 16] when n % 16 < n_store.  Each segment
+// is summed in row order by one workgroup (no atomics).
+struct TGemmArgs {
+  int S;
+  const int* seg_start;
+  const int* seg_count;
+  const void* a;
+  int a_dtype;
+  long lda;
+  int a_c0;
+  const int* a_map;
+  int a_div;
+  const float* b;
+  long ldb;
+  int b_c0;
+  int N, M;
+  float* c_lo;
+  float* c_hi;
+  long c_sstride;
+  int ldc, n_store;
+};
+hipError_t launch_tgemm(int ty, const TGemmArgs& a, hipStream_t st);
+
 // Fragment-major copy of row-major [G][N][Kd] (type TY, group strides in
 // elements), rows padded with zeros to a multiple of 64.
 hipError_t launch_plain_to_frag(int ty, const void* in, int G, long g_stride_in, int N, int Kd, void* out,

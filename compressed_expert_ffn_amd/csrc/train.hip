@@ -241,6 +241,97 @@ __global__ void plain_to_frag_kernel(const TE<TY>* in, int G, long gsi, int N, i
   }
 }
 
+// ------------------------------------------------ thin transposed GEMM ----
+// A workgroup owns 128 columns m of A for one segment and walks the
+// segment's rows in chunks of 64: the chunk's A rows (128 contiguous values
+// each) and B rows go to LDS transposed (k = row contiguous), then wavefront
+// w takes m-block w: four 32x32x16 MFMA steps against the 32 B columns.
+template <int TY, int SA>
+__global__ void __launch_bounds__(256) tgemm_kernel(TGemmArgs a) {
+  using F = FragT<TY>;
+  constexpr int KP = 64 + (TY == DT_F32 ? 4 : 8);  // LDS row stride (16-byte rows of fragments)
+  __shared__ __attribute__((aligned(16))) TE<TY> lA[128 * KP];
+  __shared__ __attribute__((aligned(16))) TE<TY> lB[32 * KP];
+  const int s = blockIdx.y, m0 = blockIdx.x * 128;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int start = a.seg_start[s], cnt = a.seg_count[s];
+  const TE<SA>* A = static_cast<const TE<SA>*>(a.a);
+  f16v acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  const int pr = tid >> 2, q4 = tid & 3;  // loader: row pr of the chunk, quarter q4
+  for (int c0 = 0; c0 < cnt; c0 += 64) {
+    const bool ok = c0 + pr < cnt;
+    long row = 0;
+    if (ok) {
+      const long p = (long)start + c0 + pr;
+      row = a.a_map ? (long)(a.a_map[p] / a.a_div) : p;
+    }
+    __syncthreads();  // the previous chunk's fragments are read
+    // A: 32 values m = q4 * 32 .. + 31 of row pr
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = q4 * 32 + j * 8;
+      float v[8];
+      if (ok && m0 + m < a.M) {
+        const RawT<SA> raw = ld_raw<SA>(A + row * a.lda + a.a_c0 + m0 + m);
+        if constexpr (SA == DT_F32) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = raw[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t h = static_cast<uint16_t>((raw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            v[e] = SA == DT_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lA[(m + e) * KP + pr] = from_f32<TY>(v[e]);
+    }
+    // B: 8 values n = q4 * 8 .. + 7 of row pr
+    {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int n = q4 * 8 + e;
+        v[e] = (ok && n < a.N) ? a.b[((long)start + c0 + pr) * a.ldb + a.b_c0 + n] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lB[(q4 * 8 + e) * KP + pr] = from_f32<TY>(v[e]);
+    }
+    __syncthreads();
+    const TE<TY>* ar = lA + (wave * 32 + (lane & 31)) * KP + 8 * (lane >> 5);
+    const TE<TY>* br = lB + (lane & 31) * KP + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      F fa, fb;
+      if constexpr (TY == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          fa[e] = ar[ks * 16 + e];
+          fb[e] = br[ks * 16 + e];
+        }
+      } else {
+        fa = *reinterpret_cast<const F*>(ar + ks * 16);
+        fb = *reinterpret_cast<const F*>(br + ks * 16);
+      }
+      acc = mfma32<TY>(fa, fb, acc);
+    }
+  }
+  const int n = lane & 31;
+  if (n >= a.N || (n & 15) >= a.n_store) return;
+  float* cb = (n < 16 ? a.c_lo : a.c_hi) + (long)s * a.c_sstride + (n & 15);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = m0 + wave * 32 + acc32_row(v, lane);
+    if (m < a.M) cb[(long)m * a.ldc] = acc[v];
+  }
+}
+
 // ------------------------------------------------- gather + transpose ------
 // One block per 64 k-columns (a padded slice of one segment) x 64 output
 // rows; reads 64 source rows, writes 64 k-contiguous runs.
@@ -834,6 +925,25 @@ hipError_t launch_plain_to_frag(int ty, const void* in, int G, long gsi, int N, 
   else
     hipLaunchKernelGGL(plain_to_frag_kernel<DT_F16>, grid, block, 0, st, static_cast<const uint16_t*>(in), G, gsi, N,
                        Kd, static_cast<uint16_t*>(out), gso);
+  return hipGetLastError();
+}
+
+hipError_t launch_tgemm(int ty, const TGemmArgs& a, hipStream_t st) {
+  if (a.S <= 0 || a.M <= 0) return hipSuccess;
+  if (a.N < 1 || a.N > 32 || a.M % 8 || a.lda % 8 || a.a_c0 % 8) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.M + 127) / 128), (unsigned)a.S), block(256);
+#define TG(TY, SA) hipLaunchKernelGGL((tgemm_kernel<TY, SA>), grid, block, 0, st, a)
+  if (ty == DT_F32) {
+    TG(DT_F32, DT_F32);
+  } else if (ty == DT_F16) {
+    if (a.a_dtype == DT_F32) TG(DT_F16, DT_F32);
+    else if (a.a_dtype == DT_BF16) TG(DT_F16, DT_BF16);
+    else TG(DT_F16, DT_F16);
+  } else {
+    if (a.a_dtype == DT_F32) TG(DT_BF16, DT_F32);
+    else TG(DT_BF16, DT_BF16);
+  }
+#undef TG
   return hipGetLastError();
 }
 
