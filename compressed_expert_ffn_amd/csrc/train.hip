@@ -150,7 +150,7 @@ __device__ __forceinline__ long frag_index(long n, long k, long KS) {
 // main loop with plain gathered rows on the token side.  KT = 0 (an empty
 // k segment) stores zeros.
 template <int TY, int SA, int RT>
-__global__ void __launch_bounds__(256) fgemm_kernel(BGemmArgs a) {
+__global__ void __launch_bounds__(256, (TY == DT_F32 || SA == DT_F32) ? 1 : 2) fgemm_kernel(BGemmArgs a) {
   using F = FragT<TY>;
   constexpr int FM = 32 * RT, FN = 256;
   extern __shared__ __attribute__((aligned(16))) char smem[];
