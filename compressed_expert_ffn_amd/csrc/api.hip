@@ -1533,8 +1533,10 @@ int prepare_backward(moe_handle* h) {
   TRY(alloc_f(&B->part, (size_t)B->part_cap * ACT_PART));
   TRY(alloc_f(&B->Zb, (size_t)R * Pin * f));
   TRY(alloc_f(&B->D, (size_t)R * f));
-  TRY(alloc_bytes(&B->dZbar, (size_t)R * Pin * f * es));
-  TRY(alloc_bytes(&B->hbar, (size_t)R * f * es));
+  if (K > 1) {  // (one expert per group: dz and w h serve as dZbar and hbar)
+    TRY(alloc_bytes(&B->dZbar, (size_t)R * Pin * f * es));
+    TRY(alloc_bytes(&B->hbar, (size_t)R * f * es));
+  }
   TRY(alloc_f(&B->dw, (size_t)Na));
   TRY(alloc_f(&B->dXb, (size_t)R * d));
   TRY(alloc_f(&B->ds, (size_t)R * (1 + K)));
@@ -1774,12 +1776,26 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
     aa.dz = B->dz;
     aa.wh = B->wh;
     aa.part = B->part;
-    ok(launch_act(ty, aa, st));
+    if (r > 0) {
+      ok(launch_act(ty, aa, st));
+      ok(launch_act_finish(B->part, NS, (int)Na, Pin, r, B->pw, B->ea, B->arow, B->q, B->wu2, B->dw, st));
+    } else {
+      ok(launch_act_plain(ty, aa, B->arow, B->dw, st));
+    }
   }
-  ok(launch_act_finish(B->part, NS, (int)Na, Pin, r, B->pw, B->ea, B->arow, B->q, B->wu2, B->dw, st));
-  ok(launch_row_sums(ty, B->dz, B->wh, garow, B->apos, (int)R, kg, ke, k, f, Pin, B->dZbar, B->hbar, st));
+  // With one expert per group the expert lists are the group lists (the
+  // same stable order), so position p is group row p: dZbar and hbar are dz
+  // and w h themselves.
+  void* dZbar = B->dZbar;
+  void* hbar = B->hbar;
+  if (K == 1) {
+    dZbar = B->dz;
+    hbar = B->wh;
+  } else {
+    ok(launch_row_sums(ty, B->dz, B->wh, garow, B->apos, (int)R, kg, ke, k, f, Pin, dZbar, hbar, st));
+  }
   // dX: base part per group row, residual part per position, then per token
-  ok(launch_fgemm(ty, tg(rgemm(h->ws, live.gcounts, live.goffsets, G, R, B->dZbar, (long)Pin * f, ty, nullptr, 1,
+  ok(launch_fgemm(ty, tg(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dZbar, (long)Pin * f, ty, nullptr, 1,
                                B->W1F, (long)Pin * f * d, d, Pin * f, B->dXb, d)), st));
   if (r > 0)
     ok(launch_fgemm(ty, tg(rgemm(h->ws, B->counts, B->offsets, E, Na, B->q, 64, MOE_F32, nullptr, 1, B->A1F,
@@ -1816,9 +1832,9 @@ int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* 
   const long Kg = B->Kg, KgF = B->KgF;
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, X, c.x_dtype, d, 0, d, garow, kg, B->XTg,
                                  Kg, Kg), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->dZbar, ty, (long)Pin * f, 0,
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, dZbar, ty, (long)Pin * f, 0,
                                  Pin * f, nullptr, 1, B->dZT, KgF, Kg, 1), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->hbar, ty, f, 0, f, nullptr, 1,
+  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, hbar, ty, f, 0, f, nullptr, 1,
                                  B->hbT, Kg, Kg), st));
   ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, dY, c.x_dtype, d, 0, d, garow, kg,
                                  B->dYTg, KgF, Kg, 1), st));

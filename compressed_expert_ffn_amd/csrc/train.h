@@ -170,6 +170,11 @@ struct ActArgs {
 constexpr int ACT_PART = 64;
 hipError_t launch_act(int ty, const ActArgs& a, hipStream_t st);
 
+// The same for layers without residuals (a.r == 0; part, NS, ua, ea, B1p
+// and Adp unused): one wavefront per position along the columns, writing
+// dz, w h and dw[arow[p]] = <D, h> directly.
+hipError_t launch_act_plain(int ty, const ActArgs& a, const int* arow, float* dw, hipStream_t st);
+
 // Sums the NS partials of each position in split order: q[p][0..Pin 16)
 // (q[p][Pin 16..64) = 0), wu2[p] = w_p (h A2), dw[arow[p]] = <D, h> + <e, h A2>.
 hipError_t launch_act_finish(const float* part, int NS, int Na, int Pin, int r, const float* pw, const float* ea,

@@ -675,6 +675,57 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
   }
 }
 
+// Without residuals: one wavefront per position, lanes along the columns
+// (4 consecutive per lane, 256 per step), so every access is a contiguous
+// run of the row; <D, h> is summed per lane in column order, then over the
+// lanes, and written as the gate-weight gradient.
+template <int TY, int PIN>
+__global__ void __launch_bounds__(256) act_plain_kernel(ActArgs a, const int* arow, float* dw) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (p >= a.Na) return;
+  const int f = a.f, row = a.prow[p];
+  const float wt = a.pw[p];
+  const float* zrow = a.Zb + (long)row * PIN * f;
+  const float* drow = a.D + (long)row * f;
+  TE<TY>* dzo = static_cast<TE<TY>*>(a.dz) + (long)p * PIN * f;
+  TE<TY>* who = static_cast<TE<TY>*>(a.wh) + (long)p * f;
+  float dd = 0.f;
+  for (int c = lane * 4; c < f; c += 256) {
+    const float4 zg4 = *reinterpret_cast<const float4*>(zrow + c);
+    float4 zu4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (PIN > 1) zu4 = *reinterpret_cast<const float4*>(zrow + f + c);
+    const float4 d4 = *reinterpret_cast<const float4*>(drow + c);
+    const float zgv[4] = {zg4.x, zg4.y, zg4.z, zg4.w}, zuv[4] = {zu4.x, zu4.y, zu4.z, zu4.w};
+    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+    float og[4], ou[4], oh[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float zg = zgv[j], zu = zuv[j], dh = wt * dv[j];
+      float h, dzg, dzu = 0.f;
+      if (a.act == ACT_SWIGLU) {
+        const float sg = sigm(zg), sl = zg * sg;
+        h = sl * zu;
+        dzu = dh * sl;
+        dzg = dh * zu * sg * (1.0f + zg * (1.0f - sg));
+      } else {
+        float dg;
+        h = gelu_t(zg, dg);
+        dzg = dh * dg;
+      }
+      og[j] = dzg;
+      ou[j] = dzu;
+      oh[j] = wt * h;
+      dd += dv[j] * h;
+    }
+    store4<TY>(dzo + c, og);
+    if (PIN > 1) store4<TY>(dzo + f + c, ou);
+    store4<TY>(who + c, oh);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) dd += __shfl_xor(dd, o);
+  if (lane == 0) dw[arow[p]] = dd;
+}
+
 // One wavefront per position: lane x < 49 sums value x over the splits.
 __global__ void __launch_bounds__(256) act_finish_kernel(const float* part, int NS, int Na, int Pin, int r,
                                                          const float* pw, const float* ea, const int* arow, float* q,
@@ -1018,6 +1069,24 @@ hipError_t launch_act(int ty, const ActArgs& a, hipStream_t st) {
     default: AK(DT_BF16); break;
   }
 #undef AK
+  return hipGetLastError();
+}
+
+hipError_t launch_act_plain(int ty, const ActArgs& a, const int* arow, float* dw, hipStream_t st) {
+  if (a.Na <= 0) return hipSuccess;
+  if (a.f % 4 || a.r || a.Pin < 1 || a.Pin > 2) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.Na + 3) / 4)), block(256);
+#define AP(TY)                                                                                  \
+  do {                                                                                          \
+    if (a.Pin == 2) hipLaunchKernelGGL((act_plain_kernel<TY, 2>), grid, block, 0, st, a, arow, dw); \
+    else hipLaunchKernelGGL((act_plain_kernel<TY, 1>), grid, block, 0, st, a, arow, dw);          \
+  } while (0)
+  switch (ty) {
+    case DT_F32: AP(DT_F32); break;
+    case DT_F16: AP(DT_F16); break;
+    default: AP(DT_BF16); break;
+  }
+#undef AP
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ CASES = [
     (1, dict(T=130, top_groups=2, G=4, K=4, resid="int4_g32", r=12)),
     (1, dict(T=1)),
     (4, dict(T=3)),
+    (1, dict(T=100, r=0, resid="none")),
 ]
 
 
@@ -60,8 +61,19 @@ def test_backward_matches_oracle(wi, chg):
         errs = {"dX": _rel(out["dX"].float().cpu().numpy(), ref["dX"]),
                 "dW_grp": _rel(out["dW_grp"].cpu().numpy(), ref["dW_grp"])}
         if w.K > 1:
-            errs["dW_exp"] = _rel(out["dW_exp"].cpu().numpy(), ref["dW_exp"])
-            errs["d_expert_bias"] = _rel(out["d_expert_bias"].cpu().numpy(), ref["d_expert_bias"])
+            # Without residuals the experts of a group are identical, so the
+            # exact expert-logit gradients vanish and only rounding noise is
+            # left: these two are measured against at least 1% of the scale
+            # of the first base gradient (also X^T times a pre-activation
+            # gradient), which leaves the bar unchanged when they do not vanish.
+            floor = 1e-2 * float(np.abs(ref["dbase"][0]).max())
+
+            def _rel_floor(a, b):
+                a = np.asarray(a, dtype=np.float64)
+                den = max(float(np.abs(b).max()), floor)
+                return float(np.abs(a - b).max() / (den if den > 0 else 1.0))
+            errs["dW_exp"] = _rel_floor(out["dW_exp"].cpu().numpy(), ref["dW_exp"])
+            errs["d_expert_bias"] = _rel_floor(out["d_expert_bias"].cpu().numpy(), ref["d_expert_bias"])
         errs["d_group_bias"] = _rel(out["d_group_bias"].cpu().numpy(), ref["d_group_bias"])
         for p in range(w.P):
             errs[f"dbase{p}"] = _rel(out["dbase"][p].cpu().numpy(), ref["dbase"][p])
