@@ -15,9 +15,13 @@
 //   dA1_j = X^T (dz_j B1_j),  dB1_j = dz_j^T (x A1_j),
 //   dA2_j = (w_j h_j)^T e_j,  dB2_j = dY^T (w_j h_j A2_j)
 // and dw_j = <D, h_j> + <e_j, h_j A2_j> feeds the softmax backward of the
-// gate.  Every GEMM here is one MFMA kernel over k-major operands (rows
-// gathered on load, or k ranges that are segments of transposed, gathered
-// rows); the elementwise steps run per row and per token.
+// gate.  The wide GEMMs run the forward pass's tile engine (rows through
+// LDS, fragment-major column operands), over row segments (a group's rows,
+// an expert's positions) or k segments (a group's rows, transposed); the
+// thin factor gradients are sums over an expert's positions with the rows
+// transposed in LDS; the activation step walks tiles of one expert's
+// positions with that expert's factor rows in LDS; dX and the gate's
+// softmax backward are assembled per token.
 #include "common.h"
 #include "tile.h"
 #include "train.h"
