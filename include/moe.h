@@ -214,7 +214,11 @@ typedef struct {
  * the loss function / training strategy section).  INT4 residuals are
  * differentiated at their dequantised values.  X and dY: device [T][d] in
  * x_dtype.  The first call allocates the backward layouts and workspace for
- * T_max tokens (synchronous); later calls only enqueue on stream. */
+ * T_max tokens (synchronous); later calls only enqueue on stream.  Every sum
+ * runs in a fixed order, so equal inputs give equal bits.  T = 0 writes
+ * zeros to every gradient.  Errors: MOE_ERR_INVALID_ARG (T outside
+ * [0, T_max], a null buffer the layer needs), MOE_ERR_UNSUPPORTED (the
+ * handle's groups are offloaded), MOE_ERR_OOM (first call). */
 int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* dX,
                  const moe_grads* grads, void* stream);
 
