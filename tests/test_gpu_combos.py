@@ -77,6 +77,24 @@ def test_combination_matches_oracle(combo):
                         assert np.array_equal(sc, s_ref.view(np.uint16)), (p, which, e)
                         assert np.array_equal(vals.view(np.uint32),
                                               O.dequantize_int4_g32(q_ref, s_ref).view(np.uint32))
+        # the backward pass of the same combination against the backward
+        # oracle (dX and every weight gradient, bars as in the backward tests)
+        from compressed_expert_ffn_amd import synth
+        from oracle import backward_oracle as BO
+        dYs = synth.to_storage(np.random.default_rng(23).standard_normal((wT.T, w.d)).astype(np.float32),
+                               w.x_dtype)
+        g = lay.backward(X, x_to_device(dYs, w.x_dtype))
+        torch.cuda.synchronize()
+        gref = BO.backward(layer, synth.storage_to_f64(dYs, w.x_dtype))
+        btol = 1e-5 if w.x_dtype == "f32" else 2e-2
+        pairs = [("dX", g["dX"].float(), gref["dX"])]
+        pairs += [(f"dbase{p}", g["dbase"][p], gref["dbase"][p]) for p in range(w.P)]
+        if w.r:
+            pairs += [(f"dA{p}", g["dA"][p], gref["dA"][p]) for p in range(w.P)]
+            pairs += [(f"dB{p}", g["dB"][p], gref["dB"][p]) for p in range(w.P)]
+        for name, got, ref_g in pairs:
+            e = rel_err(got.cpu().numpy(), ref_g)
+            assert e <= btol, (name, e)
     finally:
         lay.close()
 
