@@ -679,6 +679,179 @@ __global__ void __launch_bounds__(256) act_kernel(ActArgs a) {
   }
 }
 
+// Activation backward on MFMAs (16-bit MFMA types, residual layers).  The
+// tile's 64 positions x 64-column chunk is four 32 x 32 blocks, one per
+// wavefront (position block pb = wave & 1, column block cb = wave >> 1),
+// held like the forward pass's accumulators: lane = position, 16 columns
+// per lane.  z_gate = Z + B1_gate u_gate is one 32x32x16 MFMA with Z as the
+// accumulator (z_up and D + A2 e likewise); the column sums dz_gate B1_gate,
+// dz_up B1_up and h A2 are MFMAs over the block's 32 columns with dz and h
+// straight from registers (their k order is the columns a lane holds) and
+// the factor rows read from LDS in that same order.  The two column-block
+// wavefronts of a position block meet in LDS (fixed order) at the end.
+template <int TY, int PIN>
+__global__ void __launch_bounds__(256) act_mfma_kernel(ActArgs a) {
+  using F = FragT<TY>;
+  __shared__ float4 fs[3][64][4];
+  __shared__ float xs[2][32][49];
+  const int tile = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  if (tile * 64 >= a.kpad[a.E]) return;
+  int lo = 0, hi = a.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.kpad[mid] <= tile * 64) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int p0 = a.offsets[e] + (tile * 64 - a.kpad[e]);
+  const int n = min(64, a.offsets[e] + a.counts[e] - p0);
+  const int wave = tid >> 6, lane = tid & 63, pb = wave & 1, cb = wave >> 1, hh = lane >> 5;
+  const int pl = pb * 32 + (lane & 31);
+  const bool valid = pl < n;
+  const int p = valid ? p0 + pl : p0;
+  const int f = a.f, row = a.prow[p];
+  const float wt = valid ? a.pw[p] : 0.f;
+  float tmp[8];
+  // second operands of the expansions (k = rank index 8 hh .. 8 hh + 7)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tmp[i] = a.ua[(long)p * 64 + 8 * hh + i];
+  const F fug = to_frag<TY>(tmp);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tmp[i] = PIN > 1 ? a.ua[(long)p * 64 + 16 + 8 * hh + i] : 0.f;
+  const F fuu = to_frag<TY>(tmp);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tmp[i] = a.ea[(long)p * 16 + 8 * hh + i];
+  const F fe = to_frag<TY>(tmp);
+  f16v qg, qu, u2;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) qg[v] = qu[v] = u2[v] = 0.f;
+  float dd = 0.f;
+  const int nch = f / 64;
+  const int ch0 = (int)((long)split * nch / a.NS), ch1 = (int)((long)(split + 1) * nch / a.NS);
+  const float4* b1g = reinterpret_cast<const float4*>(a.B1p + (long)e * PIN * f * 16);
+  const float4* b1u = reinterpret_cast<const float4*>(a.B1p + ((long)e * PIN + (PIN - 1)) * f * 16);
+  const float4* adp = reinterpret_cast<const float4*>(a.Adp + (long)e * f * 16);
+  TE<TY>* dzo = static_cast<TE<TY>*>(a.dz) + (long)p * PIN * f;
+  TE<TY>* who = static_cast<TE<TY>*>(a.wh) + (long)p * f;
+  const int cc = cb * 32, rho = lane & 31;
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int c0 = ch * 64;
+    __syncthreads();
+    fs[0][tid >> 2][tid & 3] = b1g[(long)c0 * 4 + tid];
+    if (PIN > 1) fs[1][tid >> 2][tid & 3] = b1u[(long)c0 * 4 + tid];
+    fs[2][tid >> 2][tid & 3] = adp[(long)c0 * 4 + tid];
+    __syncthreads();
+    // first operands of the expansions: row = column cc + lane % 32
+    auto rowfrag = [&](int which) {
+      const float4 x0 = fs[which][cc + (lane & 31)][2 * hh], x1 = fs[which][cc + (lane & 31)][2 * hh + 1];
+      const float v8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      return to_frag<TY>(v8);
+    };
+    const F fbg = rowfrag(0);
+    const F fad = rowfrag(2);
+    // accumulators: element v is column cc + 8 (v / 4) + 4 hh + v % 4
+    f16v zg, zu, dh;
+    float dv[16];
+    const float* zr = a.Zb + (long)row * PIN * f + c0 + cc + 4 * hh;
+    const float* dr = a.D + (long)row * f + c0 + cc + 4 * hh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 z4 = *reinterpret_cast<const float4*>(zr + 8 * q);
+      const float4 d4 = *reinterpret_cast<const float4*>(dr + 8 * q);
+      zg[4 * q] = z4.x; zg[4 * q + 1] = z4.y; zg[4 * q + 2] = z4.z; zg[4 * q + 3] = z4.w;
+      dv[4 * q] = d4.x; dv[4 * q + 1] = d4.y; dv[4 * q + 2] = d4.z; dv[4 * q + 3] = d4.w;
+      dh[4 * q] = d4.x; dh[4 * q + 1] = d4.y; dh[4 * q + 2] = d4.z; dh[4 * q + 3] = d4.w;
+      if (PIN > 1) {
+        const float4 u4 = *reinterpret_cast<const float4*>(zr + f + 8 * q);
+        zu[4 * q] = u4.x; zu[4 * q + 1] = u4.y; zu[4 * q + 2] = u4.z; zu[4 * q + 3] = u4.w;
+      } else {
+        zu[4 * q] = zu[4 * q + 1] = zu[4 * q + 2] = zu[4 * q + 3] = 0.f;
+      }
+    }
+    zg = mfma32<TY>(fbg, fug, zg);
+    if (PIN > 1) zu = mfma32<TY>(rowfrag(1), fuu, zu);
+    dh = mfma32<TY>(fad, fe, dh);
+    float og[16], ou[16], oh[16], hv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float dhv = wt * dh[v];
+      float h, dzg, dzu = 0.f;
+      if (a.act == ACT_SWIGLU) {
+        const float sg = sigm(zg[v]), sl = zg[v] * sg;
+        h = sl * zu[v];
+        dzu = dhv * sl;
+        dzg = dhv * zu[v] * sg * (1.0f + zg[v] * (1.0f - sg));
+      } else {
+        float dgl;
+        h = gelu_t(zg[v], dgl);
+        dzg = dhv * dgl;
+      }
+      og[v] = dzg;
+      ou[v] = dzu;
+      oh[v] = wt * h;
+      hv[v] = h;
+      dd += dv[v] * h;
+    }
+    if (valid) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c0 + cc + 8 * q + 4 * hh;
+        const float g4[4] = {og[4 * q], og[4 * q + 1], og[4 * q + 2], og[4 * q + 3]};
+        store4<TY>(dzo + col, g4);
+        if (PIN > 1) {
+          const float u4[4] = {ou[4 * q], ou[4 * q + 1], ou[4 * q + 2], ou[4 * q + 3]};
+          store4<TY>(dzo + f + col, u4);
+        }
+        const float h4[4] = {oh[4 * q], oh[4 * q + 1], oh[4 * q + 2], oh[4 * q + 3]};
+        store4<TY>(who + col, h4);
+      }
+    }
+    // column sums: k-step s takes v = 8 s .. 8 s + 7, i.e. the columns
+    // cc + 16 s + 8 (i / 4) + 4 hh + i % 4; factor rows rho < 16 (zero past)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float tg[8], tu[8], ta[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int col = cc + 16 * s + 8 * (i >> 2) + 4 * hh + (i & 3);
+        tg[i] = rho < 16 ? reinterpret_cast<const float*>(&fs[0][col][0])[rho] : 0.f;
+        tu[i] = (PIN > 1 && rho < 16) ? reinterpret_cast<const float*>(&fs[1][col][0])[rho] : 0.f;
+        ta[i] = rho < 16 ? reinterpret_cast<const float*>(&fs[2][col][0])[rho] : 0.f;
+      }
+      qg = mfma32<TY>(to_frag<TY>(tg), to_frag<TY>(og + 8 * s), qg);
+      if (PIN > 1) qu = mfma32<TY>(to_frag<TY>(tu), to_frag<TY>(ou + 8 * s), qu);
+      u2 = mfma32<TY>(to_frag<TY>(ta), to_frag<TY>(hv + 8 * s), u2);
+    }
+  }
+  // <D, h>: the two lane halves hold the block's two column halves
+  dd += __shfl_xor(dd, 32);
+  // lane (position lane % 32) holds rank index acc32_row(v, lane) for v < 8;
+  // column block 1 hands its sums to column block 0
+  __syncthreads();
+  if (cb == 1) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int r = acc32_row(v, lane);
+      xs[pb][lane & 31][r] = qg[v];
+      xs[pb][lane & 31][16 + r] = qu[v];
+      xs[pb][lane & 31][32 + r] = u2[v];
+    }
+    if (hh == 0) xs[pb][lane & 31][48] = dd;
+  }
+  __syncthreads();
+  if (cb == 0 && valid) {
+    float* po = a.part + ((long)split * a.Na + p) * ACT_PART;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int r = acc32_row(v, lane);
+      po[r] = qg[v] + xs[pb][lane & 31][r];
+      po[16 + r] = qu[v] + xs[pb][lane & 31][16 + r];
+      po[32 + r] = u2[v] + xs[pb][lane & 31][32 + r];
+    }
+    if (hh == 0) po[48] = dd + xs[pb][lane & 31][48];
+  }
+}
+
 // Without residuals: one wavefront per position, lanes along the columns
 // (4 consecutive per lane, 256 per step), so every access is a contiguous
 // run of the row; <D, h> is summed per lane in column order, then over the
@@ -1067,6 +1240,18 @@ hipError_t launch_act(int ty, const ActArgs& a, hipStream_t st) {
       else hipLaunchKernelGGL((act_kernel<TY, 1, false>), grid, block, 0, st, a);     \
     }                                                                              \
   } while (0)
+  // 16-bit residual layers: the expansions and column sums on MFMAs (large
+  // INT4 layer 839 -> 511 us); fp32 layers keep exact fp32 sums
+  if (a.r && ty != DT_F32) {
+    if (ty == DT_F16) {
+      if (a.Pin == 2) hipLaunchKernelGGL((act_mfma_kernel<DT_F16, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((act_mfma_kernel<DT_F16, 1>), grid, block, 0, st, a);
+    } else {
+      if (a.Pin == 2) hipLaunchKernelGGL((act_mfma_kernel<DT_BF16, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((act_mfma_kernel<DT_BF16, 1>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+  }
   switch (ty) {
     case DT_F32: AK(DT_F32); break;
     case DT_F16: AK(DT_F16); break;
