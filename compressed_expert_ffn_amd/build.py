@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcefn.so")
-SOURCES = ["route.hip", "gemm.hip", "train.hip", "api.hip", "pack.cpp", "cluster.cpp"]
+SOURCES = ["route.hip", "gemm.hip", "train.hip", "api.hip", "backward.hip", "offload.hip", "pack.cpp",
+           "cluster.cpp"]
 ARCH = "gfx950"
 
 

@@ -25,15 +25,12 @@
 #include <string>
 #include <vector>
 
-#include "moe.h"
-#include "common.h"
-#include "kernels.h"
-#include "pack.h"
-#include "train.h"
+#include "api_internal.h"
 
 using namespace cefn;
+using namespace cefn_api;
 
-namespace {
+namespace cefn_api {
 
 thread_local std::string g_err;
 
@@ -50,9 +47,8 @@ int fail(int code, const char* fmt, ...) {
 long roundup(long x, long m) { return (x + m - 1) / m * m; }
 
 const char* kStageNames[] = {"router", "scatter", "ugemm", "gemm1", "vreduce", "gemm2", "combine"};
-constexpr int kStages = 7;
 
-}  // namespace
+}  // namespace cefn_api
 
 namespace cefn {
 int report_error(int code, const char* fmt, ...) {
@@ -73,7 +69,7 @@ int report_error(int code, const char* fmt, ...) {
 constexpr size_t kScratchBytes = (size_t)96 << 20;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
-namespace {
+namespace cefn_api {
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -97,65 +93,9 @@ int scratch_for_device(int dev, char** out) {
   return MOE_OK;
 }
 
-}  // namespace
+}  // namespace cefn_api
 
-// Workspace of one forward pass, carved out of one device buffer for a
-// capacity of T_cap tokens: the handle's own buffer (carved once for T_max)
-// or the static scratch array of the no-allocation entry point (carved per
-// call for that call's T).  Only the per-chunk counters cc must be zero when
-// a pass starts; every other piece is written before it is read.
-struct Workspace {
-  long T_cap = 0;
-  int *idx = nullptr, *gidx = nullptr, *counts = nullptr, *offsets = nullptr;
-  int *gcounts = nullptr, *goffsets = nullptr, *garow = nullptr, *garow_sorted = nullptr;
-  int* cc = nullptr;  // per-chunk counters: [nch_e_max][E] then [nch_g_max][G]
-  int nch_e_max = 0, nch_g_max = 0, cc_n = 0;
-  uint16_t* X16 = nullptr;  // fp16 copy of bf16 activations (fp16 MFMAs)
-  float* w = nullptr;
-  float* L = nullptr;   // router scores (k-split partials)
-  void* U = nullptr;    // [T*kg][NU]
-  float* V = nullptr;   // [T*kg][NV]
-  float* Vp = nullptr;  // [G1 column tiles][T_cap*kg][ke][16]
-  int nt1k = 0;         // column tiles of the k-split G1 (0: its partials do not fit)
-  void* H = nullptr;    // [T*kg][f]
-  float* ypart = nullptr;
-};
-
-struct moe_handle {
-  moe_config cfg{};
-  int E = 0, k = 0, P = 0, P_in = 0, mma = 0, NU = 0, NV = 0;
-  int device = 0;
-  bool dirty = false;
-  // weights
-  float *Wr = nullptr, *gbias = nullptr, *ebias = nullptr;
-  uint16_t* Wb = nullptr;  // bf16 parts of Wr (16-bit activations)
-  int NCp = 0;         // router score columns, padded to 32
-  float* L = nullptr;  // router scores (k-split partials)
-  void *W1 = nullptr, *W2 = nullptr, *At = nullptr, *B1 = nullptr, *Ad = nullptr, *Bd = nullptr;
-  uint16_t *At_s = nullptr, *B1_s = nullptr, *Ad_s = nullptr, *Bd_s = nullptr;
-  long w1_gs = 0, w2_gs = 0, at_gs = 0, at_sgs = 0, bd_gs = 0;
-  Workspace ws;         // the handle's own workspace, carved for T_max
-  int nt1 = 0;          // column tiles of gemm1 (partials of V per row)
-  std::vector<void*> allocs;
-  int64_t weight_bytes = 0;
-  // tile rows and stage depth per GEMM (0 = chosen per call); set from the
-  // tile overrides read from CEFN_BM_{U,G1,G2} (token rows per tile) and
-  // CEFN_KS_G2 (k splits of the down projection) at create, for tuning
-  int bm_env[3] = {0, 0, 0}, ks_env = 0;
-  int g2k_env = -1;  // CEFN_G2K: 1 / 0 forces the in-workgroup k split of G2 on / off
-  int g1k_env = -1;  // CEFN_G1K: 1 / 0 forces the k-split tiles of G1 on / off
-  int ut_env = -1;   // CEFN_UT: 1 / 0 forces the tile-engine U GEMM on / off
-  int gsort_env = -1;  // CEFN_GSORT: 1 / 0 forces the per-group row sort on / off
-  // profiling
-  bool prof = false;
-  int prof_max = 0, prof_calls = 0, prof_mask = -1;
-  std::vector<hipEvent_t> ev;          // [prof_max][kStages][2]
-  std::vector<unsigned char> ev_used;  // [prof_max][kStages]
-  struct BwdState* bwd = nullptr;      // backward-pass layouts and workspace (built on first use)
-  struct OffloadState* off = nullptr;  // idle-group offload (moe_offload_enable)
-};
-
-namespace {
+namespace cefn_api {
 
 int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
@@ -224,7 +164,6 @@ void compute_stats(const moe_config& c, moe_stats_t* s) {
   s->stored_bytes = bytes;
 }
 
-constexpr int kMaxSplits = 4;  // k splits of the down projection (ypart holds this many)
 
 // Lay the workspace for T tokens out from `base` (256-byte aligned pieces);
 // returns the bytes it spans.  base == nullptr only measures.
@@ -279,20 +218,6 @@ size_t carve_workspace(const moe_handle* h, long T, char* base, Workspace* ws) {
 }
 
 template <class T>
-int dalloc(moe_handle* h, T** p, size_t n) {
-  *p = nullptr;
-  if (n == 0) return MOE_OK;
-  void* q = nullptr;
-  if (hipMalloc(&q, n * sizeof(T)) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(MOE_ERR_OOM, "hipMalloc of %zu bytes failed", n * sizeof(T));
-  }
-  h->allocs.push_back(q);
-  *p = static_cast<T*>(q);
-  return MOE_OK;
-}
-
-template <class T>
 int upload(moe_handle* h, T** dst, const std::vector<T>& src) {
   int rc = dalloc(h, dst, src.size());
   if (rc) return rc;
@@ -310,12 +235,6 @@ int upload_raw(moe_handle* h, void** dst, const std::vector<T>& src) {
   *dst = p;
   return rc;
 }
-
-#define TRY(x)            \
-  do {                    \
-    int rc_ = (x);        \
-    if (rc_) return rc_;  \
-  } while (0)
 
 // Build every device weight array.  TS is the storage type of the MFMA
 // dtype: float (F32) or uint16_t bits (F16/BF16), which is also the storage
@@ -611,22 +530,6 @@ int max_mtiles(int T, int kg, int G, int bm) {
   return (int)((rows + bm - 1) / bm + std::min<long>(G, rows));
 }
 
-struct Prof {
-  moe_handle* h;
-  hipStream_t st;
-  int call;
-  bool on(int s) const { return call >= 0 && ((h->prof_mask >> s) & 1); }
-  void begin(int s) {
-    if (on(s)) (void)hipEventRecord(h->ev[((size_t)call * kStages + s) * 2], st);
-  }
-  void end(int s) {
-    if (on(s)) {
-      (void)hipEventRecord(h->ev[((size_t)call * kStages + s) * 2 + 1], st);
-      h->ev_used[(size_t)call * kStages + s] = 1;
-    }
-  }
-};
-
 int hip_fail(moe_handle* h, hipError_t e, const char* what) {
   h->dirty = true;
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -678,86 +581,11 @@ int weights_to_host(const moe_config& c, const moe_weights* w, moe_weights* hw,
   return MOE_OK;
 }
 
-}  // namespace
+}  // namespace cefn_api
 
-// ---------------------------------------------------------- backward ----
-// Plain k-major weight copies and the workspace of moe_backward, built on
-// its first call from the device layouts (no host copy of the weights is
-// kept).  U, E and the residual factors are kept as float32 for the
-// elementwise steps; GEMM operands are in the MFMA type.
-struct BwdState {
-  // fragment-major (tile engine layout) B operands: W1^T [d][Pin f], W2^T
-  // [f][d], stacked A1 [NUp][d] and B2 [NEp][d] per group, A1 [d][64] per expert
-  void *W1F = nullptr, *W2F = nullptr, *AtF = nullptr, *BdF = nullptr, *A1F = nullptr;
-  float *Atp = nullptr, *B1p = nullptr, *Adp = nullptr;
-  int NUb = 0, NEb = 0, NUp = 0, NEp = 0;  // stacked factor rows, and rounded up to 64
-  long Kg = 0, KgF = 0, part_cap = 0;
-  int *counts = nullptr, *offsets = nullptr, *perm = nullptr, *arow = nullptr, *apos = nullptr, *prow = nullptr;
-  int *grow = nullptr, *kpad_g = nullptr, *kpad_e = nullptr, *toff_g = nullptr, *toff_e = nullptr;
-  float *Zb = nullptr, *U = nullptr, *D = nullptr, *Eb = nullptr, *pw = nullptr, *part = nullptr;
-  float *q = nullptr, *wu2 = nullptr, *dw = nullptr, *ua = nullptr, *ea = nullptr, *dXb = nullptr, *dXr = nullptr;
-  float *ds = nullptr;
-  void *dz = nullptr, *wh = nullptr, *dZbar = nullptr, *hbar = nullptr;
-  void *XTg = nullptr, *dZT = nullptr, *hbT = nullptr, *dYTg = nullptr, *dsdeT = nullptr;
-};
-
-// ------------------------------------------------------ group offload ----
-// Whole groups' weights live in pinned host memory; `slots` device slots
-// hold the groups in use.  One entry per weight array: the handle's pointer
-// field is repointed at the slot cache, so the GEMMs address group g's
-// weights at slot gslot[g] with the array's usual per-group stride.
-struct OffloadArray {
-  void** field;     // handle member that the kernels read
-  char* host;       // pinned: every group, group-major
-  char* cache;      // device: slots x group_bytes
-  size_t group_bytes;
-};
-
-struct OffloadState {
-  int slots = 0;
-  std::vector<OffloadArray> arrays;
-  std::vector<int> slot_of;        // [G] slot holding the group, or -1
-  std::vector<int> group_in;       // [slots] group in the slot, or -1
-  std::vector<long> last_use;      // [slots] use stamp (least recently used is evicted)
-  std::vector<double> heat;        // [G] moving average of the group's share of rows
-  long stamp = 0;
-  hipStream_t copy = nullptr;      // host-to-device copies (default priority)
-  std::vector<hipEvent_t> slot_free;   // compute stream: last pass that read the slot is done
-  std::vector<hipEvent_t> slot_ready;  // copy stream: the slot's copies are done
-  int* pass_dev = nullptr;         // device [G][2][G]: per pass gslot then gcounts
-  int* pass_host = nullptr;        // pinned staging of the same
-  int* gcounts_host = nullptr;     // pinned [G]
-  moe_offload_stats_t st{};
-};
-
-namespace {
-
-void delete_offload(moe_handle* h) {
-  OffloadState* o = h->off;
-  if (!o) return;
-  if (o->copy) (void)hipStreamSynchronize(o->copy);
-  for (auto& a : o->arrays) (void)hipHostFree(a.host);
-  if (o->pass_host) (void)hipHostFree(o->pass_host);
-  if (o->gcounts_host) (void)hipHostFree(o->gcounts_host);
-  for (hipEvent_t e : o->slot_free) (void)hipEventDestroy(e);
-  for (hipEvent_t e : o->slot_ready) (void)hipEventDestroy(e);
-  if (o->copy) (void)hipStreamDestroy(o->copy);
-  delete o;
-  h->off = nullptr;
-}
-
-void delete_bwd(moe_handle* h) {
-  delete h->bwd;
-  h->bwd = nullptr;
-}
+namespace cefn_api {
 
 // router + scatter into the workspace (and the caller's buffers where given)
-// Where the routing pass left the lists the GEMMs read.
-struct RouteLive {
-  int *gcounts, *goffsets, *idx, *gidx;
-  float* w;
-};
-
 int run_route(moe_handle* h, Workspace& ws, const void* X, int T, const moe_route_out* ro, bool need_experts,
               hipStream_t st, Prof& pf, RouteLive& live) {
   const moe_config& c = h->cfg;
@@ -832,7 +660,7 @@ int run_route(moe_handle* h, Workspace& ws, const void* X, int T, const moe_rout
   return MOE_OK;
 }
 
-}  // namespace
+}  // namespace cefn_api
 
 extern "C" {
 
@@ -993,17 +821,7 @@ int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out,
 
 }  // extern "C"
 
-namespace {
-
-// Where one residual factor (projection p, A or B, expert i) lives in the
-// device layouts, in the terms of the decode kernel (kinds: 0 At, 1 B1,
-// 2 Ad, 3 Bd).
-struct FactorLoc {
-  int kind, n, aux0, aux1;
-  const void* src;
-  const uint16_t* sc;
-  long base, sbase;
-};
+namespace cefn_api {
 
 FactorLoc locate_factor(const moe_handle* h, int proj, int which, int expert) {
   const moe_config& c = h->cfg;
@@ -1047,17 +865,6 @@ FactorLoc locate_factor(const moe_handle* h, int proj, int which, int expert) {
   }
   return L;
 }
-
-// State a forward pass carries from its routing to its GEMMs and combine.
-struct FwdState {
-  Prof pf;
-  RouteLive live;
-  const int* garow;
-  bool gsorted;
-  const void* xg;  // activations the row GEMMs read (X, or its fp16 copy)
-  int xt;
-  int splits;
-};
 
 // Routing, the optional per-group row sort and the activation conversion.
 int fwd_prelude(moe_handle* h, Workspace& ws, const void* X, int T, const moe_route_out* routing, hipStream_t st,
@@ -1274,7 +1081,7 @@ int forward_impl(moe_handle* h, Workspace& ws, const void* X, int T, void* Y, co
   return fwd_combine(h, ws, T, Y, st, fs);
 }
 
-}  // namespace
+}  // namespace cefn_api
 
 extern "C" {
 
@@ -1435,685 +1242,3 @@ int moe_profile_end(moe_handle* h, float* stage_ms, int32_t n_stages_cap, int32_
 
 }  // extern "C"
 
-// ---- backward pass -------------------------------------------------------
-namespace {
-
-// Build the backward layouts and workspace (first moe_backward call).
-int prepare_backward(moe_handle* h) {
-  if (h->bwd) return MOE_OK;
-  const moe_config& c = h->cfg;
-  std::unique_ptr<BwdState> B(new BwdState());
-  const int G = c.G, K = c.K, E = h->E, Pin = h->P_in, d = c.d, f = c.f, r = c.r, ty = h->mma;
-  const size_t es = elem_bytes(ty);
-  const long T = c.T_max, R = T * c.top_groups, Na = T * h->k;
-  hipStream_t st = nullptr;
-  hipError_t e;
-  char* tmp = nullptr;
-  auto alloc_bytes = [&](void** p, size_t bytes) -> int {
-    char* q = nullptr;
-    TRY(dalloc(h, &q, bytes + 256));
-    *p = q;
-    return MOE_OK;
-  };
-  auto alloc_f = [&](float** p, size_t n) { return dalloc(h, p, n + 64); };
-  auto alloc_i = [&](int** p, size_t n) { return dalloc(h, p, n + 64); };
-  // plain copies go through one scratch buffer into the fragment-major images
-  size_t tmp_bytes = (size_t)G * Pin * f * d * es;
-  if (r > 0) tmp_bytes = std::max({tmp_bytes, (size_t)E * d * 64 * es, (size_t)G * K * Pin * 16 * d * es});
-  struct Tmp {
-    char* p = nullptr;
-    ~Tmp() {
-      if (p) (void)hipFree(p);
-    }
-  } scratch;
-  if (hipMalloc(&scratch.p, tmp_bytes) != hipSuccess) return fail(MOE_ERR_OOM, "backward set-up scratch");
-  tmp = scratch.p;
-  TRY(alloc_bytes(&B->W1F, (size_t)G * Pin * f * d * es));
-  TRY(alloc_bytes(&B->W2F, (size_t)G * f * d * es));
-  const int swf = Pin > 1 ? f : 0;
-  e = launch_frag_to_plain(ty, h->W1, G, h->w1_gs, Pin * f, d, swf, true, tmp, (long)Pin * f * d, (long)Pin * f, st);
-  if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)Pin * f * d, d, Pin * f, B->W1F, (long)Pin * f * d, st);
-  if (e == hipSuccess) e = launch_frag_to_plain(ty, h->W2, G, h->w2_gs, d, f, 0, true, tmp, (long)f * d, d, st);
-  if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)f * d, f, d, B->W2F, (long)f * d, st);
-  if (e != hipSuccess) return hip_fail(h, e, "backward weight repack");
-  if (r > 0) {
-    B->NUb = K * Pin * 16;
-    B->NEb = K * 16;
-    B->NUp = (B->NUb + 63) / 64 * 64;
-    B->NEp = (B->NEb + 63) / 64 * 64;
-    TRY(alloc_f(&B->Atp, (size_t)E * Pin * d * 16));
-    TRY(alloc_f(&B->B1p, (size_t)E * Pin * f * 16));
-    TRY(alloc_f(&B->Adp, (size_t)E * f * 16));
-    float* Bdp = nullptr;
-    TRY(alloc_f(&Bdp, (size_t)E * d * 16));
-    e = launch_zero_f(B->Atp, (long)E * Pin * d * 16, st);
-    if (e == hipSuccess) e = launch_zero_f(B->B1p, (long)E * Pin * f * 16, st);
-    if (e == hipSuccess) e = launch_zero_f(B->Adp, (long)E * f * 16, st);
-    if (e == hipSuccess) e = launch_zero_f(Bdp, (long)E * d * 16, st);
-    for (int i = 0; i < E && e == hipSuccess; ++i)
-      for (int p = 0; p < h->P && e == hipSuccess; ++p)
-        for (int which = 0; which < 2 && e == hipSuccess; ++which) {
-          const FactorLoc L = locate_factor(h, p, which, i);
-          float* out;
-          if (p < Pin) out = which == 0 ? B->Atp + ((size_t)i * Pin + p) * d * 16 : B->B1p + ((size_t)i * Pin + p) * f * 16;
-          else out = which == 0 ? B->Adp + (size_t)i * f * 16 : Bdp + (size_t)i * d * 16;
-          e = launch_debug_decode(ty, c.resid, L.kind, L.src, L.sc, L.base, L.sbase, L.n, r, L.aux0, L.aux1, out, 16, st);
-        }
-    if (e != hipSuccess) return hip_fail(h, e, "backward factor decode");
-    TRY(alloc_bytes(&B->AtF, (size_t)G * B->NUp * d * es));
-    TRY(alloc_bytes(&B->BdF, (size_t)G * B->NEp * d * es));
-    TRY(alloc_bytes(&B->A1F, (size_t)E * d * 64 * es));
-    e = launch_stack_factors(ty, B->Atp, G, K, Pin, d, B->NUb, tmp, st);
-    if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)B->NUb * d, B->NUb, d, B->AtF, (long)B->NUp * d, st);
-    if (e == hipSuccess) e = launch_stack_factors(ty, Bdp, G, K, 1, d, B->NEb, tmp, st);
-    if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, G, (long)B->NEb * d, B->NEb, d, B->BdF, (long)B->NEp * d, st);
-    if (e == hipSuccess) e = launch_a1t(ty, B->Atp, E, Pin, d, tmp, st);
-    if (e == hipSuccess) e = launch_plain_to_frag(ty, tmp, E, (long)d * 64, d, 64, B->A1F, (long)d * 64, st);
-    if (e != hipSuccess) return hip_fail(h, e, "backward factor stacking");
-  }
-  if (hipStreamSynchronize(st) != hipSuccess) return fail(MOE_ERR_HIP, "backward weight repack failed");
-  // workspace for T_max tokens
-  // (multiples of 64, so every transposed row starts 128-byte aligned)
-  B->Kg = (R + 64L * G + 63) / 64 * 64;
-  B->KgF = B->Kg;
-  // act_splits(Na, E, f) * Na <= 1024 * 64 + Na for every Na
-  B->part_cap = 1024L * 64 + Na;
-  TRY(alloc_i(&B->counts, E));
-  TRY(alloc_i(&B->offsets, E + 1));
-  TRY(alloc_i(&B->perm, Na));
-  TRY(alloc_i(&B->arow, Na));
-  TRY(alloc_i(&B->apos, Na));
-  TRY(alloc_i(&B->prow, Na));
-  TRY(alloc_i(&B->grow, R));
-  TRY(alloc_i(&B->kpad_g, G + 1));
-  TRY(alloc_i(&B->kpad_e, E + 1));
-  TRY(alloc_i(&B->toff_g, G + 1));
-  TRY(alloc_i(&B->toff_e, E + 1));
-  TRY(alloc_f(&B->pw, (size_t)Na));
-  TRY(alloc_f(&B->part, (size_t)B->part_cap * ACT_PART));
-  TRY(alloc_f(&B->Zb, (size_t)R * Pin * f));
-  TRY(alloc_f(&B->D, (size_t)R * f));
-  if (K > 1) {  // (one expert per group: dz and w h serve as dZbar and hbar)
-    TRY(alloc_bytes(&B->dZbar, (size_t)R * Pin * f * es));
-    TRY(alloc_bytes(&B->hbar, (size_t)R * f * es));
-  }
-  TRY(alloc_f(&B->dw, (size_t)Na));
-  TRY(alloc_f(&B->dXb, (size_t)R * d));
-  TRY(alloc_f(&B->ds, (size_t)R * (1 + K)));
-  TRY(alloc_bytes(&B->dz, (size_t)Na * Pin * f * es));
-  TRY(alloc_bytes(&B->wh, (size_t)Na * f * es));
-  TRY(alloc_bytes(&B->XTg, (size_t)d * B->Kg * es));
-  TRY(alloc_bytes(&B->dZT, (size_t)Pin * f * B->KgF * es));
-  TRY(alloc_bytes(&B->hbT, (size_t)f * B->Kg * es));
-  TRY(alloc_bytes(&B->dYTg, (size_t)d * B->KgF * es));
-  TRY(alloc_bytes(&B->dsdeT, (size_t)(1 + K) * B->Kg * es));
-  if (r > 0) {
-    TRY(alloc_f(&B->U, (size_t)R * B->NUb));
-    TRY(alloc_f(&B->Eb, (size_t)R * B->NEb));
-    TRY(alloc_f(&B->q, (size_t)Na * 64));
-    TRY(alloc_f(&B->wu2, (size_t)Na * 16));
-    TRY(alloc_f(&B->ua, (size_t)Na * 64));
-    TRY(alloc_f(&B->ea, (size_t)Na * 16));
-    TRY(alloc_f(&B->dXr, (size_t)Na * d));
-  }
-  (void)tmp;
-  if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_ERR_HIP, "backward set-up failed");
-  h->bwd = B.release();
-  return MOE_OK;
-}
-
-// Column splits of the activation backward: enough workgroups for the chip
-// (about 1024) when there are few 64-position tiles.
-int act_splits(long Na, int E, int f) {
-  // tiles: full ones plus about half of the experts' partial ones
-  const long tiles = std::max(1L, (Na + 63) / 64 + std::min<long>(E, Na) / 2);
-  long ns = (1024 + tiles - 1) / tiles;
-  ns = std::min<long>(ns, f / 64);
-  return (int)std::max(1L, ns);
-}
-
-BGemmArgs rgemm(const Workspace& ws, const int* gcounts, const int* goffsets, int G, long R, const void* a, long lda,
-                int a_dtype, const int* a_map, int a_div, const void* b, long b_sstride, int N, int K, float* c,
-                long ldc) {
-  (void)ws;
-  BGemmArgs g{};
-  g.mode = 0;
-  g.S = G;
-  g.seg_start = goffsets;
-  g.seg_count = gcounts;
-  g.a = a;
-  g.lda = lda;
-  g.a_dtype = a_dtype;
-  g.a_map = a_map;
-  g.a_div = a_div;
-  g.b = b;
-  g.ldb = K;
-  g.b_sstride = b_sstride;
-  g.c = c;
-  g.ldc = ldc;
-  g.N = N;
-  g.K = K;
-  g.n_store = N;
-  g.max_rows = (int)R;
-  return g;
-}
-
-// the wide kernel's N (a multiple of 64) over a B padded to that many rows
-BGemmArgs widen(BGemmArgs g, int n_padded) {
-  g.N = n_padded;
-  return g;
-}
-
-BGemmArgs kgemm(int S, const int* kpad, int ty, const void* a, long lda, const void* b, long ldb, int M, int N,
-                float* c, long c_sstride, long ldc, int n_store) {
-  BGemmArgs g{};
-  g.mode = 1;
-  g.S = S;
-  g.kpad_off = kpad;
-  g.a = a;
-  g.lda = lda;
-  g.a_dtype = ty;
-  g.b = b;
-  g.ldb = ldb;
-  g.c = c;
-  g.c_sstride = c_sstride;
-  g.ldc = ldc;
-  g.M = M;
-  g.N = N;
-  g.n_store = n_store;
-  return g;
-}
-
-TransArgs tgather(int S, const int* start, const int* count, const int* kpad, const void* in, int in_dtype, long ld_in,
-                  int c0, int ncols, const int* map, int div, void* out, long ld_out, long max_k, int frag = 0) {
-  TransArgs t{};
-  t.frag = frag;
-  t.S = S;
-  t.start = start;
-  t.count = count;
-  t.kpad_off = kpad;
-  t.in = in;
-  t.in_dtype = in_dtype;
-  t.ld_in = ld_in;
-  t.c0 = c0;
-  t.ncols = ncols;
-  t.in_map = map;
-  t.in_div = div;
-  t.out = out;
-  t.ld_out = ld_out;
-  t.max_cols_k = (int)max_k;
-  return t;
-}
-
-}  // namespace
-
-extern "C" {
-
-int moe_backward(moe_handle* h, const void* X, int32_t T, const void* dY, void* dX, const moe_grads* gr,
-                 void* stream) {
-  if (!h || !gr) return fail(MOE_ERR_INVALID_ARG, "null handle or gradients");
-  const moe_config& c = h->cfg;
-  if (T < 0 || T > c.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, c.T_max);
-  if (T > 0 && (!X || !dY || !dX)) return fail(MOE_ERR_INVALID_ARG, "null X, dY or dX");
-  const int G = c.G, K = c.K, E = h->E, Pin = h->P_in, P = h->P, d = c.d, f = c.f, r = c.r, ty = h->mma;
-  const int kg = c.top_groups, k = h->k;
-  for (int p = 0; p < P; ++p)
-    if (!gr->dbase[p] || (r > 0 && (!gr->dA[p] || !gr->dB[p])))
-      return fail(MOE_ERR_INVALID_ARG, "gradient buffer of projection %d is null", p);
-  if (!gr->dW_grp) return fail(MOE_ERR_INVALID_ARG, "dW_grp is null");
-  if (h->off) return fail(MOE_ERR_UNSUPPORTED, "the handle's groups are offloaded");
-  TRY(prepare_backward(h));
-  BwdState* B = h->bwd;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; };
-  if (T == 0) {
-    for (int p = 0; p < P; ++p) {
-      int di, dn;
-      dims(c, p, di, dn);
-      ok(launch_zero_f(gr->dbase[p], (long)G * di * dn, st));
-      if (r > 0) {
-        ok(launch_zero_f(gr->dA[p], (long)E * di * r, st));
-        ok(launch_zero_f(gr->dB[p], (long)E * dn * r, st));
-      }
-    }
-    ok(launch_zero_f(gr->dW_grp, (long)d * G, st));
-    if (gr->dW_exp) ok(launch_zero_f(gr->dW_exp, (long)G * d * K, st));
-    if (gr->d_group_bias) ok(launch_zero_f(gr->d_group_bias, G, st));
-    if (gr->d_expert_bias) ok(launch_zero_f(gr->d_expert_bias, E, st));
-    return e == hipSuccess ? MOE_OK : hip_fail(h, e, "backward (no tokens)");
-  }
-  // routing again (the forward pass's decisions), with the expert lists
-  Prof pf{h, st, -1};
-  RouteLive live{};
-  moe_route_out ro{};
-  ro.counts = B->counts;
-  ro.offsets = B->offsets;
-  ro.perm = B->perm;
-  TRY(run_route(h, h->ws, X, T, &ro, true, st, pf, live));
-  ok(launch_zero(h->ws.cc, h->ws.cc_n, st));
-  const long R = (long)T * kg, Na = (long)T * k;
-  const int* garow = h->ws.garow;
-  const size_t es = elem_bytes(ty);
-  // forward intermediates: Z = X W1_base per group row, U = X A1 stacked
-  // row tiles of the wide GEMMs per group and per expert
-  const int fm = fgemm_rows(ty);
-  ok(launch_tile_scan(live.gcounts, G, fm, B->toff_g, st));
-  ok(launch_tile_scan(B->counts, E, fm, B->toff_e, st));
-  auto tg = [&](BGemmArgs g) {
-    g.tile_off = g.S == E && g.seg_count == B->counts ? B->toff_e : B->toff_g;
-    return g;
-  };
-  // (the forward pass's own fragment-major W1, SwiGLU-interleaved columns)
-  {
-    BGemmArgs g = rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, h->W1, h->w1_gs,
-                        Pin * f, d, B->Zb, (long)Pin * f);
-    g.swf = Pin > 1 ? f : 0;
-    ok(launch_fgemm(ty, tg(g), st));
-  }
-  if (r > 0)
-    ok(launch_fgemm(ty, tg(widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, X, d, c.x_dtype, garow, kg, B->AtF,
-                                       (long)B->NUp * d, B->NUb, d, B->U, B->NUb), B->NUp)), st));
-  // D = dY W2_base^T, E = dY B2 stacked
-  ok(launch_fgemm(ty, tg(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->W2F,
-                               (long)f * d, f, d, B->D, f)), st));
-  if (r > 0)
-    ok(launch_fgemm(ty, tg(widen(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dY, d, c.x_dtype, garow, kg, B->BdF,
-                                       (long)B->NEp * d, B->NEb, d, B->Eb, B->NEb), B->NEp)), st));
-  // per expert-list position: assignment, row, weight, u and e
-  const int ke = c.top_experts;
-  ok(launch_invert_rows(garow, (int)R, B->grow, st));
-  ok(launch_pad_scan(B->counts, E, B->kpad_e, st));
-  {
-    AssignArgs as{};
-    as.Na = (int)Na;
-    as.E = E;
-    as.K = K;
-    as.k = k;
-    as.ke = ke;
-    as.Pin = Pin;
-    as.r = r;
-    as.perm = B->perm;
-    as.offsets = B->offsets;
-    as.idx = live.idx;
-    as.w = live.w;
-    as.grow = B->grow;
-    as.U = B->U;
-    as.NU = B->NUb;
-    as.Eb = B->Eb;
-    as.NE = B->NEb;
-    as.arow = B->arow;
-    as.apos = B->apos;
-    as.prow = B->prow;
-    as.pw = B->pw;
-    as.ua = B->ua;
-    as.ea = B->ea;
-    ok(launch_gather_assign(as, st));
-  }
-  // activation backward over expert tiles, then the per-position sums
-  const int NS = act_splits(Na, E, f);
-  if ((long)NS * Na > B->part_cap) return fail(MOE_ERR_UNSUPPORTED, "activation partials exceed their buffer");
-  {
-    ActArgs aa{};
-    aa.Na = (int)Na;
-    aa.E = E;
-    aa.f = f;
-    aa.Pin = Pin;
-    aa.act = c.act == MOE_ACT_SWIGLU ? ACT_SWIGLU : ACT_GELU;
-    aa.r = r;
-    aa.NS = NS;
-    aa.offsets = B->offsets;
-    aa.counts = B->counts;
-    aa.kpad = B->kpad_e;
-    aa.prow = B->prow;
-    aa.pw = B->pw;
-    aa.ua = B->ua;
-    aa.ea = B->ea;
-    aa.Zb = B->Zb;
-    aa.D = B->D;
-    aa.B1p = B->B1p;
-    aa.Adp = B->Adp;
-    aa.dz = B->dz;
-    aa.wh = B->wh;
-    aa.part = B->part;
-    if (r > 0) {
-      ok(launch_act(ty, aa, st));
-      ok(launch_act_finish(B->part, NS, (int)Na, Pin, r, B->pw, B->ea, B->arow, B->q, B->wu2, B->dw, st));
-    } else {
-      ok(launch_act_plain(ty, aa, B->arow, B->dw, st));
-    }
-  }
-  // With one expert per group the expert lists are the group lists (the
-  // same stable order), so position p is group row p: dZbar and hbar are dz
-  // and w h themselves.
-  void* dZbar = B->dZbar;
-  void* hbar = B->hbar;
-  if (K == 1) {
-    dZbar = B->dz;
-    hbar = B->wh;
-  } else {
-    ok(launch_row_sums(ty, B->dz, B->wh, garow, B->apos, (int)R, kg, ke, k, f, Pin, dZbar, hbar, st));
-  }
-  // dX: base part per group row, residual part per position, then per token
-  ok(launch_fgemm(ty, tg(rgemm(h->ws, live.gcounts, live.goffsets, G, R, dZbar, (long)Pin * f, ty, nullptr, 1,
-                               B->W1F, (long)Pin * f * d, d, Pin * f, B->dXb, d)), st));
-  if (r > 0)
-    ok(launch_fgemm(ty, tg(rgemm(h->ws, B->counts, B->offsets, E, Na, B->q, 64, MOE_F32, nullptr, 1, B->A1F,
-                                 (long)d * 64, d, 64, B->dXr, d)), st));
-  {
-    TokArgs ta{};
-    ta.T = T;
-    ta.d = d;
-    ta.G = G;
-    ta.K = K;
-    ta.kg = kg;
-    ta.ke = ke;
-    ta.k = k;
-    ta.r = r;
-    // few tokens: several workgroups per token
-    ta.cols = T >= 1024 ? (d + 3) / 4 * 4 : 512;
-    ta.idx = live.idx;
-    ta.gidx = live.gidx;
-    ta.w = live.w;
-    ta.dw = B->dw;
-    ta.grow = B->grow;
-    ta.apos = B->apos;
-    ta.dXb = B->dXb;
-    ta.dXr = B->dXr;
-    ta.Wr = h->Wr;
-    ta.NCp = h->NCp;
-    ta.ds = B->ds;
-    ta.dX = dX;
-    ta.x_dtype = c.x_dtype;
-    ok(launch_tok(ta, st));
-  }
-  // weight gradients over each group's rows
-  ok(launch_pad_scan(live.gcounts, G, B->kpad_g, st));
-  const long Kg = B->Kg, KgF = B->KgF;
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, X, c.x_dtype, d, 0, d, garow, kg, B->XTg,
-                                 Kg, Kg), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, dZbar, ty, (long)Pin * f, 0,
-                                 Pin * f, nullptr, 1, B->dZT, KgF, Kg, 1), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, hbar, ty, f, 0, f, nullptr, 1,
-                                 B->hbT, Kg, Kg), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, dY, c.x_dtype, d, 0, d, garow, kg,
-                                 B->dYTg, KgF, Kg, 1), st));
-  ok(launch_gather_t(ty, tgather(G, live.goffsets, live.gcounts, B->kpad_g, B->ds, MOE_F32, 1 + K, 0, 1 + K, garow, 1,
-                                 B->dsdeT, Kg, Kg), st));
-  for (int p = 0; p < Pin; ++p)
-    ok(launch_fgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, static_cast<char*>(B->dZT) + (size_t)p * f * KgF * es,
-                              KgF, d, f, gr->dbase[p], (long)d * f, f, f), st));
-  ok(launch_fgemm(ty, kgemm(G, B->kpad_g, ty, B->hbT, Kg, B->dYTg, KgF, f, d, gr->dbase[P - 1], (long)f * d, d, d),
-                  st));
-  // router weights and biases
-  ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, B->dsdeT, Kg, d, 1, gr->dW_grp, 1, G, 1), st));
-  if (K > 1 && gr->dW_exp)
-    ok(launch_bgemm(ty, kgemm(G, B->kpad_g, ty, B->XTg, Kg, static_cast<char*>(B->dsdeT) + (size_t)Kg * es, Kg, d, K,
-                              gr->dW_exp, (long)d * K, K, K), st));
-  else if (gr->dW_exp)
-    ok(launch_zero_f(gr->dW_exp, (long)G * d * K, st));
-  if (gr->d_group_bias)
-    ok(launch_seg_colsum(B->ds, 1 + K, 1, live.goffsets, live.gcounts, garow, G, gr->d_group_bias, 1, st));
-  if (gr->d_expert_bias) {
-    if (K > 1)
-      ok(launch_seg_colsum(B->ds + 1, 1 + K, K, live.goffsets, live.gcounts, garow, G, gr->d_expert_bias, K, st));
-    else
-      ok(launch_zero_f(gr->d_expert_bias, E, st));
-  }
-  // residual factor gradients over each expert's assignments (position
-  // order), the row operands transposed on the fly
-  if (r > 0) {
-    auto tg = [&](const void* A, int adt, long lda, int ac0, const int* amap, int adiv, const float* Bm, long ldb,
-                  int bc0, int N, int M, float* clo, float* chi) {
-      TGemmArgs t{};
-      t.S = E;
-      t.seg_start = B->offsets;
-      t.seg_count = B->counts;
-      t.a = A;
-      t.a_dtype = adt;
-      t.lda = lda;
-      t.a_c0 = ac0;
-      t.a_map = amap;
-      t.a_div = adiv;
-      t.b = Bm;
-      t.ldb = ldb;
-      t.b_c0 = bc0;
-      t.N = N;
-      t.M = M;
-      t.c_lo = clo;
-      t.c_hi = chi;
-      t.c_sstride = (long)M * r;
-      t.ldc = r;
-      t.n_store = r;
-      ok(launch_tgemm(ty, t, st));
-    };
-    // dA1_p = X^T q_p (both input projections in one pass over X)
-    tg(X, c.x_dtype, d, 0, B->arow, k, B->q, 64, 0, Pin * 16, d, gr->dA[0], Pin > 1 ? gr->dA[1] : nullptr);
-    // dB1_p = dz_p^T u_p
-    for (int p = 0; p < Pin; ++p)
-      tg(B->dz, ty, (long)Pin * f, p * f, nullptr, 1, B->ua, 64, p * 16, 16, f, gr->dB[p], nullptr);
-    // dA2 = (w h)^T e, dB2 = dY^T (w h A2)
-    tg(B->wh, ty, f, 0, nullptr, 1, B->ea, 16, 0, 16, f, gr->dA[P - 1], nullptr);
-    tg(dY, c.x_dtype, d, 0, B->arow, k, B->wu2, 16, 0, 16, d, gr->dB[P - 1], nullptr);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "backward launch");
-  return MOE_OK;
-}
-
-}  // extern "C"
-
-// ---- idle-group offload ----------------------------------------------------
-namespace {
-
-int enqueue_group_copy(moe_handle* h, int g, int slot) {
-  OffloadState* o = h->off;
-  if (hipStreamWaitEvent(o->copy, o->slot_free[slot], 0) != hipSuccess) return fail(MOE_ERR_HIP, "copy wait");
-  for (const auto& a : o->arrays)
-    if (hipMemcpyAsync(a.cache + (size_t)slot * a.group_bytes, a.host + (size_t)g * a.group_bytes, a.group_bytes,
-                       hipMemcpyHostToDevice, o->copy) != hipSuccess)
-      return fail(MOE_ERR_HIP, "group copy");
-  if (hipEventRecord(o->slot_ready[slot], o->copy) != hipSuccess) return fail(MOE_ERR_HIP, "copy event");
-  if (o->group_in[slot] >= 0) o->slot_of[o->group_in[slot]] = -1;
-  o->group_in[slot] = g;
-  o->slot_of[g] = slot;
-  for (const auto& a : o->arrays) o->st.bytes_h2d += (int64_t)a.group_bytes;
-  return MOE_OK;
-}
-
-// Slot to load a group into: an empty one, else the least recently used
-// whose group is not in `keep`.
-int pick_slot(const OffloadState* o, const std::vector<char>& keep) {
-  int best = -1;
-  for (int s = 0; s < o->slots; ++s) {
-    const int g = o->group_in[s];
-    if (g < 0) return s;
-    if (keep[g]) continue;
-    if (best < 0 || o->last_use[s] < o->last_use[best]) best = s;
-  }
-  return best;
-}
-
-}  // namespace
-
-extern "C" {
-
-int moe_offload_enable(moe_handle* h, int32_t slots) {
-  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
-  const moe_config& c = h->cfg;
-  if (h->off) return fail(MOE_ERR_INVALID_ARG, "offload already enabled");
-  if (slots < 1 || slots > c.G) return fail(MOE_ERR_INVALID_ARG, "slots=%d outside [1, G=%d]", slots, c.G);
-  if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_ERR_HIP, "synchronise");
-  delete_bwd(h);  // the backward layouts are not kept for an offloaded handle
-  std::unique_ptr<OffloadState> o(new OffloadState());
-  o->slots = slots;
-  const size_t es = elem_bytes(h->mma);
-  const bool int4 = c.resid == MOE_RESID_INT4_G32;
-  const size_t K = c.K, Pin = h->P_in, f = c.f, d = c.d;
-  auto add = [&](void** field, size_t gb) {
-    if (*field && gb) o->arrays.push_back(OffloadArray{field, nullptr, nullptr, gb});
-  };
-  add(&h->W1, h->w1_gs * es);
-  add(&h->W2, h->w2_gs * es);
-  if (c.r > 0) {
-    add(&h->At, int4 ? h->at_gs * 4 : h->at_gs * es);
-    if (int4) add(reinterpret_cast<void**>(&h->At_s), h->at_sgs * 2);
-    add(&h->B1, K * (int4 ? Pin * f * 8 : Pin * f * 16 * es));
-    if (int4) add(reinterpret_cast<void**>(&h->B1_s), K * Pin * (f / 32) * RPAD * 2);
-    add(&h->Ad, K * (f / 32) * 2 * 64 * (int4 ? 4 : 8 * es));
-    if (int4) add(reinterpret_cast<void**>(&h->Ad_s), K * (f / 32) * RPAD * 2);
-    add(&h->Bd, int4 ? h->bd_gs * 4 : h->bd_gs * es);
-    if (int4) add(reinterpret_cast<void**>(&h->Bd_s), K * (d / 32) * RPAD * 2);
-  }
-  h->off = o.get();  // so delete_offload can clean up a partial set-up
-  o.release();
-  OffloadState* off = h->off;
-  auto undo = [&](int code, const char* what) {
-    delete_offload(h);
-    return fail(code, "%s", what);
-  };
-  for (auto& a : off->arrays) {
-    const size_t total = a.group_bytes * c.G;
-    void* host = nullptr;
-    if (hipHostMalloc(&host, total, hipHostMallocDefault) != hipSuccess) return undo(MOE_ERR_OOM, "pinned host memory");
-    a.host = static_cast<char*>(host);
-    if (hipMemcpy(a.host, *a.field, total, hipMemcpyDeviceToHost) != hipSuccess) return undo(MOE_ERR_HIP, "copy out");
-  }
-  // device slot caches replace the full arrays
-  for (auto& a : off->arrays) {
-    char* cache = nullptr;
-    if (dalloc(h, &cache, a.group_bytes * slots)) return undo(MOE_ERR_OOM, "slot cache");
-    void* old = *a.field;
-    auto it = std::find(h->allocs.begin(), h->allocs.end(), old);
-    if (it != h->allocs.end()) {
-      h->allocs.erase(it);
-      (void)hipFree(old);
-    }
-    a.cache = cache;
-    *a.field = cache;
-  }
-  const int G = c.G;
-  off->slot_of.assign(G, -1);
-  off->group_in.assign(slots, -1);
-  off->last_use.assign(slots, 0);
-  off->heat.assign(G, 0.0);
-  if (dalloc(h, &off->pass_dev, (size_t)G * 2 * G)) return undo(MOE_ERR_OOM, "pass tables");
-  void* ph = nullptr;
-  if (hipHostMalloc(&ph, sizeof(int) * (size_t)G * 2 * G, hipHostMallocDefault) != hipSuccess)
-    return undo(MOE_ERR_OOM, "pinned staging");
-  off->pass_host = static_cast<int*>(ph);
-  if (hipHostMalloc(&ph, sizeof(int) * (size_t)G, hipHostMallocDefault) != hipSuccess)
-    return undo(MOE_ERR_OOM, "pinned counts");
-  off->gcounts_host = static_cast<int*>(ph);
-  if (hipStreamCreateWithFlags(&off->copy, hipStreamNonBlocking) != hipSuccess) return undo(MOE_ERR_HIP, "copy stream");
-  off->slot_free.assign(slots, nullptr);
-  off->slot_ready.assign(slots, nullptr);
-  for (int s2 = 0; s2 < slots; ++s2)
-    if (hipEventCreateWithFlags(&off->slot_free[s2], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&off->slot_ready[s2], hipEventDisableTiming) != hipSuccess)
-      return undo(MOE_ERR_HIP, "events");
-  // warm start: the first groups, in order
-  for (int g = 0; g < slots; ++g)
-    if (enqueue_group_copy(h, g, g)) return undo(MOE_ERR_HIP, "initial copies");
-  off->st.bytes_h2d = 0;
-  if (hipStreamSynchronize(off->copy) != hipSuccess) return undo(MOE_ERR_HIP, "initial copies");
-  return MOE_OK;
-}
-
-int moe_offload_stats(const moe_handle* h, moe_offload_stats_t* out) {
-  if (!h || !out) return fail(MOE_ERR_INVALID_ARG, "null handle or stats");
-  if (!h->off) return fail(MOE_ERR_INVALID_ARG, "offload not enabled");
-  *out = h->off->st;
-  return MOE_OK;
-}
-
-int moe_forward_offload(moe_handle* h, const void* X, int32_t T, void* Y, const moe_route_out* routing,
-                        void* stream) {
-  if (!h) return fail(MOE_ERR_INVALID_ARG, "null handle");
-  OffloadState* o = h->off;
-  if (!o) return fail(MOE_ERR_INVALID_ARG, "offload not enabled (moe_offload_enable)");
-  const moe_config& c = h->cfg;
-  if (T < 0 || T > c.T_max) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, T_max=%d]", T, c.T_max);
-  if (T == 0) return routing ? moe_route(h, X, 0, routing, stream) : MOE_OK;
-  if (!X || !Y) return fail(MOE_ERR_INVALID_ARG, "null X or Y");
-  if (X == Y) return fail(MOE_ERR_INVALID_ARG, "X and Y may not alias");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int G = c.G;
-  ++o->st.calls;
-  FwdState fs{};
-  TRY(fwd_prelude(h, h->ws, X, T, routing, st, fs));
-  // which groups this batch touches
-  if (hipMemcpyAsync(o->gcounts_host, fs.live.gcounts, sizeof(int) * G, hipMemcpyDeviceToHost, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    return fail(MOE_ERR_HIP, "group counts to host");
-  const int* gc = o->gcounts_host;
-  std::vector<int> need;
-  for (int g = 0; g < G; ++g)
-    if (gc[g] > 0 && o->slot_of[g] >= 0) need.push_back(g);  // resident first
-  for (int g = 0; g < G; ++g)
-    if (gc[g] > 0 && o->slot_of[g] < 0) need.push_back(g);
-  const int n = (int)need.size();
-  const int per = n <= o->slots ? n : std::max(1, o->slots / 2);
-  int pass = 0;
-  for (int b = 0; b < n; b += per, ++pass) {
-    const int e = std::min(n, b + per);
-    std::vector<char> keep(G, 0);
-    for (int q = b; q < e; ++q) keep[need[q]] = 1;
-    for (int q = b; q < e; ++q) {
-      const int g = need[q];
-      if (o->slot_of[g] >= 0) {
-        ++o->st.group_hits;
-        continue;
-      }
-      const int slot = pick_slot(o, keep);
-      if (slot < 0) return fail(MOE_ERR_HIP, "no free slot");
-      TRY(enqueue_group_copy(h, g, slot));
-      ++o->st.group_loads;
-    }
-    int* tab = o->pass_host + (size_t)pass * 2 * G;
-    for (int g = 0; g < G; ++g) {
-      tab[g] = keep[g] ? o->slot_of[g] : 0;
-      tab[G + g] = keep[g] ? gc[g] : 0;
-    }
-    int* dtab = o->pass_dev + (size_t)pass * 2 * G;
-    if (hipMemcpyAsync(dtab, tab, sizeof(int) * 2 * G, hipMemcpyHostToDevice, st) != hipSuccess)
-      return fail(MOE_ERR_HIP, "pass table copy");
-    for (int q = b; q < e; ++q)
-      if (hipStreamWaitEvent(st, o->slot_ready[o->slot_of[need[q]]], 0) != hipSuccess)
-        return fail(MOE_ERR_HIP, "wait for group copy");
-    TRY(fwd_gemms(h, h->ws, X, T, Y, st, fs, dtab + G, dtab));
-    for (int q = b; q < e; ++q) {
-      const int slot = o->slot_of[need[q]];
-      o->last_use[slot] = ++o->stamp;
-      if (hipEventRecord(o->slot_free[slot], st) != hipSuccess) return fail(MOE_ERR_HIP, "slot event");
-    }
-  }
-  o->st.passes += pass;
-  TRY(fwd_combine(h, h->ws, T, Y, st, fs));
-  // prefetch: groups used most in recent batches, into slots of groups used less
-  double rows = 0;
-  for (int g = 0; g < G; ++g) rows += gc[g];
-  for (int g = 0; g < G; ++g) o->heat[g] = 0.5 * o->heat[g] + 0.5 * (rows > 0 ? gc[g] / rows : 0.0);
-  std::vector<int> cand;
-  for (int g = 0; g < G; ++g)
-    if (o->slot_of[g] < 0 && o->heat[g] > 0) cand.push_back(g);
-  std::stable_sort(cand.begin(), cand.end(), [&](int a, int b2) { return o->heat[a] > o->heat[b2]; });
-  int budget = std::max(1, o->slots / 2);
-  for (int g : cand) {
-    if (budget-- <= 0) break;
-    int victim = -1;
-    for (int s2 = 0; s2 < o->slots; ++s2) {
-      const int r = o->group_in[s2];
-      if (r < 0) {
-        victim = s2;
-        break;
-      }
-      if (o->heat[r] < o->heat[g] && (victim < 0 || o->heat[r] < o->heat[o->group_in[victim]])) victim = s2;
-    }
-    if (victim < 0) break;
-    TRY(enqueue_group_copy(h, g, victim));
-    ++o->st.prefetched;
-  }
-  return MOE_OK;
-}
-
-}  // extern "C"

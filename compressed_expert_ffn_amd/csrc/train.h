@@ -1,5 +1,5 @@
 // Internal interface of the backward-pass kernels (train.hip) used by
-// api.hip.  All matrices the backward GEMMs read are row-major with the
+// backward.hip.  All matrices the backward GEMMs read are row-major with the
 // contraction index k contiguous ("k-major"), in the MFMA type TY unless
 // noted; k ranges are padded to multiples of 64 with zeros.
 #pragma once
