@@ -85,7 +85,8 @@ def traffic_for(workload_name: str, kernel: str):
 
 KERNEL_STAGE = (("route_fused", "router"), ("logits_kernel", "router"), ("select_kernel", "router"),
                 ("scatter", "scatter"), ("group_sort", "scatter"), ("cvt_bf16", "ugemm"), ("ugemm", "ugemm"), ("gemm1", "gemm1"),
-                ("vreduce", "vreduce"), ("gemm2", "gemm2"), ("combine", "combine"), ("zero_kernel", "zero"))
+                ("vreduce", "vreduce"), ("gemm2", "gemm2"), ("tailfix", "tailfix"), ("combine", "combine"),
+                ("zero_kernel", "zero"))
 
 
 def stage_of(kernel_name: str):

@@ -66,6 +66,7 @@ struct moe_handle {
   int g1k_env = -1;  // CEFN_G1K: 1 / 0 forces the k-split tiles of G1 on / off
   int ut_env = -1;   // CEFN_UT: 1 / 0 forces the tile-engine U GEMM on / off
   int gsort_env = -1;  // CEFN_GSORT: 1 / 0 forces the per-group row sort on / off
+  int tail_env = -1;   // CEFN_TAIL_SLOTS: 0 turns G2's last-round split off, N > 0 sets its round size
   // profiling
   bool prof = false;
   int prof_max = 0, prof_calls = 0, prof_mask = -1;

@@ -49,17 +49,15 @@ struct TileCoord {
 
 // The group counts (G <= 256) are loaded by all lanes at once and walked
 // with lane reads, so a workgroup pays one load latency here, not G.
-// S > 1 (a k split of the down projection): the logical tiles are the S
-// splits of every tile with the split outermost, so an XCD's contiguous run
-// stays inside one split, where neighbouring tiles share rows or weight
-// columns (the splits of one tile share nothing); *split receives it.
-__device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileCoord& tc, int S = 1,
-                         int* split = nullptr) {
-  const int lane = threadIdx.x & 63;
+struct GroupCounts {
   int cnt[4];
+  __device__ GroupCounts(const int* gcounts, int G) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) cnt[q] = (64 * q + lane < G) ? gcounts[64 * q + lane] : 0;
-  auto count_of = [&](int gg) {
+    for (int q = 0; q < 4; ++q) cnt[q] = (64 * q + lane < G) ? gcounts[64 * q + lane] : 0;
+  }
+  // rows of group gg (gg wave-uniform)
+  __device__ int of(int gg) const {
     const int l = gg & 63;
     switch (gg >> 6) {
       case 0: return __builtin_amdgcn_readlane(cnt[0], l);
@@ -67,32 +65,101 @@ __device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileC
       case 2: return __builtin_amdgcn_readlane(cnt[2], l);
       default: return __builtin_amdgcn_readlane(cnt[3], l);
     }
-  };
-  int total = 0;
-  for (int gg = 0; gg < G; ++gg) total += (count_of(gg) + BM - 1) / BM * NT;
-  const int all = total * S;
-  if (i >= all) return false;
+  }
+  __device__ int tiles(int G, int BM, int NT) const {
+    int total = 0;
+    for (int gg = 0; gg < G; ++gg) total += (of(gg) + BM - 1) / BM * NT;
+    return total;
+  }
+  // logical tile L (0 <= L < tiles) -> group, first row, column tile
+  __device__ bool locate(int L, int G, int BM, int NT, TileCoord& tc) const {
+    for (int gg = 0; gg < G; ++gg) {
+      const int Mg = of(gg);
+      const int mt = (Mg + BM - 1) / BM;
+      if (L < mt * NT) {
+        const int nb = max(1, 32 / mt);
+        const int blk = L / (mt * nb);
+        const int within = L - blk * mt * nb;
+        tc.g = gg;
+        tc.M = Mg;
+        tc.m0 = (within % mt) * BM;
+        tc.nt = blk * nb + within / mt;
+        return true;
+      }
+      L -= mt * NT;
+    }
+    return false;
+  }
+};
+
+// workgroup i of `all` -> logical tile: XCD i % 8 walks one contiguous run
+__device__ __forceinline__ int xcd_order(int i, int all) {
   const int x = i & 7, j = i >> 3;
   const int q = all >> 3, rem = all & 7;
-  int L = x * q + min(x, rem) + j;
+  return x * q + min(x, rem) + j;
+}
+
+// S > 1 (a k split of the down projection): the logical tiles are the S
+// splits of every tile with the split outermost, so an XCD's contiguous run
+// stays inside one split, where neighbouring tiles share rows or weight
+// columns (the splits of one tile share nothing); *split receives it.
+__device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileCoord& tc, int S = 1,
+                         int* split = nullptr) {
+  const GroupCounts gc(gcounts, G);
+  const int total = gc.tiles(G, BM, NT);
+  const int all = total * S;
+  if (i >= all) return false;
+  int L = xcd_order(i, all);
   if (split) *split = L / total;
-  L %= total;
-  for (int gg = 0; gg < G; ++gg) {
-    const int Mg = count_of(gg);
-    const int mt = (Mg + BM - 1) / BM;
-    if (L < mt * NT) {
-      const int nb = max(1, 32 / mt);
-      const int blk = L / (mt * nb);
-      const int within = L - blk * mt * nb;
-      tc.g = gg;
-      tc.M = Mg;
-      tc.m0 = (within % mt) * BM;
-      tc.nt = blk * nb + within / mt;
-      return true;
-    }
-    L -= mt * NT;
-  }
-  return false;
+  return gc.locate(L % total, G, BM, NT, tc);
+}
+
+// Last-round split of the down projection.  With equal tiles, `total` tiles
+// over `slots` resident workgroups leave a last round of total % slots
+// tiles that keeps most compute units idle.  When at least one round is
+// full and the last one is at most half full, the tiles of that last round
+// (the final ones in logical order) are cut along k into S pieces each, so
+// that their pieces fill the round; every piece keeps at least 8 stages and
+// the pieces past the first fit in max_pieces partial tiles.
+struct TailPlan {
+  int F;     // tiles run whole (logical tiles 0 .. F-1)
+  int tail;  // tiles F .. F+tail-1, each in S pieces
+  int S;
+};
+
+__device__ __forceinline__ TailPlan tail_plan(int total, int slots, int smax, int KT, int max_pieces) {
+  TailPlan p{total, 0, 1};
+  if (slots <= 0 || total <= slots) return p;
+  const int tail = total % slots;
+  if (tail == 0 || 2 * tail > slots) return p;
+  int S = min(min(smax, slots / tail), KT / 8);
+  while (S > 1 && tail * (S - 1) > max_pieces) --S;
+  if (S < 2) return p;
+  p.F = total - tail;
+  p.tail = tail;
+  p.S = S;
+  return p;
+}
+
+// Workgroup i under the last-round split: the first F workgroups take the
+// whole tiles (XCD-aware order), the next tail * S the pieces, the pieces of
+// one tile side by side.  piece: 0 .. S-1; tidx: the tile's index among the
+// tail tiles (-1 for a whole tile).
+__device__ bool map_tile_tail(int i, const int* gcounts, int G, int BM, int NT, int slots, int smax, int KT,
+                              int max_pieces, TileCoord& tc, int& piece, int& npieces, int& tidx) {
+  const GroupCounts gc(gcounts, G);
+  const int total = gc.tiles(G, BM, NT);
+  const TailPlan tp = tail_plan(total, slots, smax, KT, max_pieces);
+  piece = 0;
+  npieces = 1;
+  tidx = -1;
+  if (i < tp.F) return gc.locate(xcd_order(i, tp.F), G, BM, NT, tc);
+  const int j = i - tp.F;
+  if (j >= tp.tail * tp.S) return false;
+  tidx = j / tp.S;
+  piece = j - tidx * tp.S;
+  npieces = tp.S;
+  return gc.locate(tp.F + tidx, G, BM, NT, tc);
 }
 
 // Element v of a transposed 32x32 accumulator held by lane l: feature row
@@ -721,10 +788,18 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
   if (blockIdx.x == 0 && a.zero_ptr) {
     for (int i = threadIdx.x; i < a.zero_n; i += 256) a.zero_ptr[i] = 0;
   }
-  const int S = a.ksplit;
-  int split = 0;
+  const int NT = (a.d + BNF - 1) / BNF;
+  int S = a.ksplit;
+  int split = 0, tidx = -1;
   TileCoord tc;
-  if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, (a.d + BNF - 1) / BNF, tc, S, &split)) return;
+  if (a.tail_slots > 0) {
+    // (only with one k split and fp32 partials out)
+    if (!map_tile_tail(blockIdx.x, a.gcounts, a.G, BMT, NT, a.tail_slots, a.tail_smax, a.f / KB,
+                       a.tail_max_pieces, tc, split, S, tidx))
+      return;
+  } else if (!map_tile(blockIdx.x, a.gcounts, a.G, BMT, NT, tc, S, &split)) {
+    return;
+  }
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -764,7 +839,20 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
     }
   }
   if (!active) return;
-  const bool direct = a.kg == 1 && S == 1;
+  if (tidx >= 0 && split > 0) {
+    // a later piece of a last-round tile: the accumulators as they are
+    // (register order), summed into the first piece's partials by
+    // tailfix_kernel
+    float* dst = a.tailpart + ((long)(tidx * (S - 1) + split - 1) * 4 + wave) * (RT * CB * 16 * 64) + lane;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[((t * CB + c) * 16 + v) * 64] = acc[t][c][v];
+    return;
+  }
+  const bool direct = a.kg == 1 && a.ksplit == 1 && a.tail_slots == 0;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int m = t * 32 + (lane & 31);
@@ -784,6 +872,64 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
         }
       }
   }
+}
+
+// Last-round split, second half: one workgroup per (tail tile, 32-row
+// block) adds the later pieces, summed in piece order, to the partials the
+// first piece wrote (same tile walk and lane mapping as the gemm2
+// epilogue).  A lane's 32 values of one piece are loaded together.
+template <int RT>
+__global__ __launch_bounds__(256) void tailfix_kernel(GemmArgs a) {
+  constexpr int BMT = 32 * RT;
+  constexpr int PER = RT * CB * 16 * 64;  // floats of one wavefront's partial tile
+  const int NT = (a.d + BNF - 1) / BNF;
+  const GroupCounts gc(a.gcounts, a.G);
+  const TailPlan tp = tail_plan(gc.tiles(a.G, BMT, NT), a.tail_slots, a.tail_smax, a.f / KB, a.tail_max_pieces);
+  const int tidx = blockIdx.x / RT, t = blockIdx.x - tidx * RT;
+  if (tidx >= tp.tail) return;
+  TileCoord tc;
+  if (!gc.locate(tp.F + tidx, a.G, BMT, NT, tc)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nbw = (tc.nt * BNF + wave * 64) / 32;
+  const int m = t * 32 + (lane & 31);
+  if (nbw * 32 >= a.d || tc.m0 + m >= tc.M) return;
+  const int S = tp.S;
+  const float* src = a.tailpart + ((long)tidx * (S - 1) * 4 + wave) * PER + t * CB * 16 * 64 + lane;
+  float sum[CB][16];
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum[c][v] = 0.f;
+  for (int p = 0; p < S - 1; ++p) {
+    const float* e = src + (long)p * 4 * PER;
+    float x[CB][16];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[c][v] = e[(c * 16 + v) * 64];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sum[c][v] += x[c][v];
+  }
+  const long aid = a.garow[a.goffsets[tc.g] + tc.m0 + m];
+  const int n = nbw * 32 + 4 * (lane >> 5);
+  f4v y[CB][4];
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[c][q] = *reinterpret_cast<const f4v*>(a.ypart + aid * a.d + n + c * 32 + 8 * q);
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f4v o = y[c][q];
+      o[0] += sum[c][4 * q];
+      o[1] += sum[c][4 * q + 1];
+      o[2] += sum[c][4 * q + 2];
+      o[3] += sum[c][4 * q + 3];
+      *reinterpret_cast<f4v*>(a.ypart + aid * a.d + n + c * 32 + 8 * q) = o;
+    }
 }
 
 // ------------------------------------ G2, k split inside the workgroup --
@@ -1303,6 +1449,19 @@ hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st) {
     case DT_F32: hipLaunchKernelGGL(combine_kernel<DT_F32>, dim3(blocks), dim3(256), 0, st, a); break;
     case DT_F16: hipLaunchKernelGGL(combine_kernel<DT_F16>, dim3(blocks), dim3(256), 0, st, a); break;
     case DT_BF16: hipLaunchKernelGGL(combine_kernel<DT_BF16>, dim3(blocks), dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tailfix(int bm, const GemmArgs& a, hipStream_t st) {
+  if (a.tail_slots <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.tail_slots / 2 * (bm / 32)));  // a tail is at most half a round
+  switch (bm) {
+    case 32: hipLaunchKernelGGL(tailfix_kernel<1>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(tailfix_kernel<2>, grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(tailfix_kernel<4>, grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL(tailfix_kernel<8>, grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
