@@ -515,12 +515,12 @@ void pick_g2(const moe_handle* h, int rows, int ntiles, int& bm, int& splits) {
       // share its MFMA pipe, so residency hides latency (in eff) but does
       // not add throughput
       double t = (double)((tiles + 255) / 256) * wg;
-      // one split with fp32 partials out: a last round at most half full is
-      // cut along k over the whole chip (see the launch), so the rounds
-      // count as a fraction, plus a tenth of a round for the pieces
+      // one split: a last round at most half full is cut along k over the
+      // whole chip (see the launch), so the rounds count as a fraction,
+      // plus a tenth of a round for the pieces
       const long slots = b == 128 ? 512 : 256;
-      const bool tail = s == 1 && c.top_groups > 1 && h->mma != MOE_F32 && b >= 128 && h->tail_env != 0 &&
-                        tiles > slots && 2 * (tiles % slots) <= slots;
+      const bool tail = s == 1 && h->mma != MOE_F32 && b >= 128 && h->tail_env != 0 && tiles > slots &&
+                        2 * (tiles % slots) <= slots;
       if (tail) t = ((double)tiles / 256 + 0.1) * wg;
       if (s > 1 || c.top_groups > 1) t += ((double)s * rows * c.d * 4 + (double)rows / c.top_groups * c.d * 2) / 5e12;
       if (t < best) {
@@ -1056,23 +1056,23 @@ int fwd_gemms(moe_handle* h, Workspace& ws, const void* X, int T, void* Y, hipSt
       int bm = 128;
       pick_g2(h, rows, nt, bm, splits);
       g2.ksplit = splits;
-      // Last-round split: with one k split and fp32 partials out (more than
-      // one chosen group), a last round of tiles that would leave most
-      // compute units idle is cut along k (the pieces land in the unused
-      // split slices of ypart and a small kernel adds them).  Round size:
-      // 256 compute units x two resident 128-row tiles of 16-bit types (one
-      // 256-row tile); shorter tiles are left alone.
+      // Last-round split: with one k split, a last round of tiles that
+      // would leave most compute units idle is cut along k (the first piece
+      // writes fp32 partials, the others land in the unused split slices of
+      // ypart, and a small kernel adds them into the partials or Y).  Round
+      // size: 256 compute units x two resident 128-row tiles of 16-bit types
+      // (one 256-row tile); shorter tiles are left alone.
       int slots = (h->mma != MOE_F32 && bm >= 128) ? (bm == 128 ? 512 : 256) : 0;
       if (h->tail_env >= 0) slots = h->tail_env;
       const long room = ((long)kMaxSplits * ws.T_cap * kg - rows) * c.d;  // floats after slice 0
-      if (splits == 1 && kg > 1 && slots > 0 && room >= (long)bm * 256) {
+      if (splits == 1 && slots > 0 && room >= (long)bm * 256) {
         g2.tail_slots = slots;
         g2.tail_smax = 8;
         g2.tail_max_pieces = (int)std::min<long>(room / ((long)bm * 256), 1L << 20);
         g2.tailpart = ws.ypart + (long)rows * c.d;
         // whole tiles plus at most one round of pieces
         e = launch_gemm(GK_G2, c.x_dtype, h->mma, bm, g2, max_mtiles(T, kg, c.G, bm) * nt + slots, 1, 1, st);
-        if (e == hipSuccess) e = launch_tailfix(bm, g2, st);
+        if (e == hipSuccess) e = launch_tailfix(c.x_dtype, bm, g2, st);
       } else {
         e = launch_gemm(GK_G2, c.x_dtype, h->mma, bm, g2, max_mtiles(T, kg, c.G, bm), nt, splits, st);
       }

@@ -119,7 +119,7 @@ __device__ bool map_tile(int i, const int* gcounts, int G, int BM, int NT, TileC
 // tiles that keeps most compute units idle.  When at least one round is
 // full and the last one is at most half full, the tiles of that last round
 // (the final ones in logical order) are cut along k into S pieces each, so
-// that their pieces fill the round; every piece keeps at least 8 stages and
+// that their pieces fill the round; every piece keeps at least 4 stages and
 // the pieces past the first fit in max_pieces partial tiles.
 struct TailPlan {
   int F;     // tiles run whole (logical tiles 0 .. F-1)
@@ -132,7 +132,7 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int slots, int smax, in
   if (slots <= 0 || total <= slots) return p;
   const int tail = total % slots;
   if (tail == 0 || 2 * tail > slots) return p;
-  int S = min(min(smax, slots / tail), KT / 8);
+  int S = min(min(smax, slots / tail), KT / 4);
   while (S > 1 && tail * (S - 1) > max_pieces) --S;
   if (S < 2) return p;
   p.F = total - tail;
@@ -793,7 +793,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
   int split = 0, tidx = -1;
   TileCoord tc;
   if (a.tail_slots > 0) {
-    // (only with one k split and fp32 partials out)
+    // (only with one k split)
     if (!map_tile_tail(blockIdx.x, a.gcounts, a.G, BMT, NT, a.tail_slots, a.tail_smax, a.f / KB,
                        a.tail_max_pieces, tc, split, S, tidx))
       return;
@@ -852,7 +852,8 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
         for (int v = 0; v < 16; ++v) dst[((t * CB + c) * 16 + v) * 64] = acc[t][c][v];
     return;
   }
-  const bool direct = a.kg == 1 && a.ksplit == 1 && a.tail_slots == 0;
+  // (a last-round tile's first piece leaves fp32 partials for tailfix)
+  const bool direct = a.kg == 1 && a.ksplit == 1 && tidx < 0;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int m = t * 32 + (lane & 31);
@@ -877,8 +878,9 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && RT == 4) ? 2 : 1) void gemm2_
 // Last-round split, second half: one workgroup per (tail tile, 32-row
 // block) adds the later pieces, summed in piece order, to the partials the
 // first piece wrote (same tile walk and lane mapping as the gemm2
-// epilogue).  A lane's 32 values of one piece are loaded together.
-template <int RT>
+// epilogue), into those partials or, with one chosen group, into Y.  A
+// lane's 32 values of one piece are loaded together.
+template <int XT, int RT>
 __global__ __launch_bounds__(256) void tailfix_kernel(GemmArgs a) {
   constexpr int BMT = 32 * RT;
   constexpr int PER = RT * CB * 16 * 64;  // floats of one wavefront's partial tile
@@ -928,7 +930,10 @@ __global__ __launch_bounds__(256) void tailfix_kernel(GemmArgs a) {
       o[1] += sum[c][4 * q + 1];
       o[2] += sum[c][4 * q + 2];
       o[3] += sum[c][4 * q + 3];
-      *reinterpret_cast<f4v*>(a.ypart + aid * a.d + n + c * 32 + 8 * q) = o;
+      if (a.kg == 1)
+        store4<XT>(static_cast<TE<XT>*>(a.Y) + aid * a.d + n + c * 32 + 8 * q, o[0], o[1], o[2], o[3]);
+      else
+        *reinterpret_cast<f4v*>(a.ypart + aid * a.d + n + c * 32 + 8 * q) = o;
     }
 }
 
@@ -1454,17 +1459,27 @@ hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_tailfix(int bm, const GemmArgs& a, hipStream_t st) {
-  if (a.tail_slots <= 0) return hipSuccess;
+template <int XT>
+hipError_t launch_tailfix_t(int bm, const GemmArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.tail_slots / 2 * (bm / 32)));  // a tail is at most half a round
   switch (bm) {
-    case 32: hipLaunchKernelGGL(tailfix_kernel<1>, grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(tailfix_kernel<2>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(tailfix_kernel<4>, grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL(tailfix_kernel<8>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((tailfix_kernel<XT, 1>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((tailfix_kernel<XT, 2>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((tailfix_kernel<XT, 4>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((tailfix_kernel<XT, 8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_tailfix(int x_dtype, int bm, const GemmArgs& a, hipStream_t st) {
+  if (a.tail_slots <= 0) return hipSuccess;
+  switch (x_dtype) {
+    case DT_F32: return launch_tailfix_t<DT_F32>(bm, a, st);
+    case DT_F16: return launch_tailfix_t<DT_F16>(bm, a, st);
+    case DT_BF16: return launch_tailfix_t<DT_BF16>(bm, a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_debug_decode(int mma_dtype, int resid, int kind, const void* src, const uint16_t* scales,

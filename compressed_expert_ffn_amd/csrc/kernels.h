@@ -122,7 +122,7 @@ struct GemmArgs {
   int zero_n;
   int rows_sorted;      // G1: group lists already ordered by expert set (tiles keep that order)
   const int* gslot;     // weights of group g sit at slot gslot[g] of the weight arrays (null: g)
-  // G2 last-round split (tail_slots > 0; one k split, fp32 partials out):
+  // G2 last-round split (tail_slots > 0; one k split):
   // resident workgroups per round, most pieces per tile, room in tailpart
   // for this many partial tiles of BM x 256 floats
   int tail_slots, tail_smax, tail_max_pieces;
@@ -207,7 +207,7 @@ __host__ __device__ inline G1Lds g1_lds(bool ks, int mma_dtype, int bm, int K, i
 hipError_t launch_vreduce(int mma_dtype, const VReduceArgs& a, hipStream_t st);
 hipError_t launch_combine(int x_dtype, const CombineArgs& a, hipStream_t st);
 // after a G2 launch with tail_slots > 0 (same arguments and tile height)
-hipError_t launch_tailfix(int bm, const GemmArgs& a, hipStream_t st);
+hipError_t launch_tailfix(int x_dtype, int bm, const GemmArgs& a, hipStream_t st);
 
 // Device-side decode of stored residual factors (test export).
 hipError_t launch_debug_decode(int mma_dtype, int resid, int kind, const void* src,

@@ -3,7 +3,8 @@
 When the down projection's tiles fill at least one round of resident
 workgroups and leave a last round at most half full, the tiles of that
 round are cut along k into pieces; the later pieces' partial tiles are added
-to the first piece's in a fixed order by a second kernel.  Here the round
+to the first piece's in a fixed order by a second kernel, which writes the
+fp32 partials (several chosen groups) or Y (one).  Here the round
 size is set small (CEFN_TAIL_SLOTS) so that layers of test size take that
 path, with the split count the plan picks checked on the host first.
 
@@ -32,7 +33,7 @@ def plan(total: int, slots: int, smax: int, KT: int):
     tail = total % slots
     if tail == 0 or 2 * tail > slots:
         return total, 0, 1
-    S = min(smax, slots // tail, KT // 8)
+    S = min(smax, slots // tail, KT // 4)
     if S < 2:
         return total, 0, 1
     return total - tail, tail, S
@@ -58,7 +59,10 @@ def _workload(case):
     return WORKLOADS[kind].with_T(T), bm
 
 
-CASES = [(2, 300, 128), (2, 520, 256), (4, 64, 32), ("combo", 257, 64)]
+# two chosen groups (fp32 partials and the combine after the fixup) and one
+# chosen group (the fixup writes Y), 16-bit and INT4 residual tails included
+CASES = [(2, 300, 128), (2, 520, 256), (4, 64, 32), ("combo", 257, 64), (1, 700, 128), (3, 1000, 128),
+         (3, 600, 64)]
 
 
 @pytest.mark.timeout(900)
