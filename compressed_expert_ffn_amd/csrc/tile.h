@@ -105,8 +105,13 @@ __device__ __forceinline__ void st_frag(FragT<TY>* p, const FragT<TY>& f) { *p =
 // per 64 bytes; the fragment-order mapping touched 64 tags per
 // instruction, and the vector L1 tag rate then bounded the main loop).
 // The LDS image is fragment-major with a swizzle: fragment (block, k-step s)
-// holds logical lane L in slot L ^ s, which keeps the four pieces a lane
-// quad writes in different banks; a reader of k-step s takes slot lane ^ s.
+// holds logical lane L (token row r = L % 32, k half h = L / 32) in slot
+// L ^ (s + 4h + 8 (r & 1)).  A store instruction's 16 lanes cover two rows
+// x both k halves x the four k-steps: the s term spreads a lane quad's
+// four pieces, the h term the other half of the row (32 slots on, the same
+// banks without it), the r term the next row, so the 16 pieces land in 16
+// different groups of 4 banks; each 16 lanes of a read take 16 consecutive
+// slots, permuted.  A reader of k-step s takes slot lane ^ (s + 4h + 8 (r & 1)).
 template <int SRC, int TY, int RT>
 struct TDirect {
   using Raw = RawT<SRC>;
@@ -152,7 +157,7 @@ struct TShared {
       const long src = row_of(blk, r);
       ok[q] = src >= 0;
       rowp[q] = base + (ok[q] ? src : 0) * ld + 32 * hh + 8 * sq;
-      lofs[q] = (blk * 4 + sq) * 64 + ((32 * hh + r) ^ sq);
+      lofs[q] = (blk * 4 + sq) * 64 + ((32 * hh + r) ^ (sq + 4 * hh + 8 * (r & 1)));
     }
   }
   __device__ void fetch(int kt, Raw (&r)[SEG]) const {
@@ -172,7 +177,7 @@ struct TShared {
     for (int q = 0; q < SEG; ++q) st_frag<TY>(buf + lofs[q], ok[q] ? cvt_frag<SRC, TY>(r[q]) : zero_frag<TY>());
   }
   // slot of logical lane `lane` in fragment (block, k-step s)
-  __device__ static int slot(int lane, int s) { return lane ^ s; }
+  __device__ static int slot(int lane, int s) { return lane ^ (s + 4 * (lane >> 5) + 8 * (lane & 1)); }
   static constexpr int frags_per_stage = NB * 4 * 64;
 };
 
