@@ -959,7 +959,7 @@ int fwd_gemms(moe_handle* h, Workspace& ws, const void* X, int T, void* Y, hipSt
   ga.ksplit = 1;
   ga.rows_total = (long)rows;
   int splits = 1;
-  bool g1k = false;  // gemm1 ran with the k-split tiles
+  bool g1k = false, g1k2 = false;  // gemm1 ran with the k-split tiles (d in four, in two)
   hipError_t e;
   const void* xg = fs.xg;
   const int xt = fs.xt;
@@ -999,16 +999,22 @@ int fwd_gemms(moe_handle* h, Workspace& ws, const void* X, int T, void* Y, hipSt
     g1.ad_scale = h->Ad_s;
     const int nt = (h->P_in * c.f + 255) / 256;
     const int bm = pick_bm(h, GK_G1, rows, nt, 1);
-    // very few tiles: 32-row x 64-column tiles with d split over the
-    // wavefronts, when the 256-column tiling at 32 rows has under half a
-    // round of workgroups (measured: tiny layers gain, the decode layer's
-    // 132 tiles do not)
+    // few tiles: 32-row tiles with d split over the wavefronts.  Under half
+    // a round of 256-column tiles at 32 rows: 64-column tiles, d in four
+    // (tiny layers gain: fp32 layer 29 -> 18 us).  128-column tiles with d
+    // in two (CEFN_G1K=2) are never picked: on the decode layer (about
+    // 132 tiles of 256 columns) they measured 93 us against 75 us, the
+    // four-part tiles 80 us.
     const bool k_ok = c.r == 0 || ws.nt1k > 0;
-    g1k = k_ok && (h->g1k_env == 1 || (h->g1k_env != 0 && h->bm_env[GK_G1] == 0 && bm == 32 &&
-                                        (long)max_mtiles(T, kg, c.G, 32) * nt < 128));
+    const bool auto_k = h->g1k_env < 0 && h->bm_env[GK_G1] == 0 && bm == 32;
+    g1k = k_ok && (h->g1k_env == 1 || (auto_k && (long)max_mtiles(T, kg, c.G, 32) * nt < 128));
+    g1k2 = !g1k && k_ok && h->g1k_env == 2;
     pf.begin(3);
     if (g1k)
       e = launch_gemm(GK_G1K, xt, h->mma, 32, g1, max_mtiles(T, kg, c.G, 32), h->P_in * c.f / 64, 1, st);
+    else if (g1k2)
+      e = launch_gemm(GK_G1K2, xt, h->mma, 32, g1, max_mtiles(T, kg, c.G, 32), (h->P_in * c.f + 127) / 128, 1,
+                      st);
     else
       e = launch_gemm(GK_G1, xt, h->mma, bm, g1, max_mtiles(T, kg, c.G, bm), nt, 1, st);
     if (e != hipSuccess) return hip_fail(h, e, "gemm1 launch");
@@ -1023,7 +1029,7 @@ int fwd_gemms(moe_handle* h, Workspace& ws, const void* X, int T, void* Y, hipSt
     va.idx = live.idx;
     va.vp_rows = ws.T_cap * kg;
     va.rows = rows;
-    va.ntiles = g1k ? ws.nt1k : h->nt1;
+    va.ntiles = g1k ? ws.nt1k : g1k2 ? (h->P_in * c.f + 127) / 128 : h->nt1;
     va.NV = h->NV;
     va.K = c.K;
     va.kg = kg;

@@ -63,7 +63,7 @@ struct moe_handle {
   // CEFN_KS_G2 (k splits of the down projection) at create, for tuning
   int bm_env[3] = {0, 0, 0}, ks_env = 0;
   int g2k_env = -1;  // CEFN_G2K: 1 / 0 forces the in-workgroup k split of G2 on / off
-  int g1k_env = -1;  // CEFN_G1K: 1 / 0 forces the k-split tiles of G1 on / off
+  int g1k_env = -1;  // CEFN_G1K: 1 / 2 forces the k-split tiles of G1 (d in four / in two), 0 off
   int ut_env = -1;   // CEFN_UT: 1 / 0 forces the tile-engine U GEMM on / off
   int gsort_env = -1;  // CEFN_GSORT: 1 / 0 forces the per-group row sort on / off
   int tail_env = -1;   // CEFN_TAIL_SLOTS: 0 turns G2's last-round split off, N > 0 sets its round size

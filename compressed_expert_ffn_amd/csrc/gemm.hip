@@ -349,18 +349,23 @@ struct EOps {
   int slot;           // position of j in the token's chosen list (-1: not chosen)
 };
 
-// KS (with RT = 1): for few rows per group, a workgroup owns 32 rows x one
-// wavefront's 64 columns and its 4 wavefronts walk consecutive quarters of d
-// for that tile (rows and weights straight into registers); the partial
-// tiles meet in LDS and every wavefront takes their sum, then the expert
-// steps of the block are dealt round-robin to the wavefronts and their h
-// sums meet in LDS before the store.  Four times the workgroups of the
-// 256-column tiling, each with a quarter of the dependent chain.
-template <int XT, int TY, int RT, int ACT, int RES, bool KS = false>
-__global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT_SWIGLU))) ? 2 : 1) void gemm1_kernel(GemmArgs a) {
+// KSN = 4 or 2 (with RT = 1): for few rows per group, a workgroup owns 32
+// rows x 64 * (4 / KSN) columns; its wavefronts are KSN consecutive parts
+// of d times 4 / KSN column blocks of 64 (wavefront w: part w / (4 / KSN),
+// block w % (4 / KSN)), rows and weights straight into registers.  The
+// partial tiles of a column block meet in LDS and each of its wavefronts
+// takes their sum, then the block's expert steps are dealt round-robin to
+// those KSN wavefronts and their h sums meet in LDS before the store.
+// KSN times the workgroups of the 256-column tiling over 4 / KSN, each
+// wavefront with 1 / KSN of the dependent chain.
+template <int XT, int TY, int RT, int ACT, int RES, int KSN = 0>
+__global__ __launch_bounds__(256, (TY != DT_F32 && (KSN > 0 || (RT == 4 && ACT == ACT_SWIGLU))) ? 2 : 1) void gemm1_kernel(GemmArgs a) {
+  constexpr bool KS = KSN > 0;
+  constexpr int NCS = KS ? 4 / KSN : 1;  // column blocks of 64 per k-split tile
   static_assert(!KS || RT == 1, "the k-split tile is 32 rows");
+  static_assert(KSN == 0 || KSN == 2 || KSN == 4, "d in 2 or 4 parts");
   constexpr int BMT = 32 * RT;
-  constexpr int BNFT = KS ? CB * 32 : BNF;  // columns of a tile
+  constexpr int BNFT = KS ? NCS * CB * 32 : BNF;  // columns of a tile
   constexpr int PIN = (ACT == ACT_SWIGLU) ? 2 : 1;
   constexpr int NFB = (ACT == ACT_SWIGLU) ? 1 : 2;  // f-blocks per wavefront
   using F = FragT<TY>;
@@ -371,7 +376,8 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   const int g = tc.g, m0 = tc.m0, M = tc.M;
   const int wg = a.gslot ? a.gslot[g] : g;  // where the group's weights sit
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nbw = KS ? tc.nt * CB : (tc.nt * BNF + wave * 64) / 32;
+  const int ksid = wave / NCS, csid = wave % NCS;  // (KS) part of d, column block
+  const int nbw = KS ? (tc.nt * NCS + csid) * CB : (tc.nt * BNF + wave * 64) / 32;
   const bool active = nbw * 32 < N;
   const int nb0 = active ? nbw : N / 32 - CB;
   // first f-block of this wavefront: SwiGLU interleaves gate and up blocks
@@ -480,7 +486,7 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   zero_acc<RT, CB>(acc);
   if constexpr (KS) {
     const int KT = a.d / KB;
-    const int k0 = wave * KT / 4, k1 = (wave + 1) * KT / 4;
+    const int k0 = ksid * KT / KSN, k1 = (ksid + 1) * KT / KSN;
     using TD = TDirect<XT, TY, 1>;
     TD td;
     td.init(static_cast<const TE<XT>*>(a.X) + (long)k0 * KB, a.d, lane, [&](int) -> long {
@@ -494,7 +500,8 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     wo.nb0 = nb0;
     Mainloop<TY, 1, CB, TD, WO, 2> ml{td, wo, lane};
     if (k1 > k0) ml.template run<typename TD::Raw[1][4], typename WO::Raw[CB][4]>(k1 - k0, acc);
-    // the four partial tiles meet in LDS; every wavefront takes the sum
+    // the partial tiles of a column block meet in LDS; each of its
+    // wavefronts takes the sum
     float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int c = 0; c < CB; ++c)
@@ -505,8 +512,10 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
     for (int c = 0; c < CB; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float* q = red + (c * 16 + v) * 64 + lane;
-        acc[0][c][v] = (q[0] + q[CB * 16 * 64]) + (q[2 * CB * 16 * 64] + q[3 * CB * 16 * 64]);
+        const float* q = red + ((csid * CB + c) * 16 + v) * 64 + lane;
+        constexpr int W = NCS * CB * 16 * 64;  // to the same block's next part
+        if constexpr (KSN == 4) acc[0][c][v] = (q[0] + q[W]) + (q[2 * W] + q[3 * W]);
+        else acc[0][c][v] = q[0] + q[W];
       }
     __syncthreads();
   } else {
@@ -552,13 +561,13 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
   }
   auto first_j = [](uint32_t lo, uint32_t hi) { return lo ? __builtin_ctz(lo) : 32 + __builtin_ctz(hi); };
   if constexpr (KS) {
-    // expert steps of the block dealt round-robin: the r-th set bit to
-    // wavefront r % 4
+    // expert steps of the block dealt round-robin over the wavefronts of a
+    // column block: the r-th set bit to the one of part r % KSN
     uint32_t lo = mlo[0], hi = mhi[0], flo = 0u, fhi = 0u;
     for (int r = 0; lo | hi; ++r) {
       const int j = first_j(lo, hi);
       if (lo) lo &= lo - 1; else hi &= hi - 1;
-      if ((r & 3) == wave) {
+      if ((r % KSN) == ksid) {
         if (j < 32) flo |= 1u << j; else fhi |= 1u << (j - 32);
       }
     }
@@ -719,23 +728,25 @@ __global__ __launch_bounds__(256, (TY != DT_F32 && (KS || (RT == 4 && ACT == ACT
       }
     }
     if constexpr (KS) {
-      // h sums of the four wavefronts' expert steps meet in LDS
+      // h sums of a column block's wavefronts meet in LDS
 #pragma unroll
       for (int c = 0; c < NFB; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s_h[((wave * NFB + c) * 16 + v) * 64 + lane] = hbar[c][v];
       __syncthreads();
-      if (wave == 0) {
+      if (ksid == 0) {
 #pragma unroll
         for (int c = 0; c < NFB; ++c)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float* q = s_h + (c * 16 + v) * 64 + lane;
-            hbar[c][v] = (q[0] + q[NFB * 16 * 64]) + (q[2 * NFB * 16 * 64] + q[3 * NFB * 16 * 64]);
+            const float* q = s_h + ((csid * NFB + c) * 16 + v) * 64 + lane;
+            constexpr int W = NCS * NFB * 16 * 64;
+            if constexpr (KSN == 4) hbar[c][v] = (q[0] + q[W]) + (q[2 * W] + q[3 * W]);
+            else hbar[c][v] = q[0] + q[W];
           }
       }
     }
-    if (active && m0 + m < M && (!KS || wave == 0)) {  // (idle wavefronts computed nothing above)
+    if (active && m0 + m < M && (!KS || ksid == 0)) {  // (idle wavefronts computed nothing above)
       TE<TY>* hrow = H + (long)(row0 + s_perm[m]) * a.f + 4 * h;
 #pragma unroll
       for (int c = 0; c < NFB; ++c)
@@ -1249,24 +1260,24 @@ hipError_t go(KF kfn, dim3 grid, size_t lds, const GemmArgs& a, hipStream_t st) 
 // Residual storage kinds valid for a (activation type, MFMA type) pair:
 // plain residuals are stored in the MFMA type (F32 with an F32 base, F16 with
 // an F16 base), INT4 needs a 16-bit base.
-template <int XT, int TY, int RT, int ACT, bool KS>
+template <int XT, int TY, int RT, int ACT, int KSN>
 hipError_t launch_g1_act(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (a.resid == RS_NONE) return go(gemm1_kernel<XT, TY, RT, ACT, ER_NONE, KS>, grid, lds, a, st);
+  if (a.resid == RS_NONE) return go(gemm1_kernel<XT, TY, RT, ACT, ER_NONE, KSN>, grid, lds, a, st);
   if constexpr (TY == DT_F32) {
-    if (a.resid == RS_F32) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN, KS>, grid, lds, a, st);
+    if (a.resid == RS_F32) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN, KSN>, grid, lds, a, st);
   } else {
-    if (a.resid == RS_INT4) return go(gemm1_kernel<XT, TY, RT, ACT, ER_INT4, KS>, grid, lds, a, st);
+    if (a.resid == RS_INT4) return go(gemm1_kernel<XT, TY, RT, ACT, ER_INT4, KSN>, grid, lds, a, st);
     if constexpr (TY == DT_F16) {
-      if (a.resid == RS_F16) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN, KS>, grid, lds, a, st);
+      if (a.resid == RS_F16) return go(gemm1_kernel<XT, TY, RT, ACT, ER_PLAIN, KSN>, grid, lds, a, st);
     }
   }
   return hipErrorInvalidValue;
 }
 
-template <int XT, int TY, int RT, bool KS = false>
+template <int XT, int TY, int RT, int KSN = 0>
 hipError_t launch_g1(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (a.act == ACT_SWIGLU) return launch_g1_act<XT, TY, RT, ACT_SWIGLU, KS>(a, grid, lds, st);
-  if constexpr (RT <= 4) return launch_g1_act<XT, TY, RT, ACT_GELU, KS>(a, grid, lds, st);
+  if (a.act == ACT_SWIGLU) return launch_g1_act<XT, TY, RT, ACT_SWIGLU, KSN>(a, grid, lds, st);
+  if constexpr (RT <= 4) return launch_g1_act<XT, TY, RT, ACT_GELU, KSN>(a, grid, lds, st);
   return hipErrorInvalidValue;
 }
 
@@ -1293,7 +1304,10 @@ hipError_t launch_rt(int kind, const GemmArgs& a, dim3 grid, hipStream_t st) {
     case GK_G1:
       return launch_g1<XT, TY, RT>(a, grid, lds, st);
     case GK_G1K:
-      if constexpr (RT == 1) return launch_g1<XT, TY, 1, true>(a, grid, lds, st);
+      if constexpr (RT == 1) return launch_g1<XT, TY, 1, 4>(a, grid, lds, st);
+      return hipErrorInvalidValue;
+    case GK_G1K2:
+      if constexpr (RT == 1) return launch_g1<XT, TY, 1, 2>(a, grid, lds, st);
       return hipErrorInvalidValue;
     case GK_G2:
       if (int4) return go(gemm2_kernel<XT, TY, RT, true>, grid, lds, a, st);
@@ -1326,8 +1340,8 @@ hipError_t launch_types(int kind, int bm, const GemmArgs& a, dim3 grid, hipStrea
 size_t gemm_lds(int kind, int ty, int bm, int K, int ke) {
   const size_t fb = ty == DT_F32 ? 32 : 16;
   const size_t tbytes = 2 * (size_t)(bm / 32) * 4 * 64 * fb;
-  if (kind != GK_G1 && kind != GK_G1K) return tbytes;
-  return g1_lds(kind == GK_G1K, ty, bm, K, ke).total;
+  if (kind != GK_G1 && kind != GK_G1K && kind != GK_G1K2) return tbytes;
+  return g1_lds(kind != GK_G1, ty, bm, K, ke).total;
 }
 
 template <class KF>

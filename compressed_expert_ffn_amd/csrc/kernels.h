@@ -147,9 +147,11 @@ struct CombineArgs {
 
 // G2K: G2 with the k split inside a workgroup.  G1K: G1 with 32-row x
 // 64-column tiles and d split over the four wavefronts (few rows per group;
-// bm = 32, ntiles counted for 64 columns).  UT: U on the tile engine
-// (BM-row x 256-column tiles; many rows).
-enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2, GK_G2K = 3, GK_G1K = 4, GK_UT = 5 };
+// bm = 32, ntiles counted for 64 columns); G1K2: 32-row x 128-column tiles,
+// d in two halves, each over two wavefronts of 64 columns (ntiles counted
+// for 128 columns).  UT: U on the tile engine (BM-row x 256-column tiles;
+// many rows).
+enum GemmKind { GK_U = 0, GK_G1 = 1, GK_G2 = 2, GK_G2K = 3, GK_G1K = 4, GK_UT = 5, GK_G1K2 = 6 };
 
 // most k splits of the router score GEMM (the selection sums that many
 // partial score sets)

@@ -332,6 +332,7 @@ TILE_VARIANTS = [
     {"CEFN_BM_G1": "128", "CEFN_BM_G2": "32", "CEFN_KS_G2": "4", "CEFN_G2K": "0", "CEFN_UT": "0", "CEFN_GSORT": "0"},
     {"CEFN_BM_G1": "32", "CEFN_BM_G2": "128", "CEFN_KS_G2": "2", "CEFN_G2K": "1", "CEFN_G1K": "1"},
     {"CEFN_BM_G1": "64", "CEFN_BM_G2": "64", "CEFN_KS_G2": "3", "CEFN_G2K": "1", "CEFN_G1K": "0"},
+    {"CEFN_BM_G1": "32", "CEFN_BM_G2": "32", "CEFN_KS_G2": "1", "CEFN_G1K": "2", "CEFN_TAIL_SLOTS": "0"},
 ]
 
 
@@ -351,6 +352,27 @@ def test_tile_variants_match_oracle(wi, T, vi, monkeypatch):
         y = y_to_host(lay.forward(x_to_device(inputs["X"], w.x_dtype)))
         err = rel_err(y, O.forward(layer))
         say(f"[tiles {vi}] {w.name} T={T}: rel err {err:.3e}")
+        assert err <= TOL[w.x_dtype]
+    finally:
+        lay.close()
+
+
+@pytest.mark.parametrize("g1k", ["1", "2"])
+@pytest.mark.parametrize("act,resid", [("gelu_tanh", "int4_g32"), ("gelu_tanh", "f16"), ("swiglu", "int4_g32")])
+def test_k_split_tiles_ragged_columns(g1k, act, resid, monkeypatch):
+    """The k-split input-projection tiles (d in four parts over 64 columns,
+    or in two over 128) on a hidden width of 320: with GELU the last
+    128-column tile has one idle column block."""
+    from tests.test_gpu_combos import combo_workload
+    L = _lib()
+    monkeypatch.setenv("CEFN_G1K", g1k)
+    w = combo_workload(act, "f16", "f16", resid, 16, (4, 4), 2, 2, 150, d=256, f=320)
+    wT, inputs, layer = make_parity_layer(w)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        y = y_to_host(lay.forward(x_to_device(inputs["X"], w.x_dtype)))
+        err = rel_err(y, O.forward(layer))
+        say(f"[k-split tiles {g1k}] {w.name} f=320: rel err {err:.3e}")
         assert err <= TOL[w.x_dtype]
     finally:
         lay.close()
