@@ -56,3 +56,39 @@ def test_graph_replays_equal_the_eager_pass(wi, T):
         say(f"[graph] {w.name} T={T}: 4 replays equal the eager pass, rel err {err:.3e}")
     finally:
         lay.close()
+
+
+@pytest.mark.parametrize("wi,T", [(1, 512), (4, 64), (3, 300)], ids=["w1-T512", "w4-T64", "w3-T300"])
+def test_graph_replays_of_the_no_allocation_entry(wi, T):
+    """moe_forward_noalloc (the entry point for callers that cannot allocate,
+    such as code under graph capture) captured and replayed: every replay
+    equals moe_forward's eager result bit for bit."""
+    import torch
+    from compressed_expert_ffn_amd import _lib as L
+    w = WORKLOADS[wi].with_T(T)
+    wT, inputs, layer = make_parity_layer(w)
+    lay = L.Layer(L.config_from_workload(wT), inputs)
+    try:
+        X = x_to_device(inputs["X"], w.x_dtype)
+        eager = lay.forward(X)
+        torch.cuda.synchronize()
+        Y = torch.empty_like(eager)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            lay.forward_noalloc(X, Y)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lay.forward_noalloc(X, Y)
+        for rep in range(4):
+            Y.zero_()
+            lay.forward(X)  # an eager pass on the handle's own workspace between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Y.view(torch.int16), eager.view(torch.int16)), f"replay {rep} differs"
+        say(f"[graph noalloc] {w.name} T={T}: 4 replays equal moe_forward")
+    finally:
+        lay.close()
