@@ -169,8 +169,11 @@ int moe_route(moe_handle* h, const void* X, int32_t T, const moe_route_out* out,
  * expert FFN.  X, Y: device [T][d] in x_dtype (may not alias).  routing may
  * be NULL; otherwise its non-NULL fields receive the routing as in
  * moe_route (T = 0 included: zero counts and offsets).  Enqueue only: no
- * allocation, no host synchronisation.  One handle is not re-entrant: calls
- * on it must be ordered (one stream). */
+ * allocation, no host synchronisation, and the counters a pass needs are
+ * cleared by its own kernels (no memset), so a call may be captured into a
+ * HIP graph and replayed; replays give the same Y bit for bit.  One handle
+ * is not re-entrant: calls on it must be ordered (one stream); distinct
+ * handles are independent. */
 int moe_forward(moe_handle* h, const void* X, int32_t T, void* Y,
                 const moe_route_out* routing, void* stream);
 
